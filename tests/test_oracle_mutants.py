@@ -1,0 +1,132 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin (no GPU).
+
+This shows the pins are strong enough: a dropped term, a wrong sign, a
+wrong index or a transposed operand anywhere in the oracle is caught.
+Mutants are built here, on the CPU, from the oracle's own functions; the
+oracle itself is never modified.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from pins import PINS
+
+
+def _ns(mod, **over):
+    d = {k: getattr(mod, k) for k in dir(mod) if not k.startswith("_")}
+    d.update(over)
+    return types.SimpleNamespace(**d)
+
+
+ws, silu, sm, xe = oracle.weighted_sum, oracle.scaled_silu, oracle.softmax, oracle.softmax_xent
+
+
+def _ws_bwd_no_batch_reduction(dy, x, w, grad_w_old=None):
+    gx, _ = ws.bwd(dy, x, w, grad_w_old)
+    return gx, x[0] * dy[0]                       # correct at batch 1 only
+
+
+def _ws_bwd_transposed(dy, x, w, grad_w_old=None):
+    gx, gw = ws.bwd(dy, x, w, grad_w_old)
+    return gx, np.sum(x * dy[:, None], axis=1)[: w.size] if x.shape[0] >= w.size else gw * 0
+
+
+def _ws_bwd_overwrites(dy, x, w, grad_w_old=None):
+    return ws.bwd(dy, x, w, None)                  # ignores the existing gradient
+
+
+def _ws_partials_off_by_one(x, dy, rows_per_tile):
+    P = ws.partials(x, dy, rows_per_tile)
+    P[-1] = np.sum(x[(P.shape[0] - 1) * rows_per_tile + 1:] * dy[(P.shape[0] - 1) * rows_per_tile + 1:, None], axis=0)
+    return P
+
+
+def _silu_bwd_missing_term(dy, x, w, dw_old=None):
+    s = silu.sigmoid(x)
+    dx = dy * w * s                               # drops the x s (1 - s) term
+    return dx, silu.bwd(dy, x, w, dw_old)[1]
+
+
+def _silu_bwd_sign(dy, x, w, dw_old=None):
+    s = silu.sigmoid(x)
+    dx = dy * w * (s - x * s * (1 - s))
+    return dx, silu.bwd(dy, x, w, dw_old)[1]
+
+
+def _silu_dw_without_x(dy, x, w, dw_old=None):
+    dx, _ = silu.bwd(dy, x, w, None)
+    dw = float(np.sum(dy * silu.sigmoid(x)))
+    return dx, dw if dw_old is None else dw + dw_old
+
+
+def _silu_sigmoid_sign(x):
+    return 1.0 / (1.0 + np.exp(np.clip(x, -700, 700)))
+
+
+def _sm_bwd_sign(dy, y):
+    return y * (dy + np.sum(dy * y, axis=-1, keepdims=True))
+
+
+def _sm_bwd_wrong_axis(dy, y):
+    return y * (dy - np.sum(dy * y, axis=0, keepdims=True))
+
+
+def _sm_fwd_no_normalise(x):
+    return np.exp(x - np.max(x, axis=-1, keepdims=True))
+
+
+def _xent_no_onehot(z, t, grad_scale):
+    out = xe.fwd_bwd(z, t, grad_scale)
+    from scipy.special import softmax
+
+    out["dz"] = grad_scale * softmax(z, axis=1)
+    return out
+
+
+def _xent_sum_not_mean(z, t, grad_scale):
+    out = xe.fwd_bwd(z, t, grad_scale)
+    out["loss"] = float(np.sum(out["row_loss"]))
+    return out
+
+
+def _xent_lse_without_max(z, t, grad_scale):
+    out = xe.fwd_bwd(z, t, grad_scale)
+    with np.errstate(over="ignore"):
+        out["row_lse"] = np.log(np.sum(np.exp(z), axis=1)) - 0.0 * out["row_max"]
+    out["row_lse"] = out["row_lse"] + (out["row_max"] > 100) * 1.0
+    return out
+
+
+MUTANTS = [
+    ("weighted_sum", "bwd_no_batch_reduction", _ns(ws, bwd=_ws_bwd_no_batch_reduction)),
+    ("weighted_sum", "bwd_transposed_reduction", _ns(ws, bwd=_ws_bwd_transposed)),
+    ("weighted_sum", "bwd_overwrites_grad", _ns(ws, bwd=_ws_bwd_overwrites)),
+    ("weighted_sum", "fwd_sign", _ns(ws, fwd=lambda x, w: -ws.fwd(x, w))),
+    ("weighted_sum", "partials_off_by_one", _ns(ws, partials=_ws_partials_off_by_one)),
+    ("scaled_silu", "bwd_missing_term", _ns(silu, bwd=_silu_bwd_missing_term)),
+    ("scaled_silu", "bwd_sign", _ns(silu, bwd=_silu_bwd_sign)),
+    ("scaled_silu", "dw_without_x", _ns(silu, bwd=_silu_dw_without_x)),
+    ("scaled_silu", "sigmoid_sign", _ns(silu, sigmoid=_silu_sigmoid_sign)),
+    ("softmax", "bwd_sign", _ns(sm, bwd=_sm_bwd_sign)),
+    ("softmax", "bwd_wrong_axis", _ns(sm, bwd=_sm_bwd_wrong_axis)),
+    ("softmax", "fwd_not_normalised", _ns(sm, fwd=_sm_fwd_no_normalise)),
+    ("softmax_xent", "no_onehot", _ns(xe, fwd_bwd=_xent_no_onehot)),
+    ("softmax_xent", "sum_not_mean", _ns(xe, fwd_bwd=_xent_sum_not_mean)),
+    ("softmax_xent", "lse_wrong", _ns(xe, fwd_bwd=_xent_lse_without_max)),
+]
+
+
+@pytest.mark.parametrize("op,name,impl", MUTANTS, ids=[f"{m[0]}-{m[1]}" for m in MUTANTS])
+def test_mutant_is_caught(op, name, impl):
+    failed = []
+    for pin_name, fn, thr in PINS[op]:
+        try:
+            with np.errstate(all="ignore"):
+                err = fn(impl)
+        except Exception:  # a crash also counts as caught
+            err = np.inf
+        if not (np.isfinite(err) and err <= thr):
+            failed.append(pin_name)
+    assert failed, f"planted mistake {op}/{name} passed every pin"
