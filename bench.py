@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Throughput of the VJP hot path on one MI355X.
+
+One step is one forward and one backward of every op at its large workload,
+in autograd order (all forwards, then the backwards in reverse):
+
+  weighted_sum fwd   x bf16 [1048576, 256], w bf16 [256]
+  scaled_silu fwd    x fp16 [2^24], w fp32 = 0.75
+  softmax fwd        x bf16 [32768, 4096]
+  softmax_xent       logits bf16 [16384, 32000] (fused forward + backward)
+  softmax bwd        dy, y bf16 [32768, 4096]
+  scaled_silu bwd    dy, x fp16 [2^24]         (+ fixed-order dw reduction)
+  weighted_sum bwd   dy bf16 [1048576], x      (+ fixed-order grad_w reduction)
+
+Every input is synthetic, seeded and already resident in HBM when timing
+starts.  `value` is the step's algorithmic HBM bytes (what each kernel must
+read and write once; listed per op in `per_op`) divided by the measured step
+time.  Per-op durations come from HIP events recorded on the stream the
+kernels are launched on.  The `roofline` object is for the op with the
+largest share of the step; `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workloads on one host core.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd achieved HBM GB/s and % of MI355X peak; elements/s per op"
+PEAK_GBS = 8000.0          # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_softmax_xent_bf16_16384x32000.json")
+
+
+def source_digest() -> str:
+    """Hash of every kernel source, so stored counter readings expire when a kernel changes."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "row_wise_backward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- bytes
+# Algorithmic HBM bytes per call: every input read once, every output written once,
+# stage-1 partials written once and read once by stage 2.
+
+def bytes_weighted_sum_fwd(n, d, es=2, ws=2):
+    return n * d * es + d * ws + n * es
+
+
+def bytes_weighted_sum_bwd(n, d, T, es=2, ws=2):
+    return n * es + n * d * es + d * ws + n * d * es + 2 * T * d * 4 + d * 4
+
+
+def bytes_silu_fwd(n, es=2):
+    return 2 * n * es + 4
+
+
+def bytes_silu_bwd(n, T, es=2):
+    return 3 * n * es + 4 + 2 * T * 4 + 4
+
+
+def bytes_softmax_fwd(r, c, es=2):
+    return 2 * r * c * es
+
+
+def bytes_softmax_bwd(r, c, es=2):
+    return 3 * r * c * es
+
+
+def bytes_xent(r, c, es=2):
+    # logits read, dlogits written, targets read (main kernel and finalize),
+    # row_max / row_lse written, row losses written then read, loss + count written
+    return 2 * r * c * es + 2 * r * 4 + 2 * r * 4 + 2 * r * 4 + 8
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(scale: float = 1.0):
+    """The oracle (fp64 numpy, one thread) on a bounded sample of each workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    n_silu = int((1 << 23) * scale)
+    n_ws = int(131072 * scale)
+    r_sm = int(4096 * scale)
+    r_xe = int(1024 * scale)
+    # inputs first (not timed), then the oracle: decode to fp64, forward, backward
+    x = synth.normal((n_silu,), 2.0, "f16", 1001, 0)
+    g = synth.normal((n_silu,), 1.0, "f16", 1001, 2)
+    xw = synth.normal((n_ws, 256), 1.0, "bf16", 1002, 0)
+    ww = synth.normal((256,), 0.1, "bf16", 1002, 1)
+    gw = synth.normal((n_ws,), 1.0, "bf16", 1002, 2)
+    xs = synth.normal((r_sm, 4096), 3.0, "bf16", 1003, 0)
+    gs = synth.normal((r_sm, 4096), 1.0, "bf16", 1003, 2)
+    z = synth.normal((r_xe, 32000), 2.0, "bf16", 1004, 0)
+    t = synth.targets(r_xe, 32000, 1004)
+    total_bytes = (bytes_silu_fwd(n_silu) + bytes_silu_bwd(n_silu, 1)
+                   + bytes_weighted_sum_fwd(n_ws, 256) + bytes_weighted_sum_bwd(n_ws, 256, 1)
+                   + bytes_softmax_fwd(r_sm, 4096) + bytes_softmax_bwd(r_sm, 4096)
+                   + bytes_xent(r_xe, 32000))
+    t0 = time.perf_counter()
+    x64, g64 = synth.to_f64(x, "f16"), synth.to_f64(g, "f16")
+    oracle.scaled_silu.fwd(x64, 0.75)
+    oracle.scaled_silu.bwd(g64, x64, 0.75)
+    xw64, ww64, gw64 = synth.to_f64(xw, "bf16"), synth.to_f64(ww, "bf16"), synth.to_f64(gw, "bf16")
+    oracle.weighted_sum.fwd(xw64, ww64)
+    oracle.weighted_sum.bwd(gw64, xw64, ww64)
+    ys = oracle.softmax.fwd(synth.to_f64(xs, "bf16"))
+    oracle.softmax.bwd(synth.to_f64(gs, "bf16"), ys)
+    oracle.softmax_xent.fwd_bwd(synth.to_f64(z, "bf16"), t, 1.0 / 16384)
+    dt = time.perf_counter() - t0
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    return {
+        "value": round(total_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"fwd+bwd of scaled_silu n={n_silu}, weighted_sum {n_ws}x256, softmax "
+                   f"{r_sm}x4096, softmax_xent {r_xe}x32000 (same distributions and seeds), "
+                   f"fp64 numpy, input decode included; {dt:.1f} s"),
+    }
+
+
+# ----------------------------------------------------------------------------- GPU
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-scale", type=float, default=1.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy before timing (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the ops shard by rows with no exchange except one small grad_w all-reduce, "
+              "which is not built here)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import row_wise_backward_amd as rwb
+    import synth
+    from synth.workloads import SILU_16M, SOFTMAX, WS_LARGE, XENT
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = rwb.lib
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}; generating inputs", file=sys.stderr, flush=True)
+
+    # inputs (seeded, drawn on the device) and outputs
+    n_ws, d_ws = WS_LARGE.shape
+    wx = synth.normal_device((n_ws, d_ws), WS_LARGE.sigma_x, "bf16", WS_LARGE.seed, 0, dev)
+    ww = synth.normal_device((d_ws,), WS_LARGE.sigma_w, "bf16", WS_LARGE.seed, 1, dev)
+    wg = synth.normal_device((n_ws,), WS_LARGE.sigma_dy, "bf16", WS_LARGE.seed, 2, dev)
+    wy = torch.empty(n_ws, dtype=torch.bfloat16, device=dev)
+    wdx = torch.empty_like(wx)
+    wdw = torch.empty(d_ws, dtype=torch.float32, device=dev)
+    T_ws = rwb.vjp_weighted_sum_bwd_workspace_size(n_ws, d_ws) // (4 * d_ws)
+    wws = torch.empty(rwb.vjp_weighted_sum_bwd_workspace_size(n_ws, d_ws), dtype=torch.uint8, device=dev)
+
+    n_s = SILU_16M.shape[0]
+    sx = synth.normal_device((n_s,), SILU_16M.sigma_x, "f16", SILU_16M.seed, 0, dev)
+    sg = synth.normal_device((n_s,), SILU_16M.sigma_dy, "f16", SILU_16M.seed, 2, dev)
+    sw = torch.tensor([SILU_16M.w_value], dtype=torch.float32, device=dev)
+    sy, sdx = torch.empty_like(sx), torch.empty_like(sx)
+    sdw = torch.empty(1, dtype=torch.float32, device=dev)
+    T_s = rwb.vjp_scaled_silu_bwd_workspace_size(n_s) // 4
+    sws = torch.empty(rwb.vjp_scaled_silu_bwd_workspace_size(n_s), dtype=torch.uint8, device=dev)
+
+    r_m, c_m = SOFTMAX.shape
+    mx = synth.normal_device((r_m, c_m), SOFTMAX.sigma_x, "bf16", SOFTMAX.seed, 0, dev)
+    mg = synth.normal_device((r_m, c_m), SOFTMAX.sigma_dy, "bf16", SOFTMAX.seed, 2, dev)
+    my, mdx = torch.empty_like(mx), torch.empty_like(mx)
+
+    r_x, c_x = XENT.shape
+    z = synth.normal_device((r_x, c_x), XENT.sigma_x, "bf16", XENT.seed, 0, dev)
+    tg = synth.targets_device(r_x, c_x, XENT.seed, dev)
+    dz = torch.empty_like(z)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    rmax = torch.empty(r_x, dtype=torch.float32, device=dev)
+    rlse = torch.empty(r_x, dtype=torch.float32, device=dev)
+    ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    xws = torch.empty(rwb.vjp_softmax_xent_workspace_size(r_x), dtype=torch.uint8, device=dev)
+    scale = XENT.extra["grad_scale"]
+
+    # one checked pass through the binding (host-side shape guards) ...
+    rwb.vjp_weighted_sum_fwd(wx, ww, y=wy)
+    rwb.vjp_scaled_silu_fwd(sx, sw, y=sy)
+    rwb.vjp_softmax_fwd(mx, y=my)
+    rwb.vjp_softmax_xent_fwd_bwd(z, tg, grad_scale=scale, dlogits=dz, loss=loss, row_max=rmax,
+                                 row_lse=rlse, n_invalid=ninv, workspace=xws)
+    rwb.vjp_softmax_bwd(mg, my, dx=mdx)
+    rwb.vjp_scaled_silu_bwd(sg, sx, sw, dx=sdx, dw=sdw, workspace=sws)
+    rwb.vjp_weighted_sum_bwd(wg, wx, ww, dx=wdx, dw=wdw, workspace=wws)
+    torch.cuda.synchronize()
+
+    # ... then the same C calls with their arguments marshalled once
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    BF16, F16 = rwb.VJP_BF16, rwb.VJP_F16
+    ops = [
+        ("weighted_sum_fwd", L.vjp_weighted_sum_fwd,
+         (P(wx), d_ws, P(ww), P(wy), n_ws, d_ws, BF16, BF16, stream),
+         bytes_weighted_sum_fwd(n_ws, d_ws), n_ws * d_ws),
+        ("scaled_silu_fwd", L.vjp_scaled_silu_fwd, (P(sx), P(sw), P(sy), n_s, F16, stream),
+         bytes_silu_fwd(n_s), n_s),
+        ("softmax_fwd", L.vjp_softmax_fwd, (P(mx), c_m, P(my), c_m, r_m, c_m, BF16, stream),
+         bytes_softmax_fwd(r_m, c_m), r_m * c_m),
+        ("softmax_xent_fwd_bwd", L.vjp_softmax_xent_fwd_bwd,
+         (P(z), c_x, P(tg), r_x, c_x, BF16, ctypes.c_float(scale), P(loss), P(rmax), P(rlse), P(dz),
+          c_x, P(ninv), P(xws), xws.numel(), stream),
+         bytes_xent(r_x, c_x), r_x * c_x),
+        ("softmax_bwd", L.vjp_softmax_bwd, (P(mg), c_m, P(my), c_m, P(mdx), c_m, r_m, c_m, BF16, stream),
+         bytes_softmax_bwd(r_m, c_m), r_m * c_m),
+        ("scaled_silu_bwd", L.vjp_scaled_silu_bwd,
+         (P(sg), P(sx), P(sw), P(sdx), P(sdw), 0, n_s, F16, P(sws), sws.numel(), stream),
+         bytes_silu_bwd(n_s, T_s), n_s),
+        ("weighted_sum_bwd", L.vjp_weighted_sum_bwd,
+         (P(wg), P(wx), d_ws, P(ww), P(wdx), d_ws, P(wdw), 0, n_ws, d_ws, 0, BF16, BF16, P(wws),
+          wws.numel(), stream),
+         bytes_weighted_sum_bwd(n_ws, d_ws, T_ws), n_ws * d_ws),
+    ]
+    step_bytes = sum(o[3] for o in ops)
+
+    def step(evs=None):
+        for i, (name, fn, a, _, _) in enumerate(ops):
+            if evs is not None:
+                evs[i][0].record()
+            st = fn(*a)
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st} ({rwb.vjp_last_error()})")
+            if evs is not None:
+                evs[i][1].record()
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / args.steps * 1e3
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    per_op = []
+    for i, (name, _, _, nbytes, nelem) in enumerate(ops):
+        ms = sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)) / args.steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        per_op.append({"op": name, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
+                       "frac_of_peak": round(gbs / PEAK_GBS, 4),
+                       "elements_per_s": round(nelem / (ms * 1e-3), 1)})
+    dom = max(per_op, key=lambda o: o["ms"])
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("op") == dom["op"] and tr.get("source_digest") == source_digest():
+            traffic = tr.get("bytes_per_launch")
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal draws on the device; uniform int32 targets)",
+        "config": {
+            "workload": ("one fwd+bwd of each op: weighted_sum bf16 1048576x256, scaled_silu "
+                         "fp16 n=16777216, softmax bf16 32768x4096, softmax_xent bf16 16384x32000"),
+            "step_bytes": step_bytes,
+            "frac_of_peak": round(value / PEAK_GBS, 4),
+        },
+        "per_op": per_op,
+        "roofline": {
+            "kernel": dom["op"],
+            "bound": "hbm",
+            "achieved": dom["GB/s"],
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom["GB/s"] / PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_scale)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

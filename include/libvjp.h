@@ -1,0 +1,200 @@
+/*
+ * libvjp -- paired forward / backward (vector-Jacobian product) kernels for
+ * small fused ops on AMD Instinct MI355X (gfx950).
+ *
+ * A backward call reads the upstream gradient plus what its forward saved
+ * and returns one gradient per differentiable input, never forming the
+ * Jacobian ("Backprop for kernel writers", section 01 "The only idea";
+ * "Backward in Triton -- autograd.Function and the backward grid", section
+ * "The mental model: two kernels, one node").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory      Every pointer argument is a DEVICE pointer owned by the caller,
+ *             except where a comment says otherwise.  The library allocates
+ *             no device memory and keeps no state between calls; tensors
+ *             saved by a forward for its backward (x, w, y, row_lse, ...) are
+ *             the caller's buffers.
+ * Layout      Matrices are row-major with unit stride along a row and a
+ *             leading dimension ld (in elements, ld >= number of columns)
+ *             between rows.  Vectors are contiguous.
+ * Dtypes      `act` names the storage type of activations and of their
+ *             gradients (x, y, dy, dx, logits, dlogits): VJP_F32, VJP_F16
+ *             or VJP_BF16.  All arithmetic is fp32; every reduction
+ *             accumulates in fp32.  Parameter gradients (dw, grad_w) and
+ *             row statistics are always fp32 ("Backward in Triton", section
+ *             "fp32 accumulation, and why gradients use +=").
+ * Reductions  Parameter gradients are reduced in two stages with no float
+ *             atomics: stage 1 writes one fp32 partial per tile into the
+ *             caller's workspace, a second kernel sums the partials in a
+ *             fixed order.  The tile count depends only on the problem
+ *             size, so results are bitwise reproducible run to run.
+ *             ("Writing Triton Kernels with Autograd: A Minimal End-to-End
+ *             Example", section 3; "Backward in Triton", section "The
+ *             backward grid is not the forward grid").
+ * accumulate  0: the parameter gradient is overwritten.  1: the new gradient
+ *             is added into the existing fp32 value ("Backward in Triton",
+ *             section "fp32 accumulation, and why gradients use +=").
+ * Streams     Every call is asynchronous on `stream` (a hipStream_t; NULL is
+ *             the default stream) and never synchronises the host.
+ * Errors      Every call returns VJP_OK or a VJP_E* code.  On an error
+ *             detected before launch nothing is launched and no output is
+ *             touched; vjp_last_error() gives a per-thread message.
+ *             VJP_EHIP means a launch failed; outputs are then undefined.
+ * Empty       n = 0 or rows = 0 is valid: nothing is read, parameter
+ *             gradients become 0 (or stay unchanged with accumulate = 1),
+ *             the cross-entropy mean loss of zero rows is NaN.
+ * Alignment   Pointers must be aligned to their element size (fp32 outputs
+ *             and workspaces to 4 bytes).  16-byte alignment of base
+ *             pointers and of ld * element size selects 128-bit loads;
+ *             anything else runs the same algorithm with element loads.
+ * Aliasing    An output range that overlaps an input range or another output
+ *             is rejected with VJP_EALIAS.
+ */
+#ifndef LIBVJP_H
+#define LIBVJP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VJP_VERSION 1
+
+typedef enum { VJP_F32 = 0, VJP_F16 = 1, VJP_BF16 = 2 } vjp_dtype_t;
+
+typedef enum {
+  VJP_OK = 0,
+  VJP_EINVAL = 1,     /* bad size, null pointer, ld < cols, bad flag value */
+  VJP_EDTYPE = 2,     /* unknown dtype code */
+  VJP_EALIGN = 3,     /* pointer not aligned to its element size */
+  VJP_EWORKSPACE = 4, /* workspace missing or smaller than the *_workspace_size query */
+  VJP_EALIAS = 5,     /* an output overlaps an input or another output */
+  VJP_EHIP = 6        /* the HIP runtime reported an error at launch */
+} vjp_status_t;
+
+typedef void* vjp_stream_t; /* hipStream_t */
+
+/* Library version (VJP_VERSION). */
+int vjp_version(void);
+/* Static text for a status code. */
+const char* vjp_status_string(int status);
+/* Text of the calling thread's last error ("" if none). */
+const char* vjp_last_error(void);
+
+/* ---------------------------------------------------------------- weighted sum
+ * y[i] = sum_j x[i, j] * w[j];  x [n_rows, d] (ld_x), w [d], y [n_rows].
+ * Backward: grad_x[i, j] = dy[i] * w[j]   (elementwise map, same shape as x)
+ *           grad_w[j]    = sum_i x[i, j] * dy[i]   (reduction over the batch)
+ * Source: "Writing Triton Kernels with Autograd: A Minimal End-to-End
+ * Example", sections 1-4 (problem setup, forward tiled over rows with a loop
+ * over D, gradients, two-stage grad_w: one partial row per tile of rows).
+ */
+
+/* x, y, dy, dx in `act`; w in `w_dtype`.  y has n_rows elements in `act`. */
+int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
+                         int64_t n_rows, int64_t d, int act, int w_dtype,
+                         vjp_stream_t stream);
+
+/* Rows per tile actually used for a request (0 = automatic: a function of
+ * n_rows only, 32 * ceil(ceil(n_rows / 2048) / 32), at least 32).  Returns
+ * -1 for invalid arguments. */
+int64_t vjp_weighted_sum_rows_per_tile(int64_t n_rows, int64_t rows_per_tile);
+
+/* Workspace bytes for vjp_weighted_sum_bwd: T * d * 4 with
+ * T = ceil(n_rows / rows_per_tile) (rows_per_tile resolved as above).
+ * Layout: fp32 partials P[T][d] row-major at offset 0, where
+ * P[t][j] = sum over rows i of tile t of x[i, j] * dy[i]. */
+size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d, int64_t rows_per_tile);
+
+/* dy [n_rows] (act), x [n_rows, d] (ld_x, act), w [d] (w_dtype) ->
+ * dx [n_rows, d] (ld_dx, act), dw [d] fp32 (overwritten or, with
+ * accumulate = 1, added into).  workspace: see the size query.
+ * grad_w[j] = sum over t = 0..T-1 of P[t][j] in this fixed order: 64 row
+ * lanes r (1024 / min(16, next_pow2(d)) row lanes when d < 16) each sum
+ * P[r][j], P[r + RL][j], ... in increasing t, then a pairwise tree
+ * v[r] += v[r + s] for s = RL/2, ..., 1; finally dw[j] = v[0] (or dw[j] + v[0]). */
+int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
+                         void* dx, int64_t ld_dx, float* dw, int accumulate,
+                         int64_t n_rows, int64_t d, int64_t rows_per_tile,
+                         int act, int w_dtype, void* workspace, size_t workspace_bytes,
+                         vjp_stream_t stream);
+
+/* ---------------------------------------------------------------- scaled SiLU
+ * y = w * x * sigmoid(x), elementwise over n elements; w is ONE fp32 value
+ * held in device memory (read by the kernels, no host synchronisation).
+ * Backward (sigmoid recomputed from x, not saved):
+ *   dx = dy * w * (s + x s (1 - s)),  s = sigmoid(x)
+ *   dw = sum over all elements of dy * x * s   (fp32)
+ * Source: "Backward in Triton -- autograd.Function and the backward grid",
+ * sections "A complete minimal example -- fused scaled-SiLU, end to end" and
+ * "Save vs recompute -- the decision at the Triton level".  The page's
+ * single-cell atomic add of per-block partials is replaced by the two-stage
+ * reduction described above.
+ */
+int vjp_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, int act,
+                        vjp_stream_t stream);
+
+/* Elements per dw tile: max(2048, 2048 * ceil(ceil(n / 2048) / 2048)). -1 if n < 0. */
+int64_t vjp_scaled_silu_elems_per_tile(int64_t n);
+
+/* Workspace bytes: T * 4, T = ceil(n / elems_per_tile).  Layout: fp32
+ * partials P[T] at offset 0, P[t] = sum over elements k of tile t of
+ * dy[k] * x[k] * s[k]. */
+size_t vjp_scaled_silu_bwd_workspace_size(int64_t n);
+
+/* dy, x [n] (act), w [1] fp32 -> dx [n] (act), dw [1] fp32.  dw is the
+ * fixed-order sum of P (1024 row lanes, then the pairwise tree, as for
+ * vjp_weighted_sum_bwd with d = 1). */
+int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx, float* dw,
+                        int accumulate, int64_t n, int act, void* workspace,
+                        size_t workspace_bytes, vjp_stream_t stream);
+
+/* ---------------------------------------------------------------- row softmax
+ * y[r, j] = exp(x[r, j] - m_r) / sum_k exp(x[r, k] - m_r), m_r = max_k x[r, k].
+ * The backward needs only the saved y: with s_r = sum_j dy[r, j] y[r, j],
+ * dx[r, j] = y[r, j] (dy[r, j] - s_r); the cols x cols Jacobian is never
+ * formed.  Source: "Backprop for kernel writers", section 01 and the softmax
+ * section after 04 "The duality" (one row scalar, O(cols) time, O(1) extra
+ * memory; the max shift adds no backward term).
+ */
+int vjp_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                    int64_t cols, int act, vjp_stream_t stream);
+
+int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, void* dx,
+                    int64_t ld_dx, int64_t rows, int64_t cols, int act, vjp_stream_t stream);
+
+/* ---------------------------------------------------------------- softmax + cross-entropy
+ * Fused forward and backward of the mean cross-entropy of a row softmax:
+ *   row_max[r] = m_r = max_j z[r, j]
+ *   row_lse[r] = m_r + log sum_j exp(z[r, j] - m_r)
+ *   loss       = (1 / rows) * sum_r (row_lse[r] - z[r, t_r])        (fp32, [1])
+ *   dlogits    = grad_scale * (exp(z - row_lse) - onehot(t_r))       (act)
+ * grad_scale is the upstream gradient of the mean loss divided by rows
+ * (1 / rows for a unit upstream gradient).  The probabilities are rebuilt
+ * on chip from the row statistics and never written to memory.
+ * Source: "Backprop for kernel writers", section 02 "See it move" (softmax
+ * and cross-entropy derivatives cancel into softmax minus one-hot) and
+ * section 07 "Fusion" (keep only m and log-sum-exp per row, rebuild P).
+ * targets [rows] int32.  A target outside [0, classes) is not an error: that
+ * row's loss is NaN (so is the mean), its dlogits row has no one-hot term,
+ * and it is counted in *n_invalid (int32, optional: NULL skips the count).
+ * workspace: vjp_softmax_xent_workspace_size(rows) bytes; layout: fp32 row
+ * losses [rows] at offset 0.  The mean is their fixed-order sum (1024 row
+ * lanes, pairwise tree) divided by rows.
+ */
+size_t vjp_softmax_xent_workspace_size(int64_t rows);
+
+int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32_t* targets,
+                             int64_t rows, int64_t classes, int act, float grad_scale,
+                             float* loss, float* row_max, float* row_lse, void* dlogits,
+                             int64_t ld_dlogits, int32_t* n_invalid, void* workspace,
+                             size_t workspace_bytes, vjp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBVJP_H */

@@ -1,0 +1,379 @@
+// The libvjp C ABI (declared in include/libvjp.h): argument validation,
+// workspace sizing, choice of the 128-bit or element-wise kernel variant,
+// and the launch sequence of each entry point.  Nothing here allocates device
+// memory or synchronises the host.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <initializer_list>
+
+#include "launch.hpp"
+#include "libvjp.h"
+
+#define VJP_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace vjp;
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return VJP_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(VJP_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Sizes beyond this are rejected so that no element offset can overflow int64.
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+// Rows per launch of the row kernels (keeps every grid far below 2^31 threads).
+constexpr int64_t kRowsPerLaunch = int64_t(1) << 20;
+
+bool dtype_ok(int dt) { return dt == kF32 || dt == kF16 || dt == kBF16; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+  const char* name = "";
+};
+
+Range span(const void* p, int64_t bytes, const char* name) {
+  Range r;
+  r.name = name;
+  if (p && bytes > 0) {
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + uint64_t(bytes);
+  }
+  return r;
+}
+
+// Bytes touched by a row-major [rows, cols] matrix with leading dimension ld.
+int64_t mat_bytes(int64_t rows, int64_t cols, int64_t ld, int esize) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((rows - 1) * ld + cols) * esize;
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi;
+}
+
+int check_alias(std::initializer_list<Range> outs, std::initializer_list<Range> ins) {
+  for (const Range* o = outs.begin(); o != outs.end(); ++o) {
+    for (const Range& i : ins)
+      if (overlaps(*o, i)) return fail(VJP_EALIAS, "output %s overlaps input %s", o->name, i.name);
+    for (const Range* p = o + 1; p != outs.end(); ++p)
+      if (overlaps(*o, *p)) return fail(VJP_EALIAS, "outputs %s and %s overlap", o->name, p->name);
+  }
+  return VJP_OK;
+}
+
+int check_matrix(const char* name, const void* p, int64_t rows, int64_t cols, int64_t ld,
+                 int esize) {
+  if (ld < cols) return fail(VJP_EINVAL, "%s: ld (%lld) < columns (%lld)", name, (long long)ld, (long long)cols);
+  if (rows > 0 && cols > 0) {
+    if (!p) return fail(VJP_EINVAL, "%s is NULL", name);
+    if (!aligned(p, esize)) return fail(VJP_EALIGN, "%s is not aligned to its element size", name);
+    if (ld > kMaxElems || rows > kMaxElems || (rows - 1) > kMaxElems / (ld > 0 ? ld : 1))
+      return fail(VJP_EINVAL, "%s: size too large", name);
+  }
+  return VJP_OK;
+}
+
+int check_vector(const char* name, const void* p, int64_t n, int esize) {
+  if (n > 0) {
+    if (!p) return fail(VJP_EINVAL, "%s is NULL", name);
+    if (!aligned(p, esize)) return fail(VJP_EALIGN, "%s is not aligned to its element size", name);
+  }
+  return VJP_OK;
+}
+
+// 128-bit accesses need 16-byte aligned rows.
+bool rows_vec_ok(const void* p, int64_t ld, int esize) {
+  return aligned(p, 16) && ((ld * esize) % 16) == 0;
+}
+
+#define VJP_TRY(expr)          \
+  do {                         \
+    const int _st = (expr);    \
+    if (_st != VJP_OK) return _st; \
+  } while (0)
+
+int64_t resolve_rows_per_tile(int64_t n_rows, int64_t rpt) {
+  if (rpt > 0) return rpt;
+  const int64_t per = (n_rows + 2047) / 2048;
+  const int64_t r = ((per + 31) / 32) * 32;
+  return r < 32 ? 32 : r;
+}
+
+int64_t resolve_elems_per_tile(int64_t n) {
+  const int64_t per = (n + 2047) / 2048;
+  const int64_t e = ((per + 2047) / 2048) * 2048;
+  return e < 2048 ? 2048 : e;
+}
+
+}  // namespace
+
+VJP_API int vjp_version(void) { return VJP_VERSION; }
+
+VJP_API const char* vjp_status_string(int status) {
+  switch (status) {
+    case VJP_OK: return "ok";
+    case VJP_EINVAL: return "invalid argument";
+    case VJP_EDTYPE: return "unknown dtype";
+    case VJP_EALIGN: return "misaligned pointer";
+    case VJP_EWORKSPACE: return "workspace missing or too small";
+    case VJP_EALIAS: return "output overlaps another buffer";
+    case VJP_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+VJP_API const char* vjp_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------ weighted sum
+
+VJP_API int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
+                                 int64_t n_rows, int64_t d, int act, int w_dtype,
+                                 vjp_stream_t stream) {
+  if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (n_rows < 0 || d < 0) return fail(VJP_EINVAL, "negative size");
+  const int es = dtype_size(act), ws = dtype_size(w_dtype);
+  VJP_TRY(check_matrix("x", x, n_rows, d, ld_x, es));
+  VJP_TRY(check_vector("w", w, d, ws));
+  VJP_TRY(check_vector("y", y, n_rows, es));
+  VJP_TRY(check_alias({span(y, n_rows * es, "y")},
+                      {span(x, mat_bytes(n_rows, d, ld_x, es), "x"), span(w, d * ws, "w")}));
+  if (n_rows == 0) return ok();
+  const bool vec = rows_vec_ok(x, ld_x, es);
+  return hip_status(launch_weighted_sum_fwd(x, ld_x, w, y, n_rows, d, act, w_dtype, vec,
+                                            static_cast<hipStream_t>(stream)),
+                    "weighted_sum_fwd");
+}
+
+VJP_API int64_t vjp_weighted_sum_rows_per_tile(int64_t n_rows, int64_t rows_per_tile) {
+  if (n_rows < 0 || rows_per_tile < 0) return -1;
+  return resolve_rows_per_tile(n_rows, rows_per_tile);
+}
+
+VJP_API size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d,
+                                                   int64_t rows_per_tile) {
+  if (n_rows < 0 || d < 0 || rows_per_tile < 0) return 0;
+  const int64_t r = resolve_rows_per_tile(n_rows, rows_per_tile);
+  const int64_t T = (n_rows + r - 1) / r;
+  return size_t(T) * size_t(d) * sizeof(float);
+}
+
+VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
+                                 void* dx, int64_t ld_dx, float* dw, int accumulate,
+                                 int64_t n_rows, int64_t d, int64_t rows_per_tile, int act,
+                                 int w_dtype, void* workspace, size_t workspace_bytes,
+                                 vjp_stream_t stream) {
+  if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (n_rows < 0 || d < 0 || rows_per_tile < 0) return fail(VJP_EINVAL, "negative size");
+  if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
+  const int es = dtype_size(act), ws = dtype_size(w_dtype);
+  VJP_TRY(check_vector("dy", dy, n_rows, es));
+  VJP_TRY(check_matrix("x", x, n_rows, d, ld_x, es));
+  VJP_TRY(check_vector("w", w, d, ws));
+  VJP_TRY(check_matrix("dx", dx, n_rows, d, ld_dx, es));
+  VJP_TRY(check_vector("dw", dw, d, 4));
+  const size_t need = vjp_weighted_sum_bwd_workspace_size(n_rows, d, rows_per_tile);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(VJP_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned(workspace, 4)) return fail(VJP_EALIGN, "workspace is not 4-byte aligned");
+  }
+  VJP_TRY(check_alias({span(dx, mat_bytes(n_rows, d, ld_dx, es), "dx"), span(dw, d * 4, "dw"),
+                       span(workspace, int64_t(need), "workspace")},
+                      {span(dy, n_rows * es, "dy"), span(x, mat_bytes(n_rows, d, ld_x, es), "x"),
+                       span(w, d * ws, "w")}));
+  if (d == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rpt = resolve_rows_per_tile(n_rows, rows_per_tile);
+  const int64_t T = (n_rows + rpt - 1) / rpt;
+  float* P = static_cast<float*>(workspace);
+  if (T > 0) {
+    const bool vec = rows_vec_ok(x, ld_x, es) && rows_vec_ok(dx, ld_dx, es);
+    const hipError_t e = launch_weighted_sum_bwd_stage1(dy, x, ld_x, w, dx, ld_dx, P, n_rows, d,
+                                                        rpt, act, w_dtype, vec, s);
+    if (e != hipSuccess) return hip_status(e, "weighted_sum_bwd stage 1");
+  }
+  return hip_status(launch_reduce_partials(P, T, d, dw, accumulate, s), "weighted_sum_bwd stage 2");
+}
+
+// ------------------------------------------------------------------ scaled SiLU
+
+VJP_API int vjp_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, int act,
+                                vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (n < 0) return fail(VJP_EINVAL, "negative size");
+  if (n > kMaxElems) return fail(VJP_EINVAL, "size too large");
+  const int es = dtype_size(act);
+  VJP_TRY(check_vector("x", x, n, es));
+  VJP_TRY(check_vector("w", w, n > 0 ? 1 : 0, 4));
+  VJP_TRY(check_vector("y", y, n, es));
+  VJP_TRY(check_alias({span(y, n * es, "y")}, {span(x, n * es, "x"), span(w, 4, "w")}));
+  if (n == 0) return ok();
+  const bool vec = aligned(x, 16) && aligned(y, 16);
+  return hip_status(launch_scaled_silu_fwd(x, w, y, n, act, vec, static_cast<hipStream_t>(stream)),
+                    "scaled_silu_fwd");
+}
+
+VJP_API int64_t vjp_scaled_silu_elems_per_tile(int64_t n) {
+  if (n < 0) return -1;
+  return resolve_elems_per_tile(n);
+}
+
+VJP_API size_t vjp_scaled_silu_bwd_workspace_size(int64_t n) {
+  if (n < 0) return 0;
+  const int64_t e = resolve_elems_per_tile(n);
+  return size_t((n + e - 1) / e) * sizeof(float);
+}
+
+VJP_API int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx,
+                                float* dw, int accumulate, int64_t n, int act, void* workspace,
+                                size_t workspace_bytes, vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (n < 0) return fail(VJP_EINVAL, "negative size");
+  if (n > kMaxElems) return fail(VJP_EINVAL, "size too large");
+  if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
+  const int es = dtype_size(act);
+  VJP_TRY(check_vector("dy", dy, n, es));
+  VJP_TRY(check_vector("x", x, n, es));
+  VJP_TRY(check_vector("w", w, n > 0 ? 1 : 0, 4));
+  VJP_TRY(check_vector("dx", dx, n, es));
+  VJP_TRY(check_vector("dw", dw, 1, 4));
+  const size_t need = vjp_scaled_silu_bwd_workspace_size(n);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(VJP_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned(workspace, 4)) return fail(VJP_EALIGN, "workspace is not 4-byte aligned");
+  }
+  VJP_TRY(check_alias({span(dx, n * es, "dx"), span(dw, 4, "dw"),
+                       span(workspace, int64_t(need), "workspace")},
+                      {span(dy, n * es, "dy"), span(x, n * es, "x"), span(w, n > 0 ? 4 : 0, "w")}));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ept = resolve_elems_per_tile(n);
+  const int64_t T = (n + ept - 1) / ept;
+  float* P = static_cast<float*>(workspace);
+  if (T > 0) {
+    const bool vec = aligned(dy, 16) && aligned(x, 16) && aligned(dx, 16);
+    const hipError_t e = launch_scaled_silu_bwd_stage1(dy, x, w, dx, P, n, ept, act, vec, s);
+    if (e != hipSuccess) return hip_status(e, "scaled_silu_bwd stage 1");
+  }
+  return hip_status(launch_reduce_partials(P, T, 1, dw, accumulate, s), "scaled_silu_bwd stage 2");
+}
+
+// ------------------------------------------------------------------ softmax
+
+VJP_API int vjp_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                            int64_t cols, int act, vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (rows < 0 || cols < 0) return fail(VJP_EINVAL, "negative size");
+  if (rows > 0 && cols == 0) return fail(VJP_EINVAL, "softmax over zero columns");
+  const int es = dtype_size(act);
+  VJP_TRY(check_matrix("x", x, rows, cols, ld_x, es));
+  VJP_TRY(check_matrix("y", y, rows, cols, ld_y, es));
+  VJP_TRY(check_alias({span(y, mat_bytes(rows, cols, ld_y, es), "y")},
+                      {span(x, mat_bytes(rows, cols, ld_x, es), "x")}));
+  const bool vec = rows_vec_ok(x, ld_x, es) && rows_vec_ok(y, ld_y, es);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
+    const hipError_t e = launch_softmax_fwd(static_cast<const char*>(x) + r0 * ld_x * es, ld_x,
+                                            static_cast<char*>(y) + r0 * ld_y * es, ld_y, nr,
+                                            cols, act, vec, s);
+    if (e != hipSuccess) return hip_status(e, "softmax_fwd");
+  }
+  return ok();
+}
+
+VJP_API int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y,
+                            void* dx, int64_t ld_dx, int64_t rows, int64_t cols, int act,
+                            vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (rows < 0 || cols < 0) return fail(VJP_EINVAL, "negative size");
+  if (rows > 0 && cols == 0) return fail(VJP_EINVAL, "softmax over zero columns");
+  const int es = dtype_size(act);
+  VJP_TRY(check_matrix("dy", dy, rows, cols, ld_dy, es));
+  VJP_TRY(check_matrix("y", y, rows, cols, ld_y, es));
+  VJP_TRY(check_matrix("dx", dx, rows, cols, ld_dx, es));
+  VJP_TRY(check_alias({span(dx, mat_bytes(rows, cols, ld_dx, es), "dx")},
+                      {span(dy, mat_bytes(rows, cols, ld_dy, es), "dy"),
+                       span(y, mat_bytes(rows, cols, ld_y, es), "y")}));
+  const bool vec = rows_vec_ok(dy, ld_dy, es) && rows_vec_ok(y, ld_y, es) &&
+                   rows_vec_ok(dx, ld_dx, es);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
+    const hipError_t e = launch_softmax_bwd(
+        static_cast<const char*>(dy) + r0 * ld_dy * es, ld_dy,
+        static_cast<const char*>(y) + r0 * ld_y * es, ld_y,
+        static_cast<char*>(dx) + r0 * ld_dx * es, ld_dx, nr, cols, act, vec, s);
+    if (e != hipSuccess) return hip_status(e, "softmax_bwd");
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ softmax cross-entropy
+
+VJP_API size_t vjp_softmax_xent_workspace_size(int64_t rows) {
+  return rows > 0 ? size_t(rows) * sizeof(float) : 0;
+}
+
+VJP_API int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32_t* targets,
+                                     int64_t rows, int64_t classes, int act, float grad_scale,
+                                     float* loss, float* row_max, float* row_lse, void* dlogits,
+                                     int64_t ld_dlogits, int32_t* n_invalid, void* workspace,
+                                     size_t workspace_bytes, vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (rows < 0 || classes < 0) return fail(VJP_EINVAL, "negative size");
+  if (classes == 0) return fail(VJP_EINVAL, "cross-entropy over zero classes");
+  if (classes > INT32_MAX) return fail(VJP_EINVAL, "classes beyond int32 targets");
+  const int es = dtype_size(act);
+  VJP_TRY(check_matrix("logits", logits, rows, classes, ld, es));
+  VJP_TRY(check_vector("targets", targets, rows, 4));
+  VJP_TRY(check_vector("loss", loss, 1, 4));
+  VJP_TRY(check_vector("row_max", row_max, rows, 4));
+  VJP_TRY(check_vector("row_lse", row_lse, rows, 4));
+  VJP_TRY(check_matrix("dlogits", dlogits, rows, classes, ld_dlogits, es));
+  if (n_invalid && !aligned(n_invalid, 4)) return fail(VJP_EALIGN, "n_invalid is not 4-byte aligned");
+  const size_t need = vjp_softmax_xent_workspace_size(rows);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(VJP_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned(workspace, 4)) return fail(VJP_EALIGN, "workspace is not 4-byte aligned");
+  }
+  VJP_TRY(check_alias({span(loss, 4, "loss"), span(row_max, rows * 4, "row_max"),
+                       span(row_lse, rows * 4, "row_lse"),
+                       span(dlogits, mat_bytes(rows, classes, ld_dlogits, es), "dlogits"),
+                       span(n_invalid, n_invalid ? 4 : 0, "n_invalid"),
+                       span(workspace, int64_t(need), "workspace")},
+                      {span(logits, mat_bytes(rows, classes, ld, es), "logits"),
+                       span(targets, rows * 4, "targets")}));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float* row_loss = static_cast<float*>(workspace);
+  const bool vec = rows_vec_ok(logits, ld, es) && rows_vec_ok(dlogits, ld_dlogits, es);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
+    const hipError_t e = launch_softmax_xent(
+        static_cast<const char*>(logits) + r0 * ld * es, ld, targets + r0, nr, classes, act,
+        grad_scale, row_max + r0, row_lse + r0, row_loss + r0,
+        static_cast<char*>(dlogits) + r0 * ld_dlogits * es, ld_dlogits, vec, s);
+    if (e != hipSuccess) return hip_status(e, "softmax_xent");
+  }
+  return hip_status(launch_xent_finalize(row_loss, targets, rows, classes, loss, n_invalid, s),
+                    "softmax_xent finalize");
+}

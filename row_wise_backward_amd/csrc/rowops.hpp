@@ -1,0 +1,140 @@
+// Row-wise building blocks for the softmax and softmax-cross-entropy
+// kernels: the register-resident row layout and workgroup reductions.
+//
+// Resident layout.  A row is owned by WAVES waves (WAVES = 1: one wave per
+// row, four rows per 256-thread workgroup).  Lane `lane` of wave `wv` holds
+// kChunks vectors of VEC elements; vector k starts at column
+//   (k * WAVES * 64 + wv * 64 + lane) * VEC,
+// so each step k reads WAVES * 64 * VEC contiguous elements (1 KB per wave
+// for 16-byte vectors).  Capacity: WAVES * 64 * kChunks * VEC columns.  The
+// whole row stays in VGPRs between the statistics pass and the output pass,
+// so it is read from HBM exactly once.
+#pragma once
+
+#include "common.hpp"
+
+namespace vjp {
+
+constexpr int kChunks = 8;
+
+template <typename T> __device__ __forceinline__ T neg_inf_of();
+template <> __device__ __forceinline__ float neg_inf_of<float>() { return -__builtin_inff(); }
+template <> __device__ __forceinline__ _Float16 neg_inf_of<_Float16>() {
+  return __builtin_bit_cast(_Float16, uint16_t(0xfc00));
+}
+template <> __device__ __forceinline__ bf16 neg_inf_of<bf16>() { return bf16{0xff80}; }
+
+template <typename T> __device__ __forceinline__ T zero_of() { return T{}; }
+
+// Load vector `col` of a row; elements at or beyond `cols` read as `fill`.
+// Returns true when the whole vector lies inside the row.
+template <typename T, int VEC>
+__device__ __forceinline__ bool load_row_vec(const T* __restrict__ row, int64_t col, int64_t cols,
+                                             T fill, Vec<T, VEC>& r) {
+  if (col + VEC <= cols) {
+    r = *reinterpret_cast<const Vec<T, VEC>*>(row + col);
+    return true;
+  }
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) r.v[i] = (col + i < cols) ? row[col + i] : fill;
+  return false;
+}
+
+// Store vector `col` of a row, dropping elements at or beyond `cols`.
+template <typename T, int VEC>
+__device__ __forceinline__ void store_row_vec(T* __restrict__ row, int64_t col, int64_t cols,
+                                              const float (&v)[VEC]) {
+  store_f32_tail<T, VEC>(row + col, cols - col, v);
+}
+
+// Workgroup-wide reductions for rows owned by WAVES > 1 waves.  Every thread
+// receives the same value; waves are combined in wave order.  `buf` holds
+// WAVES floats; the leading barrier protects reuse of `buf`.
+template <int WAVES>
+__device__ __forceinline__ float row_reduce_max(float v, float* buf) {
+  v = wave_max(v);
+  if constexpr (WAVES > 1) {
+    __syncthreads();
+    if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
+    __syncthreads();
+    v = buf[0];
+#pragma unroll
+    for (int k = 1; k < WAVES; ++k) v = fmaxf(v, buf[k]);
+  }
+  return v;
+}
+
+template <int WAVES>
+__device__ __forceinline__ float row_reduce_sum(float v, float* buf) {
+  v = wave_sum(v);
+  if constexpr (WAVES > 1) {
+    __syncthreads();
+    if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
+    __syncthreads();
+    v = buf[0];
+#pragma unroll
+    for (int k = 1; k < WAVES; ++k) v += buf[k];
+  }
+  return v;
+}
+
+// 2^t without flushing subnormal results: v_exp_f32 is only trusted for
+// results >= 2^-126, below that the argument is shifted up by 64 and the
+// result scaled back (an exact power-of-two scaling, one rounding).
+__device__ __forceinline__ float exp2_denorm_safe(float t) {
+  return t < -126.0f ? exp2_fast(t + 64.0f) * 5.421010862427522e-20f /* 2^-64 */
+                     : exp2_fast(t);
+}
+
+// Streaming-path workgroup: 256 threads per row.
+constexpr int kStreamThreads = 256;
+
+// Combine per-thread online-softmax states (m, l) with l relative to m:
+// M = max m_i, L = sum_i l_i * 2^((m_i - M) log2 e), threads in index order
+// (wave butterflies, then waves in order).
+__device__ __forceinline__ void block_merge_ml(float& m, float& l, float* bm, float* bl) {
+  constexpr int W = kStreamThreads / kWave;
+  float M = wave_max(m);
+  float contrib = (m == -__builtin_inff()) ? 0.0f : l * exp2_denorm_safe((m - M) * kLog2e);
+  float Lw = wave_sum(contrib);
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) {
+    bm[threadIdx.x / kWave] = M;
+    bl[threadIdx.x / kWave] = Lw;
+  }
+  __syncthreads();
+  float Mg = bm[0];
+#pragma unroll
+  for (int k = 1; k < W; ++k) Mg = fmaxf(Mg, bm[k]);
+  float Lg = 0.0f;
+#pragma unroll
+  for (int k = 0; k < W; ++k)
+    Lg += (bm[k] == -__builtin_inff()) ? 0.0f : bl[k] * exp2_denorm_safe((bm[k] - Mg) * kLog2e);
+  m = Mg;
+  l = Lg;
+}
+
+// One element of an online softmax: fold x into the running (m, l).  An
+// element equal to -inf adds nothing; a NaN element turns l into NaN.
+__device__ __forceinline__ void online_step(float x, float& m, float& l) {
+  if (x > m) {
+    l = (m == -__builtin_inff()) ? 1.0f : fmaf(l, exp2_denorm_safe((m - x) * kLog2e), 1.0f);
+    m = x;
+  } else if (x != -__builtin_inff()) {
+    l += exp2_denorm_safe((x - m) * kLog2e);
+  }
+}
+
+template <int W>
+__device__ __forceinline__ float block_sum_stream(float v, float* buf) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float s = buf[0];
+#pragma unroll
+  for (int k = 1; k < W; ++k) s += buf[k];
+  return s;
+}
+
+}  // namespace vjp

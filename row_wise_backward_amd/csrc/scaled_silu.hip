@@ -1,0 +1,157 @@
+// Fused scaled-SiLU y = w * x * sigmoid(x): forward and stage-1 backward.
+//
+// Source: "Backward in Triton -- autograd.Function and the backward grid",
+// section "A complete minimal example -- fused scaled-SiLU, end to end"
+// (fp32 compute; dx = dy * w * (s + silu (1 - s)); dw = sum dy * silu, a
+// scalar reduced over every element) and section "Save vs recompute -- the
+// decision at the Triton level" (the backward reads x and recomputes
+// s = sigmoid(x) instead of reading a saved s).  The page combines per-block
+// dw partials with one float atomic per block; here each tile writes its
+// fp32 partial to P[t] and the fixed-order stage-2 kernel sums them.
+//
+// gfx950 mapping: flat elementwise stream, 16-byte accesses (8 x fp16/bf16,
+// 4 x fp32) per lane, 256-thread workgroups, kUnroll vectors loaded per lane
+// before use.  sigmoid(x) = 1 / (1 + 2^(-x log2 e)) on v_exp_f32 and
+// v_rcp_f32 (both accurate to about 1 ulp in fp32).  The scalar w is read
+// from device memory by every workgroup (no host synchronisation).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace vjp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void silu_fwd_kernel(const T* __restrict__ x,
+                                                            const float* __restrict__ w,
+                                                            T* __restrict__ y, int64_t n,
+                                                            int64_t elems_per_block) {
+  const float wv = *w;
+  const int64_t beg = int64_t(blockIdx.x) * elems_per_block;
+  const int64_t end = min(beg + elems_per_block, n);
+  const int64_t stride = int64_t(kThreads) * VEC;
+  for (int64_t base = beg + int64_t(threadIdx.x) * VEC; base < end; base += kUnroll * stride) {
+    float xv[kUnroll][VEC];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i0 = base + u * stride;
+      if (i0 < end) load_f32_tail<T, VEC>(x + i0, end - i0, 0.0f, xv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i0 = base + u * stride;
+      if (i0 < end) {
+        float yv[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) yv[i] = wv * xv[u][i] * sigmoid(xv[u][i]);
+        store_f32_tail<T, VEC>(y + i0, end - i0, yv);
+      }
+    }
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void silu_bwd_kernel(
+    const T* __restrict__ dy, const T* __restrict__ x, const float* __restrict__ w,
+    T* __restrict__ dx, float* __restrict__ P, int64_t n, int64_t elems_per_tile) {
+  __shared__ float red[kThreads / kWave];
+  const float wv = *w;
+  const int64_t tile = blockIdx.x;
+  const int64_t beg = tile * elems_per_tile;
+  const int64_t end = min(beg + elems_per_tile, n);
+  const int64_t stride = int64_t(kThreads) * VEC;
+  float acc = 0.0f;
+  for (int64_t base = beg + int64_t(threadIdx.x) * VEC; base < end; base += kUnroll * stride) {
+    float xv[kUnroll][VEC], gv[kUnroll][VEC];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i0 = base + u * stride;
+      if (i0 < end) {
+        load_f32_tail<T, VEC>(x + i0, end - i0, 0.0f, xv[u]);
+        load_f32_tail<T, VEC>(dy + i0, end - i0, 0.0f, gv[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) xv[u][i] = gv[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i0 = base + u * stride;
+      float dxv[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float s = sigmoid(xv[u][i]);
+        const float silu = xv[u][i] * s;
+        dxv[i] = gv[u][i] * wv * fmaf(silu, 1.0f - s, s);
+        acc = fmaf(gv[u][i], silu, acc);
+      }
+      if (i0 < end) store_f32_tail<T, VEC>(dx + i0, end - i0, dxv);
+    }
+  }
+  acc = wave_sum(acc);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float s = red[0];
+#pragma unroll
+    for (int k = 1; k < kThreads / kWave; ++k) s += red[k];
+    P[tile] = s;
+  }
+}
+
+template <typename T>
+hipError_t fwd_typed(const void* x, const float* w, void* y, int64_t n, bool vec,
+                     hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  const int64_t epb = int64_t(kThreads) * (vec ? V : 1) * kUnroll;
+  const dim3 grid(unsigned((n + epb - 1) / epb));
+  if (vec)
+    silu_fwd_kernel<T, V><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), w,
+                                                    static_cast<T*>(y), n, epb);
+  else
+    silu_fwd_kernel<T, 1><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), w,
+                                                    static_cast<T*>(y), n, epb);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t bwd_typed(const void* dy, const void* x, const float* w, void* dx, float* P,
+                     int64_t n, int64_t ept, bool vec, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  const dim3 grid(unsigned((n + ept - 1) / ept));
+  if (vec)
+    silu_bwd_kernel<T, V><<<grid, kThreads, 0, s>>>(static_cast<const T*>(dy),
+                                                    static_cast<const T*>(x), w,
+                                                    static_cast<T*>(dx), P, n, ept);
+  else
+    silu_bwd_kernel<T, 1><<<grid, kThreads, 0, s>>>(static_cast<const T*>(dy),
+                                                    static_cast<const T*>(x), w,
+                                                    static_cast<T*>(dx), P, n, ept);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, int act,
+                                  bool vec, hipStream_t s) {
+  switch (act) {
+    case kF32: return fwd_typed<float>(x, w, y, n, vec, s);
+    case kF16: return fwd_typed<_Float16>(x, w, y, n, vec, s);
+    default: return fwd_typed<bf16>(x, w, y, n, vec, s);
+  }
+}
+
+hipError_t launch_scaled_silu_bwd_stage1(const void* dy, const void* x, const float* w,
+                                         void* dx, float* P, int64_t n, int64_t elems_per_tile,
+                                         int act, bool vec, hipStream_t s) {
+  switch (act) {
+    case kF32: return bwd_typed<float>(dy, x, w, dx, P, n, elems_per_tile, vec, s);
+    case kF16: return bwd_typed<_Float16>(dy, x, w, dx, P, n, elems_per_tile, vec, s);
+    default: return bwd_typed<bf16>(dy, x, w, dx, P, n, elems_per_tile, vec, s);
+  }
+}
+
+}  // namespace vjp

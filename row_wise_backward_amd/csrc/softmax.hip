@@ -1,0 +1,294 @@
+// Row softmax forward (saves y) and backward (needs only y).
+//
+// Source: "Backprop for kernel writers".  Section 01 "The only idea": the
+// backward is a vector-Jacobian product and the cols x cols softmax Jacobian
+// is never formed.  The softmax section after 04 "The duality": the VJP
+// collapses to one row scalar s = sum_j dy_j y_j accumulated in one pass and
+// applied elementwise, dx_j = y_j (dy_j - s), in a second; the backward is a
+// function of y alone; the forward's max shift is free (shift invariance).
+// "Backward in Triton -- autograd.Function and the backward grid", section
+// "Save vs recompute": the row max is a one-scalar-per-row statistic the
+// forward recomputes on chip.
+//
+// Resident path (rows up to 8 waves * 64 * 8 * VEC columns): the row is read
+// once into VGPRs (layout in rowops.hpp), the statistics are reduced with
+// wave butterflies and, for multi-wave rows, LDS in wave order, and the
+// output pass works from the registers.  Streaming path (wider rows): 256
+// threads per row, an online max / sum pass and an output pass, so x (or
+// dy and y) is read twice.
+#include "launch.hpp"
+#include "rowops.hpp"
+
+namespace vjp {
+
+namespace {
+
+template <int WAVES> constexpr int block_threads() { return WAVES == 1 ? 256 : WAVES * kWave; }
+
+template <typename T, int VEC, int WAVES>
+__global__ __launch_bounds__(block_threads<WAVES>()) void softmax_fwd_resident(
+    const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y, int64_t rows,
+    int64_t cols) {
+  __shared__ float buf[WAVES];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * 4 + wave : int64_t(blockIdx.x);
+  const int wv = WAVES == 1 ? 0 : wave;
+  if (WAVES == 1 && row >= rows) return;
+  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
+  const int64_t lane_col = (int64_t(wv) * kWave + lane) * VEC;
+  const T* xr = x + row * ld_x;
+
+  Vec<T, VEC> raw[kChunks];
+  float mx = -__builtin_inff(), mn = __builtin_inff();
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    if (k * kStep < cols) {
+      const int64_t col = k * kStep + lane_col;
+      if (load_row_vec<T, VEC>(xr, col, cols, neg_inf_of<T>(), raw[k])) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float f = to_f32(raw[k].v[i]);
+          mx = fmaxf(mx, f);
+          mn = fminf(mn, f);
+        }
+      } else {  // ragged end of the row: padding counts for neither max nor min
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float f = to_f32(raw[k].v[i]);
+          mx = fmaxf(mx, f);
+          mn = fminf(mn, col + i < cols ? f : __builtin_inff());
+        }
+      }
+    }
+  }
+  const float m = row_reduce_max<WAVES>(mx, buf);
+
+  float e[kChunks][VEC];
+  float l = 0.0f;
+  if (!((mn - m) * kLog2e < -126.0f)) {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      if (k * kStep < cols) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          e[k][i] = exp2_fast((to_f32(raw[k].v[i]) - m) * kLog2e);
+          l += e[k][i];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      if (k * kStep < cols) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          e[k][i] = exp2_denorm_safe((to_f32(raw[k].v[i]) - m) * kLog2e);
+          l += e[k][i];
+        }
+      }
+    }
+  }
+  l = row_reduce_sum<WAVES>(l, buf);
+  const float inv = 1.0f / l;
+
+  T* yr = y + row * ld_y;
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    if (k * kStep < cols) {
+      const int64_t col = k * kStep + lane_col;
+      if (col < cols) {
+        float o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = e[k][i] * inv;
+        store_row_vec<T, VEC>(yr, col, cols, o);
+      }
+    }
+  }
+}
+
+template <typename T, int VEC, int WAVES>
+__global__ __launch_bounds__(block_threads<WAVES>()) void softmax_bwd_resident(
+    const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ y, int64_t ld_y,
+    T* __restrict__ dx, int64_t ld_dx, int64_t rows, int64_t cols) {
+  __shared__ float buf[WAVES];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * 4 + wave : int64_t(blockIdx.x);
+  const int wv = WAVES == 1 ? 0 : wave;
+  if (WAVES == 1 && row >= rows) return;
+  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
+  const int64_t lane_col = (int64_t(wv) * kWave + lane) * VEC;
+  const T* gr = dy + row * ld_dy;
+  const T* yr = y + row * ld_y;
+
+  Vec<T, VEC> rg[kChunks], ry[kChunks];
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    if (k * kStep < cols) {
+      const int64_t col = k * kStep + lane_col;
+      load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), rg[k]);
+      load_row_vec<T, VEC>(yr, col, cols, zero_of<T>(), ry[k]);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    if (k * kStep < cols) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(rg[k].v[i]), to_f32(ry[k].v[i]), s);
+    }
+  }
+  s = row_reduce_sum<WAVES>(s, buf);
+
+  T* dr = dx + row * ld_dx;
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    if (k * kStep < cols) {
+      const int64_t col = k * kStep + lane_col;
+      if (col < cols) {
+        float o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = to_f32(ry[k].v[i]) * (to_f32(rg[k].v[i]) - s);
+        store_row_vec<T, VEC>(dr, col, cols, o);
+      }
+    }
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream(
+    const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y, int64_t cols) {
+  __shared__ float bm[kStreamThreads / kWave], bl[kStreamThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * ld_x;
+  T* yr = y + row * ld_y;
+  float m = -__builtin_inff(), l = 0.0f;
+  for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
+    Vec<T, VEC> r;
+    load_row_vec<T, VEC>(xr, col, cols, neg_inf_of<T>(), r);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) online_step(to_f32(r.v[i]), m, l);
+  }
+  block_merge_ml(m, l, bm, bl);
+  const float inv = 1.0f / l;
+  for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
+    Vec<T, VEC> r;
+    load_row_vec<T, VEC>(xr, col, cols, neg_inf_of<T>(), r);
+    float o[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = exp2_denorm_safe((to_f32(r.v[i]) - m) * kLog2e) * inv;
+    store_row_vec<T, VEC>(yr, col, cols, o);
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream(
+    const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ y, int64_t ld_y,
+    T* __restrict__ dx, int64_t ld_dx, int64_t cols) {
+  __shared__ float buf[kStreamThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const T* gr = dy + row * ld_dy;
+  const T* yr = y + row * ld_y;
+  T* dr = dx + row * ld_dx;
+  float s = 0.0f;
+  for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
+    Vec<T, VEC> a, b;
+    load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), a);
+    load_row_vec<T, VEC>(yr, col, cols, zero_of<T>(), b);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(a.v[i]), to_f32(b.v[i]), s);
+  }
+  s = block_sum_stream<kStreamThreads / kWave>(s, buf);
+  for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
+    Vec<T, VEC> a, b;
+    load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), a);
+    load_row_vec<T, VEC>(yr, col, cols, zero_of<T>(), b);
+    float o[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = to_f32(b.v[i]) * (to_f32(a.v[i]) - s);
+    store_row_vec<T, VEC>(dr, col, cols, o);
+  }
+}
+
+// Smallest WAVES in {1, 2, 4, 8} whose resident capacity holds `cols`;
+// 0 means the row needs the streaming path.
+int resident_waves(int64_t cols, int vec) {
+  for (int w = 1; w <= 8; w <<= 1)
+    if (int64_t(w) * kWave * kChunks * vec >= cols) return w;
+  return 0;
+}
+
+template <typename T, int VEC>
+hipError_t fwd_vec(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                   int64_t cols, hipStream_t s) {
+  const T* xp = static_cast<const T*>(x);
+  T* yp = static_cast<T*>(y);
+  const int w = resident_waves(cols, VEC);
+  const unsigned rb = unsigned(rows);
+  switch (w) {
+    case 1: softmax_fwd_resident<T, VEC, 1><<<unsigned((rows + 3) / 4), 256, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
+    case 2: softmax_fwd_resident<T, VEC, 2><<<rb, 128, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
+    case 4: softmax_fwd_resident<T, VEC, 4><<<rb, 256, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
+    case 8: softmax_fwd_resident<T, VEC, 8><<<rb, 512, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
+    default: softmax_fwd_stream<T, VEC><<<rb, kStreamThreads, 0, s>>>(xp, ld_x, yp, ld_y, cols); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int VEC>
+hipError_t bwd_vec(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, void* dx,
+                   int64_t ld_dx, int64_t rows, int64_t cols, hipStream_t s) {
+  const T* gp = static_cast<const T*>(dy);
+  const T* yp = static_cast<const T*>(y);
+  T* dp = static_cast<T*>(dx);
+  const int w = resident_waves(cols, VEC);
+  const unsigned rb = unsigned(rows);
+  switch (w) {
+    case 1: softmax_bwd_resident<T, VEC, 1><<<unsigned((rows + 3) / 4), 256, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
+    case 2: softmax_bwd_resident<T, VEC, 2><<<rb, 128, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
+    case 4: softmax_bwd_resident<T, VEC, 4><<<rb, 256, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
+    case 8: softmax_bwd_resident<T, VEC, 8><<<rb, 512, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
+    default: softmax_bwd_stream<T, VEC><<<rb, kStreamThreads, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, cols); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t fwd_typed(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                     int64_t cols, bool vec, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  return vec ? fwd_vec<T, V>(x, ld_x, y, ld_y, rows, cols, s)
+             : fwd_vec<T, 1>(x, ld_x, y, ld_y, rows, cols, s);
+}
+
+template <typename T>
+hipError_t bwd_typed(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, void* dx,
+                     int64_t ld_dx, int64_t rows, int64_t cols, bool vec, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  return vec ? bwd_vec<T, V>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, s)
+             : bwd_vec<T, 1>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, s);
+}
+
+}  // namespace
+
+hipError_t launch_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                              int64_t cols, int act, bool vec, hipStream_t s) {
+  switch (act) {
+    case kF32: return fwd_typed<float>(x, ld_x, y, ld_y, rows, cols, vec, s);
+    case kF16: return fwd_typed<_Float16>(x, ld_x, y, ld_y, rows, cols, vec, s);
+    default: return fwd_typed<bf16>(x, ld_x, y, ld_y, rows, cols, vec, s);
+  }
+}
+
+hipError_t launch_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y,
+                              void* dx, int64_t ld_dx, int64_t rows, int64_t cols, int act,
+                              bool vec, hipStream_t s) {
+  switch (act) {
+    case kF32: return bwd_typed<float>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, vec, s);
+    case kF16: return bwd_typed<_Float16>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, vec, s);
+    default: return bwd_typed<bf16>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, vec, s);
+  }
+}
+
+}  // namespace vjp

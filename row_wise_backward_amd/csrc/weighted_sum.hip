@@ -1,0 +1,250 @@
+// Row-wise weighted sum y = x . w: forward and the stage-1 backward.
+//
+// Source: "Writing Triton Kernels with Autograd: A Minimal End-to-End
+// Example" -- section 1 (y[i] = sum_j x[i, j] w[j]), section 2 (tile over
+// rows, loop over D, accumulate locally), section 3 (grad_x = dy outer w is
+// a map over x; grad_w reduces over the batch, so each tile of rows writes
+// one partial row and a second pass sums them), section 4 (the backward
+// kernel writes grad_x and the partial row of its tile).
+//
+// gfx950 mapping.  A row is spread over L consecutive lanes of a wave64
+// (L = smallest power of two with L * VEC >= d, at most 64), each lane
+// moving VEC elements per access (16 bytes: 8 x bf16/fp16 or 4 x fp32) so a
+// wave reads 64 * 16 B contiguous bytes per instruction.  A wave therefore
+// covers G = 64 / L rows at once and a 256-thread workgroup 4 G rows; U such
+// row groups are loaded before any is used so every lane keeps U 128-bit
+// loads in flight.  Rows wider than 64 * VEC loop over column chunks.
+//
+// Forward: per-lane fp32 dot over its columns, then a butterfly over the L
+// lanes of the row.  Backward stage 1: workgroup (t, cb) owns row tile t and
+// column block cb (64 * VEC columns at most); each lane keeps VEC fp32
+// partial sums for its columns over the rows it visits, lanes holding the
+// same columns are combined by a butterfly, the 4 waves through LDS in wave
+// order, and the tile's partial row is written to P[t][.] -- no atomics.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace vjp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ float load_param(const void* __restrict__ w, int64_t j, int dt) {
+  if (dt == kF32) return static_cast<const float*>(w)[j];
+  if (dt == kF16) return to_f32(static_cast<const _Float16*>(w)[j]);
+  return to_f32(static_cast<const bf16*>(w)[j]);
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_params(const void* __restrict__ w, int64_t col, int64_t d,
+                                            int dt, float (&out)[VEC]) {
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) out[i] = (col + i < d) ? load_param(w, col + i, dt) : 0.0f;
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ x, int64_t ld,
+                                                          const void* __restrict__ w, int wdt,
+                                                          T* __restrict__ y, int64_t n, int64_t d,
+                                                          int L, int64_t rows_per_block) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int G = kWave / L;
+  const int sub = lane / L;
+  const int c = lane % L;
+  const int64_t cw = int64_t(L) * VEC;                 // columns per chunk
+  const int64_t row_beg = int64_t(blockIdx.x) * rows_per_block;
+  const int64_t row_end = min(row_beg + rows_per_block, n);
+  const int64_t step = int64_t(kWavesPerBlock) * G;    // rows per workgroup step
+
+  float w0[VEC];
+  load_params<VEC>(w, int64_t(c) * VEC, d, wdt, w0);
+
+  for (int64_t base = row_beg + int64_t(wave) * G + sub; base < row_end; base += kUnroll * step) {
+    float xv[kUnroll][VEC];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = base + u * step;
+      const int64_t col = int64_t(c) * VEC;
+      if (row < row_end)
+        load_f32_tail<T, VEC>(x + row * ld + col, d - col, 0.0f, xv[u]);
+      else
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) xv[u][i] = 0.0f;
+    }
+    float acc[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a = fmaf(xv[u][i], w0[i], a);
+      acc[u] = a;
+    }
+    // Remaining column chunks (rows wider than 64 * VEC elements).
+    for (int64_t col0 = cw; col0 < d; col0 += cw) {
+      const int64_t col = col0 + int64_t(c) * VEC;
+      float wk[VEC];
+      load_params<VEC>(w, col, d, wdt, wk);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t row = base + u * step;
+        float xk[VEC];
+        if (row < row_end)
+          load_f32_tail<T, VEC>(x + row * ld + col, d - col, 0.0f, xk);
+        else
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) xk[i] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[u] = fmaf(xk[i], wk[i], acc[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float a = acc[u];
+      for (int o = 1; o < L; o <<= 1) a += __shfl_xor(a, o, kWave);
+      const int64_t row = base + u * step;
+      if (c == 0 && row < row_end) y[row] = from_f32<T>(a);
+    }
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
+    const T* __restrict__ dy, const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
+    int wdt, T* __restrict__ dx, int64_t ld_dx, float* __restrict__ P, int64_t n, int64_t d,
+    int L, int64_t rows_per_tile) {
+  __shared__ float red[kWavesPerBlock][kWave * VEC];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int G = kWave / L;
+  const int sub = lane / L;
+  const int c = lane % L;
+  const int64_t tile = blockIdx.x;
+  const int64_t col = int64_t(blockIdx.y) * L * VEC + int64_t(c) * VEC;
+  const int64_t row_beg = tile * rows_per_tile;
+  const int64_t row_end = min(row_beg + rows_per_tile, n);
+  const int64_t step = int64_t(kWavesPerBlock) * G;
+
+  float wr[VEC];
+  load_params<VEC>(w, col, d, wdt, wr);
+  float acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+
+  for (int64_t base = row_beg + int64_t(wave) * G + sub; base < row_end; base += kUnroll * step) {
+    float xv[kUnroll][VEC];
+    float g[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = base + u * step;
+      if (row < row_end) {
+        g[u] = to_f32(dy[row]);
+        load_f32_tail<T, VEC>(x + row * ld_x + col, d - col, 0.0f, xv[u]);
+      } else {
+        g[u] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) xv[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = base + u * step;
+      float gx[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) gx[i] = g[u] * wr[i];
+      if (row < row_end && col < d) store_f32_tail<T, VEC>(dx + row * ld_dx + col, d - col, gx);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(xv[u][i], g[u], acc[i]);
+    }
+  }
+
+  // Lanes c, c + L, c + 2L, ... hold the same columns: butterfly over them.
+#pragma unroll
+  for (int i = 0; i < VEC; ++i)
+    for (int o = L; o < kWave; o <<= 1) acc[i] += __shfl_xor(acc[i], o, kWave);
+  if (sub == 0) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) red[wave][c * VEC + i] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0 && sub == 0) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      float s = red[0][c * VEC + i];
+#pragma unroll
+      for (int k = 1; k < kWavesPerBlock; ++k) s += red[k][c * VEC + i];
+      if (col + i < d) P[tile * d + col + i] = s;
+    }
+  }
+}
+
+int lanes_per_row(int64_t d, int vec) {
+  int L = 1;
+  while (L < kWave && int64_t(L) * vec < d) L <<= 1;
+  return L;
+}
+
+template <typename T>
+hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, int wdt, void* y, int64_t n,
+                     int64_t d, bool vec, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  const int v = vec ? V : 1;
+  const int L = lanes_per_row(d, v);
+  const int64_t rows_per_block = int64_t(kWavesPerBlock) * (kWave / L) * kUnroll * 2;
+  const dim3 grid(unsigned((n + rows_per_block - 1) / rows_per_block));
+  if (vec)
+    ws_fwd_kernel<T, V><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), ld_x, w, wdt,
+                                                  static_cast<T*>(y), n, d, L, rows_per_block);
+  else
+    ws_fwd_kernel<T, 1><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), ld_x, w, wdt,
+                                                  static_cast<T*>(y), n, d, L, rows_per_block);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t bwd_typed(const void* dy, const void* x, int64_t ld_x, const void* w, int wdt,
+                     void* dx, int64_t ld_dx, float* P, int64_t n, int64_t d,
+                     int64_t rows_per_tile, bool vec, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  const int v = vec ? V : 1;
+  const int L = lanes_per_row(d, v);
+  const int64_t cw = int64_t(L) * v;
+  const dim3 grid(unsigned((n + rows_per_tile - 1) / rows_per_tile), unsigned((d + cw - 1) / cw));
+  if (vec)
+    ws_bwd_kernel<T, V><<<grid, kThreads, 0, s>>>(
+        static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
+        ld_dx, P, n, d, L, rows_per_tile);
+  else
+    ws_bwd_kernel<T, 1><<<grid, kThreads, 0, s>>>(
+        static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
+        ld_dx, P, n, d, L, rows_per_tile);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
+                                   int64_t n, int64_t d, int act, int wdt, bool vec,
+                                   hipStream_t s) {
+  switch (act) {
+    case kF32: return fwd_typed<float>(x, ld_x, w, wdt, y, n, d, vec, s);
+    case kF16: return fwd_typed<_Float16>(x, ld_x, w, wdt, y, n, d, vec, s);
+    default: return fwd_typed<bf16>(x, ld_x, w, wdt, y, n, d, vec, s);
+  }
+}
+
+hipError_t launch_weighted_sum_bwd_stage1(const void* dy, const void* x, int64_t ld_x,
+                                          const void* w, void* dx, int64_t ld_dx, float* P,
+                                          int64_t n, int64_t d, int64_t rows_per_tile,
+                                          int act, int wdt, bool vec, hipStream_t s) {
+  switch (act) {
+    case kF32: return bwd_typed<float>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, rows_per_tile, vec, s);
+    case kF16: return bwd_typed<_Float16>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, rows_per_tile, vec, s);
+    default: return bwd_typed<bf16>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, rows_per_tile, vec, s);
+  }
+}
+
+}  // namespace vjp

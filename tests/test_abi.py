@@ -1,0 +1,184 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, sizes workspaces as documented, and rejects bad arguments
+before launching anything (every call here returns before any HIP call).
+Fake device addresses are used only for argument checking and are never
+dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libvjp.h")
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "row_wise_backward_amd", "libvjp.so")
+    if not os.path.exists(lib):
+        subprocess.run(["python", os.path.join(ROOT, "row_wise_backward_amd", "build.py"), "-q"],
+                       check=True)
+
+
+_ensure_built()
+import row_wise_backward_amd as rwb  # noqa: E402
+
+L = rwb.lib
+P = ctypes.c_void_p
+OK, EINVAL, EDTYPE, EALIGN, EWORKSPACE, EALIAS = 0, 1, 2, 3, 4, 5
+A, B, C, D = 0x10000000, 0x20000000, 0x30000000, 0x40000000  # fake, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vjp_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ["vjp_weighted_sum_fwd", "vjp_weighted_sum_bwd", "vjp_scaled_silu_fwd",
+              "vjp_scaled_silu_bwd", "vjp_softmax_fwd", "vjp_softmax_bwd",
+              "vjp_softmax_xent_fwd_bwd"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in libvjp.h but not exported"
+    nm = subprocess.run(["nm", "-D", "--defined-only", rwb.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (vjp_\w+)", nm))
+    assert exported == set(declared_functions()), exported ^ set(declared_functions())
+
+
+def test_binding_covers_every_entry_point():
+    for n in declared_functions():
+        assert n in rwb.EXPORTED and callable(getattr(rwb, n))
+
+
+def test_version_and_strings():
+    assert rwb.vjp_version() == 1
+    assert rwb.vjp_status_string(OK) == "ok"
+    assert "alias" in rwb.vjp_status_string(EALIAS) or "overlap" in rwb.vjp_status_string(EALIAS)
+
+
+def test_tiling_queries():
+    # the worked example: 100 rows in tiles of 32 -> 4 partial rows of 64 fp32
+    assert rwb.vjp_weighted_sum_rows_per_tile(100, 32) == 32
+    assert rwb.vjp_weighted_sum_bwd_workspace_size(100, 64, 32) == 4 * 64 * 4
+    # automatic tiling depends only on the row count
+    assert rwb.vjp_weighted_sum_rows_per_tile(100, 0) == 32
+    assert rwb.vjp_weighted_sum_rows_per_tile(1 << 20, 0) == 512
+    assert rwb.vjp_weighted_sum_bwd_workspace_size(1 << 20, 256, 0) == 2048 * 256 * 4
+    assert rwb.vjp_weighted_sum_rows_per_tile(-1, 0) == -1
+    assert rwb.vjp_scaled_silu_elems_per_tile(1 << 24) == 8192
+    assert rwb.vjp_scaled_silu_bwd_workspace_size(1 << 24) == 2048 * 4
+    assert rwb.vjp_scaled_silu_elems_per_tile(7) == 2048
+    assert rwb.vjp_scaled_silu_bwd_workspace_size(0) == 0
+    assert rwb.vjp_softmax_xent_workspace_size(16384) == 16384 * 4
+
+
+def _ws_fwd(**kw):
+    a = dict(x=A, ld=64, w=B, y=C, n=10, d=64, act=0, wdt=0)
+    a.update(kw)
+    return L.vjp_weighted_sum_fwd(P(a["x"]), a["ld"], P(a["w"]), P(a["y"]), a["n"], a["d"],
+                                  a["act"], a["wdt"], None)
+
+
+def test_weighted_sum_fwd_rejections():
+    assert _ws_fwd(n=-1) == EINVAL
+    assert _ws_fwd(ld=63) == EINVAL
+    assert _ws_fwd(act=3) == EDTYPE
+    assert _ws_fwd(wdt=-1) == EDTYPE
+    assert _ws_fwd(x=0) == EINVAL
+    assert _ws_fwd(x=A + 2) == EALIGN
+    assert _ws_fwd(act=1, x=A + 1) == EALIGN
+    assert _ws_fwd(y=A + 64) == EALIAS                    # y inside x
+    assert _ws_fwd(y=B + 8) == EALIAS                     # y inside w
+    assert "overlaps" in rwb.vjp_last_error()
+
+
+def _ws_bwd(**kw):
+    a = dict(dy=A, x=B, ld=64, w=C, dx=D, ldd=64, dw=D + 0x1000000, acc=0, n=100, d=64, rpt=32,
+             act=0, wdt=0, ws=D + 0x2000000, wsb=1024)
+    a.update(kw)
+    return L.vjp_weighted_sum_bwd(P(a["dy"]), P(a["x"]), a["ld"], P(a["w"]), P(a["dx"]), a["ldd"],
+                                  P(a["dw"]), a["acc"], a["n"], a["d"], a["rpt"], a["act"],
+                                  a["wdt"], P(a["ws"]), a["wsb"], None)
+
+
+def test_weighted_sum_bwd_rejections():
+    assert _ws_bwd(wsb=1023) == EWORKSPACE
+    assert _ws_bwd(ws=0) == EWORKSPACE
+    assert _ws_bwd(ws=D + 0x2000002) == EALIGN
+    assert _ws_bwd(acc=2) == EINVAL
+    assert _ws_bwd(rpt=-3) == EINVAL
+    assert _ws_bwd(dw=0) == EINVAL
+    assert _ws_bwd(dw=D + 0x1000002) == EALIGN
+    assert _ws_bwd(ldd=10) == EINVAL
+    assert _ws_bwd(dx=B + 4) == EALIAS                    # dx over x
+    assert _ws_bwd(dw=D + 8) == EALIAS                    # dw inside dx
+    assert _ws_bwd(ws=A) == EALIAS                        # workspace over dy
+
+
+def _silu_bwd(**kw):
+    a = dict(dy=A, x=B, w=C, dx=D, dw=D + 0x1000000, acc=0, n=1 << 20, act=1,
+             ws=D + 0x2000000, wsb=1 << 20)
+    a.update(kw)
+    return L.vjp_scaled_silu_bwd(P(a["dy"]), P(a["x"]), P(a["w"]), P(a["dx"]), P(a["dw"]), a["acc"],
+                                 a["n"], a["act"], P(a["ws"]), a["wsb"], None)
+
+
+def test_scaled_silu_rejections():
+    assert L.vjp_scaled_silu_fwd(P(A), P(B), P(A + 2), 100, 1, None) == EALIAS
+    assert L.vjp_scaled_silu_fwd(P(A), P(B + 2), P(C), 100, 1, None) == EALIGN
+    assert L.vjp_scaled_silu_fwd(P(A), P(B), P(C), -5, 1, None) == EINVAL
+    assert L.vjp_scaled_silu_fwd(P(A), P(B), P(C), 5, 7, None) == EDTYPE
+    assert _silu_bwd(wsb=4) == EWORKSPACE
+    assert _silu_bwd(w=0) == EINVAL
+    assert _silu_bwd(dx=A + 2) == EALIAS
+
+
+def test_softmax_rejections():
+    assert L.vjp_softmax_fwd(P(A), 100, P(A + 100), 100, 10, 100, 2, None) == EALIAS
+    assert L.vjp_softmax_fwd(P(A), 99, P(B), 100, 10, 100, 2, None) == EINVAL
+    assert L.vjp_softmax_fwd(P(A), 100, P(B), 100, 10, 0, 2, None) == EINVAL   # no columns
+    assert L.vjp_softmax_bwd(P(A), 100, P(B), 100, P(B), 100, 10, 100, 2, None) == EALIAS
+    assert L.vjp_softmax_bwd(P(A), 100, P(B), 100, P(C + 1), 100, 10, 100, 2, None) == EALIGN
+
+
+def _xent(**kw):
+    a = dict(z=A, ld=1000, t=B, rows=10, C=1000, act=2, loss=C, rmax=C + 64, rlse=C + 128,
+             dz=D, ldd=1000, ninv=C + 256, ws=C + 512, wsb=40)
+    a.update(kw)
+    return L.vjp_softmax_xent_fwd_bwd(P(a["z"]), a["ld"], P(a["t"]), a["rows"], a["C"], a["act"],
+                                      ctypes.c_float(0.1), P(a["loss"]), P(a["rmax"]), P(a["rlse"]),
+                                      P(a["dz"]), a["ldd"], P(a["ninv"]), P(a["ws"]), a["wsb"],
+                                      None)
+
+
+def test_softmax_xent_rejections():
+    assert _xent(C=0) == EINVAL
+    assert _xent(wsb=39) == EWORKSPACE
+    assert _xent(rlse=C + 64 + 8) == EALIAS               # row_lse over row_max
+    assert _xent(ninv=C + 2) == EALIGN
+    assert _xent(dz=A + 10) == EALIAS
+    assert _xent(t=0) == EINVAL
+    assert _xent(rmax=0) == EINVAL
+
+
+def test_binding_host_guards():
+    """The binding checks shapes, dtypes and devices before calling the C ABI."""
+    import torch
+
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        rwb.vjp_weighted_sum_fwd(x, torch.zeros(8))        # host tensors never reach a kernel
+    with pytest.raises(ValueError):
+        rwb._ld(torch.zeros(1, 8).expand(4, 8))            # overlapping rows
+    with pytest.raises(ValueError):
+        rwb._ld(torch.zeros(8, 4).t())                     # non-unit inner stride
+    with pytest.raises(ValueError):
+        rwb._expect(torch.zeros(3), (4,), None, torch.device("cpu"), "y")

@@ -1,0 +1,118 @@
+"""Scaled SiLU on the GPU vs the CPU oracle, element by element (calls the C ABI).
+
+Tolerance for dx (16-bit): 2 ulp of the oracle rounded to the dtype, or, where
+s + x s (1 - s) cancels (x near -1.28), |g - o| <= 2 ulp(o) + F with
+F = (|x| + 8)^2 u |dy w| (s + |x| s): the sigmoid is evaluated as
+1 / (1 + 2^(-x log2 e)) in fp32, whose relative error grows with |x| through
+the rounding of the exponent argument; the square bounds that error times
+the |x| factor of the silu term.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, Guarded, to_dev, to_host
+from oracle.compare import U32, pointwise, reduced
+from synth.workloads import SILU_16M
+
+pytestmark = pytest.mark.gpu
+sl = oracle.scaled_silu
+
+
+def _dx_bounds(x64, dy64, w):
+    s = sl.sigmoid(x64)
+    S = np.abs(dy64 * w) * (s + np.abs(x64) * s)
+    return S, (np.abs(x64) + 8.0) ** 2 * U32 * S
+
+
+def check(rwb, x, dy, w, act, accumulate=False, offset=0, name="scaled_silu"):
+    n = x.size
+    x64, dy64 = synth.to_f64(x, act), synth.to_f64(dy, act)
+    print(f"\n[{name}] n={n} act={act} off={offset} acc={accumulate}", flush=True)
+    tdt = synth.torch_dtype(act)
+    xb = torch.zeros(n + offset, dtype=tdt, device=DEV)
+    xb[offset:] = to_dev(x, act)
+    gb = torch.zeros(n + offset, dtype=tdt, device=DEV)
+    gb[offset:] = to_dev(dy, act)
+    xd, dyd = xb[offset:], gb[offset:]
+    wd = torch.tensor([w], dtype=torch.float32, device=DEV)
+    yg = Guarded(n, tdt)
+    rwb.vjp_scaled_silu_fwd(xd, wd, y=yg.t)
+    dxg = Guarded(n, tdt)
+    dwg = Guarded(1, torch.float32, fill=2.5 if accumulate else 0.0)
+    need = rwb.vjp_scaled_silu_bwd_workspace_size(n)
+    wsg = Guarded(need // 4, torch.float32)
+    rwb.vjp_scaled_silu_bwd(dyd, xd, wd, dx=dxg.t, dw=dwg.t, accumulate=accumulate, workspace=wsg.t)
+    torch.cuda.synchronize()
+    assert yg.intact() and dxg.intact() and dwg.intact() and wsg.intact(), "write outside an output"
+
+    reps = []
+    y_ref = sl.fwd(x64, w)
+    reps.append(pointwise(to_host(yg.t, act), y_ref, act, name="y"))
+    dx_ref, dw_ref = sl.bwd(dy64, x64, w, dw_old=2.5 if accumulate else None)
+    S, F = _dx_bounds(x64, dy64, w)
+    reps.append(pointwise(to_host(dxg.t, act), dx_ref, act, S=S, floor=F, name="dx"))
+    reps.append(reduced(to_host(dwg.t, "f32"), np.array([dw_ref]), name="dw"))
+    if n > 0:
+        ept = rwb.vjp_scaled_silu_elems_per_tile(n)
+        P_ref = sl.partials(dy64, x64, ept)
+        Pa = sl.partials(np.abs(dy64), np.abs(x64), ept)
+        reps.append(pointwise(to_host(wsg.t, "f32"), P_ref, "f32", S=Pa, name="partials"))
+    for r in reps:
+        print("   ", r, flush=True)
+    assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+
+
+@pytest.mark.parametrize("n", [1, 7, 1023, 2048, 8193, 100003])
+@pytest.mark.parametrize("act", ["f16", "bf16", "f32"])
+def test_sizes_dtypes(gpu_lib, n, act):
+    x = synth.normal((n,), 2.0, act, 31 + n, synth.STREAM_X)
+    dy = synth.normal((n,), 1.0, act, 31 + n, synth.STREAM_DY)
+    check(gpu_lib, x, dy, 0.75, act)
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_unaligned_and_accumulate(gpu_lib, act):
+    n = 50001
+    x = synth.normal((n,), 2.0, act, 41, synth.STREAM_X)
+    dy = synth.normal((n,), 1.0, act, 41, synth.STREAM_DY)
+    check(gpu_lib, x, dy, -1.5, act, offset=1)
+    check(gpu_lib, x, dy, 0.75, act, accumulate=True)
+
+
+def test_extreme_inputs(gpu_lib):
+    """Saturated sigmoid on both sides, zeros, and the fp16 range ends."""
+    x = np.array([0.0, -0.0, 1e-7, -1e-7, 15.0, -15.0, 60000.0, -60000.0, 11.5, -17.25,
+                  -1.2785, 6e-8, -6e-8] * 3, dtype=np.float16)
+    dy = np.linspace(-2, 2, x.size).astype(np.float16)
+    check(gpu_lib, x, dy, 0.75, "f16")
+
+
+def test_swamping_gpu(gpu_lib):
+    """32,768 contributions of about 1e-3: the fp32 two-stage dw matches the oracle to 1e-4."""
+    n = 32768
+    x = np.full(n, 4.0, dtype=np.float32)
+    g = np.random.default_rng(0)
+    s = sl.sigmoid(x.astype(np.float64))
+    dy = (1e-3 * (1 + 0.1 * g.standard_normal(n)) / (4.0 * s)).astype(np.float32)
+    check(gpu_lib, x, dy, 0.75, "f32", name="swamping")
+
+
+def test_empty(gpu_lib):
+    x = torch.empty(0, dtype=torch.float16, device=DEV)
+    w = torch.tensor([0.75], device=DEV)
+    gpu_lib.vjp_scaled_silu_fwd(x, w)
+    dx, dw = gpu_lib.vjp_scaled_silu_bwd(x, x, w)
+    torch.cuda.synchronize()
+    assert dx.numel() == 0 and dw.item() == 0.0
+
+
+@pytest.mark.parametrize("n", [1 << 24, (1 << 24) - 3])
+def test_full_size(gpu_lib, n):
+    """The n = 2^24 fp16 workload (and a ragged n = 2^24 - 3) compared in full."""
+    c = SILU_16M
+    x = synth.normal((n,), c.sigma_x, c.dtype, c.seed, synth.STREAM_X)
+    dy = synth.normal((n,), c.sigma_dy, c.dtype, c.seed, synth.STREAM_DY)
+    check(gpu_lib, x, dy, c.w_value, c.dtype, name="scaled_silu full")

@@ -1,0 +1,169 @@
+"""Weighted sum on the GPU vs the CPU oracle, element by element (calls the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, Guarded, empty_padded, padded, pick_rows, to_dev, to_host
+from oracle.compare import U32, exact, pointwise, reduced
+from synth.workloads import WS_LARGE, WS_SMALL
+
+pytestmark = pytest.mark.gpu
+ws = oracle.weighted_sum
+
+
+def _inputs(n, d, act, wdt, seed, sigma_w=1.0):
+    x = synth.normal((n, d), 1.0, act, seed, synth.STREAM_X)
+    w = synth.normal((d,), sigma_w, wdt, seed, synth.STREAM_W)
+    dy = synth.normal((n,), 1.0, act, seed, synth.STREAM_DY)
+    return x, w, dy
+
+
+def _dx_is_one_rounding(act, wdt):
+    # dy * w is exact in fp32 unless a 16-bit activation meets an fp32 weight
+    return act == "f32" or wdt != "f32"
+
+
+def run_case(rwb, n, d, act, wdt, seed, ld=None, offset=0, rows_per_tile=0, accumulate=False):
+    x, w, dy = _inputs(n, d, act, wdt, seed)
+    x64, w64, dy64 = synth.to_f64(x, act), synth.to_f64(w, wdt), synth.to_f64(dy, act)
+    print(f"\n[weighted_sum] n={n} d={d} act={act} w={wdt} ld={ld} off={offset} "
+          f"rpt={rows_per_tile} acc={accumulate}", flush=True)
+    xd = padded(x, act, ld, offset)
+    wd = to_dev(w, wdt)
+    dyd = to_dev(dy, act)
+    yg = Guarded(n, synth.torch_dtype(act))
+    rwb.vjp_weighted_sum_fwd(xd, wd, y=yg.t)
+    dx, _ = empty_padded(n, d, act, ld, offset)
+    g = np.random.default_rng(seed)
+    old = g.standard_normal(d).astype(np.float32)
+    dwg = Guarded(d, torch.float32, fill=0.0)
+    if accumulate:
+        dwg.t.copy_(torch.from_numpy(old))
+    need = rwb.vjp_weighted_sum_bwd_workspace_size(n, d, rows_per_tile)
+    wsg = Guarded(need // 4, torch.float32)
+    rwb.vjp_weighted_sum_bwd(dyd, xd, wd, dx=dx, dw=dwg.t, accumulate=accumulate,
+                             rows_per_tile=rows_per_tile, workspace=wsg.t)
+    torch.cuda.synchronize()
+    assert yg.intact() and dwg.intact() and wsg.intact(), "write outside an output"
+
+    reps = []
+    S = ws.fwd(np.abs(x64), np.abs(w64))
+    reps.append(pointwise(to_host(yg.t, act), ws.fwd(x64, w64), act, S=S,
+                          floor=d * U32 * S, name="y"))
+    gx_ref, gw_ref = ws.bwd(dy64, x64, w64, grad_w_old=old.astype(np.float64) if accumulate else None)
+    from oracle.rounding import round_to, to_storage
+    dx_host = to_host(dx, act)
+    if _dx_is_one_rounding(act, wdt):
+        reps.append(exact(dx_host, to_storage(round_to(gx_ref, act), act), act, name="dx"))
+    else:
+        reps.append(pointwise(dx_host, gx_ref, act, name="dx"))
+    reps.append(reduced(to_host(dwg.t, "f32"), gw_ref, name="dw"))
+    rpt = rwb.vjp_weighted_sum_rows_per_tile(n, rows_per_tile)
+    if n > 0 and d > 0:
+        P = to_host(wsg.t, "f32").reshape(-1, d)
+        P_ref = ws.partials(x64, dy64, rpt)
+        assert P.shape == P_ref.shape
+        reps.append(pointwise(P, P_ref, "f32", S=ws.partials(np.abs(x64), np.abs(dy64), rpt),
+                              name="partials"))
+    for r in reps:
+        print("   ", r, flush=True)
+    assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+    return reps
+
+
+def test_worked_tiling_case(gpu_lib):
+    """100 rows, tiles of 32 rows, D = 64, fp32: four partial rows of 64, then grad_w [64]."""
+    c = WS_SMALL
+    assert gpu_lib.vjp_weighted_sum_bwd_workspace_size(100, 64, 32) == 4 * 64 * 4
+    run_case(gpu_lib, 100, 64, "f32", "f32", c.seed, rows_per_tile=32)
+    run_case(gpu_lib, 100, 64, "f32", "f32", c.seed, rows_per_tile=32, accumulate=True)
+
+
+SHAPES = [(1, 1), (7, 7), (7, 64), (1, 256), (333, 256), (1000, 100), (257, 600), (64, 1030),
+          (2049, 33)]
+DTYPES = [("f32", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32"),
+          ("f32", "bf16")]
+
+
+@pytest.mark.parametrize("n,d", SHAPES)
+@pytest.mark.parametrize("act,wdt", DTYPES)
+def test_shapes_dtypes(gpu_lib, n, d, act, wdt):
+    run_case(gpu_lib, n, d, act, wdt, seed=7 + n + d)
+
+
+@pytest.mark.parametrize("n,d", [(7, 64), (333, 256), (257, 600)])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["padded_ld", "unaligned"])
+def test_layouts(gpu_lib, n, d, act, layout):
+    ld, off = (d + 8, 0) if layout == "padded_ld" else (d + 1, 1)
+    run_case(gpu_lib, n, d, act, act, seed=11 + d, ld=ld, offset=off)
+
+
+@pytest.mark.parametrize("rpt", [1, 7, 32, 100, 5000])
+def test_rows_per_tile(gpu_lib, rpt):
+    run_case(gpu_lib, 1000, 64, "bf16", "bf16", seed=13, rows_per_tile=rpt, accumulate=True)
+
+
+def test_batch1_vs_batch7(gpu_lib):
+    """A missing batch reduction passes at batch 1 and fails at batch 7."""
+    run_case(gpu_lib, 1, 64, "f32", "f32", seed=17)
+    run_case(gpu_lib, 7, 64, "f32", "f32", seed=17)
+
+
+def test_empty_batch(gpu_lib):
+    x = torch.empty((0, 64), dtype=torch.float32, device=DEV)
+    w = torch.ones(64, dtype=torch.float32, device=DEV)
+    y = gpu_lib.vjp_weighted_sum_fwd(x, w)
+    assert y.shape == (0,)
+    dw = torch.full((64,), 3.0, device=DEV)
+    gpu_lib.vjp_weighted_sum_bwd(torch.empty(0, device=DEV), x, w, dw=dw, accumulate=True)
+    torch.cuda.synchronize()
+    assert bool((dw == 3.0).all())
+    gpu_lib.vjp_weighted_sum_bwd(torch.empty(0, device=DEV), x, w, dw=dw, accumulate=False)
+    torch.cuda.synchronize()
+    assert bool((dw == 0.0).all())
+
+
+def test_large_batch_full_size(gpu_lib):
+    """The 1,048,576 x 256 bf16 workload in the benchmark's launch configuration:
+    grad_w and every tile partial in full, y and grad_x on sampled rows."""
+    c = WS_LARGE
+    n, d = c.shape
+    x = synth.normal((n, d), c.sigma_x, c.dtype, c.seed, synth.STREAM_X)
+    w = synth.normal((d,), c.sigma_w, c.w_dtype, c.seed, synth.STREAM_W)
+    dy = synth.normal((n,), c.sigma_dy, c.dtype, c.seed, synth.STREAM_DY)
+    print(f"\n[weighted_sum full] {n}x{d} bf16", flush=True)
+    xd, wd, dyd = to_dev(x, "bf16").view(n, d), to_dev(w, "bf16"), to_dev(dy, "bf16")
+    y = gpu_lib.vjp_weighted_sum_fwd(xd, wd)
+    dx, dw = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd)
+    rpt = gpu_lib.vjp_weighted_sum_rows_per_tile(n, 0)
+    need = gpu_lib.vjp_weighted_sum_bwd_workspace_size(n, d, 0)
+    wsb = torch.empty(need // 4, dtype=torch.float32, device=DEV)
+    dx2, dw2 = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd, workspace=wsb)
+    torch.cuda.synchronize()
+    assert rpt == 512 and need == 2048 * 256 * 4
+
+    w64, dy64 = synth.to_f64(w, "bf16"), synth.to_f64(dy, "bf16")
+    rows = pick_rows(n, 4096, 1)
+    xs = synth.to_f64(x[rows], "bf16")
+    S = ws.fwd(np.abs(xs), np.abs(w64))
+    y_host = to_host(y, "bf16")[rows]
+    r_y = pointwise(y_host, ws.fwd(xs, w64), "bf16", S=S, floor=d * U32 * S, name="y(sampled)")
+    from oracle.rounding import round_to, to_storage
+    gx_ref, _ = ws.bwd(dy64[rows], xs, w64)
+    r_dx = exact(to_host(dx, "bf16")[rows], to_storage(round_to(gx_ref, "bf16"), "bf16"), "bf16",
+                 name="dx(sampled)")
+    # grad_w and the stage-1 partials over all rows, from the oracle's partials
+    P_ref = np.concatenate([ws.partials(synth.to_f64(x[i:i + 65536], "bf16"), dy64[i:i + 65536], rpt)
+                            for i in range(0, n, 65536)])
+    Pa = np.concatenate([ws.partials(np.abs(synth.to_f64(x[i:i + 65536], "bf16")), np.abs(dy64[i:i + 65536]), rpt)
+                         for i in range(0, n, 65536)])
+    r_P = pointwise(to_host(wsb, "f32").reshape(-1, d), P_ref, "f32", S=Pa, name="partials")
+    r_dw = reduced(to_host(dw2, "f32"), P_ref.sum(axis=0), name="dw")
+    for r in (r_y, r_dx, r_P, r_dw):
+        print("   ", r, flush=True)
+    assert r_y.ok and r_dx.ok and r_P.ok and r_dw.ok
+    # determinism: two calls, bitwise identical
+    assert torch.equal(dw, dw2) and torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
