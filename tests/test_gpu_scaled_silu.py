@@ -54,7 +54,8 @@ def check(rwb, x, dy, w, act, accumulate=False, offset=0, name="scaled_silu"):
     dx_ref, dw_ref = sl.bwd(dy64, x64, w, dw_old=2.5 if accumulate else None)
     S, F = _dx_bounds(x64, dy64, w)
     reps.append(pointwise(to_host(dxg.t, act), dx_ref, act, S=S, floor=F, name="dx"))
-    reps.append(reduced(to_host(dwg.t, "f32"), np.array([dw_ref]), name="dw"))
+    s_abs = float(np.sum(np.abs(dy64 * x64 * sl.sigmoid(x64)))) + (2.5 if accumulate else 0.0)
+    reps.append(reduced(to_host(dwg.t, "f32"), np.array([dw_ref]), name="dw", S=[s_abs]))
     if n > 0:
         ept = rwb.vjp_scaled_silu_elems_per_tile(n)
         P_ref = sl.partials(dy64, x64, ept)
