@@ -86,7 +86,7 @@ def bytes_xent(r, c, es=2):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(scale: float = 1.0):
+def cpu_baseline(scale: float = 1.0, min_seconds: float = 10.0):
     """The oracle (fp64 numpy, one thread) on a bounded sample of each workload."""
     import numpy as np
 
@@ -115,17 +115,24 @@ def cpu_baseline(scale: float = 1.0):
                    + bytes_weighted_sum_fwd(n_ws, 256) + bytes_weighted_sum_bwd(n_ws, 256, 1)
                    + bytes_softmax_fwd(r_sm, 4096) + bytes_softmax_bwd(r_sm, 4096)
                    + bytes_xent(r_xe, 32000))
+    # the whole sample is repeated until at least `min_seconds` of CPU work is timed
+    reps = 0
     t0 = time.perf_counter()
-    x64, g64 = synth.to_f64(x, "f16"), synth.to_f64(g, "f16")
-    oracle.scaled_silu.fwd(x64, 0.75)
-    oracle.scaled_silu.bwd(g64, x64, 0.75)
-    xw64, ww64, gw64 = synth.to_f64(xw, "bf16"), synth.to_f64(ww, "bf16"), synth.to_f64(gw, "bf16")
-    oracle.weighted_sum.fwd(xw64, ww64)
-    oracle.weighted_sum.bwd(gw64, xw64, ww64)
-    ys = oracle.softmax.fwd(synth.to_f64(xs, "bf16"))
-    oracle.softmax.bwd(synth.to_f64(gs, "bf16"), ys)
-    oracle.softmax_xent.fwd_bwd(synth.to_f64(z, "bf16"), t, 1.0 / 16384)
-    dt = time.perf_counter() - t0
+    while True:
+        x64, g64 = synth.to_f64(x, "f16"), synth.to_f64(g, "f16")
+        oracle.scaled_silu.fwd(x64, 0.75)
+        oracle.scaled_silu.bwd(g64, x64, 0.75)
+        xw64, ww64, gw64 = synth.to_f64(xw, "bf16"), synth.to_f64(ww, "bf16"), synth.to_f64(gw, "bf16")
+        oracle.weighted_sum.fwd(xw64, ww64)
+        oracle.weighted_sum.bwd(gw64, xw64, ww64)
+        ys = oracle.softmax.fwd(synth.to_f64(xs, "bf16"))
+        oracle.softmax.bwd(synth.to_f64(gs, "bf16"), ys)
+        oracle.softmax_xent.fwd_bwd(synth.to_f64(z, "bf16"), t, 1.0 / 16384)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    total_bytes *= reps
     if limiter is not None and hasattr(limiter, "unregister"):
         limiter.unregister()
     return {
@@ -135,7 +142,7 @@ def cpu_baseline(scale: float = 1.0):
         "kind": "oracle",
         "sample": (f"fwd+bwd of scaled_silu n={n_silu}, weighted_sum {n_ws}x256, softmax "
                    f"{r_sm}x4096, softmax_xent {r_xe}x32000 (same distributions and seeds), "
-                   f"fp64 numpy, input decode included; {dt:.1f} s"),
+                   f"fp64 numpy, input decode included; {reps} repetitions, {dt:.1f} s"),
     }
 
 

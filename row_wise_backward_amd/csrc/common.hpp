@@ -36,9 +36,45 @@ template <typename T, int N> struct alignas(sizeof(T) * N) Vec {
   T v[N];
 };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Streaming accesses: data read or written exactly once by the kernel are
+// moved with the nontemporal hint, which on gfx950 lets a 128-bit load stream
+// reach close to the HBM peak instead of being held in the caches.
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> load_stream(const T* __restrict__ p) {
+  constexpr int kBytes = sizeof(T) * N;
+  if constexpr (kBytes == 16) {
+    return __builtin_bit_cast(Vec<T, N>, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  } else if constexpr (kBytes == 8) {
+    return __builtin_bit_cast(Vec<T, N>, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
+  } else if constexpr (kBytes == 4) {
+    return __builtin_bit_cast(Vec<T, N>, __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p)));
+  } else {
+    static_assert(kBytes == 2, "unsupported vector width");
+    return __builtin_bit_cast(Vec<T, N>, __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p)));
+  }
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void store_stream(T* __restrict__ p, const Vec<T, N>& v) {
+  constexpr int kBytes = sizeof(T) * N;
+  if constexpr (kBytes == 16) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
+  } else if constexpr (kBytes == 8) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2_t, v), reinterpret_cast<u32x2_t*>(p));
+  } else if constexpr (kBytes == 4) {
+    __builtin_nontemporal_store(__builtin_bit_cast(unsigned, v), reinterpret_cast<unsigned*>(p));
+  } else {
+    static_assert(kBytes == 2, "unsupported vector width");
+    __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, v), reinterpret_cast<unsigned short*>(p));
+  }
+}
+
 template <typename T, int N>
 __device__ __forceinline__ void load_f32(const T* __restrict__ p, float (&out)[N]) {
-  Vec<T, N> r = *reinterpret_cast<const Vec<T, N>*>(p);
+  const Vec<T, N> r = load_stream<T, N>(p);
 #pragma unroll
   for (int i = 0; i < N; ++i) out[i] = to_f32(r.v[i]);
 }
@@ -48,7 +84,7 @@ __device__ __forceinline__ void store_f32(T* __restrict__ p, const float (&in)[N
   Vec<T, N> r;
 #pragma unroll
   for (int i = 0; i < N; ++i) r.v[i] = from_f32<T>(in[i]);
-  *reinterpret_cast<Vec<T, N>*>(p) = r;
+  store_stream<T, N>(p, r);
 }
 
 // Guarded variants for the ragged end of a row or array: a full vector when
@@ -77,20 +113,50 @@ __device__ __forceinline__ void store_f32_tail(T* __restrict__ p, int64_t avail,
 }
 
 // ------------------------------------------------------------------ wave reductions
-// Butterfly over lanes that differ in bits [lo, 64): every lane ends with the
-// same bitwise result (each step adds the same two operands on both sides).
+// Full-wave reductions on DPP.  Within each row of 16 lanes: swap neighbours
+// (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror the half-row,
+// mirror the row -- after these four steps every lane of a row holds the row
+// total, and because each step adds the same two operands on both sides the
+// lanes of a row agree bitwise.  The four row totals are then read from lanes
+// 0, 16, 32 and 48 and combined as (r0 + r1) + (r2 + r3), so every lane of the
+// wave receives the same value in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppSwap1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<kDppSwap1>(v);
+  v += dpp_f32<kDppSwap2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppSwap1>(v));
+  v = fmaxf(v, dpp_f32<kDppSwap2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+               fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+// Butterfly over lanes that differ in bits [LO, 64) (lanes sharing the low
+// bits are combined): every lane ends with the same bitwise result.
 template <int LO = 1>
 __device__ __forceinline__ float wave_sum_from(float v) {
 #pragma unroll
   for (int o = LO; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) { return wave_sum_from<1>(v); }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
 

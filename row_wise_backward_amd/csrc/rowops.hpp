@@ -3,19 +3,22 @@
 //
 // Resident layout.  A row is owned by WAVES waves (WAVES = 1: one wave per
 // row, four rows per 256-thread workgroup).  Lane `lane` of wave `wv` holds
-// kChunks vectors of VEC elements; vector k starts at column
+// K vectors of VEC elements; vector k starts at column
 //   (k * WAVES * 64 + wv * 64 + lane) * VEC,
 // so each step k reads WAVES * 64 * VEC contiguous elements (1 KB per wave
-// for 16-byte vectors).  Capacity: WAVES * 64 * kChunks * VEC columns.  The
-// whole row stays in VGPRs between the statistics pass and the output pass,
-// so it is read from HBM exactly once.
+// for 16-byte vectors).  Capacity: WAVES * 64 * K * VEC columns.  The whole
+// row stays in VGPRs (as loaded, in its storage type) between the statistics
+// pass and the output pass, so it is read from HBM exactly once.
 #pragma once
 
 #include "common.hpp"
 
 namespace vjp {
 
-constexpr int kChunks = 8;
+template <int WAVES> constexpr int row_block_threads() { return WAVES == 1 ? 256 : WAVES * kWave; }
+
+// Launch geometry of a resident row kernel: rows per workgroup and grid size.
+template <int WAVES> constexpr int rows_per_block() { return WAVES == 1 ? 256 / kWave : 1; }
 
 template <typename T> __device__ __forceinline__ T neg_inf_of();
 template <> __device__ __forceinline__ float neg_inf_of<float>() { return -__builtin_inff(); }
@@ -32,7 +35,7 @@ template <typename T, int VEC>
 __device__ __forceinline__ bool load_row_vec(const T* __restrict__ row, int64_t col, int64_t cols,
                                              T fill, Vec<T, VEC>& r) {
   if (col + VEC <= cols) {
-    r = *reinterpret_cast<const Vec<T, VEC>*>(row + col);
+    r = load_stream<T, VEC>(row + col);
     return true;
   }
 #pragma unroll
@@ -84,6 +87,96 @@ __device__ __forceinline__ float row_reduce_sum(float v, float* buf) {
 __device__ __forceinline__ float exp2_denorm_safe(float t) {
   return t < -126.0f ? exp2_fast(t + 64.0f) * 5.421010862427522e-20f /* 2^-64 */
                      : exp2_fast(t);
+}
+
+// e[i] = exp(x_i - m) for one vector of a row, x_i as stored.  Lanes whose
+// row range can produce results below 2^-126 (flagged by `safe`) take the
+// subnormal-preserving form; the two forms agree wherever both are exact.
+template <typename T, int VEC>
+__device__ __forceinline__ void exp_vec(const Vec<T, VEC>& r, float m, bool safe,
+                                        float (&e)[VEC]) {
+  if (!safe) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) e[i] = exp2_fast((to_f32(r.v[i]) - m) * kLog2e);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) e[i] = exp2_denorm_safe((to_f32(r.v[i]) - m) * kLog2e);
+  }
+}
+
+// Loads the lane's K vectors of a row (padding reads as -inf) and returns the
+// lane's max over its elements and min over its valid elements.
+template <typename T, int VEC, int WAVES, int K>
+__device__ __forceinline__ void load_row_minmax(const T* __restrict__ row, int64_t cols,
+                                                int64_t lane_col, Vec<T, VEC> (&raw)[K],
+                                                float& mx, float& mn) {
+  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
+  mx = -__builtin_inff();
+  mn = __builtin_inff();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (k * kStep < cols) {
+      const int64_t col = k * kStep + lane_col;
+      if (load_row_vec<T, VEC>(row, col, cols, neg_inf_of<T>(), raw[k])) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float f = to_f32(raw[k].v[i]);
+          mx = fmaxf(mx, f);
+          mn = fminf(mn, f);
+        }
+      } else {  // ragged end of the row: padding counts for neither max nor min
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float f = to_f32(raw[k].v[i]);
+          mx = fmaxf(mx, f);
+          mn = fminf(mn, col + i < cols ? f : __builtin_inff());
+        }
+      }
+    }
+  }
+}
+
+// Register barrier on a loaded vector: the compiler must treat its contents
+// as new, so values converted from it in an earlier phase are not kept alive
+// for reuse.  This keeps only the packed storage-type row in VGPRs between
+// phases (the conversion is redone, one VALU op per element) and raises the
+// number of rows in flight per CU.  Emits no instruction.
+template <typename T, int N>
+__device__ __forceinline__ void fence_vec(Vec<T, N>& r) {
+  constexpr int kBytes = sizeof(T) * N;
+  if constexpr (kBytes == 16) {
+    u32x4_t u = __builtin_bit_cast(u32x4_t, r);
+    asm volatile("" : "+v"(u));
+    r = __builtin_bit_cast(Vec<T, N>, u);
+  } else if constexpr (kBytes == 8) {
+    u32x2_t u = __builtin_bit_cast(u32x2_t, r);
+    asm volatile("" : "+v"(u));
+    r = __builtin_bit_cast(Vec<T, N>, u);
+  } else if constexpr (kBytes == 4) {
+    unsigned u = __builtin_bit_cast(unsigned, r);
+    asm volatile("" : "+v"(u));
+    r = __builtin_bit_cast(Vec<T, N>, u);
+  }
+}
+
+template <typename T, int VEC, int K>
+__device__ __forceinline__ void fence_row(Vec<T, VEC> (&raw)[K]) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) fence_vec<T, VEC>(raw[k]);
+}
+
+// Whether a lane needs the subnormal-preserving exponential: its smallest
+// element lies more than 126 binades below the row max.
+__device__ __forceinline__ bool needs_denorm_exp(float lane_min, float m) {
+  return (lane_min - m) * kLog2e < -126.0f;
+}
+
+// Smallest WAVES in {1, 2, 4, 8} whose resident capacity with K vectors per
+// lane holds `cols`; 0 means the row needs the streaming path.
+inline int resident_waves(int64_t cols, int vec, int k) {
+  for (int w = 1; w <= 8; w <<= 1)
+    if (int64_t(w) * kWave * k * vec >= cols) return w;
+  return 0;
 }
 
 // Streaming-path workgroup: 256 threads per row.

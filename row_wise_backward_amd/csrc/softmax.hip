@@ -10,7 +10,7 @@
 // "Save vs recompute": the row max is a one-scalar-per-row statistic the
 // forward recomputes on chip.
 //
-// Resident path (rows up to 8 waves * 64 * 8 * VEC columns): the row is read
+// Resident path (rows up to 8 waves * 64 * K * VEC columns): the row is read
 // once into VGPRs (layout in rowops.hpp), the statistics are reduced with
 // wave butterflies and, for multi-wave rows, LDS in wave order, and the
 // output pass works from the registers.  Streaming path (wider rows): 256
@@ -23,98 +23,79 @@ namespace vjp {
 
 namespace {
 
-template <int WAVES> constexpr int block_threads() { return WAVES == 1 ? 256 : WAVES * kWave; }
-
-template <typename T, int VEC, int WAVES>
-__global__ __launch_bounds__(block_threads<WAVES>()) void softmax_fwd_resident(
+// Forward, resident.  KEEP = true holds exp(x - m) in fp32 VGPRs between
+// the sum and the output pass; KEEP = false recomputes it from the stored row
+// (more VALU work, far fewer VGPRs, so more rows in flight per CU).  Both
+// produce bitwise identical results.
+template <typename T, int VEC, int WAVES, int K, bool KEEP>
+__global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_fwd_resident(
     const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y, int64_t rows,
     int64_t cols) {
   __shared__ float buf[WAVES];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * 4 + wave : int64_t(blockIdx.x);
+  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
+                                 : int64_t(blockIdx.x);
   const int wv = WAVES == 1 ? 0 : wave;
   if (WAVES == 1 && row >= rows) return;
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
   const int64_t lane_col = (int64_t(wv) * kWave + lane) * VEC;
-  const T* xr = x + row * ld_x;
 
-  Vec<T, VEC> raw[kChunks];
-  float mx = -__builtin_inff(), mn = __builtin_inff();
-#pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
-    if (k * kStep < cols) {
-      const int64_t col = k * kStep + lane_col;
-      if (load_row_vec<T, VEC>(xr, col, cols, neg_inf_of<T>(), raw[k])) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float f = to_f32(raw[k].v[i]);
-          mx = fmaxf(mx, f);
-          mn = fminf(mn, f);
-        }
-      } else {  // ragged end of the row: padding counts for neither max nor min
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float f = to_f32(raw[k].v[i]);
-          mx = fmaxf(mx, f);
-          mn = fminf(mn, col + i < cols ? f : __builtin_inff());
-        }
-      }
-    }
-  }
+  Vec<T, VEC> raw[K];
+  float mx, mn;
+  load_row_minmax<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, raw, mx, mn);
   const float m = row_reduce_max<WAVES>(mx, buf);
+  const bool safe = needs_denorm_exp(mn, m);
+  fence_row<T, VEC, K>(raw);
 
-  float e[kChunks][VEC];
+  float keep[KEEP ? K : 1][VEC];
   float l = 0.0f;
-  if (!((mn - m) * kLog2e < -126.0f)) {
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      if (k * kStep < cols) {
+  for (int k = 0; k < K; ++k) {
+    if (k * kStep < cols) {
+      float e[VEC];
+      exp_vec<T, VEC>(raw[k], m, safe, e);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          e[k][i] = exp2_fast((to_f32(raw[k].v[i]) - m) * kLog2e);
-          l += e[k][i];
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      if (k * kStep < cols) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          e[k][i] = exp2_denorm_safe((to_f32(raw[k].v[i]) - m) * kLog2e);
-          l += e[k][i];
-        }
+      for (int i = 0; i < VEC; ++i) {
+        l += e[i];
+        if constexpr (KEEP) keep[k][i] = e[i];
       }
     }
   }
   l = row_reduce_sum<WAVES>(l, buf);
   const float inv = 1.0f / l;
+  if constexpr (!KEEP) fence_row<T, VEC, K>(raw);
 
   T* yr = y + row * ld_y;
 #pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
+  for (int k = 0; k < K; ++k) {
     if (k * kStep < cols) {
       const int64_t col = k * kStep + lane_col;
       if (col < cols) {
         float o[VEC];
+        if constexpr (KEEP) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) o[i] = e[k][i] * inv;
+          for (int i = 0; i < VEC; ++i) o[i] = keep[k][i];
+        } else {
+          exp_vec<T, VEC>(raw[k], m, safe, o);
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] *= inv;
         store_row_vec<T, VEC>(yr, col, cols, o);
       }
     }
   }
 }
 
-template <typename T, int VEC, int WAVES>
-__global__ __launch_bounds__(block_threads<WAVES>()) void softmax_bwd_resident(
+template <typename T, int VEC, int WAVES, int K>
+__global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_resident(
     const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ y, int64_t ld_y,
     T* __restrict__ dx, int64_t ld_dx, int64_t rows, int64_t cols) {
   __shared__ float buf[WAVES];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * 4 + wave : int64_t(blockIdx.x);
+  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
+                                 : int64_t(blockIdx.x);
   const int wv = WAVES == 1 ? 0 : wave;
   if (WAVES == 1 && row >= rows) return;
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
@@ -122,9 +103,9 @@ __global__ __launch_bounds__(block_threads<WAVES>()) void softmax_bwd_resident(
   const T* gr = dy + row * ld_dy;
   const T* yr = y + row * ld_y;
 
-  Vec<T, VEC> rg[kChunks], ry[kChunks];
+  Vec<T, VEC> rg[K], ry[K];
 #pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
+  for (int k = 0; k < K; ++k) {
     if (k * kStep < cols) {
       const int64_t col = k * kStep + lane_col;
       load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), rg[k]);
@@ -133,17 +114,19 @@ __global__ __launch_bounds__(block_threads<WAVES>()) void softmax_bwd_resident(
   }
   float s = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
+  for (int k = 0; k < K; ++k) {
     if (k * kStep < cols) {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(rg[k].v[i]), to_f32(ry[k].v[i]), s);
     }
   }
   s = row_reduce_sum<WAVES>(s, buf);
+  fence_row<T, VEC, K>(rg);
+  fence_row<T, VEC, K>(ry);
 
   T* dr = dx + row * ld_dx;
 #pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
+  for (int k = 0; k < K; ++k) {
     if (k * kStep < cols) {
       const int64_t col = k * kStep + lane_col;
       if (col < cols) {
@@ -211,12 +194,30 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream(
   }
 }
 
-// Smallest WAVES in {1, 2, 4, 8} whose resident capacity holds `cols`;
-// 0 means the row needs the streaming path.
-int resident_waves(int64_t cols, int vec) {
-  for (int w = 1; w <= 8; w <<= 1)
-    if (int64_t(w) * kWave * kChunks * vec >= cols) return w;
-  return 0;
+// Launch tiers, smallest first: (waves per row, vectors per lane, keep the
+// exponentials in VGPRs).  The first tier whose capacity WAVES * 64 * K * VEC
+// holds the row is used; wider rows take the streaming path.  Measured on
+// MI355X: rows of 4096 16-bit values run best as 4 waves x 2 vectors with
+// the exponentials kept (forward) and 8 waves x 1 vector (backward); K >= 4
+// recomputes the exponentials so that the row fits in fewer VGPRs.
+template <typename T, int VEC, int WAVES, int K, bool KEEP>
+bool fwd_try(const T* xp, int64_t ld_x, T* yp, int64_t ld_y, int64_t rows, int64_t cols,
+             hipStream_t s) {
+  if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
+  const unsigned grid = unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
+  softmax_fwd_resident<T, VEC, WAVES, K, KEEP>
+      <<<grid, row_block_threads<WAVES>(), 0, s>>>(xp, ld_x, yp, ld_y, rows, cols);
+  return true;
+}
+
+template <typename T, int VEC, int WAVES, int K>
+bool bwd_try(const T* gp, int64_t ld_dy, const T* yp, int64_t ld_y, T* dp, int64_t ld_dx,
+             int64_t rows, int64_t cols, hipStream_t s) {
+  if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
+  const unsigned grid = unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
+  softmax_bwd_resident<T, VEC, WAVES, K>
+      <<<grid, row_block_threads<WAVES>(), 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols);
+  return true;
 }
 
 template <typename T, int VEC>
@@ -224,15 +225,13 @@ hipError_t fwd_vec(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t r
                    int64_t cols, hipStream_t s) {
   const T* xp = static_cast<const T*>(x);
   T* yp = static_cast<T*>(y);
-  const int w = resident_waves(cols, VEC);
-  const unsigned rb = unsigned(rows);
-  switch (w) {
-    case 1: softmax_fwd_resident<T, VEC, 1><<<unsigned((rows + 3) / 4), 256, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
-    case 2: softmax_fwd_resident<T, VEC, 2><<<rb, 128, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
-    case 4: softmax_fwd_resident<T, VEC, 4><<<rb, 256, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
-    case 8: softmax_fwd_resident<T, VEC, 8><<<rb, 512, 0, s>>>(xp, ld_x, yp, ld_y, rows, cols); break;
-    default: softmax_fwd_stream<T, VEC><<<rb, kStreamThreads, 0, s>>>(xp, ld_x, yp, ld_y, cols); break;
-  }
+  if (!(fwd_try<T, VEC, 1, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
+        fwd_try<T, VEC, 2, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
+        fwd_try<T, VEC, 4, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
+        fwd_try<T, VEC, 8, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
+        fwd_try<T, VEC, 8, 4, false>(xp, ld_x, yp, ld_y, rows, cols, s) ||
+        fwd_try<T, VEC, 8, 8, false>(xp, ld_x, yp, ld_y, rows, cols, s)))
+    softmax_fwd_stream<T, VEC><<<unsigned(rows), kStreamThreads, 0, s>>>(xp, ld_x, yp, ld_y, cols);
   return hipGetLastError();
 }
 
@@ -242,15 +241,15 @@ hipError_t bwd_vec(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, v
   const T* gp = static_cast<const T*>(dy);
   const T* yp = static_cast<const T*>(y);
   T* dp = static_cast<T*>(dx);
-  const int w = resident_waves(cols, VEC);
-  const unsigned rb = unsigned(rows);
-  switch (w) {
-    case 1: softmax_bwd_resident<T, VEC, 1><<<unsigned((rows + 3) / 4), 256, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
-    case 2: softmax_bwd_resident<T, VEC, 2><<<rb, 128, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
-    case 4: softmax_bwd_resident<T, VEC, 4><<<rb, 256, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
-    case 8: softmax_bwd_resident<T, VEC, 8><<<rb, 512, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols); break;
-    default: softmax_bwd_stream<T, VEC><<<rb, kStreamThreads, 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, cols); break;
-  }
+  if (!(bwd_try<T, VEC, 1, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
+        bwd_try<T, VEC, 2, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
+        bwd_try<T, VEC, 4, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
+        bwd_try<T, VEC, 8, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
+        bwd_try<T, VEC, 8, 2>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
+        bwd_try<T, VEC, 8, 4>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
+        bwd_try<T, VEC, 8, 8>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s)))
+    softmax_bwd_stream<T, VEC><<<unsigned(rows), kStreamThreads, 0, s>>>(gp, ld_dy, yp, ld_y, dp,
+                                                                        ld_dx, cols);
   return hipGetLastError();
 }
 

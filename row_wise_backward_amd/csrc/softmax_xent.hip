@@ -25,8 +25,6 @@ namespace vjp {
 
 namespace {
 
-template <int WAVES> constexpr int block_threads() { return WAVES == 1 ? 256 : WAVES * kWave; }
-
 __device__ __forceinline__ void write_row_stats(int64_t row, float m, float lse, float zt,
                                                 bool valid, float* __restrict__ row_max,
                                                 float* __restrict__ row_lse,
@@ -36,15 +34,21 @@ __device__ __forceinline__ void write_row_stats(int64_t row, float m, float lse,
   row_loss[row] = valid ? lse - zt : __builtin_nanf("");
 }
 
-template <typename T, int VEC, int WAVES>
-__global__ __launch_bounds__(block_threads<WAVES>()) void xent_resident(
+__device__ __forceinline__ float row_lse_of(float m, float l) { return m + log2_fast(l) * kLn2; }
+
+// Resident kernel: the row is loaded once; KEEP = true holds exp(z - m) in
+// fp32 VGPRs for the gradient pass, KEEP = false recomputes it from the
+// stored row (bitwise the same values, fewer VGPRs, more rows per CU).
+template <typename T, int VEC, int WAVES, int K, bool KEEP>
+__global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
     const T* __restrict__ z, int64_t ld, const int32_t* __restrict__ targets, int64_t rows,
     int64_t C, float scale, float* __restrict__ row_max, float* __restrict__ row_lse,
     float* __restrict__ row_loss, T* __restrict__ dz, int64_t ld_dz) {
   __shared__ float buf[WAVES];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * 4 + wave : int64_t(blockIdx.x);
+  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
+                                 : int64_t(blockIdx.x);
   const int wv = WAVES == 1 ? 0 : wave;
   if (WAVES == 1 && row >= rows) return;
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
@@ -53,79 +57,64 @@ __global__ __launch_bounds__(block_threads<WAVES>()) void xent_resident(
   const int64_t t = targets[row];
   const bool valid = t >= 0 && t < C;
 
-  Vec<T, VEC> raw[kChunks];
-  float mx = -__builtin_inff(), mn = __builtin_inff();
-#pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
-    if (k * kStep < C) {
-      const int64_t col = k * kStep + lane_col;
-      if (load_row_vec<T, VEC>(zr, col, C, neg_inf_of<T>(), raw[k])) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float f = to_f32(raw[k].v[i]);
-          mx = fmaxf(mx, f);
-          mn = fminf(mn, f);
-        }
-      } else {  // ragged end of the row: padding counts for neither max nor min
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float f = to_f32(raw[k].v[i]);
-          mx = fmaxf(mx, f);
-          mn = fminf(mn, col + i < C ? f : __builtin_inff());
-        }
-      }
-    }
-  }
+  Vec<T, VEC> raw[K];
+  float mx, mn;
+  load_row_minmax<T, VEC, WAVES, K>(zr, C, lane_col, raw, mx, mn);
   const float m = row_reduce_max<WAVES>(mx, buf);
+  const bool safe = needs_denorm_exp(mn, m);
+  fence_row<T, VEC, K>(raw);
 
-  float e[kChunks][VEC];
+  float keep[KEEP ? K : 1][VEC];
   float l = 0.0f;
-  if (!((mn - m) * kLog2e < -126.0f)) {
 #pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      if (k * kStep < C) {
+  for (int k = 0; k < K; ++k) {
+    if (k * kStep < C) {
+      float e[VEC];
+      exp_vec<T, VEC>(raw[k], m, safe, e);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          e[k][i] = exp2_fast((to_f32(raw[k].v[i]) - m) * kLog2e);
-          l += e[k][i];
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      if (k * kStep < C) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          e[k][i] = exp2_denorm_safe((to_f32(raw[k].v[i]) - m) * kLog2e);
-          l += e[k][i];
-        }
+      for (int i = 0; i < VEC; ++i) {
+        l += e[i];
+        if constexpr (KEEP) keep[k][i] = e[i];
       }
     }
   }
   l = row_reduce_sum<WAVES>(l, buf);
   const float inv = 1.0f / l;
+  if constexpr (!KEEP) fence_row<T, VEC, K>(raw);
   const float ps = scale * inv;
 
+  const float lse = row_lse_of(m, l);
   if (wv == 0 && lane == 0) {
-    const float lse = m + log2_fast(l) * kLn2;
-    write_row_stats(row, m, lse, valid ? to_f32(zr[t]) : 0.0f, valid, row_max, row_lse,
-                    row_loss);
+    row_max[row] = m;
+    row_lse[row] = lse;
+    if (!valid) row_loss[row] = __builtin_nanf("");
   }
 
   T* dr = dz + row * ld_dz;
 #pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
+  for (int k = 0; k < K; ++k) {
     if (k * kStep < C) {
       const int64_t col = k * kStep + lane_col;
       if (col < C) {
+        if (uint64_t(t - col) < uint64_t(VEC)) {  // the lane holding z_t writes the row loss
+#pragma unroll
+          for (int i = 0; i < VEC; ++i)
+            if (col + i == t) row_loss[row] = lse - to_f32(raw[k].v[i]);
+        }
+        float e[VEC];
+        if constexpr (KEEP) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) e[i] = keep[k][i];
+        } else {
+          exp_vec<T, VEC>(raw[k], m, safe, e);
+        }
         float o[VEC];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) o[i] = e[k][i] * ps;
+        for (int i = 0; i < VEC; ++i) o[i] = e[i] * ps;
         if (uint64_t(t - col) < uint64_t(VEC)) {  // this vector holds the target column
 #pragma unroll
           for (int i = 0; i < VEC; ++i)
-            if (col + i == t) o[i] = (e[k][i] * inv - 1.0f) * scale;
+            if (col + i == t) o[i] = (e[i] * inv - 1.0f) * scale;
         }
         store_row_vec<T, VEC>(dr, col, C, o);
       }
@@ -155,9 +144,8 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream(
   const float inv = 1.0f / l;
   const float ps = scale * inv;
   if (threadIdx.x == 0) {
-    const float lse = m + log2_fast(l) * kLn2;
-    write_row_stats(row, m, lse, valid ? to_f32(zr[t]) : 0.0f, valid, row_max, row_lse,
-                    row_loss);
+    write_row_stats(row, m, row_lse_of(m, l), valid ? to_f32(zr[t]) : 0.0f, valid, row_max,
+                    row_lse, row_loss);
   }
   for (int64_t col = int64_t(threadIdx.x) * VEC; col < C; col += int64_t(kStreamThreads) * VEC) {
     Vec<T, VEC> r;
@@ -172,10 +160,19 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream(
   }
 }
 
-int resident_waves(int64_t cols, int vec) {
-  for (int w = 1; w <= 8; w <<= 1)
-    if (int64_t(w) * kWave * kChunks * vec >= cols) return w;
-  return 0;
+// Launch tiers, smallest first, as for the softmax forward: (waves per row,
+// vectors per lane, keep the exponentials).  Measured on MI355X: rows of
+// 32000 16-bit logits run best as 8 waves x 8 vectors recomputing the
+// exponentials (54 VGPRs, four rows in flight per CU).
+template <typename T, int VEC, int WAVES, int K, bool KEEP>
+bool resident_try(const T* zp, int64_t ld, const int32_t* tg, int64_t rows, int64_t C,
+                  float scale, float* rmax, float* rlse, float* rloss, T* dp, int64_t ld_dz,
+                  hipStream_t s) {
+  if (int64_t(WAVES) * kWave * K * VEC < C) return false;
+  const unsigned grid = unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
+  xent_resident<T, VEC, WAVES, K, KEEP><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+      zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz);
+  return true;
 }
 
 template <typename T, int VEC>
@@ -184,14 +181,13 @@ hipError_t run_vec(const void* z, int64_t ld, const int32_t* tg, int64_t rows, i
                    hipStream_t s) {
   const T* zp = static_cast<const T*>(z);
   T* dp = static_cast<T*>(dz);
-  const unsigned rb = unsigned(rows);
-  switch (resident_waves(C, VEC)) {
-    case 1: xent_resident<T, VEC, 1><<<unsigned((rows + 3) / 4), 256, 0, s>>>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz); break;
-    case 2: xent_resident<T, VEC, 2><<<rb, 128, 0, s>>>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz); break;
-    case 4: xent_resident<T, VEC, 4><<<rb, 256, 0, s>>>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz); break;
-    case 8: xent_resident<T, VEC, 8><<<rb, 512, 0, s>>>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz); break;
-    default: xent_stream<T, VEC><<<rb, kStreamThreads, 0, s>>>(zp, ld, tg, C, scale, rmax, rlse, rloss, dp, ld_dz); break;
-  }
+#define VJP_XENT_TRY(W, K, KEEP) \
+  resident_try<T, VEC, W, K, KEEP>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz, s)
+  if (!(VJP_XENT_TRY(1, 2, true) || VJP_XENT_TRY(2, 2, true) || VJP_XENT_TRY(4, 2, true) ||
+        VJP_XENT_TRY(8, 2, true) || VJP_XENT_TRY(8, 4, false) || VJP_XENT_TRY(8, 8, false)))
+    xent_stream<T, VEC><<<unsigned(rows), kStreamThreads, 0, s>>>(zp, ld, tg, C, scale, rmax,
+                                                                  rlse, rloss, dp, ld_dz);
+#undef VJP_XENT_TRY
   return hipGetLastError();
 }
 
