@@ -99,8 +99,8 @@ int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
                          vjp_stream_t stream);
 
 /* Rows per tile actually used for a request (0 = automatic: a function of
- * n_rows only, 32 * ceil(ceil(n_rows / 2048) / 32), at least 32).  Returns
- * -1 for invalid arguments. */
+ * n_rows only, 32 * ceil(ceil(n_rows / 2048) / 32), at least 32; an explicit
+ * request must not exceed 2^30).  Returns -1 for invalid arguments. */
 int64_t vjp_weighted_sum_rows_per_tile(int64_t n_rows, int64_t rows_per_tile);
 
 /* Workspace bytes for vjp_weighted_sum_bwd: T * d * 4 with
@@ -112,10 +112,11 @@ size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d, int64_t ro
 /* dy [n_rows] (act), x [n_rows, d] (ld_x, act), w [d] (w_dtype) ->
  * dx [n_rows, d] (ld_dx, act), dw [d] fp32 (overwritten or, with
  * accumulate = 1, added into).  workspace: see the size query.
- * grad_w[j] = sum over t = 0..T-1 of P[t][j] in this fixed order: 64 row
- * lanes r (1024 / min(16, next_pow2(d)) row lanes when d < 16) each sum
- * P[r][j], P[r + RL][j], ... in increasing t, then a pairwise tree
- * v[r] += v[r + s] for s = RL/2, ..., 1; finally dw[j] = v[0] (or dw[j] + v[0]). */
+ * grad_w[j] = sum over t = 0..T-1 of P[t][j] in this fixed order (d >= 2):
+ * RL = 1024 / min(16, next_pow2(d)) row lanes each sum P[r][j], P[r + RL][j],
+ * ... in increasing t, then a pairwise tree v[r] += v[r + s] for
+ * s = RL/2, ..., 1; finally dw[j] = v[0] (or dw[j] + v[0]).  For d = 1 the
+ * order of vjp_scaled_silu_bwd's dw applies. */
 int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
                          void* dx, int64_t ld_dx, float* dw, int accumulate,
                          int64_t n_rows, int64_t d, int64_t rows_per_tile,
@@ -137,7 +138,8 @@ int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void
 int vjp_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, int act,
                         vjp_stream_t stream);
 
-/* Elements per dw tile: max(2048, 2048 * ceil(ceil(n / 2048) / 2048)). -1 if n < 0. */
+/* Elements per dw tile: max(2048, 2048 * ceil(ceil(n / 4096) / 2048)), a
+ * function of n only (4096 tiles of 4096 elements for n = 2^24).  -1 if n < 0. */
 int64_t vjp_scaled_silu_elems_per_tile(int64_t n);
 
 /* Workspace bytes: T * 4, T = ceil(n / elems_per_tile).  Layout: fp32
@@ -146,8 +148,10 @@ int64_t vjp_scaled_silu_elems_per_tile(int64_t n);
 size_t vjp_scaled_silu_bwd_workspace_size(int64_t n);
 
 /* dy, x [n] (act), w [1] fp32 -> dx [n] (act), dw [1] fp32.  dw is the
- * fixed-order sum of P (1024 row lanes, then the pairwise tree, as for
- * vjp_weighted_sum_bwd with d = 1). */
+ * fixed-order sum of P: 256 threads, thread r summing P[r], P[r + 256], ...
+ * in increasing t; each wave's 64 sums combined by a fixed DPP tree
+ * (neighbour swap, pair swap, half-row mirror, row mirror, then 16-lane rows
+ * (0 + 1) + (2 + 3)); the four wave sums added in wave order. */
 int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx, float* dw,
                         int accumulate, int64_t n, int act, void* workspace,
                         size_t workspace_bytes, vjp_stream_t stream);
@@ -182,8 +186,8 @@ int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, 
  * row's loss is NaN (so is the mean), its dlogits row has no one-hot term,
  * and it is counted in *n_invalid (int32, optional: NULL skips the count).
  * workspace: vjp_softmax_xent_workspace_size(rows) bytes; layout: fp32 row
- * losses [rows] at offset 0.  The mean is their fixed-order sum (1024 row
- * lanes, pairwise tree) divided by rows.
+ * losses [rows] at offset 0.  The mean is their fixed-order sum (the order
+ * of the dw sum of vjp_scaled_silu_bwd) divided by rows.
  */
 size_t vjp_softmax_xent_workspace_size(int64_t rows);
 

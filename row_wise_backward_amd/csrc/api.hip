@@ -118,7 +118,7 @@ int64_t resolve_rows_per_tile(int64_t n_rows, int64_t rpt) {
 }
 
 int64_t resolve_elems_per_tile(int64_t n) {
-  const int64_t per = (n + 2047) / 2048;
+  const int64_t per = (n + 4095) / 4096;
   const int64_t e = ((per + 2047) / 2048) * 2048;
   return e < 2048 ? 2048 : e;
 }
@@ -182,6 +182,7 @@ VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, co
                                  vjp_stream_t stream) {
   if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n_rows < 0 || d < 0 || rows_per_tile < 0) return fail(VJP_EINVAL, "negative size");
+  if (rows_per_tile > (int64_t(1) << 30)) return fail(VJP_EINVAL, "rows_per_tile above 2^30");
   if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
   const int es = dtype_size(act), ws = dtype_size(w_dtype);
   VJP_TRY(check_vector("dy", dy, n_rows, es));

@@ -100,6 +100,17 @@ __device__ __forceinline__ void load_f32_tail(const T* __restrict__ p, int64_t a
   }
 }
 
+// Raw (storage-type) load of up to N elements: a streaming vector when all N
+// lie below `avail`, else element by element with zeros past the end.
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> load_raw_tail(const T* __restrict__ p, int64_t avail) {
+  if (avail >= N) return load_stream<T, N>(p);
+  Vec<T, N> r;
+#pragma unroll
+  for (int i = 0; i < N; ++i) r.v[i] = (i < avail) ? p[i] : T{};
+  return r;
+}
+
 template <typename T, int N>
 __device__ __forceinline__ void store_f32_tail(T* __restrict__ p, int64_t avail,
                                                const float (&in)[N]) {
@@ -149,6 +160,32 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f32<kDppMirror>(v));
   return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
                fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppSwap1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppSwap2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// Sum within aligned groups of L consecutive lanes (L a power of two, 1..64,
+// wave-uniform), on DPP: every lane of a group receives the group total, the
+// same bitwise value across the group.  Groups of 32 and 64 combine the
+// 16-lane row totals read from lanes 0 / 16 (and 32 / 48) in that order.
+__device__ __forceinline__ float group_sum_dpp(float v, int L) {
+  if (L >= 2) v += dpp_f32<kDppSwap1>(v);
+  if (L >= 4) v += dpp_f32<kDppSwap2>(v);
+  if (L >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if (L >= 16) v += dpp_f32<kDppMirror>(v);
+  if (L >= 32) {
+    const float a = readlane_f32(v, 0) + readlane_f32(v, 16);
+    const float b = readlane_f32(v, 32) + readlane_f32(v, 48);
+    v = L == 64 ? a + b : ((threadIdx.x & 32) ? b : a);
+  }
+  return v;
 }
 
 // Butterfly over lanes that differ in bits [LO, 64) (lanes sharing the low

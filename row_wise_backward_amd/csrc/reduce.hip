@@ -9,11 +9,17 @@
 // deterministic choice.  Here the second pass is a HIP kernel with a fixed
 // summation order, so the result does not depend on scheduling:
 //
-//   CL = min(16, next_pow2(d)) column lanes, RL = 1024 / CL row lanes;
-//   thread (r, c) of block b owns column j = b * CL + c and sums
+//   d >= 2: CL = min(16, next_pow2(d)) column lanes, RL = 1024 / CL row
+//   lanes; thread (r, c) of block b owns column j = b * CL + c and sums
 //   P[r][j], P[r + RL][j], P[r + 2 RL][j], ... in increasing t, starting
 //   from 0; the RL per-thread sums are then combined by the pairwise tree
 //   v[r] += v[r + s] for s = RL / 2, RL / 4, ..., 1.
+//
+//   d = 1 (and the cross-entropy mean): one workgroup of 256 threads; thread
+//   r sums P[r], P[r + 256], ... in increasing t, starting from 0; each
+//   wave's 64 sums are combined by the DPP tree of wave_sum (neighbour swap,
+//   pair swap, half-row mirror, row mirror, then rows (0 + 1) + (2 + 3)); the
+//   four wave sums are added in wave order, ((w0 + w1) + w2) + w3.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -44,8 +50,32 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
   if (r == 0 && j < d) out[j] = accumulate ? out[j] + red[c] : red[c];
 }
 
+constexpr int kScalarThreads = 256;
+constexpr int kScalarWaves = kScalarThreads / kWave;
+
+__global__ __launch_bounds__(kScalarThreads) void reduce_scalar_kernel(
+    const float* __restrict__ P, int64_t T, float* __restrict__ out, int accumulate) {
+  __shared__ float red[kScalarWaves];
+  float v = 0.0f;
+#pragma unroll 8
+  for (int64_t t = threadIdx.x; t < T; t += kScalarThreads) v += P[t];
+  v = wave_sum(v);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float s = red[0];
+#pragma unroll
+    for (int k = 1; k < kScalarWaves; ++k) s += red[k];
+    *out = accumulate ? *out + s : s;
+  }
+}
+
 hipError_t launch_reduce_partials(const float* P, int64_t T, int64_t d, float* out,
                                   int accumulate, hipStream_t s) {
+  if (d == 1) {
+    reduce_scalar_kernel<<<1, kScalarThreads, 0, s>>>(P, T, out, accumulate);
+    return hipGetLastError();
+  }
   int cl = 1;
   while (cl < d && cl < 16) cl <<= 1;
   const dim3 grid(unsigned((d + cl - 1) / cl)), block(kReduceThreads);
@@ -60,44 +90,46 @@ hipError_t launch_reduce_partials(const float* P, int64_t T, int64_t d, float* o
 }
 
 // Mean cross-entropy over rows: the row losses are summed in the same fixed
-// order as above with d = 1 (1024 row lanes, then the pairwise tree) and the
-// sum is divided by rows.  Targets outside [0, classes) are counted exactly
-// in integers.
-__global__ __launch_bounds__(kReduceThreads) void xent_finalize_kernel(
+// order as the d = 1 reduction above (256 threads, DPP wave tree, waves in
+// order) and the sum is divided by rows.  Targets outside [0, classes) are
+// counted exactly in integers.
+__global__ __launch_bounds__(kScalarThreads) void xent_finalize_kernel(
     const float* __restrict__ row_loss, const int32_t* __restrict__ targets, int64_t rows,
     int64_t classes, float* __restrict__ loss, int32_t* __restrict__ n_invalid) {
-  __shared__ float red[kReduceThreads];
-  __shared__ int cnt[kReduceThreads];
-  const int r = threadIdx.x;
+  __shared__ float red[kScalarWaves];
+  __shared__ int cnt[kScalarWaves];
   float v = 0.0f;
   int bad = 0;
 #pragma unroll 4
-  for (int64_t t = r; t < rows; t += kReduceThreads) {
+  for (int64_t t = threadIdx.x; t < rows; t += kScalarThreads) {
     v += row_loss[t];
     const int32_t tg = targets[t];
     bad += (tg < 0 || int64_t(tg) >= classes) ? 1 : 0;
   }
-  red[r] = v;
-  cnt[r] = bad;
-  __syncthreads();
-#pragma unroll
-  for (int s = kReduceThreads / 2; s > 0; s >>= 1) {
-    if (r < s) {
-      red[r] += red[r + s];
-      cnt[r] += cnt[r + s];
-    }
-    __syncthreads();
+  v = wave_sum(v);
+  bad = wave_sum_i32(bad);
+  if (threadIdx.x % kWave == 0) {
+    red[threadIdx.x / kWave] = v;
+    cnt[threadIdx.x / kWave] = bad;
   }
-  if (r == 0) {
-    *loss = rows > 0 ? red[0] / float(rows) : __builtin_nanf("");
-    if (n_invalid) *n_invalid = cnt[0];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float s = red[0];
+    int c = cnt[0];
+#pragma unroll
+    for (int k = 1; k < kScalarWaves; ++k) {
+      s += red[k];
+      c += cnt[k];
+    }
+    *loss = rows > 0 ? s / float(rows) : __builtin_nanf("");
+    if (n_invalid) *n_invalid = c;
   }
 }
 
 hipError_t launch_xent_finalize(const float* row_loss, const int32_t* targets, int64_t rows,
                                 int64_t classes, float* loss, int32_t* n_invalid,
                                 hipStream_t s) {
-  xent_finalize_kernel<<<1, kReduceThreads, 0, s>>>(row_loss, targets, rows, classes, loss,
+  xent_finalize_kernel<<<1, kScalarThreads, 0, s>>>(row_loss, targets, rows, classes, loss,
                                                     n_invalid);
   return hipGetLastError();
 }

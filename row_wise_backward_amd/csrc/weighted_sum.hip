@@ -12,11 +12,11 @@
 // moving VEC elements per access (16 bytes: 8 x bf16/fp16 or 4 x fp32) so a
 // wave reads 64 * 16 B contiguous bytes per instruction.  A wave therefore
 // covers G = 64 / L rows at once and a 256-thread workgroup 4 G rows; U such
-// row groups are loaded before any is used so every lane keeps U 128-bit
-// loads in flight.  Rows wider than 64 * VEC loop over column chunks.
+// row groups are loaded before any is used.  Rows wider than 64 * VEC loop
+// over column chunks.
 //
-// Forward: per-lane fp32 dot over its columns, then a butterfly over the L
-// lanes of the row.  Backward stage 1: workgroup (t, cb) owns row tile t and
+// Forward: per-lane fp32 dot over its columns, then a DPP reduction over the
+// L lanes of the row.  Backward stage 1: workgroup (t, cb) owns row tile t and
 // column block cb (64 * VEC columns at most); each lane keeps VEC fp32
 // partial sums for its columns over the rows it visits, lanes holding the
 // same columns are combined by a butterfly, the 4 waves through LDS in wave
@@ -30,7 +30,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kUnroll = 4;
 
 __device__ __forceinline__ float load_param(const void* __restrict__ w, int64_t j, int dt) {
   if (dt == kF32) return static_cast<const float*>(w)[j];
@@ -45,7 +44,9 @@ __device__ __forceinline__ void load_params(const void* __restrict__ w, int64_t 
   for (int i = 0; i < VEC; ++i) out[i] = (col + i < d) ? load_param(w, col + i, dt) : 0.0f;
 }
 
-template <typename T, int VEC>
+// Forward.  The row loop is uniform across the wave (lanes past the end of
+// the block carry zeros), so the per-row DPP reductions always see every lane.
+template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ x, int64_t ld,
                                                           const void* __restrict__ w, int wdt,
                                                           T* __restrict__ y, int64_t n, int64_t d,
@@ -63,11 +64,11 @@ __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ 
   float w0[VEC];
   load_params<VEC>(w, int64_t(c) * VEC, d, wdt, w0);
 
-  for (int64_t base = row_beg + int64_t(wave) * G + sub; base < row_end; base += kUnroll * step) {
-    float xv[kUnroll][VEC];
+  for (int64_t wbase = row_beg + int64_t(wave) * G; wbase < row_end; wbase += U * step) {
+    float xv[U][VEC];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t row = base + u * step;
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = wbase + sub + u * step;
       const int64_t col = int64_t(c) * VEC;
       if (row < row_end)
         load_f32_tail<T, VEC>(x + row * ld + col, d - col, 0.0f, xv[u]);
@@ -75,9 +76,9 @@ __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ 
 #pragma unroll
         for (int i = 0; i < VEC; ++i) xv[u][i] = 0.0f;
     }
-    float acc[kUnroll];
+    float acc[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       float a = 0.0f;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) a = fmaf(xv[u][i], w0[i], a);
@@ -89,8 +90,8 @@ __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ 
       float wk[VEC];
       load_params<VEC>(w, col, d, wdt, wk);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t row = base + u * step;
+      for (int u = 0; u < U; ++u) {
+        const int64_t row = wbase + sub + u * step;
         float xk[VEC];
         if (row < row_end)
           load_f32_tail<T, VEC>(x + row * ld + col, d - col, 0.0f, xk);
@@ -102,31 +103,45 @@ __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ 
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float a = acc[u];
-      for (int o = 1; o < L; o <<= 1) a += __shfl_xor(a, o, kWave);
-      const int64_t row = base + u * step;
+    for (int u = 0; u < U; ++u) {
+      const float a = group_sum_dpp(acc[u], L);
+      const int64_t row = wbase + sub + u * step;
       if (c == 0 && row < row_end) y[row] = from_f32<T>(a);
     }
   }
 }
 
-template <typename T, int VEC>
+// Backward stage 1.  Workgroup (t, cb): row tile t, column block cb.  Each
+// lane accumulates VEC fp32 partials over its rows in row order; the lanes
+// holding the same columns are combined by a butterfly and the four waves
+// through LDS in wave order.
+template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
     int wdt, T* __restrict__ dx, int64_t ld_dx, float* __restrict__ P, int64_t n, int64_t d,
     int L, int64_t rows_per_tile) {
   __shared__ float red[kWavesPerBlock][kWave * VEC];
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform per wave
   const int G = kWave / L;
   const int sub = lane / L;
   const int c = lane % L;
   const int64_t tile = blockIdx.x;
-  const int64_t col = int64_t(blockIdx.y) * L * VEC + int64_t(c) * VEC;
-  const int64_t row_beg = tile * rows_per_tile;
-  const int64_t row_end = min(row_beg + rows_per_tile, n);
-  const int64_t step = int64_t(kWavesPerBlock) * G;
+  const int64_t col0 = int64_t(blockIdx.y) * L * VEC;
+  const int64_t col = col0 + int64_t(c) * VEC;
+  const int64_t tile_beg = tile * rows_per_tile;
+  const int nrows = int(min(tile_beg + rows_per_tile, n) - tile_beg);
+  const int64_t cols_left = d - col;
+  // The four waves interleave: one workgroup step covers 4 G consecutive rows
+  // (wave w takes rows w G .. w G + G - 1 of it, one per L-lane group), so a
+  // workgroup streams one contiguous window of the tile.  Row indices are
+  // relative to the tile; loop bounds are uniform across the wave.
+  const int wg_rows = kWavesPerBlock * G;
+  const int my_row = wave * G + sub;
+  const T* __restrict__ gw = dy + tile_beg;
+  const T* __restrict__ xp = x + (tile_beg + my_row) * ld_x + col;
+  T* __restrict__ dp = dx + (tile_beg + my_row) * ld_dx + col;
+  const int64_t xstep = int64_t(wg_rows) * ld_x, dstep = int64_t(wg_rows) * ld_dx;
 
   float wr[VEC];
   load_params<VEC>(w, col, d, wdt, wr);
@@ -134,31 +149,33 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
 
-  for (int64_t base = row_beg + int64_t(wave) * G + sub; base < row_end; base += kUnroll * step) {
-    float xv[kUnroll][VEC];
-    float g[kUnroll];
+  for (int base = 0; base < nrows; base += U * wg_rows) {
+    Vec<T, VEC> xr[U];   // rows stay in storage type until used
+    float g[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t row = base + u * step;
-      if (row < row_end) {
-        g[u] = to_f32(dy[row]);
-        load_f32_tail<T, VEC>(x + row * ld_x + col, d - col, 0.0f, xv[u]);
+    for (int u = 0; u < U; ++u) {
+      const int r = base + u * wg_rows + my_row;
+      if (r < nrows) {
+        g[u] = to_f32(gw[r]);
+        xr[u] = load_raw_tail<T, VEC>(xp + u * xstep, cols_left);
       } else {
         g[u] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) xv[u][i] = 0.0f;
+        for (int i = 0; i < VEC; ++i) xr[u].v[i] = T{};
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t row = base + u * step;
+    for (int u = 0; u < U; ++u) {
+      const int r = base + u * wg_rows + my_row;
       float gx[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) gx[i] = g[u] * wr[i];
-      if (row < row_end && col < d) store_f32_tail<T, VEC>(dx + row * ld_dx + col, d - col, gx);
+      if (r < nrows && cols_left > 0) store_f32_tail<T, VEC>(dp + u * dstep, cols_left, gx);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(xv[u][i], g[u], acc[i]);
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(to_f32(xr[u].v[i]), g[u], acc[i]);
     }
+    xp += U * xstep;
+    dp += U * dstep;
   }
 
   // Lanes c, c + L, c + 2L, ... hold the same columns: butterfly over them.
@@ -187,20 +204,32 @@ int lanes_per_row(int64_t d, int vec) {
   return L;
 }
 
+// Launch shapes (measured on MI355X for 1048576 x 256 bf16): the forward
+// loads one row group per lane per step and gives each workgroup enough steps
+// that about 2048 workgroups cover the rows; the backward loads one row group
+// per step (46 VGPRs, eight workgroups per CU).
+constexpr int kFwdUnroll = 1;
+constexpr int64_t kFwdTargetBlocks = 2048;
+constexpr int64_t kFwdMaxSteps = 64;
+constexpr int kBwdUnroll = 1;
+
 template <typename T>
 hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, int wdt, void* y, int64_t n,
                      int64_t d, bool vec, hipStream_t s) {
   constexpr int V = 16 / sizeof(T);
   const int v = vec ? V : 1;
   const int L = lanes_per_row(d, v);
-  const int64_t rows_per_block = int64_t(kWavesPerBlock) * (kWave / L) * kUnroll * 2;
+  const int64_t rows_per_step = int64_t(kWavesPerBlock) * (kWave / L) * kFwdUnroll;
+  int64_t steps = (n + rows_per_step * kFwdTargetBlocks - 1) / (rows_per_step * kFwdTargetBlocks);
+  steps = steps < 1 ? 1 : (steps > kFwdMaxSteps ? kFwdMaxSteps : steps);
+  const int64_t rows_per_block = rows_per_step * steps;
   const dim3 grid(unsigned((n + rows_per_block - 1) / rows_per_block));
   if (vec)
-    ws_fwd_kernel<T, V><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), ld_x, w, wdt,
-                                                  static_cast<T*>(y), n, d, L, rows_per_block);
+    ws_fwd_kernel<T, V, kFwdUnroll><<<grid, kThreads, 0, s>>>(
+        static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(y), n, d, L, rows_per_block);
   else
-    ws_fwd_kernel<T, 1><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), ld_x, w, wdt,
-                                                  static_cast<T*>(y), n, d, L, rows_per_block);
+    ws_fwd_kernel<T, 1, kFwdUnroll><<<grid, kThreads, 0, s>>>(
+        static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(y), n, d, L, rows_per_block);
   return hipGetLastError();
 }
 
@@ -214,11 +243,11 @@ hipError_t bwd_typed(const void* dy, const void* x, int64_t ld_x, const void* w,
   const int64_t cw = int64_t(L) * v;
   const dim3 grid(unsigned((n + rows_per_tile - 1) / rows_per_tile), unsigned((d + cw - 1) / cw));
   if (vec)
-    ws_bwd_kernel<T, V><<<grid, kThreads, 0, s>>>(
+    ws_bwd_kernel<T, V, kBwdUnroll><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
         ld_dx, P, n, d, L, rows_per_tile);
   else
-    ws_bwd_kernel<T, 1><<<grid, kThreads, 0, s>>>(
+    ws_bwd_kernel<T, 1, kBwdUnroll><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
         ld_dx, P, n, d, L, rows_per_tile);
   return hipGetLastError();

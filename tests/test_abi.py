@@ -73,8 +73,8 @@ def test_tiling_queries():
     assert rwb.vjp_weighted_sum_rows_per_tile(1 << 20, 0) == 512
     assert rwb.vjp_weighted_sum_bwd_workspace_size(1 << 20, 256, 0) == 2048 * 256 * 4
     assert rwb.vjp_weighted_sum_rows_per_tile(-1, 0) == -1
-    assert rwb.vjp_scaled_silu_elems_per_tile(1 << 24) == 8192
-    assert rwb.vjp_scaled_silu_bwd_workspace_size(1 << 24) == 2048 * 4
+    assert rwb.vjp_scaled_silu_elems_per_tile(1 << 24) == 4096
+    assert rwb.vjp_scaled_silu_bwd_workspace_size(1 << 24) == 4096 * 4
     assert rwb.vjp_scaled_silu_elems_per_tile(7) == 2048
     assert rwb.vjp_scaled_silu_bwd_workspace_size(0) == 0
     assert rwb.vjp_softmax_xent_workspace_size(16384) == 16384 * 4
