@@ -148,10 +148,10 @@ int64_t vjp_scaled_silu_elems_per_tile(int64_t n);
 size_t vjp_scaled_silu_bwd_workspace_size(int64_t n);
 
 /* dy, x [n] (act), w [1] fp32 -> dx [n] (act), dw [1] fp32.  dw is the
- * fixed-order sum of P: 256 threads, thread r summing P[r], P[r + 256], ...
- * in increasing t; each wave's 64 sums combined by a fixed DPP tree
+ * fixed-order sum of P: 1024 threads, thread r summing P[r], P[r + 1024],
+ * ... in increasing t; each wave's 64 sums combined by a fixed DPP tree
  * (neighbour swap, pair swap, half-row mirror, row mirror, then 16-lane rows
- * (0 + 1) + (2 + 3)); the four wave sums added in wave order. */
+ * (0 + 1) + (2 + 3)); the sixteen wave sums added in wave order. */
 int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx, float* dw,
                         int accumulate, int64_t n, int act, void* workspace,
                         size_t workspace_bytes, vjp_stream_t stream);

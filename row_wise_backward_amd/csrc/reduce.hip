@@ -15,11 +15,11 @@
 //   from 0; the RL per-thread sums are then combined by the pairwise tree
 //   v[r] += v[r + s] for s = RL / 2, RL / 4, ..., 1.
 //
-//   d = 1 (and the cross-entropy mean): one workgroup of 256 threads; thread
-//   r sums P[r], P[r + 256], ... in increasing t, starting from 0; each
-//   wave's 64 sums are combined by the DPP tree of wave_sum (neighbour swap,
-//   pair swap, half-row mirror, row mirror, then rows (0 + 1) + (2 + 3)); the
-//   four wave sums are added in wave order, ((w0 + w1) + w2) + w3.
+//   d = 1 (and the cross-entropy mean): one workgroup of 1024 threads;
+//   thread r sums P[r], P[r + 1024], ... in increasing t, starting from 0;
+//   each wave's 64 sums are combined by the DPP tree of wave_sum (neighbour
+//   swap, pair swap, half-row mirror, row mirror, then rows (0 + 1) + (2 + 3));
+//   the sixteen wave sums are added in wave order, ((w0 + w1) + w2) + ... .
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
   if (r == 0 && j < d) out[j] = accumulate ? out[j] + red[c] : red[c];
 }
 
-constexpr int kScalarThreads = 256;
+constexpr int kScalarThreads = 1024;
 constexpr int kScalarWaves = kScalarThreads / kWave;
 
 __global__ __launch_bounds__(kScalarThreads) void reduce_scalar_kernel(
@@ -90,8 +90,8 @@ hipError_t launch_reduce_partials(const float* P, int64_t T, int64_t d, float* o
 }
 
 // Mean cross-entropy over rows: the row losses are summed in the same fixed
-// order as the d = 1 reduction above (256 threads, DPP wave tree, waves in
-// order) and the sum is divided by rows.  Targets outside [0, classes) are
+// order as the d = 1 reduction above (1024 threads, DPP wave tree, waves
+// in order) and the sum is divided by rows.  Targets outside [0, classes) are
 // counted exactly in integers.
 __global__ __launch_bounds__(kScalarThreads) void xent_finalize_kernel(
     const float* __restrict__ row_loss, const int32_t* __restrict__ targets, int64_t rows,

@@ -52,12 +52,12 @@ __device__ __forceinline__ void store_row_vec(T* __restrict__ row, int64_t col, 
 
 // Workgroup-wide reductions for rows owned by WAVES > 1 waves.  Every thread
 // receives the same value; waves are combined in wave order.  `buf` holds
-// WAVES floats; the leading barrier protects reuse of `buf`.
+// WAVES floats and must not be reused until every wave has read it (the
+// kernels give each reduction of a row its own slot).
 template <int WAVES>
 __device__ __forceinline__ float row_reduce_max(float v, float* buf) {
   v = wave_max(v);
   if constexpr (WAVES > 1) {
-    __syncthreads();
     if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
     __syncthreads();
     v = buf[0];
@@ -71,7 +71,6 @@ template <int WAVES>
 __device__ __forceinline__ float row_reduce_sum(float v, float* buf) {
   v = wave_sum(v);
   if constexpr (WAVES > 1) {
-    __syncthreads();
     if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
     __syncthreads();
     v = buf[0];
@@ -89,9 +88,11 @@ __device__ __forceinline__ float exp2_denorm_safe(float t) {
                      : exp2_fast(t);
 }
 
-// e[i] = exp(x_i - m) for one vector of a row, x_i as stored.  Lanes whose
-// row range can produce results below 2^-126 (flagged by `safe`) take the
-// subnormal-preserving form; the two forms agree wherever both are exact.
+// e[i] = exp(x_i - m) = 2^((x_i - m) log2 e) for one vector of a row, x_i
+// as stored.  x_i - m is exact for 16-bit inputs, so the row max maps to
+// exactly 1.  Lanes whose row range can produce results below 2^-126
+// (flagged by `safe`) take the subnormal-preserving form; the two forms
+// agree wherever both are exact.
 template <typename T, int VEC>
 __device__ __forceinline__ void exp_vec(const Vec<T, VEC>& r, float m, bool safe,
                                         float (&e)[VEC]) {

@@ -31,7 +31,7 @@ template <typename T, int VEC, int WAVES, int K, bool KEEP>
 __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_fwd_resident(
     const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y, int64_t rows,
     int64_t cols) {
-  __shared__ float buf[WAVES];
+  __shared__ float buf[2][WAVES];   // one slot per reduction of the row
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_fwd_reside
   Vec<T, VEC> raw[K];
   float mx, mn;
   load_row_minmax<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, raw, mx, mn);
-  const float m = row_reduce_max<WAVES>(mx, buf);
+  const float m = row_reduce_max<WAVES>(mx, buf[0]);
   const bool safe = needs_denorm_exp(mn, m);
   fence_row<T, VEC, K>(raw);
 
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_fwd_reside
       }
     }
   }
-  l = row_reduce_sum<WAVES>(l, buf);
+  l = row_reduce_sum<WAVES>(l, buf[1]);
   const float inv = 1.0f / l;
   if constexpr (!KEEP) fence_row<T, VEC, K>(raw);
 
@@ -91,7 +91,7 @@ template <typename T, int VEC, int WAVES, int K>
 __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_resident(
     const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ y, int64_t ld_y,
     T* __restrict__ dx, int64_t ld_dx, int64_t rows, int64_t cols) {
-  __shared__ float buf[WAVES];
+  __shared__ float buf[2][WAVES];   // one slot per reduction of the row
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_reside
       for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(rg[k].v[i]), to_f32(ry[k].v[i]), s);
     }
   }
-  s = row_reduce_sum<WAVES>(s, buf);
+  s = row_reduce_sum<WAVES>(s, buf[0]);
   fence_row<T, VEC, K>(rg);
   fence_row<T, VEC, K>(ry);
 

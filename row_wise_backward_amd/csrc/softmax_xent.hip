@@ -44,7 +44,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
     const T* __restrict__ z, int64_t ld, const int32_t* __restrict__ targets, int64_t rows,
     int64_t C, float scale, float* __restrict__ row_max, float* __restrict__ row_lse,
     float* __restrict__ row_loss, T* __restrict__ dz, int64_t ld_dz) {
-  __shared__ float buf[WAVES];
+  __shared__ float buf[2][WAVES];   // one slot per reduction of the row
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
   Vec<T, VEC> raw[K];
   float mx, mn;
   load_row_minmax<T, VEC, WAVES, K>(zr, C, lane_col, raw, mx, mn);
-  const float m = row_reduce_max<WAVES>(mx, buf);
+  const float m = row_reduce_max<WAVES>(mx, buf[0]);
   const bool safe = needs_denorm_exp(mn, m);
   fence_row<T, VEC, K>(raw);
 
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
       }
     }
   }
-  l = row_reduce_sum<WAVES>(l, buf);
+  l = row_reduce_sum<WAVES>(l, buf[1]);
   const float inv = 1.0f / l;
   if constexpr (!KEEP) fence_row<T, VEC, K>(raw);
   const float ps = scale * inv;
