@@ -98,25 +98,35 @@ int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
                          int64_t n_rows, int64_t d, int act, int w_dtype,
                          vjp_stream_t stream);
 
-/* Rows per tile actually used for a request (0 = automatic: a function of
- * n_rows only, 32 * ceil(ceil(n_rows / 2048) / 32), at least 32; an explicit
- * request must not exceed 2^30).  Returns -1 for invalid arguments. */
-int64_t vjp_weighted_sum_rows_per_tile(int64_t n_rows, int64_t rows_per_tile);
+/* Row tiling of the backward's stage 1.  The rows are cut into blocks of
+ * block_rows consecutive rows (the last one may be shorter) and tile t holds
+ * blocks t, t + tiles, t + 2 * tiles, ...
+ *   rows_per_tile > 0: block_rows = rows_per_tile, tiles = ceil(n_rows /
+ *     rows_per_tile), so tile t is the contiguous rows [t * rows_per_tile,
+ *     (t + 1) * rows_per_tile); rows_per_tile must not exceed 2^30.
+ *   rows_per_tile = 0 (automatic, a function of n_rows only): block_rows =
+ *     32, tiles = min(1024, ceil(n_rows / 32)); the blocks are dealt to the
+ *     tiles round-robin.
+ * block_rows and tiles are HOST pointers written on success.  Returns VJP_OK,
+ * or VJP_EINVAL for negative sizes, rows_per_tile > 2^30 or NULL outputs. */
+int vjp_weighted_sum_tiling(int64_t n_rows, int64_t rows_per_tile, int64_t* block_rows,
+                            int64_t* tiles);
 
-/* Workspace bytes for vjp_weighted_sum_bwd: T * d * 4 with
- * T = ceil(n_rows / rows_per_tile) (rows_per_tile resolved as above).
- * Layout: fp32 partials P[T][d] row-major at offset 0, where
- * P[t][j] = sum over rows i of tile t of x[i, j] * dy[i]. */
+/* Workspace bytes for vjp_weighted_sum_bwd: tiles * d * 4 (tiles as above;
+ * 0 for invalid arguments).  Layout: fp32 partials P[tiles][d] row-major at
+ * offset 0, where P[t][j] = sum over the rows i of tile t of x[i, j] * dy[i]. */
 size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d, int64_t rows_per_tile);
 
 /* dy [n_rows] (act), x [n_rows, d] (ld_x, act), w [d] (w_dtype) ->
  * dx [n_rows, d] (ld_dx, act), dw [d] fp32 (overwritten or, with
  * accumulate = 1, added into).  workspace: see the size query.
- * grad_w[j] = sum over t = 0..T-1 of P[t][j] in this fixed order (d >= 2):
- * RL = 1024 / min(16, next_pow2(d)) row lanes each sum P[r][j], P[r + RL][j],
- * ... in increasing t, then a pairwise tree v[r] += v[r + s] for
- * s = RL/2, ..., 1; finally dw[j] = v[0] (or dw[j] + v[0]).  For d = 1 the
- * order of vjp_scaled_silu_bwd's dw applies. */
+ * grad_w[j] = sum over t = 0..tiles-1 of P[t][j] in this fixed order (d >= 2):
+ * 128 row lanes r each sum P[r][j], P[r + 128][j], P[r + 256][j], ... in
+ * increasing t, starting from 0, then a pairwise tree v[r] += v[r + s] for
+ * s = 64, 32, ..., 1; finally dw[j] = v[0] (or dw[j] + v[0]).  For d = 1 the
+ * order of vjp_scaled_silu_bwd's dw applies.  Within a tile each partial is
+ * accumulated in fp32 in an order fixed by the tiling, so the whole result is
+ * bitwise reproducible. */
 int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
                          void* dx, int64_t ld_dx, float* dw, int accumulate,
                          int64_t n_rows, int64_t d, int64_t rows_per_tile,

@@ -42,18 +42,22 @@ def n_tiles(n_rows: int, rows_per_tile: int) -> int:
     return -(-int(n_rows) // int(rows_per_tile))
 
 
-def partials(x: np.ndarray, dy: np.ndarray, rows_per_tile: int) -> np.ndarray:
+def partials(x: np.ndarray, dy: np.ndarray, block_rows: int, tiles: int | None = None) -> np.ndarray:
     """Stage-1 partial rows P[t, j] = sum over rows i of tile t of x[i, j] * dy[i].
 
-    Tile t holds rows [t * rows_per_tile, min((t + 1) * rows_per_tile, N)).
-    Summing P over t gives grad_w.
+    The rows are cut into blocks of ``block_rows`` consecutive rows (the last
+    one may be shorter) and block b belongs to tile b mod ``tiles``.  With
+    ``tiles`` left out it is the number of blocks, so tile t is the page's
+    row tile [t * block_rows, min((t + 1) * block_rows, N)).  However the
+    rows are dealt to tiles, summing P over t gives grad_w.
     """
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
     n = x.shape[0]
-    T = n_tiles(n, rows_per_tile)
+    nblocks = n_tiles(n, block_rows)
+    T = nblocks if tiles is None else int(tiles)
     P = np.zeros((T, x.shape[1]), np.float64)
-    for t in range(T):
-        lo, hi = t * rows_per_tile, min((t + 1) * rows_per_tile, n)
-        P[t] = np.sum(x[lo:hi] * dy[lo:hi, None], axis=0)
+    for b in range(nblocks):
+        lo, hi = b * block_rows, min((b + 1) * block_rows, n)
+        P[b % T] += np.sum(x[lo:hi] * dy[lo:hi, None], axis=0)
     return P

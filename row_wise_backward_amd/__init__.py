@@ -41,7 +41,7 @@ _SIGS = {
     "vjp_status_string": ([_int], ctypes.c_char_p),
     "vjp_last_error": ([], ctypes.c_char_p),
     "vjp_weighted_sum_fwd": ([_vp, _i64, _vp, _vp, _i64, _i64, _int, _int, _vp], _int),
-    "vjp_weighted_sum_rows_per_tile": ([_i64, _i64], _i64),
+    "vjp_weighted_sum_tiling": ([_i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], ctypes.c_int),
     "vjp_weighted_sum_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
     "vjp_weighted_sum_bwd": ([_vp, _vp, _i64, _vp, _vp, _i64, _vp, _int, _i64, _i64, _i64,
                               _int, _int, _vp, _sz, _vp], _int),
@@ -162,8 +162,12 @@ def vjp_weighted_sum_fwd(x, w, y=None):
     return y
 
 
-def vjp_weighted_sum_rows_per_tile(n_rows: int, rows_per_tile: int = 0) -> int:
-    return int(lib.vjp_weighted_sum_rows_per_tile(n_rows, rows_per_tile))
+def vjp_weighted_sum_tiling(n_rows: int, rows_per_tile: int = 0):
+    """(block_rows, tiles): tile t holds row blocks t, t + tiles, ... of block_rows rows."""
+    br, tl = _i64(), _i64()
+    _check(lib.vjp_weighted_sum_tiling(n_rows, rows_per_tile, ctypes.byref(br), ctypes.byref(tl)),
+           "vjp_weighted_sum_tiling")
+    return int(br.value), int(tl.value)
 
 
 def vjp_weighted_sum_bwd_workspace_size(n_rows: int, d: int, rows_per_tile: int = 0) -> int:

@@ -110,11 +110,25 @@ bool rows_vec_ok(const void* p, int64_t ld, int esize) {
     if (_st != VJP_OK) return _st; \
   } while (0)
 
-int64_t resolve_rows_per_tile(int64_t n_rows, int64_t rpt) {
-  if (rpt > 0) return rpt;
-  const int64_t per = (n_rows + 2047) / 2048;
-  const int64_t r = ((per + 31) / 32) * 32;
-  return r < 32 ? 32 : r;
+// Row tiling of the weighted-sum backward.  An explicit rows_per_tile gives
+// contiguous tiles of that many rows.  The automatic tiling cuts the rows into
+// blocks of kAutoBlockRows and deals them round-robin to at most kAutoTiles
+// tiles, so that the workgroups, one per tile, stream neighbouring blocks at
+// the same time (measured on MI355X: about 15 % more bandwidth than
+// contiguous tiles of 512 rows for 1048576 x 256 bf16; 1024 tiles, four
+// workgroups per CU, beat 512, 768, 1280, 1536, 2048 and 4096).
+constexpr int64_t kAutoBlockRows = 32;
+constexpr int64_t kMaxRowsPerTile = int64_t(1) << 30;
+constexpr int64_t kAutoTiles = 1024;
+
+struct WsTiling {
+  int64_t block_rows, tiles;
+};
+
+WsTiling resolve_ws_tiling(int64_t n_rows, int64_t rpt) {
+  if (rpt > 0) return {rpt, (n_rows + rpt - 1) / rpt};
+  const int64_t blocks = (n_rows + kAutoBlockRows - 1) / kAutoBlockRows;
+  return {kAutoBlockRows, blocks < kAutoTiles ? blocks : kAutoTiles};
 }
 
 int64_t resolve_elems_per_tile(int64_t n) {
@@ -162,17 +176,21 @@ VJP_API int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, voi
                     "weighted_sum_fwd");
 }
 
-VJP_API int64_t vjp_weighted_sum_rows_per_tile(int64_t n_rows, int64_t rows_per_tile) {
-  if (n_rows < 0 || rows_per_tile < 0) return -1;
-  return resolve_rows_per_tile(n_rows, rows_per_tile);
+VJP_API int vjp_weighted_sum_tiling(int64_t n_rows, int64_t rows_per_tile, int64_t* block_rows,
+                                    int64_t* tiles) {
+  if (n_rows < 0 || rows_per_tile < 0) return fail(VJP_EINVAL, "negative size");
+  if (rows_per_tile > kMaxRowsPerTile) return fail(VJP_EINVAL, "rows_per_tile above 2^30");
+  if (!block_rows || !tiles) return fail(VJP_EINVAL, "null output pointer");
+  const WsTiling t = resolve_ws_tiling(n_rows, rows_per_tile);
+  *block_rows = t.block_rows;
+  *tiles = t.tiles;
+  return ok();
 }
 
 VJP_API size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d,
                                                    int64_t rows_per_tile) {
-  if (n_rows < 0 || d < 0 || rows_per_tile < 0) return 0;
-  const int64_t r = resolve_rows_per_tile(n_rows, rows_per_tile);
-  const int64_t T = (n_rows + r - 1) / r;
-  return size_t(T) * size_t(d) * sizeof(float);
+  if (n_rows < 0 || d < 0 || rows_per_tile < 0 || rows_per_tile > kMaxRowsPerTile) return 0;
+  return size_t(resolve_ws_tiling(n_rows, rows_per_tile).tiles) * size_t(d) * sizeof(float);
 }
 
 VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
@@ -182,7 +200,7 @@ VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, co
                                  vjp_stream_t stream) {
   if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n_rows < 0 || d < 0 || rows_per_tile < 0) return fail(VJP_EINVAL, "negative size");
-  if (rows_per_tile > (int64_t(1) << 30)) return fail(VJP_EINVAL, "rows_per_tile above 2^30");
+  if (rows_per_tile > kMaxRowsPerTile) return fail(VJP_EINVAL, "rows_per_tile above 2^30");
   if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
   const int es = dtype_size(act), ws = dtype_size(w_dtype);
   VJP_TRY(check_vector("dy", dy, n_rows, es));
@@ -202,13 +220,14 @@ VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, co
                        span(w, d * ws, "w")}));
   if (d == 0) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t rpt = resolve_rows_per_tile(n_rows, rows_per_tile);
-  const int64_t T = (n_rows + rpt - 1) / rpt;
+  const WsTiling tl = resolve_ws_tiling(n_rows, rows_per_tile);
+  const int64_t T = tl.tiles;
   float* P = static_cast<float*>(workspace);
   if (T > 0) {
     const bool vec = rows_vec_ok(x, ld_x, es) && rows_vec_ok(dx, ld_dx, es);
     const hipError_t e = launch_weighted_sum_bwd_stage1(dy, x, ld_x, w, dx, ld_dx, P, n_rows, d,
-                                                        rpt, act, w_dtype, vec, s);
+                                                        int(tl.block_rows), T, act, w_dtype, vec,
+                                                        s);
     if (e != hipSuccess) return hip_status(e, "weighted_sum_bwd stage 1");
   }
   return hip_status(launch_reduce_partials(P, T, d, dw, accumulate, s), "weighted_sum_bwd stage 2");

@@ -22,7 +22,7 @@ hipError_t launch_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, v
                                    hipStream_t s);
 hipError_t launch_weighted_sum_bwd_stage1(const void* dy, const void* x, int64_t ld_x,
                                           const void* w, void* dx, int64_t ld_dx, float* P,
-                                          int64_t n, int64_t d, int64_t rows_per_tile,
+                                          int64_t n, int64_t d, int block_rows, int64_t tiles,
                                           int act, int wdt, bool vec, hipStream_t s);
 
 // Scaled SiLU.

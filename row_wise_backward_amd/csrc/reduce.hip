@@ -9,11 +9,14 @@
 // deterministic choice.  Here the second pass is a HIP kernel with a fixed
 // summation order, so the result does not depend on scheduling:
 //
-//   d >= 2: CL = min(16, next_pow2(d)) column lanes, RL = 1024 / CL row
-//   lanes; thread (r, c) of block b owns column j = b * CL + c and sums
-//   P[r][j], P[r + RL][j], P[r + 2 RL][j], ... in increasing t, starting
-//   from 0; the RL per-thread sums are then combined by the pairwise tree
-//   v[r] += v[r + s] for s = RL / 2, RL / 4, ..., 1.
+//   d >= 2: workgroup b owns the 32 columns 32 b .. 32 b + 31 (one 128-byte
+//   line of every partial row, so no line is read by two workgroups); its
+//   1024 threads are 128 row lanes r times 8 column lanes c, and lane (r, c)
+//   owns the four columns j = 32 b + 4 c + k, k = 0..3.  Each lane sums
+//   P[r][j], P[r + 128][j], P[r + 256][j], ... in increasing t, starting from
+//   0; the 128 row sums of a column are then combined by the pairwise tree
+//   v[r] += v[r + s] for s = 64, 32, ..., 1.  The 16-byte and the element
+//   load paths add the same values in the same order.
 //
 //   d = 1 (and the cross-entropy mean): one workgroup of 1024 threads;
 //   thread r sums P[r], P[r + 1024], ... in increasing t, starting from 0;
@@ -26,28 +29,63 @@
 namespace vjp {
 
 constexpr int kReduceThreads = 1024;
+constexpr int kRowLanes = 128;
+constexpr int kColLanes = kReduceThreads / kRowLanes;   // 8
+constexpr int kColsPerBlock = 4 * kColLanes;            // 32
 
-template <int CL>
+// VEC4: d % 4 == 0 and P 16-byte aligned, so a lane's four columns are one
+// aligned 16-byte load (all four in range or none).
+template <bool VEC4>
 __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
     const float* __restrict__ P, int64_t T, int64_t d, float* __restrict__ out, int accumulate) {
-  constexpr int RL = kReduceThreads / CL;
-  __shared__ float red[kReduceThreads];
-  const int c = threadIdx.x % CL;
-  const int r = threadIdx.x / CL;
-  const int64_t j = int64_t(blockIdx.x) * CL + c;
-  float v = 0.0f;
-  if (j < d) {
+  __shared__ float4 red[kRowLanes][kColLanes];
+  const int c = threadIdx.x % kColLanes;
+  const int r = threadIdx.x / kColLanes;
+  const int64_t j = int64_t(blockIdx.x) * kColsPerBlock + 4 * c;
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (VEC4) {
+    if (j < d) {
 #pragma unroll 8
-    for (int64_t t = r; t < T; t += RL) v += P[t * d + j];
+      for (int64_t t = r; t < T; t += kRowLanes) {
+        const float4 p = *reinterpret_cast<const float4*>(P + t * d + j);
+        v.x += p.x;
+        v.y += p.y;
+        v.z += p.z;
+        v.w += p.w;
+      }
+    }
+  } else {
+#pragma unroll 4
+    for (int64_t t = r; t < T; t += kRowLanes) {
+      const float* p = P + t * d + j;
+      if (j < d) v.x += p[0];
+      if (j + 1 < d) v.y += p[1];
+      if (j + 2 < d) v.z += p[2];
+      if (j + 3 < d) v.w += p[3];
+    }
   }
-  red[threadIdx.x] = v;
+  red[r][c] = v;
   __syncthreads();
 #pragma unroll
-  for (int s = RL / 2; s > 0; s >>= 1) {
-    if (r < s) red[r * CL + c] += red[(r + s) * CL + c];
+  for (int s = kRowLanes / 2; s > 0; s >>= 1) {
+    if (r < s) {
+      float4 a = red[r][c];
+      const float4 b = red[r + s][c];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+      red[r][c] = a;
+    }
     __syncthreads();
   }
-  if (r == 0 && j < d) out[j] = accumulate ? out[j] + red[c] : red[c];
+  if (r == 0) {
+    const float4 s = red[0][c];
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (j + k < d) out[j + k] = accumulate ? out[j + k] + sv[k] : sv[k];
+  }
 }
 
 constexpr int kScalarThreads = 1024;
@@ -76,16 +114,12 @@ hipError_t launch_reduce_partials(const float* P, int64_t T, int64_t d, float* o
     reduce_scalar_kernel<<<1, kScalarThreads, 0, s>>>(P, T, out, accumulate);
     return hipGetLastError();
   }
-  int cl = 1;
-  while (cl < d && cl < 16) cl <<= 1;
-  const dim3 grid(unsigned((d + cl - 1) / cl)), block(kReduceThreads);
-  switch (cl) {
-    case 1: reduce_partials_kernel<1><<<grid, block, 0, s>>>(P, T, d, out, accumulate); break;
-    case 2: reduce_partials_kernel<2><<<grid, block, 0, s>>>(P, T, d, out, accumulate); break;
-    case 4: reduce_partials_kernel<4><<<grid, block, 0, s>>>(P, T, d, out, accumulate); break;
-    case 8: reduce_partials_kernel<8><<<grid, block, 0, s>>>(P, T, d, out, accumulate); break;
-    default: reduce_partials_kernel<16><<<grid, block, 0, s>>>(P, T, d, out, accumulate); break;
-  }
+  const dim3 grid(unsigned((d + kColsPerBlock - 1) / kColsPerBlock)), block(kReduceThreads);
+  const bool vec4 = d % 4 == 0 && reinterpret_cast<uintptr_t>(P) % 16 == 0;
+  if (vec4)
+    reduce_partials_kernel<true><<<grid, block, 0, s>>>(P, T, d, out, accumulate);
+  else
+    reduce_partials_kernel<false><<<grid, block, 0, s>>>(P, T, d, out, accumulate);
   return hipGetLastError();
 }
 

@@ -111,90 +111,96 @@ __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ 
   }
 }
 
-// Backward stage 1.  Workgroup (t, cb): row tile t, column block cb.  Each
-// lane accumulates VEC fp32 partials over its rows in row order; the lanes
-// holding the same columns are combined by a butterfly and the four waves
-// through LDS in wave order.
+// Backward stage 1.  Rows are cut into blocks of block_rows rows; tile t
+// holds blocks t, t + tiles, t + 2 tiles, ... (with tiles = number of blocks
+// this is one contiguous block per tile).  Workgroup (g, cb) takes tiles g,
+// g + gridDim.x, ... and column block cb.  Each lane accumulates VEC fp32
+// partials over its rows in increasing row order; the lanes holding the same
+// columns are combined by a butterfly and the four waves through LDS in wave
+// order, and the tile's partial row is written to P[t][.].
 template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
     int wdt, T* __restrict__ dx, int64_t ld_dx, float* __restrict__ P, int64_t n, int64_t d,
-    int L, int64_t rows_per_tile) {
+    int L, int block_rows, int64_t tiles) {
   __shared__ float red[kWavesPerBlock][kWave * VEC];
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform per wave
   const int G = kWave / L;
   const int sub = lane / L;
   const int c = lane % L;
-  const int64_t tile = blockIdx.x;
   const int64_t col0 = int64_t(blockIdx.y) * L * VEC;
   const int64_t col = col0 + int64_t(c) * VEC;
-  const int64_t tile_beg = tile * rows_per_tile;
-  const int nrows = int(min(tile_beg + rows_per_tile, n) - tile_beg);
   const int64_t cols_left = d - col;
   // The four waves interleave: one workgroup step covers 4 G consecutive rows
   // (wave w takes rows w G .. w G + G - 1 of it, one per L-lane group), so a
-  // workgroup streams one contiguous window of the tile.  Row indices are
-  // relative to the tile; loop bounds are uniform across the wave.
+  // workgroup streams one contiguous window of a block.  Row indices are
+  // relative to the block; loop bounds are uniform across the wave.
   const int wg_rows = kWavesPerBlock * G;
   const int my_row = wave * G + sub;
-  const T* __restrict__ gw = dy + tile_beg;
-  const T* __restrict__ xp = x + (tile_beg + my_row) * ld_x + col;
-  T* __restrict__ dp = dx + (tile_beg + my_row) * ld_dx + col;
   const int64_t xstep = int64_t(wg_rows) * ld_x, dstep = int64_t(wg_rows) * ld_dx;
 
   float wr[VEC];
   load_params<VEC>(w, col, d, wdt, wr);
-  float acc[VEC];
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
 
-  for (int base = 0; base < nrows; base += U * wg_rows) {
-    Vec<T, VEC> xr[U];   // rows stay in storage type until used
-    float g[U];
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    float acc[VEC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = base + u * wg_rows + my_row;
-      if (r < nrows) {
-        g[u] = to_f32(gw[r]);
-        xr[u] = load_raw_tail<T, VEC>(xp + u * xstep, cols_left);
-      } else {
-        g[u] = 0.0f;
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+    for (int64_t r0 = tile * block_rows; r0 < n; r0 += tiles * block_rows) {
+      const int nrows = int(min(int64_t(block_rows), n - r0));
+      const T* __restrict__ gw = dy + r0;
+      const T* __restrict__ xp = x + (r0 + my_row) * ld_x + col;
+      T* __restrict__ dp = dx + (r0 + my_row) * ld_dx + col;
+      for (int base = 0; base < nrows; base += U * wg_rows) {
+        Vec<T, VEC> xr[U];   // rows stay in storage type until used
+        float g[U];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) xr[u].v[i] = T{};
+        for (int u = 0; u < U; ++u) {
+          const int r = base + u * wg_rows + my_row;
+          if (r < nrows) {
+            g[u] = to_f32(gw[r]);
+            xr[u] = load_raw_tail<T, VEC>(xp + u * xstep, cols_left);
+          } else {
+            g[u] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) xr[u].v[i] = T{};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int r = base + u * wg_rows + my_row;
+          float gx[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) gx[i] = g[u] * wr[i];
+          if (r < nrows && cols_left > 0) store_f32_tail<T, VEC>(dp + u * dstep, cols_left, gx);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] = fmaf(to_f32(xr[u].v[i]), g[u], acc[i]);
+        }
+        xp += U * xstep;
+        dp += U * dstep;
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = base + u * wg_rows + my_row;
-      float gx[VEC];
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) gx[i] = g[u] * wr[i];
-      if (r < nrows && cols_left > 0) store_f32_tail<T, VEC>(dp + u * dstep, cols_left, gx);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(to_f32(xr[u].v[i]), g[u], acc[i]);
-    }
-    xp += U * xstep;
-    dp += U * dstep;
-  }
 
-  // Lanes c, c + L, c + 2L, ... hold the same columns: butterfly over them.
+    // Lanes c, c + L, c + 2L, ... hold the same columns: butterfly over them.
 #pragma unroll
-  for (int i = 0; i < VEC; ++i)
-    for (int o = L; o < kWave; o <<= 1) acc[i] += __shfl_xor(acc[i], o, kWave);
-  if (sub == 0) {
+    for (int i = 0; i < VEC; ++i)
+      for (int o = L; o < kWave; o <<= 1) acc[i] += __shfl_xor(acc[i], o, kWave);
+    if (sub == 0) {
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) red[wave][c * VEC + i] = acc[i];
-  }
-  __syncthreads();
-  if (wave == 0 && sub == 0) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      float s = red[0][c * VEC + i];
-#pragma unroll
-      for (int k = 1; k < kWavesPerBlock; ++k) s += red[k][c * VEC + i];
-      if (col + i < d) P[tile * d + col + i] = s;
+      for (int i = 0; i < VEC; ++i) red[wave][c * VEC + i] = acc[i];
     }
+    __syncthreads();
+    if (wave == 0 && sub == 0) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        float s = red[0][c * VEC + i];
+#pragma unroll
+        for (int k = 1; k < kWavesPerBlock; ++k) s += red[k][c * VEC + i];
+        if (col + i < d) P[tile * d + col + i] = s;
+      }
+    }
+    __syncthreads();   // red is reused by the next tile of this workgroup
   }
 }
 
@@ -212,6 +218,7 @@ constexpr int kFwdUnroll = 1;
 constexpr int64_t kFwdTargetBlocks = 2048;
 constexpr int64_t kFwdMaxSteps = 64;
 constexpr int kBwdUnroll = 1;
+constexpr int64_t kBwdMaxGrid = int64_t(1) << 20;   // workgroups loop over tiles beyond this
 
 template <typename T>
 hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, int wdt, void* y, int64_t n,
@@ -235,21 +242,21 @@ hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, int wdt, void* 
 
 template <typename T>
 hipError_t bwd_typed(const void* dy, const void* x, int64_t ld_x, const void* w, int wdt,
-                     void* dx, int64_t ld_dx, float* P, int64_t n, int64_t d,
-                     int64_t rows_per_tile, bool vec, hipStream_t s) {
+                     void* dx, int64_t ld_dx, float* P, int64_t n, int64_t d, int block_rows,
+                     int64_t tiles, bool vec, hipStream_t s) {
   constexpr int V = 16 / sizeof(T);
   const int v = vec ? V : 1;
   const int L = lanes_per_row(d, v);
   const int64_t cw = int64_t(L) * v;
-  const dim3 grid(unsigned((n + rows_per_tile - 1) / rows_per_tile), unsigned((d + cw - 1) / cw));
+  const dim3 grid(unsigned(tiles < kBwdMaxGrid ? tiles : kBwdMaxGrid), unsigned((d + cw - 1) / cw));
   if (vec)
     ws_bwd_kernel<T, V, kBwdUnroll><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
-        ld_dx, P, n, d, L, rows_per_tile);
+        ld_dx, P, n, d, L, block_rows, tiles);
   else
     ws_bwd_kernel<T, 1, kBwdUnroll><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
-        ld_dx, P, n, d, L, rows_per_tile);
+        ld_dx, P, n, d, L, block_rows, tiles);
   return hipGetLastError();
 }
 
@@ -267,12 +274,12 @@ hipError_t launch_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, v
 
 hipError_t launch_weighted_sum_bwd_stage1(const void* dy, const void* x, int64_t ld_x,
                                           const void* w, void* dx, int64_t ld_dx, float* P,
-                                          int64_t n, int64_t d, int64_t rows_per_tile,
+                                          int64_t n, int64_t d, int block_rows, int64_t tiles,
                                           int act, int wdt, bool vec, hipStream_t s) {
   switch (act) {
-    case kF32: return bwd_typed<float>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, rows_per_tile, vec, s);
-    case kF16: return bwd_typed<_Float16>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, rows_per_tile, vec, s);
-    default: return bwd_typed<bf16>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, rows_per_tile, vec, s);
+    case kF32: return bwd_typed<float>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, block_rows, tiles, vec, s);
+    case kF16: return bwd_typed<_Float16>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, block_rows, tiles, vec, s);
+    default: return bwd_typed<bf16>(dy, x, ld_x, w, wdt, dx, ld_dx, P, n, d, block_rows, tiles, vec, s);
   }
 }
 

@@ -156,6 +156,33 @@ def ws_worked_tiling_case(impl):
     return max(rel(P.sum(axis=0), gw), rel(P[-1], last))
 
 
+def ws_interleaved_tiles(impl):
+    """Rows dealt to tiles in blocks: 100 rows, blocks of 8, 3 tiles.  A one-hot
+    dy at row 37 (block 4, so tile 1) puts x[37] into P[1] and zeros elsewhere;
+    a dy that is 1 on rows 0..7 and 48..55 (blocks 0 and 6, both tile 0) puts
+    the column sums of those rows into P[0]."""
+    g = _rng(17)
+    n, d = 100, 5
+    x = g.standard_normal((n, d))
+    dy = np.zeros(n)
+    dy[37] = 1.0
+    P = impl.partials(x, dy, 8, 3)
+    if P.shape != (3, d):
+        return np.inf
+    err = max(rel(P[1], x[37]), float(np.max(np.abs(P[[0, 2]]))))
+    dy = np.zeros(n)
+    dy[0:8] = 1.0
+    dy[48:56] = 1.0
+    P = impl.partials(x, dy, 8, 3)
+    want = np.array([math.fsum(list(x[0:8, j]) + list(x[48:56, j])) for j in range(d)])
+    err = max(err, rel(P[0], want), float(np.max(np.abs(P[1:]))))
+    # the ragged last block (rows 96..99, block 12) belongs to tile 0
+    dy = np.zeros(n)
+    dy[99] = 2.0
+    P = impl.partials(x, dy, 8, 3)
+    return max(err, rel(P[0], 2.0 * x[99]), float(np.max(np.abs(P[1:]))))
+
+
 # ----------------------------------------------------------------------------- scaled SiLU
 
 def silu_sigmoid_vs_expit(impl):
@@ -408,6 +435,7 @@ PINS = {
         ("bilinearity", ws_bilinear, 1e-13),
         ("accumulate", ws_accumulate, 1e-13),
         ("worked_tiling_case", ws_worked_tiling_case, 1e-12),
+        ("interleaved_tiles", ws_interleaved_tiles, 1e-15),
     ],
     "scaled_silu": [
         ("sigmoid_vs_expit", silu_sigmoid_vs_expit, 1e-15),

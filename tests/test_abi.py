@@ -66,13 +66,23 @@ def test_version_and_strings():
 
 def test_tiling_queries():
     # the worked example: 100 rows in tiles of 32 -> 4 partial rows of 64 fp32
-    assert rwb.vjp_weighted_sum_rows_per_tile(100, 32) == 32
+    assert rwb.vjp_weighted_sum_tiling(100, 32) == (32, 4)
     assert rwb.vjp_weighted_sum_bwd_workspace_size(100, 64, 32) == 4 * 64 * 4
-    # automatic tiling depends only on the row count
-    assert rwb.vjp_weighted_sum_rows_per_tile(100, 0) == 32
-    assert rwb.vjp_weighted_sum_rows_per_tile(1 << 20, 0) == 512
-    assert rwb.vjp_weighted_sum_bwd_workspace_size(1 << 20, 256, 0) == 2048 * 256 * 4
-    assert rwb.vjp_weighted_sum_rows_per_tile(-1, 0) == -1
+    # automatic tiling depends only on the row count: blocks of 32 rows dealt
+    # round-robin to at most 1024 tiles
+    assert rwb.vjp_weighted_sum_tiling(100, 0) == (32, 4)
+    assert rwb.vjp_weighted_sum_tiling(32768, 0) == (32, 1024)
+    assert rwb.vjp_weighted_sum_tiling(32767, 0) == (32, 1024)
+    assert rwb.vjp_weighted_sum_tiling(32736, 0) == (32, 1023)
+    assert rwb.vjp_weighted_sum_tiling(1 << 20, 0) == (32, 1024)
+    assert rwb.vjp_weighted_sum_tiling(0, 0) == (32, 0)
+    assert rwb.vjp_weighted_sum_bwd_workspace_size(1 << 20, 256, 0) == 1024 * 256 * 4
+    assert rwb.vjp_weighted_sum_tiling(7, 1 << 30) == (1 << 30, 1)
+    assert L.vjp_weighted_sum_tiling(-1, 0, None, None) == EINVAL
+    i64 = ctypes.c_int64
+    assert L.vjp_weighted_sum_tiling(10, (1 << 30) + 1, ctypes.byref(i64()), ctypes.byref(i64())) == EINVAL
+    assert L.vjp_weighted_sum_tiling(10, 0, None, ctypes.byref(i64())) == EINVAL
+    assert rwb.vjp_weighted_sum_bwd_workspace_size(10, 4, (1 << 30) + 1) == 0
     assert rwb.vjp_scaled_silu_elems_per_tile(1 << 24) == 4096
     assert rwb.vjp_scaled_silu_bwd_workspace_size(1 << 24) == 4096 * 4
     assert rwb.vjp_scaled_silu_elems_per_tile(7) == 2048

@@ -60,12 +60,12 @@ def run_case(rwb, n, d, act, wdt, seed, ld=None, offset=0, rows_per_tile=0, accu
     else:
         reps.append(pointwise(dx_host, gx_ref, act, name="dx"))
     reps.append(reduced(to_host(dwg.t, "f32"), gw_ref, name="dw"))
-    rpt = rwb.vjp_weighted_sum_rows_per_tile(n, rows_per_tile)
+    br, tiles = rwb.vjp_weighted_sum_tiling(n, rows_per_tile)
     if n > 0 and d > 0:
         P = to_host(wsg.t, "f32").reshape(-1, d)
-        P_ref = ws.partials(x64, dy64, rpt)
+        P_ref = ws.partials(x64, dy64, br, tiles)
         assert P.shape == P_ref.shape
-        reps.append(pointwise(P, P_ref, "f32", S=ws.partials(np.abs(x64), np.abs(dy64), rpt),
+        reps.append(pointwise(P, P_ref, "f32", S=ws.partials(np.abs(x64), np.abs(dy64), br, tiles),
                               name="partials"))
     for r in reps:
         print("   ", r, flush=True)
@@ -106,6 +106,14 @@ def test_rows_per_tile(gpu_lib, rpt):
     run_case(gpu_lib, 1000, 64, "bf16", "bf16", seed=13, rows_per_tile=rpt, accumulate=True)
 
 
+@pytest.mark.parametrize("n,d", [(32768 + 32 * 9 + 5, 64), (70001, 256), (131072, 40)])
+def test_round_robin_tiles(gpu_lib, n, d):
+    """Automatic tiling past 1024 blocks: several blocks per tile, a ragged last block."""
+    br, tiles = gpu_lib.vjp_weighted_sum_tiling(n, 0)
+    assert br == 32 and tiles == 1024
+    run_case(gpu_lib, n, d, "bf16", "bf16", seed=19 + n, accumulate=True)
+
+
 def test_batch1_vs_batch7(gpu_lib):
     """A missing batch reduction passes at batch 1 and fails at batch 7."""
     run_case(gpu_lib, 1, 64, "f32", "f32", seed=17)
@@ -138,12 +146,12 @@ def test_large_batch_full_size(gpu_lib):
     xd, wd, dyd = to_dev(x, "bf16").view(n, d), to_dev(w, "bf16"), to_dev(dy, "bf16")
     y = gpu_lib.vjp_weighted_sum_fwd(xd, wd)
     dx, dw = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd)
-    rpt = gpu_lib.vjp_weighted_sum_rows_per_tile(n, 0)
+    br, tiles = gpu_lib.vjp_weighted_sum_tiling(n, 0)
     need = gpu_lib.vjp_weighted_sum_bwd_workspace_size(n, d, 0)
     wsb = torch.empty(need // 4, dtype=torch.float32, device=DEV)
     dx2, dw2 = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd, workspace=wsb)
     torch.cuda.synchronize()
-    assert rpt == 512 and need == 2048 * 256 * 4
+    assert (br, tiles) == (32, 1024) and need == 1024 * 256 * 4
 
     w64, dy64 = synth.to_f64(w, "bf16"), synth.to_f64(dy, "bf16")
     rows = pick_rows(n, 4096, 1)
@@ -155,11 +163,16 @@ def test_large_batch_full_size(gpu_lib):
     gx_ref, _ = ws.bwd(dy64[rows], xs, w64)
     r_dx = exact(to_host(dx, "bf16")[rows], to_storage(round_to(gx_ref, "bf16"), "bf16"), "bf16",
                  name="dx(sampled)")
-    # grad_w and the stage-1 partials over all rows, from the oracle's partials
-    P_ref = np.concatenate([ws.partials(synth.to_f64(x[i:i + 65536], "bf16"), dy64[i:i + 65536], rpt)
-                            for i in range(0, n, 65536)])
-    Pa = np.concatenate([ws.partials(np.abs(synth.to_f64(x[i:i + 65536], "bf16")), np.abs(dy64[i:i + 65536]), rpt)
-                         for i in range(0, n, 65536)])
+    # grad_w and the stage-1 partials over all rows, from the oracle's partials:
+    # a chunk of br * tiles rows starts at block 0 of the round-robin, so the
+    # partials of the chunks add tile by tile
+    chunk = br * tiles
+    P_ref = np.zeros((tiles, d))
+    Pa = np.zeros((tiles, d))
+    for i in range(0, n, chunk):
+        xc = synth.to_f64(x[i:i + chunk], "bf16")
+        P_ref += ws.partials(xc, dy64[i:i + chunk], br, tiles)
+        Pa += ws.partials(np.abs(xc), np.abs(dy64[i:i + chunk]), br, tiles)
     r_P = pointwise(to_host(wsb, "f32").reshape(-1, d), P_ref, "f32", S=Pa, name="partials")
     r_dw = reduced(to_host(dw2, "f32"), P_ref.sum(axis=0), name="dw")
     for r in (r_y, r_dx, r_P, r_dw):

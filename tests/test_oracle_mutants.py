@@ -37,9 +37,23 @@ def _ws_bwd_overwrites(dy, x, w, grad_w_old=None):
     return ws.bwd(dy, x, w, None)                  # ignores the existing gradient
 
 
-def _ws_partials_off_by_one(x, dy, rows_per_tile):
-    P = ws.partials(x, dy, rows_per_tile)
-    P[-1] = np.sum(x[(P.shape[0] - 1) * rows_per_tile + 1:] * dy[(P.shape[0] - 1) * rows_per_tile + 1:, None], axis=0)
+def _ws_partials_off_by_one(x, dy, block_rows, tiles=None):
+    P = ws.partials(x, dy, block_rows, tiles)
+    if tiles is None:
+        P[-1] = np.sum(x[(P.shape[0] - 1) * block_rows + 1:] * dy[(P.shape[0] - 1) * block_rows + 1:, None], axis=0)
+    return P
+
+
+def _ws_partials_grouped(x, dy, block_rows, tiles=None):
+    """Deals consecutive runs of blocks to a tile instead of round-robin."""
+    n = x.shape[0]
+    nb = ws.n_tiles(n, block_rows)
+    T = nb if tiles is None else tiles
+    per = -(-nb // T)
+    P = np.zeros((T, x.shape[1]))
+    for b in range(nb):
+        lo, hi = b * block_rows, min((b + 1) * block_rows, n)
+        P[b // per] += np.sum(x[lo:hi] * dy[lo:hi, None], axis=0)
     return P
 
 
@@ -105,6 +119,7 @@ MUTANTS = [
     ("weighted_sum", "bwd_overwrites_grad", _ns(ws, bwd=_ws_bwd_overwrites)),
     ("weighted_sum", "fwd_sign", _ns(ws, fwd=lambda x, w: -ws.fwd(x, w))),
     ("weighted_sum", "partials_off_by_one", _ns(ws, partials=_ws_partials_off_by_one)),
+    ("weighted_sum", "partials_grouped_blocks", _ns(ws, partials=_ws_partials_grouped)),
     ("scaled_silu", "bwd_missing_term", _ns(silu, bwd=_silu_bwd_missing_term)),
     ("scaled_silu", "bwd_sign", _ns(silu, bwd=_silu_bwd_sign)),
     ("scaled_silu", "dw_without_x", _ns(silu, bwd=_silu_dw_without_x)),
