@@ -18,7 +18,10 @@ read and write once; listed per op in `per_op`) divided by the measured step
 time.  Per-op durations come from HIP events recorded on the stream the
 kernels are launched on.  The `roofline` object is for the op with the
 largest share of the step; `cpu_baseline` times the fp64 CPU oracle on a
-bounded sample of the same workloads on one host core.
+bounded sample of the same workloads on one host core.  `extras` times the
+save-the-statistics variants (softmax forward writing the row logsumexp and
+the backward rebuilding y from it; the split cross-entropy forward and
+backward) on the same inputs, after and outside the step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -82,6 +85,25 @@ def bytes_xent(r, c, es=2):
     # logits read, dlogits written, targets read (main kernel and finalize),
     # row_max / row_lse written, row losses written then read, loss + count written
     return 2 * r * c * es + 2 * r * 4 + 2 * r * 4 + 2 * r * 4 + 8
+
+
+def bytes_softmax_fwd_lse(r, c, es=2):
+    return 2 * r * c * es + 4 * r
+
+
+def bytes_softmax_bwd_lse(r, c, es=2):
+    return 3 * r * c * es + 4 * r
+
+
+def bytes_xent_fwd(r, c, es=2):
+    # logits read once, targets read (main kernel and finalize), row_lse written,
+    # row losses written then read, loss + count written
+    return r * c * es + 2 * r * 4 + r * 4 + 2 * r * 4 + 8
+
+
+def bytes_xent_bwd(r, c, es=2):
+    # logits read, dlogits written, targets and row_lse read, dloss read
+    return 2 * r * c * es + 2 * r * 4 + 4
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -291,6 +313,46 @@ def main() -> int:
                        "frac_of_peak": round(gbs / PEAK_GBS, 4),
                        "elements_per_s": round(nelem / (ms * 1e-3), 1)})
     dom = max(per_op, key=lambda o: o["ms"])
+
+    # Save-the-statistics variants (softmax with saved logsumexp, split
+    # cross-entropy), timed after the step on the same inputs; not part of it.
+    mlse = torch.empty(r_m, dtype=torch.float32, device=dev)
+    dz2 = torch.empty_like(z)
+    dloss = torch.ones(1, dtype=torch.float32, device=dev)
+    extra_ops = [
+        ("softmax_fwd_lse", L.vjp_softmax_fwd_lse,
+         (P(mx), c_m, P(my), c_m, P(mlse), r_m, c_m, BF16, stream), bytes_softmax_fwd_lse(r_m, c_m),
+         r_m * c_m),
+        ("softmax_bwd_lse", L.vjp_softmax_bwd_lse,
+         (P(mg), c_m, P(mx), c_m, P(mlse), P(mdx), c_m, r_m, c_m, BF16, stream),
+         bytes_softmax_bwd_lse(r_m, c_m), r_m * c_m),
+        ("softmax_xent_fwd", L.vjp_softmax_xent_fwd,
+         (P(z), c_x, P(tg), r_x, c_x, BF16, P(loss), None, P(rlse), P(ninv), P(xws), xws.numel(),
+          stream), bytes_xent_fwd(r_x, c_x), r_x * c_x),
+        ("softmax_xent_bwd", L.vjp_softmax_xent_bwd,
+         (P(z), c_x, P(tg), P(rlse), r_x, c_x, BF16, P(dloss), P(dz2), c_x, stream),
+         bytes_xent_bwd(r_x, c_x), r_x * c_x),
+    ]
+    n_extra = max(3, args.steps // 2)
+    xevs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+             for _ in extra_ops] for _ in range(n_extra + 1)]
+    for k in range(n_extra + 1):          # the first round is a warmup
+        for i, (name, fn, a, _, _) in enumerate(extra_ops):
+            xevs[k][i][0].record()
+            st = fn(*a)
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st} ({rwb.vjp_last_error()})")
+            xevs[k][i][1].record()
+    torch.cuda.synchronize()
+    extras = []
+    for i, (name, _, _, nbytes, nelem) in enumerate(extra_ops):
+        ms = sum(xevs[k][i][0].elapsed_time(xevs[k][i][1]) for k in range(1, n_extra + 1)) / n_extra
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        extras.append({"op": name, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
+                       "frac_of_peak": round(gbs / PEAK_GBS, 4),
+                       "elements_per_s": round(nelem / (ms * 1e-3), 1)})
+    print(f"[bench] timed the statistics-saving variants ({n_extra} rounds)", file=sys.stderr, flush=True)
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -318,6 +380,7 @@ def main() -> int:
             "frac_of_peak": round(value / PEAK_GBS, 4),
         },
         "per_op": per_op,
+        "extras": extras,
         "roofline": {
             "kernel": dom["op"],
             "bound": "hbm",

@@ -180,6 +180,23 @@ int vjp_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t 
 int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, void* dx,
                     int64_t ld_dx, int64_t rows, int64_t cols, int act, vjp_stream_t stream);
 
+/* Save-the-statistics form ("Backprop for kernel writers", the softmax
+ * section after 04: y can be recomputed from the saved max and logsumexp;
+ * section 07 "Fusion": keep only L = m + log l per row, rebuild any
+ * probability as exp(x - L)).
+ * vjp_softmax_fwd_lse: as vjp_softmax_fwd and also row_lse[r] = L_r (fp32,
+ * [rows], required).  y may be NULL (then ld_y is ignored): the call computes
+ * the row logsumexp alone, reading x once.
+ * vjp_softmax_bwd_lse: dx from dy, the forward's INPUT x and row_lse; y is
+ * rebuilt in fp32 as exp(x - L) (never rounded to the storage type), then
+ * dx = y (dy - s), s = sum_j dy_j y_j.  Reads dy and x, writes dx. */
+int vjp_softmax_fwd_lse(const void* x, int64_t ld_x, void* y, int64_t ld_y, float* row_lse,
+                        int64_t rows, int64_t cols, int act, vjp_stream_t stream);
+
+int vjp_softmax_bwd_lse(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
+                        const float* row_lse, void* dx, int64_t ld_dx, int64_t rows,
+                        int64_t cols, int act, vjp_stream_t stream);
+
 /* ---------------------------------------------------------------- softmax + cross-entropy
  * Fused forward and backward of the mean cross-entropy of a row softmax:
  *   row_max[r] = m_r = max_j z[r, j]
@@ -206,6 +223,29 @@ int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32_t* targ
                              float* loss, float* row_max, float* row_lse, void* dlogits,
                              int64_t ld_dlogits, int32_t* n_invalid, void* workspace,
                              size_t workspace_bytes, vjp_stream_t stream);
+
+/* Split form of the above ("Backprop for kernel writers", section 07
+ * "Fusion": the forward keeps only the row statistics, the backward rebuilds
+ * p = exp(z - L) from them):
+ * vjp_softmax_xent_fwd: loss, row_lse (required), row_max (optional, NULL
+ * skips it), n_invalid (optional), exactly as vjp_softmax_xent_fwd_bwd but
+ * without the logit gradient; the logits are read once.  Same workspace.
+ * vjp_softmax_xent_bwd: dlogits[r, j] = (dloss[0] / rows) * (exp(z[r, j] -
+ * row_lse[r]) - [j == t_r]); dloss is ONE fp32 value in DEVICE memory (the
+ * upstream gradient of the mean loss, read by the kernel: no host
+ * synchronisation), divided by rows in fp32.  Rows with an invalid target
+ * get no one-hot term.  dlogits may be the logits buffer itself (same
+ * pointer and leading dimension: computed in place); any other overlap is
+ * VJP_EALIAS. */
+int vjp_softmax_xent_fwd(const void* logits, int64_t ld, const int32_t* targets, int64_t rows,
+                         int64_t classes, int act, float* loss, float* row_max, float* row_lse,
+                         int32_t* n_invalid, void* workspace, size_t workspace_bytes,
+                         vjp_stream_t stream);
+
+int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* targets,
+                         const float* row_lse, int64_t rows, int64_t classes, int act,
+                         const float* dloss, void* dlogits, int64_t ld_dlogits,
+                         vjp_stream_t stream);
 
 #ifdef __cplusplus
 }

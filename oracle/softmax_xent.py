@@ -17,6 +17,11 @@ Definitions (R rows, C classes, target t_r):
 grad_scale is d(loss_total)/d(loss) / R; for the mean loss with unit upstream
 gradient it is 1 / R.
 
+Split form (section 07: the forward keeps only the row statistics and the
+backward rebuilds p = exp(z - lse)): :func:`fwd` gives the loss and the
+statistics; :func:`bwd` gives dz = (dloss / R) * (softmax(z) - onehot) for an
+upstream gradient dloss of the mean loss.
+
 Targets outside [0, C) are not defined by the pages.  Reading taken here:
 such a row's loss is NaN (so is the mean), its logit gradient has no one-hot
 term, and the rows are counted in ``n_invalid``.
@@ -50,3 +55,18 @@ def fwd_bwd(z: np.ndarray, targets: np.ndarray, grad_scale: float):
         "dz": dz,
         "n_invalid": int(np.count_nonzero(~valid)),
     }
+
+
+def fwd(z: np.ndarray, targets: np.ndarray):
+    """Returns dict(loss, row_loss, row_max, row_lse, n_invalid) -- no gradient."""
+    out = fwd_bwd(z, targets, 0.0)
+    del out["dz"]
+    return out
+
+
+def bwd(z: np.ndarray, targets: np.ndarray, dloss: float) -> np.ndarray:
+    """dz[r, j] = (dloss / R) * (softmax(z)[r, j] - [j == t_r]); no one-hot term
+    for a target outside [0, C)."""
+    z = np.asarray(z, np.float64)
+    R = z.shape[0]
+    return fwd_bwd(z, targets, float(dloss) / R if R > 0 else 0.0)["dz"]

@@ -51,7 +51,12 @@ _SIGS = {
     "vjp_scaled_silu_bwd": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _int, _vp, _sz, _vp], _int),
     "vjp_softmax_fwd": ([_vp, _i64, _vp, _i64, _i64, _i64, _int, _vp], _int),
     "vjp_softmax_bwd": ([_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _int, _vp], _int),
+    "vjp_softmax_fwd_lse": ([_vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _vp], _int),
+    "vjp_softmax_bwd_lse": ([_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _vp], _int),
     "vjp_softmax_xent_workspace_size": ([_i64], _sz),
+    "vjp_softmax_xent_fwd": ([_vp, _i64, _vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                             _int),
+    "vjp_softmax_xent_bwd": ([_vp, _i64, _vp, _vp, _i64, _i64, _int, _vp, _vp, _i64, _vp], _int),
     "vjp_softmax_xent_fwd_bwd": ([_vp, _i64, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp,
                                   _i64, _vp, _vp, _sz, _vp], _int),
 }
@@ -258,6 +263,38 @@ def vjp_softmax_bwd(dy, y, dx=None):
     return dx
 
 
+def vjp_softmax_fwd_lse(x, y=None, row_lse=None, write_y=True):
+    """(y, row_lse): softmax and the row logsumexp L = m + log l (fp32 [rows]).
+
+    write_y=False computes row_lse alone (y is returned as None)."""
+    rows, cols = x.shape
+    if write_y and y is None:
+        y = torch.empty_like(x)
+    if row_lse is None:
+        row_lse = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if y is not None:
+        _expect(y, (rows, cols), x.dtype, x.device, "y")
+    _expect(row_lse, (rows,), torch.float32, x.device, "row_lse")
+    _check(lib.vjp_softmax_fwd_lse(_ptr(x), _ld(x), _ptr(y), _ld(y) if y is not None else 0,
+                                   _ptr(row_lse), rows, cols, _dt(x), _stream(x)),
+           "vjp_softmax_fwd_lse")
+    return y, row_lse
+
+
+def vjp_softmax_bwd_lse(dy, x, row_lse, dx=None):
+    """dx from dy, the forward's input x and its row logsumexp (y rebuilt on chip)."""
+    rows, cols = x.shape
+    if dx is None:
+        dx = torch.empty_like(x)
+    _expect(dy, (rows, cols), x.dtype, x.device, "dy")
+    _expect(row_lse, (rows,), torch.float32, x.device, "row_lse")
+    _expect(dx, (rows, cols), x.dtype, x.device, "dx")
+    _check(lib.vjp_softmax_bwd_lse(_ptr(dy), _ld(dy), _ptr(x), _ld(x), _ptr(row_lse), _ptr(dx),
+                                   _ld(dx), rows, cols, _dt(x), _stream(x)),
+           "vjp_softmax_bwd_lse")
+    return dx
+
+
 # ----------------------------------------------------------------- softmax cross-entropy
 
 def vjp_softmax_xent_workspace_size(rows: int) -> int:
@@ -300,3 +337,49 @@ def vjp_softmax_xent_fwd_bwd(logits, targets, grad_scale=None, dlogits=None, los
                                         _stream(logits)), "vjp_softmax_xent_fwd_bwd")
     return {"loss": loss, "row_max": row_max, "row_lse": row_lse, "dlogits": dlogits,
             "n_invalid": n_invalid}
+
+
+def vjp_softmax_xent_fwd(logits, targets, loss=None, row_lse=None, row_max=None, want_max=False,
+                         n_invalid=None, count_invalid=True, workspace=None):
+    """Forward of the split form: dict(loss [1], row_lse [R], row_max [R] or None,
+    n_invalid [1] int32 or None).  The logits are read once; no gradient is formed."""
+    rows, classes = logits.shape
+    dev = logits.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32) if loss is None else loss
+    row_lse = torch.empty(rows, **f32) if row_lse is None else row_lse
+    if want_max and row_max is None:
+        row_max = torch.empty(rows, **f32)
+    if count_invalid and n_invalid is None:
+        n_invalid = torch.empty(1, dtype=torch.int32, device=dev)
+    _expect(targets, (rows,), torch.int32, dev, "targets")
+    _expect(loss, (1,), torch.float32, dev, "loss")
+    _expect(row_lse, (rows,), torch.float32, dev, "row_lse")
+    if row_max is not None:
+        _expect(row_max, (rows,), torch.float32, dev, "row_max")
+    if n_invalid is not None:
+        _expect(n_invalid, (1,), torch.int32, dev, "n_invalid")
+    ws = _workspace(vjp_softmax_xent_workspace_size(rows), logits, workspace)
+    _check(lib.vjp_softmax_xent_fwd(_ptr(logits), _ld(logits), _ptr(_flat(targets)), rows, classes,
+                                    _dt(logits), _ptr(loss), _ptr(row_max), _ptr(row_lse),
+                                    _ptr(n_invalid), _ptr(ws), _nbytes(ws), _stream(logits)),
+           "vjp_softmax_xent_fwd")
+    return {"loss": loss, "row_lse": row_lse, "row_max": row_max, "n_invalid": n_invalid}
+
+
+def vjp_softmax_xent_bwd(logits, targets, row_lse, dloss, dlogits=None):
+    """dlogits = (dloss / R) (exp(z - row_lse) - onehot); dloss is a one-element
+    fp32 device tensor.  dlogits may be ``logits`` itself (in place)."""
+    rows, classes = logits.shape
+    dev = logits.device
+    if dlogits is None:
+        dlogits = torch.empty_like(logits)
+    _expect(targets, (rows,), torch.int32, dev, "targets")
+    _expect(row_lse, (rows,), torch.float32, dev, "row_lse")
+    _expect(dloss, (1,), torch.float32, dev, "dloss")
+    _expect(dlogits, (rows, classes), logits.dtype, dev, "dlogits")
+    _check(lib.vjp_softmax_xent_bwd(_ptr(logits), _ld(logits), _ptr(_flat(targets)),
+                                    _ptr(row_lse), rows, classes, _dt(logits), _ptr(_flat(dloss)),
+                                    _ptr(dlogits), _ld(dlogits), _stream(logits)),
+           "vjp_softmax_xent_bwd")
+    return dlogits

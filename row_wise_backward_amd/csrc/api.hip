@@ -298,53 +298,94 @@ VJP_API int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, v
 
 // ------------------------------------------------------------------ softmax
 
-VJP_API int vjp_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
-                            int64_t cols, int act, vjp_stream_t stream) {
+namespace {
+
+// Shared body of the two softmax forwards (row_lse null: y required).
+int softmax_fwd_impl(const void* x, int64_t ld_x, void* y, int64_t ld_y, float* row_lse,
+                     int64_t rows, int64_t cols, int act, vjp_stream_t stream) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (rows < 0 || cols < 0) return fail(VJP_EINVAL, "negative size");
   if (rows > 0 && cols == 0) return fail(VJP_EINVAL, "softmax over zero columns");
   const int es = dtype_size(act);
   VJP_TRY(check_matrix("x", x, rows, cols, ld_x, es));
-  VJP_TRY(check_matrix("y", y, rows, cols, ld_y, es));
-  VJP_TRY(check_alias({span(y, mat_bytes(rows, cols, ld_y, es), "y")},
+  if (y != nullptr || row_lse == nullptr) VJP_TRY(check_matrix("y", y, rows, cols, ld_y, es));
+  if (row_lse != nullptr) VJP_TRY(check_vector("row_lse", row_lse, rows, 4));
+  VJP_TRY(check_alias({span(y, y ? mat_bytes(rows, cols, ld_y, es) : 0, "y"),
+                       span(row_lse, row_lse ? rows * 4 : 0, "row_lse")},
                       {span(x, mat_bytes(rows, cols, ld_x, es), "x")}));
-  const bool vec = rows_vec_ok(x, ld_x, es) && rows_vec_ok(y, ld_y, es);
+  const bool vec = rows_vec_ok(x, ld_x, es) && (y == nullptr || rows_vec_ok(y, ld_y, es));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
     const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
-    const hipError_t e = launch_softmax_fwd(static_cast<const char*>(x) + r0 * ld_x * es, ld_x,
-                                            static_cast<char*>(y) + r0 * ld_y * es, ld_y, nr,
-                                            cols, act, vec, s);
+    const hipError_t e = launch_softmax_fwd(
+        static_cast<const char*>(x) + r0 * ld_x * es, ld_x,
+        y ? static_cast<char*>(y) + r0 * ld_y * es : nullptr, ld_y,
+        row_lse ? row_lse + r0 : nullptr, nr, cols, act, vec, s);
     if (e != hipSuccess) return hip_status(e, "softmax_fwd");
   }
   return ok();
 }
 
-VJP_API int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y,
-                            void* dx, int64_t ld_dx, int64_t rows, int64_t cols, int act,
-                            vjp_stream_t stream) {
+// Shared body of the two softmax backwards (row_lse null: src is y, else x).
+int softmax_bwd_impl(const void* dy, int64_t ld_dy, const void* src, int64_t ld_src,
+                     const float* row_lse, void* dx, int64_t ld_dx, int64_t rows, int64_t cols,
+                     int act, vjp_stream_t stream) {
+  const char* src_name = row_lse ? "x" : "y";
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (rows < 0 || cols < 0) return fail(VJP_EINVAL, "negative size");
   if (rows > 0 && cols == 0) return fail(VJP_EINVAL, "softmax over zero columns");
   const int es = dtype_size(act);
   VJP_TRY(check_matrix("dy", dy, rows, cols, ld_dy, es));
-  VJP_TRY(check_matrix("y", y, rows, cols, ld_y, es));
+  VJP_TRY(check_matrix(src_name, src, rows, cols, ld_src, es));
   VJP_TRY(check_matrix("dx", dx, rows, cols, ld_dx, es));
   VJP_TRY(check_alias({span(dx, mat_bytes(rows, cols, ld_dx, es), "dx")},
                       {span(dy, mat_bytes(rows, cols, ld_dy, es), "dy"),
-                       span(y, mat_bytes(rows, cols, ld_y, es), "y")}));
-  const bool vec = rows_vec_ok(dy, ld_dy, es) && rows_vec_ok(y, ld_y, es) &&
+                       span(src, mat_bytes(rows, cols, ld_src, es), src_name),
+                       span(row_lse, row_lse ? rows * 4 : 0, "row_lse")}));
+  const bool vec = rows_vec_ok(dy, ld_dy, es) && rows_vec_ok(src, ld_src, es) &&
                    rows_vec_ok(dx, ld_dx, es);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
     const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
     const hipError_t e = launch_softmax_bwd(
         static_cast<const char*>(dy) + r0 * ld_dy * es, ld_dy,
-        static_cast<const char*>(y) + r0 * ld_y * es, ld_y,
-        static_cast<char*>(dx) + r0 * ld_dx * es, ld_dx, nr, cols, act, vec, s);
+        static_cast<const char*>(src) + r0 * ld_src * es, ld_src,
+        row_lse ? row_lse + r0 : nullptr, static_cast<char*>(dx) + r0 * ld_dx * es, ld_dx, nr,
+        cols, act, vec, s);
     if (e != hipSuccess) return hip_status(e, "softmax_bwd");
   }
   return ok();
+}
+
+}  // namespace
+
+VJP_API int vjp_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+                            int64_t cols, int act, vjp_stream_t stream) {
+  return softmax_fwd_impl(x, ld_x, y, ld_y, nullptr, rows, cols, act, stream);
+}
+
+VJP_API int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y,
+                            void* dx, int64_t ld_dx, int64_t rows, int64_t cols, int act,
+                            vjp_stream_t stream) {
+  return softmax_bwd_impl(dy, ld_dy, y, ld_y, nullptr, dx, ld_dx, rows, cols, act, stream);
+}
+
+VJP_API int vjp_softmax_fwd_lse(const void* x, int64_t ld_x, void* y, int64_t ld_y,
+                                float* row_lse, int64_t rows, int64_t cols, int act,
+                                vjp_stream_t stream) {
+  if (row_lse == nullptr && rows > 0) return fail(VJP_EINVAL, "row_lse is null");
+  if (y == nullptr) ld_y = cols;   // ignored
+  if (row_lse == nullptr && y == nullptr) return rows < 0 || cols < 0 ? fail(VJP_EINVAL, "negative size") : ok();
+  return softmax_fwd_impl(x, ld_x, y, ld_y, row_lse, rows, cols, act, stream);
+}
+
+VJP_API int vjp_softmax_bwd_lse(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
+                                const float* row_lse, void* dx, int64_t ld_dx, int64_t rows,
+                                int64_t cols, int act, vjp_stream_t stream) {
+  if (row_lse == nullptr && rows > 0) return fail(VJP_EINVAL, "row_lse is null");
+  if (row_lse != nullptr && !aligned(row_lse, 4)) return fail(VJP_EALIGN, "row_lse is not 4-byte aligned");
+  if (rows == 0) return softmax_bwd_impl(dy, ld_dy, x, ld_x, nullptr, dx, ld_dx, 0, cols, act, stream);
+  return softmax_bwd_impl(dy, ld_dy, x, ld_x, row_lse, dx, ld_dx, rows, cols, act, stream);
 }
 
 // ------------------------------------------------------------------ softmax cross-entropy
@@ -396,4 +437,81 @@ VJP_API int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32
   }
   return hip_status(launch_xent_finalize(row_loss, targets, rows, classes, loss, n_invalid, s),
                     "softmax_xent finalize");
+}
+
+VJP_API int vjp_softmax_xent_fwd(const void* logits, int64_t ld, const int32_t* targets,
+                                 int64_t rows, int64_t classes, int act, float* loss,
+                                 float* row_max, float* row_lse, int32_t* n_invalid,
+                                 void* workspace, size_t workspace_bytes, vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (rows < 0 || classes < 0) return fail(VJP_EINVAL, "negative size");
+  if (classes == 0) return fail(VJP_EINVAL, "cross-entropy over zero classes");
+  if (classes > INT32_MAX) return fail(VJP_EINVAL, "classes beyond int32 targets");
+  const int es = dtype_size(act);
+  VJP_TRY(check_matrix("logits", logits, rows, classes, ld, es));
+  VJP_TRY(check_vector("targets", targets, rows, 4));
+  VJP_TRY(check_vector("loss", loss, 1, 4));
+  if (row_max != nullptr) VJP_TRY(check_vector("row_max", row_max, rows, 4));
+  VJP_TRY(check_vector("row_lse", row_lse, rows, 4));
+  if (n_invalid && !aligned(n_invalid, 4)) return fail(VJP_EALIGN, "n_invalid is not 4-byte aligned");
+  const size_t need = vjp_softmax_xent_workspace_size(rows);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(VJP_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned(workspace, 4)) return fail(VJP_EALIGN, "workspace is not 4-byte aligned");
+  }
+  VJP_TRY(check_alias({span(loss, 4, "loss"), span(row_max, row_max ? rows * 4 : 0, "row_max"),
+                       span(row_lse, rows * 4, "row_lse"),
+                       span(n_invalid, n_invalid ? 4 : 0, "n_invalid"),
+                       span(workspace, int64_t(need), "workspace")},
+                      {span(logits, mat_bytes(rows, classes, ld, es), "logits"),
+                       span(targets, rows * 4, "targets")}));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float* row_loss = static_cast<float*>(workspace);
+  const bool vec = rows_vec_ok(logits, ld, es);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
+    const hipError_t e = launch_softmax_xent_stats(
+        static_cast<const char*>(logits) + r0 * ld * es, ld, targets + r0, nr, classes, act,
+        row_max ? row_max + r0 : nullptr, row_lse + r0, row_loss + r0, vec, s);
+    if (e != hipSuccess) return hip_status(e, "softmax_xent_fwd");
+  }
+  return hip_status(launch_xent_finalize(row_loss, targets, rows, classes, loss, n_invalid, s),
+                    "softmax_xent_fwd finalize");
+}
+
+VJP_API int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* targets,
+                                 const float* row_lse, int64_t rows, int64_t classes, int act,
+                                 const float* dloss, void* dlogits, int64_t ld_dlogits,
+                                 vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (rows < 0 || classes < 0) return fail(VJP_EINVAL, "negative size");
+  if (classes == 0) return fail(VJP_EINVAL, "cross-entropy over zero classes");
+  if (classes > INT32_MAX) return fail(VJP_EINVAL, "classes beyond int32 targets");
+  const int es = dtype_size(act);
+  VJP_TRY(check_matrix("logits", logits, rows, classes, ld, es));
+  VJP_TRY(check_vector("targets", targets, rows, 4));
+  VJP_TRY(check_vector("row_lse", row_lse, rows, 4));
+  VJP_TRY(check_vector("dloss", dloss, 1, 4));
+  VJP_TRY(check_matrix("dlogits", dlogits, rows, classes, ld_dlogits, es));
+  // In place (dlogits == logits, same leading dimension) is allowed; any
+  // other overlap is rejected.
+  const bool in_place = dlogits == logits && ld_dlogits == ld;
+  VJP_TRY(check_alias({span(dlogits, mat_bytes(rows, classes, ld_dlogits, es), "dlogits")},
+                      {span(targets, rows * 4, "targets"), span(row_lse, rows * 4, "row_lse"),
+                       span(dloss, 4, "dloss"),
+                       span(in_place ? nullptr : logits, mat_bytes(rows, classes, ld, es),
+                            "logits")}));
+  if (rows == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool vec = rows_vec_ok(logits, ld, es) && rows_vec_ok(dlogits, ld_dlogits, es);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
+    const hipError_t e = launch_softmax_xent_bwd(
+        static_cast<const char*>(logits) + r0 * ld * es, ld, targets + r0, row_lse + r0, dloss,
+        rows, nr, classes, act, static_cast<char*>(dlogits) + r0 * ld_dlogits * es, ld_dlogits,
+        vec, s);
+    if (e != hipSuccess) return hip_status(e, "softmax_xent_bwd");
+  }
+  return ok();
 }

@@ -32,18 +32,30 @@ hipError_t launch_scaled_silu_bwd_stage1(const void* dy, const void* x, const fl
                                          void* dx, float* P, int64_t n, int64_t elems_per_tile,
                                          int act, bool vec, hipStream_t s);
 
-// Softmax.
-hipError_t launch_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+// Softmax.  row_lse may be null (forward: not written; backward: src is the
+// saved y).  With row_lse given, the backward's src is x.  A null y in the
+// forward writes the statistics only.
+hipError_t launch_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y,
+                              float* row_lse, int64_t rows, int64_t cols, int act, bool vec,
+                              hipStream_t s);
+hipError_t launch_softmax_bwd(const void* dy, int64_t ld_dy, const void* src, int64_t ld_src,
+                              const float* row_lse, void* dx, int64_t ld_dx, int64_t rows,
                               int64_t cols, int act, bool vec, hipStream_t s);
-hipError_t launch_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y,
-                              void* dx, int64_t ld_dx, int64_t rows, int64_t cols, int act,
-                              bool vec, hipStream_t s);
 
 // Softmax cross-entropy.
 hipError_t launch_softmax_xent(const void* z, int64_t ld, const int32_t* targets, int64_t rows,
                                int64_t classes, int act, float grad_scale, float* row_max,
                                float* row_lse, float* row_loss, void* dz, int64_t ld_dz,
                                bool vec, hipStream_t s);
+// Statistics only (row_max may be null): the forward of the split form.
+hipError_t launch_softmax_xent_stats(const void* z, int64_t ld, const int32_t* targets,
+                                     int64_t rows, int64_t classes, int act, float* row_max,
+                                     float* row_lse, float* row_loss, bool vec, hipStream_t s);
+// dz = (*dloss / total_rows) * (exp(z - row_lse) - onehot(t)) for `rows` rows.
+hipError_t launch_softmax_xent_bwd(const void* z, int64_t ld, const int32_t* targets,
+                                   const float* row_lse, const float* dloss, int64_t total_rows,
+                                   int64_t rows, int64_t classes, int act, void* dz,
+                                   int64_t ld_dz, bool vec, hipStream_t s);
 hipError_t launch_xent_finalize(const float* row_loss, const int32_t* targets, int64_t rows,
                                 int64_t classes, float* loss, int32_t* n_invalid,
                                 hipStream_t s);

@@ -105,6 +105,9 @@ __device__ __forceinline__ void exp_vec(const Vec<T, VEC>& r, float m, bool safe
   }
 }
 
+// Row logsumexp from the row max m and the row sum l of exp(x - m).
+__device__ __forceinline__ float row_lse_of(float m, float l) { return m + log2_fast(l) * kLn2; }
+
 // Loads the lane's K vectors of a row (padding reads as -inf) and returns the
 // lane's max over its elements and min over its valid elements.
 template <typename T, int VEC, int WAVES, int K>

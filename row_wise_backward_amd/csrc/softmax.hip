@@ -10,6 +10,13 @@
 // "Save vs recompute": the row max is a one-scalar-per-row statistic the
 // forward recomputes on chip.
 //
+// Save-statistics variant ("Backprop for kernel writers", the softmax section
+// after 04: save y, or recompute it from the saved max and logsumexp; section
+// 07 "Fusion": store only L = m + log l per row and rebuild any probability
+// as exp(x - L)): the forward can also write row_lse (and may skip y), and
+// the backward can take x and row_lse instead of y, recomputing
+// y = exp(x - L) on chip in fp32 in both of its passes.
+//
 // Resident path (rows up to 8 waves * 64 * K * VEC columns): the row is read
 // once into VGPRs (layout in rowops.hpp), the statistics are reduced with
 // wave butterflies and, for multi-wave rows, LDS in wave order, and the
@@ -29,8 +36,8 @@ namespace {
 // produce bitwise identical results.
 template <typename T, int VEC, int WAVES, int K, bool KEEP>
 __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_fwd_resident(
-    const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y, int64_t rows,
-    int64_t cols) {
+    const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y,
+    float* __restrict__ row_lse, int64_t rows, int64_t cols) {
   __shared__ float buf[2][WAVES];   // one slot per reduction of the row
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -65,6 +72,8 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_fwd_reside
   l = row_reduce_sum<WAVES>(l, buf[1]);
   const float inv = 1.0f / l;
   if constexpr (!KEEP) fence_row<T, VEC, K>(raw);
+  if (row_lse != nullptr && wv == 0 && lane == 0) row_lse[row] = row_lse_of(m, l);
+  if (y == nullptr) return;   // statistics only (uniform across the workgroup)
 
   T* yr = y + row * ld_y;
 #pragma unroll
@@ -87,10 +96,14 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_fwd_reside
   }
 }
 
-template <typename T, int VEC, int WAVES, int K>
+// Backward, resident.  FROM_LSE = false: `src` is the saved y.  FROM_LSE =
+// true: `src` is x and y = exp(x - row_lse) is rebuilt in fp32 in the s pass
+// and again in the output pass, so only the stored rows stay in VGPRs.
+template <typename T, int VEC, int WAVES, int K, bool FROM_LSE>
 __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_resident(
-    const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ y, int64_t ld_y,
-    T* __restrict__ dx, int64_t ld_dx, int64_t rows, int64_t cols) {
+    const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ src, int64_t ld_src,
+    const float* __restrict__ row_lse, T* __restrict__ dx, int64_t ld_dx, int64_t rows,
+    int64_t cols) {
   __shared__ float buf[2][WAVES];   // one slot per reduction of the row
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -101,23 +114,38 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_reside
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
   const int64_t lane_col = (int64_t(wv) * kWave + lane) * VEC;
   const T* gr = dy + row * ld_dy;
-  const T* yr = y + row * ld_y;
+  const T* sr = src + row * ld_src;
 
   Vec<T, VEC> rg[K], ry[K];
+  float L = 0.0f;
+  bool safe = false;
+  if constexpr (FROM_LSE) {
+    float mx, mn;
+    load_row_minmax<T, VEC, WAVES, K>(sr, cols, lane_col, ry, mx, mn);   // padding = -inf
+    L = row_lse[row];
+    safe = needs_denorm_exp(mn, L);
+  }
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (k * kStep < cols) {
       const int64_t col = k * kStep + lane_col;
       load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), rg[k]);
-      load_row_vec<T, VEC>(yr, col, cols, zero_of<T>(), ry[k]);
+      if constexpr (!FROM_LSE) load_row_vec<T, VEC>(sr, col, cols, zero_of<T>(), ry[k]);
     }
   }
   float s = 0.0f;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (k * kStep < cols) {
+      float yv[VEC];
+      if constexpr (FROM_LSE) {
+        exp_vec<T, VEC>(ry[k], L, safe, yv);
+      } else {
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(rg[k].v[i]), to_f32(ry[k].v[i]), s);
+        for (int i = 0; i < VEC; ++i) yv[i] = to_f32(ry[k].v[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(rg[k].v[i]), yv[i], s);
     }
   }
   s = row_reduce_sum<WAVES>(s, buf[0]);
@@ -130,9 +158,16 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_reside
     if (k * kStep < cols) {
       const int64_t col = k * kStep + lane_col;
       if (col < cols) {
+        float yv[VEC];
+        if constexpr (FROM_LSE) {
+          exp_vec<T, VEC>(ry[k], L, safe, yv);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) yv[i] = to_f32(ry[k].v[i]);
+        }
         float o[VEC];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) o[i] = to_f32(ry[k].v[i]) * (to_f32(rg[k].v[i]) - s);
+        for (int i = 0; i < VEC; ++i) o[i] = yv[i] * (to_f32(rg[k].v[i]) - s);
         store_row_vec<T, VEC>(dr, col, cols, o);
       }
     }
@@ -141,11 +176,11 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_reside
 
 template <typename T, int VEC>
 __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream(
-    const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y, int64_t cols) {
+    const T* __restrict__ x, int64_t ld_x, T* __restrict__ y, int64_t ld_y,
+    float* __restrict__ row_lse, int64_t cols) {
   __shared__ float bm[kStreamThreads / kWave], bl[kStreamThreads / kWave];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * ld_x;
-  T* yr = y + row * ld_y;
   float m = -__builtin_inff(), l = 0.0f;
   for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
     Vec<T, VEC> r;
@@ -155,6 +190,9 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream(
   }
   block_merge_ml(m, l, bm, bl);
   const float inv = 1.0f / l;
+  if (row_lse != nullptr && threadIdx.x == 0) row_lse[row] = row_lse_of(m, l);
+  if (y == nullptr) return;
+  T* yr = y + row * ld_y;
   for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
     Vec<T, VEC> r;
     load_row_vec<T, VEC>(xr, col, cols, neg_inf_of<T>(), r);
@@ -165,31 +203,42 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_fwd_stream(
   }
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool FROM_LSE>
 __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream(
-    const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ y, int64_t ld_y,
-    T* __restrict__ dx, int64_t ld_dx, int64_t cols) {
+    const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ src, int64_t ld_src,
+    const float* __restrict__ row_lse, T* __restrict__ dx, int64_t ld_dx, int64_t cols) {
   __shared__ float buf[kStreamThreads / kWave];
   const int64_t row = blockIdx.x;
   const T* gr = dy + row * ld_dy;
-  const T* yr = y + row * ld_y;
+  const T* sr = src + row * ld_src;
   T* dr = dx + row * ld_dx;
+  const float L = FROM_LSE ? row_lse[row] : 0.0f;
+  auto y_of = [&](const Vec<T, VEC>& b, float (&yv)[VEC]) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+      yv[i] = FROM_LSE ? exp2_denorm_safe((to_f32(b.v[i]) - L) * kLog2e) : to_f32(b.v[i]);
+  };
+  const T fill = FROM_LSE ? neg_inf_of<T>() : zero_of<T>();
   float s = 0.0f;
   for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
     Vec<T, VEC> a, b;
     load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), a);
-    load_row_vec<T, VEC>(yr, col, cols, zero_of<T>(), b);
+    load_row_vec<T, VEC>(sr, col, cols, fill, b);
+    float yv[VEC];
+    y_of(b, yv);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(a.v[i]), to_f32(b.v[i]), s);
+    for (int i = 0; i < VEC; ++i) s = fmaf(to_f32(a.v[i]), yv[i], s);
   }
   s = block_sum_stream<kStreamThreads / kWave>(s, buf);
   for (int64_t col = int64_t(threadIdx.x) * VEC; col < cols; col += int64_t(kStreamThreads) * VEC) {
     Vec<T, VEC> a, b;
     load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), a);
-    load_row_vec<T, VEC>(yr, col, cols, zero_of<T>(), b);
+    load_row_vec<T, VEC>(sr, col, cols, fill, b);
+    float yv[VEC];
+    y_of(b, yv);
     float o[VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) o[i] = to_f32(b.v[i]) * (to_f32(a.v[i]) - s);
+    for (int i = 0; i < VEC; ++i) o[i] = yv[i] * (to_f32(a.v[i]) - s);
     store_row_vec<T, VEC>(dr, col, cols, o);
   }
 }
@@ -201,92 +250,99 @@ __global__ __launch_bounds__(kStreamThreads) void softmax_bwd_stream(
 // the exponentials kept (forward) and 8 waves x 1 vector (backward); K >= 4
 // recomputes the exponentials so that the row fits in fewer VGPRs.
 template <typename T, int VEC, int WAVES, int K, bool KEEP>
-bool fwd_try(const T* xp, int64_t ld_x, T* yp, int64_t ld_y, int64_t rows, int64_t cols,
-             hipStream_t s) {
+bool fwd_try(const T* xp, int64_t ld_x, T* yp, int64_t ld_y, float* lse, int64_t rows,
+             int64_t cols, hipStream_t s) {
   if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
   const unsigned grid = unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
   softmax_fwd_resident<T, VEC, WAVES, K, KEEP>
-      <<<grid, row_block_threads<WAVES>(), 0, s>>>(xp, ld_x, yp, ld_y, rows, cols);
+      <<<grid, row_block_threads<WAVES>(), 0, s>>>(xp, ld_x, yp, ld_y, lse, rows, cols);
   return true;
 }
 
-template <typename T, int VEC, int WAVES, int K>
-bool bwd_try(const T* gp, int64_t ld_dy, const T* yp, int64_t ld_y, T* dp, int64_t ld_dx,
-             int64_t rows, int64_t cols, hipStream_t s) {
+template <typename T, int VEC, int WAVES, int K, bool FROM_LSE>
+bool bwd_try(const T* gp, int64_t ld_dy, const T* sp, int64_t ld_src, const float* lse, T* dp,
+             int64_t ld_dx, int64_t rows, int64_t cols, hipStream_t s) {
   if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
   const unsigned grid = unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
-  softmax_bwd_resident<T, VEC, WAVES, K>
-      <<<grid, row_block_threads<WAVES>(), 0, s>>>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols);
+  softmax_bwd_resident<T, VEC, WAVES, K, FROM_LSE><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+      gp, ld_dy, sp, ld_src, lse, dp, ld_dx, rows, cols);
   return true;
 }
 
 template <typename T, int VEC>
-hipError_t fwd_vec(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
+hipError_t fwd_vec(const void* x, int64_t ld_x, void* y, int64_t ld_y, float* lse, int64_t rows,
                    int64_t cols, hipStream_t s) {
   const T* xp = static_cast<const T*>(x);
   T* yp = static_cast<T*>(y);
-  if (!(fwd_try<T, VEC, 1, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
-        fwd_try<T, VEC, 2, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
-        fwd_try<T, VEC, 4, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
-        fwd_try<T, VEC, 8, 2, true>(xp, ld_x, yp, ld_y, rows, cols, s) ||
-        fwd_try<T, VEC, 8, 4, false>(xp, ld_x, yp, ld_y, rows, cols, s) ||
-        fwd_try<T, VEC, 8, 8, false>(xp, ld_x, yp, ld_y, rows, cols, s)))
-    softmax_fwd_stream<T, VEC><<<unsigned(rows), kStreamThreads, 0, s>>>(xp, ld_x, yp, ld_y, cols);
+  if (!(fwd_try<T, VEC, 1, 2, true>(xp, ld_x, yp, ld_y, lse, rows, cols, s) ||
+        fwd_try<T, VEC, 2, 2, true>(xp, ld_x, yp, ld_y, lse, rows, cols, s) ||
+        fwd_try<T, VEC, 4, 2, true>(xp, ld_x, yp, ld_y, lse, rows, cols, s) ||
+        fwd_try<T, VEC, 8, 2, true>(xp, ld_x, yp, ld_y, lse, rows, cols, s) ||
+        fwd_try<T, VEC, 8, 4, false>(xp, ld_x, yp, ld_y, lse, rows, cols, s) ||
+        fwd_try<T, VEC, 8, 8, false>(xp, ld_x, yp, ld_y, lse, rows, cols, s)))
+    softmax_fwd_stream<T, VEC><<<unsigned(rows), kStreamThreads, 0, s>>>(xp, ld_x, yp, ld_y, lse,
+                                                                        cols);
   return hipGetLastError();
 }
 
-template <typename T, int VEC>
-hipError_t bwd_vec(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, void* dx,
-                   int64_t ld_dx, int64_t rows, int64_t cols, hipStream_t s) {
+// Tiers of the backward (both variants): 8 waves x 1 vector for rows of 4096
+// 16-bit values measured fastest for the saved-y form.
+template <typename T, int VEC, bool FROM_LSE>
+hipError_t bwd_vec(const void* dy, int64_t ld_dy, const void* src, int64_t ld_src,
+                   const float* lse, void* dx, int64_t ld_dx, int64_t rows, int64_t cols,
+                   hipStream_t s) {
   const T* gp = static_cast<const T*>(dy);
-  const T* yp = static_cast<const T*>(y);
+  const T* sp = static_cast<const T*>(src);
   T* dp = static_cast<T*>(dx);
-  if (!(bwd_try<T, VEC, 1, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
-        bwd_try<T, VEC, 2, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
-        bwd_try<T, VEC, 4, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
-        bwd_try<T, VEC, 8, 1>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
-        bwd_try<T, VEC, 8, 2>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
-        bwd_try<T, VEC, 8, 4>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s) ||
-        bwd_try<T, VEC, 8, 8>(gp, ld_dy, yp, ld_y, dp, ld_dx, rows, cols, s)))
-    softmax_bwd_stream<T, VEC><<<unsigned(rows), kStreamThreads, 0, s>>>(gp, ld_dy, yp, ld_y, dp,
-                                                                        ld_dx, cols);
+#define VJP_SMB_TRY(W, K) \
+  bwd_try<T, VEC, W, K, FROM_LSE>(gp, ld_dy, sp, ld_src, lse, dp, ld_dx, rows, cols, s)
+  if (!(VJP_SMB_TRY(1, 1) || VJP_SMB_TRY(2, 1) || VJP_SMB_TRY(4, 1) || VJP_SMB_TRY(8, 1) ||
+        VJP_SMB_TRY(8, 2) || VJP_SMB_TRY(8, 4) || VJP_SMB_TRY(8, 8)))
+    softmax_bwd_stream<T, VEC, FROM_LSE><<<unsigned(rows), kStreamThreads, 0, s>>>(
+        gp, ld_dy, sp, ld_src, lse, dp, ld_dx, cols);
+#undef VJP_SMB_TRY
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t fwd_typed(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
-                     int64_t cols, bool vec, hipStream_t s) {
+hipError_t fwd_typed(const void* x, int64_t ld_x, void* y, int64_t ld_y, float* lse,
+                     int64_t rows, int64_t cols, bool vec, hipStream_t s) {
   constexpr int V = 16 / sizeof(T);
-  return vec ? fwd_vec<T, V>(x, ld_x, y, ld_y, rows, cols, s)
-             : fwd_vec<T, 1>(x, ld_x, y, ld_y, rows, cols, s);
+  return vec ? fwd_vec<T, V>(x, ld_x, y, ld_y, lse, rows, cols, s)
+             : fwd_vec<T, 1>(x, ld_x, y, ld_y, lse, rows, cols, s);
 }
 
 template <typename T>
-hipError_t bwd_typed(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, void* dx,
-                     int64_t ld_dx, int64_t rows, int64_t cols, bool vec, hipStream_t s) {
+hipError_t bwd_typed(const void* dy, int64_t ld_dy, const void* src, int64_t ld_src,
+                     const float* lse, void* dx, int64_t ld_dx, int64_t rows, int64_t cols,
+                     bool vec, hipStream_t s) {
   constexpr int V = 16 / sizeof(T);
-  return vec ? bwd_vec<T, V>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, s)
-             : bwd_vec<T, 1>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, s);
+  if (lse != nullptr)
+    return vec ? bwd_vec<T, V, true>(dy, ld_dy, src, ld_src, lse, dx, ld_dx, rows, cols, s)
+               : bwd_vec<T, 1, true>(dy, ld_dy, src, ld_src, lse, dx, ld_dx, rows, cols, s);
+  return vec ? bwd_vec<T, V, false>(dy, ld_dy, src, ld_src, lse, dx, ld_dx, rows, cols, s)
+             : bwd_vec<T, 1, false>(dy, ld_dy, src, ld_src, lse, dx, ld_dx, rows, cols, s);
 }
 
 }  // namespace
 
-hipError_t launch_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
-                              int64_t cols, int act, bool vec, hipStream_t s) {
+hipError_t launch_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y,
+                              float* row_lse, int64_t rows, int64_t cols, int act, bool vec,
+                              hipStream_t s) {
   switch (act) {
-    case kF32: return fwd_typed<float>(x, ld_x, y, ld_y, rows, cols, vec, s);
-    case kF16: return fwd_typed<_Float16>(x, ld_x, y, ld_y, rows, cols, vec, s);
-    default: return fwd_typed<bf16>(x, ld_x, y, ld_y, rows, cols, vec, s);
+    case kF32: return fwd_typed<float>(x, ld_x, y, ld_y, row_lse, rows, cols, vec, s);
+    case kF16: return fwd_typed<_Float16>(x, ld_x, y, ld_y, row_lse, rows, cols, vec, s);
+    default: return fwd_typed<bf16>(x, ld_x, y, ld_y, row_lse, rows, cols, vec, s);
   }
 }
 
-hipError_t launch_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y,
-                              void* dx, int64_t ld_dx, int64_t rows, int64_t cols, int act,
-                              bool vec, hipStream_t s) {
+hipError_t launch_softmax_bwd(const void* dy, int64_t ld_dy, const void* src, int64_t ld_src,
+                              const float* row_lse, void* dx, int64_t ld_dx, int64_t rows,
+                              int64_t cols, int act, bool vec, hipStream_t s) {
   switch (act) {
-    case kF32: return bwd_typed<float>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, vec, s);
-    case kF16: return bwd_typed<_Float16>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, vec, s);
-    default: return bwd_typed<bf16>(dy, ld_dy, y, ld_y, dx, ld_dx, rows, cols, vec, s);
+    case kF32: return bwd_typed<float>(dy, ld_dy, src, ld_src, row_lse, dx, ld_dx, rows, cols, vec, s);
+    case kF16: return bwd_typed<_Float16>(dy, ld_dy, src, ld_src, row_lse, dx, ld_dx, rows, cols, vec, s);
+    default: return bwd_typed<bf16>(dy, ld_dy, src, ld_src, row_lse, dx, ld_dx, rows, cols, vec, s);
   }
 }
 

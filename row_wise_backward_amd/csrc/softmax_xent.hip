@@ -18,6 +18,12 @@
 // The probabilities are rebuilt from the exponentials held in VGPRs (resident
 // path) or recomputed from m and l (streaming path); they never reach HBM.
 // The mean loss is formed by the fixed-order xent_finalize_kernel.
+//
+// Split form (section 07: save only the row statistics, rebuild p in the
+// backward): GRAD = false runs the statistics pass alone (the logits are read
+// once, nothing of their size is written); xent_bwd_kernel is then a map over
+// the logits with dz = scale * (exp(z - lse) - [j == t]), where the upstream
+// gradient of the mean loss is read from device memory, scale = dloss / rows.
 #include "launch.hpp"
 #include "rowops.hpp"
 
@@ -29,17 +35,69 @@ __device__ __forceinline__ void write_row_stats(int64_t row, float m, float lse,
                                                 bool valid, float* __restrict__ row_max,
                                                 float* __restrict__ row_lse,
                                                 float* __restrict__ row_loss) {
-  row_max[row] = m;
+  if (row_max != nullptr) row_max[row] = m;
   row_lse[row] = lse;
   row_loss[row] = valid ? lse - zt : __builtin_nanf("");
 }
 
-__device__ __forceinline__ float row_lse_of(float m, float l) { return m + log2_fast(l) * kLn2; }
+// Backward of the split form: one workgroup per (row, chunk of 256 * VEC * U
+// columns); U vectors per lane are loaded before any is used.  In place
+// (dz == z with the same leading dimension) is safe: every element is read
+// and then written by the same lane.
+template <typename T, int VEC, int U>
+__global__ __launch_bounds__(kStreamThreads) void xent_bwd_kernel(
+    const T* z, int64_t ld, const int32_t* __restrict__ targets,
+    const float* __restrict__ row_lse, const float* __restrict__ dloss, int64_t total_rows,
+    int64_t C, T* dz, int64_t ld_dz) {
+  const int64_t row = blockIdx.x;
+  const float L = row_lse[row];
+  const int64_t t = targets[row];
+  const float scale = *dloss / float(total_rows);
+  const T* zr = z + row * ld;
+  T* dr = dz + row * ld_dz;
+  constexpr int64_t kChunk = int64_t(kStreamThreads) * VEC;
+  const int64_t c0 = int64_t(blockIdx.y) * kChunk * U + int64_t(threadIdx.x) * VEC;
+  Vec<T, VEC> r[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t col = c0 + u * kChunk;
+    if (col < C) load_row_vec<T, VEC>(zr, col, C, neg_inf_of<T>(), r[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t col = c0 + u * kChunk;
+    if (col < C) {
+      float a[VEC], e[VEC];
+      float amin = __builtin_inff();
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        a[i] = (to_f32(r[u].v[i]) - L) * kLog2e;
+        amin = fminf(amin, a[i]);
+      }
+      if (amin < -126.0f) {   // some result may be subnormal
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) e[i] = exp2_denorm_safe(a[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) e[i] = exp2_fast(a[i]);
+      }
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = e[i] * scale;
+      if (uint64_t(t - col) < uint64_t(VEC)) {   // this vector holds the target column
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+          if (col + i == t) o[i] = (e[i] - 1.0f) * scale;
+      }
+      store_row_vec<T, VEC>(dr, col, C, o);
+    }
+  }
+}
 
 // Resident kernel: the row is loaded once; KEEP = true holds exp(z - m) in
 // fp32 VGPRs for the gradient pass, KEEP = false recomputes it from the
 // stored row (bitwise the same values, fewer VGPRs, more rows per CU).
-template <typename T, int VEC, int WAVES, int K, bool KEEP>
+template <typename T, int VEC, int WAVES, int K, bool KEEP, bool GRAD>
 __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
     const T* __restrict__ z, int64_t ld, const int32_t* __restrict__ targets, int64_t rows,
     int64_t C, float scale, float* __restrict__ row_max, float* __restrict__ row_lse,
@@ -84,6 +142,14 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
   const float ps = scale * inv;
 
   const float lse = row_lse_of(m, l);
+  if constexpr (!GRAD) {
+    if (wv == 0 && lane == 0) {
+      if (row_max != nullptr) row_max[row] = m;
+      row_lse[row] = lse;
+      row_loss[row] = valid ? lse - to_f32(zr[t]) : __builtin_nanf("");
+    }
+    return;
+  }
   if (wv == 0 && lane == 0) {
     row_max[row] = m;
     row_lse[row] = lse;
@@ -122,7 +188,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
   }
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool GRAD>
 __global__ __launch_bounds__(kStreamThreads) void xent_stream(
     const T* __restrict__ z, int64_t ld, const int32_t* __restrict__ targets, int64_t C,
     float scale, float* __restrict__ row_max, float* __restrict__ row_lse,
@@ -147,6 +213,7 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream(
     write_row_stats(row, m, row_lse_of(m, l), valid ? to_f32(zr[t]) : 0.0f, valid, row_max,
                     row_lse, row_loss);
   }
+  if constexpr (!GRAD) return;
   for (int64_t col = int64_t(threadIdx.x) * VEC; col < C; col += int64_t(kStreamThreads) * VEC) {
     Vec<T, VEC> r;
     load_row_vec<T, VEC>(zr, col, C, neg_inf_of<T>(), r);
@@ -163,41 +230,62 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream(
 // Launch tiers, smallest first, as for the softmax forward: (waves per row,
 // vectors per lane, keep the exponentials).  Measured on MI355X: rows of
 // 32000 16-bit logits run best as 8 waves x 8 vectors recomputing the
-// exponentials (54 VGPRs, four rows in flight per CU).
-template <typename T, int VEC, int WAVES, int K, bool KEEP>
+// exponentials (54 VGPRs, four rows in flight per CU).  The statistics-only
+// form never keeps the exponentials.
+template <typename T, int VEC, int WAVES, int K, bool KEEP, bool GRAD>
 bool resident_try(const T* zp, int64_t ld, const int32_t* tg, int64_t rows, int64_t C,
                   float scale, float* rmax, float* rlse, float* rloss, T* dp, int64_t ld_dz,
                   hipStream_t s) {
   if (int64_t(WAVES) * kWave * K * VEC < C) return false;
   const unsigned grid = unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
-  xent_resident<T, VEC, WAVES, K, KEEP><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+  xent_resident<T, VEC, WAVES, K, KEEP && GRAD, GRAD><<<grid, row_block_threads<WAVES>(), 0, s>>>(
       zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz);
   return true;
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool GRAD>
 hipError_t run_vec(const void* z, int64_t ld, const int32_t* tg, int64_t rows, int64_t C,
                    float scale, float* rmax, float* rlse, float* rloss, void* dz, int64_t ld_dz,
                    hipStream_t s) {
   const T* zp = static_cast<const T*>(z);
   T* dp = static_cast<T*>(dz);
 #define VJP_XENT_TRY(W, K, KEEP) \
-  resident_try<T, VEC, W, K, KEEP>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz, s)
+  resident_try<T, VEC, W, K, KEEP, GRAD>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz, s)
   if (!(VJP_XENT_TRY(1, 2, true) || VJP_XENT_TRY(2, 2, true) || VJP_XENT_TRY(4, 2, true) ||
         VJP_XENT_TRY(8, 2, true) || VJP_XENT_TRY(8, 4, false) || VJP_XENT_TRY(8, 8, false)))
-    xent_stream<T, VEC><<<unsigned(rows), kStreamThreads, 0, s>>>(zp, ld, tg, C, scale, rmax,
-                                                                  rlse, rloss, dp, ld_dz);
+    xent_stream<T, VEC, GRAD><<<unsigned(rows), kStreamThreads, 0, s>>>(
+        zp, ld, tg, C, scale, rmax, rlse, rloss, dp, ld_dz);
 #undef VJP_XENT_TRY
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool GRAD>
 hipError_t run_typed(const void* z, int64_t ld, const int32_t* tg, int64_t rows, int64_t C,
                      float scale, float* rmax, float* rlse, float* rloss, void* dz,
                      int64_t ld_dz, bool vec, hipStream_t s) {
   constexpr int V = 16 / sizeof(T);
-  return vec ? run_vec<T, V>(z, ld, tg, rows, C, scale, rmax, rlse, rloss, dz, ld_dz, s)
-             : run_vec<T, 1>(z, ld, tg, rows, C, scale, rmax, rlse, rloss, dz, ld_dz, s);
+  return vec ? run_vec<T, V, GRAD>(z, ld, tg, rows, C, scale, rmax, rlse, rloss, dz, ld_dz, s)
+             : run_vec<T, 1, GRAD>(z, ld, tg, rows, C, scale, rmax, rlse, rloss, dz, ld_dz, s);
+}
+
+// Vectors per lane of the split backward (a pure map: four loads in flight).
+constexpr int kBwdUnroll = 4;
+
+template <typename T>
+hipError_t bwd_typed(const void* z, int64_t ld, const int32_t* tg, const float* rlse,
+                     const float* dloss, int64_t total_rows, int64_t rows, int64_t C, void* dz,
+                     int64_t ld_dz, bool vec, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  const int v = vec ? V : 1;
+  const int64_t per_block = int64_t(kStreamThreads) * v * kBwdUnroll;
+  const dim3 grid(unsigned(rows), unsigned((C + per_block - 1) / per_block));
+  if (vec)
+    xent_bwd_kernel<T, V, kBwdUnroll><<<grid, kStreamThreads, 0, s>>>(
+        static_cast<const T*>(z), ld, tg, rlse, dloss, total_rows, C, static_cast<T*>(dz), ld_dz);
+  else
+    xent_bwd_kernel<T, 1, kBwdUnroll><<<grid, kStreamThreads, 0, s>>>(
+        static_cast<const T*>(z), ld, tg, rlse, dloss, total_rows, C, static_cast<T*>(dz), ld_dz);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -207,9 +295,30 @@ hipError_t launch_softmax_xent(const void* z, int64_t ld, const int32_t* targets
                                float* row_lse, float* row_loss, void* dz, int64_t ld_dz,
                                bool vec, hipStream_t s) {
   switch (act) {
-    case kF32: return run_typed<float>(z, ld, targets, rows, classes, grad_scale, row_max, row_lse, row_loss, dz, ld_dz, vec, s);
-    case kF16: return run_typed<_Float16>(z, ld, targets, rows, classes, grad_scale, row_max, row_lse, row_loss, dz, ld_dz, vec, s);
-    default: return run_typed<bf16>(z, ld, targets, rows, classes, grad_scale, row_max, row_lse, row_loss, dz, ld_dz, vec, s);
+    case kF32: return run_typed<float, true>(z, ld, targets, rows, classes, grad_scale, row_max, row_lse, row_loss, dz, ld_dz, vec, s);
+    case kF16: return run_typed<_Float16, true>(z, ld, targets, rows, classes, grad_scale, row_max, row_lse, row_loss, dz, ld_dz, vec, s);
+    default: return run_typed<bf16, true>(z, ld, targets, rows, classes, grad_scale, row_max, row_lse, row_loss, dz, ld_dz, vec, s);
+  }
+}
+
+hipError_t launch_softmax_xent_stats(const void* z, int64_t ld, const int32_t* targets,
+                                     int64_t rows, int64_t classes, int act, float* row_max,
+                                     float* row_lse, float* row_loss, bool vec, hipStream_t s) {
+  switch (act) {
+    case kF32: return run_typed<float, false>(z, ld, targets, rows, classes, 0.0f, row_max, row_lse, row_loss, nullptr, 0, vec, s);
+    case kF16: return run_typed<_Float16, false>(z, ld, targets, rows, classes, 0.0f, row_max, row_lse, row_loss, nullptr, 0, vec, s);
+    default: return run_typed<bf16, false>(z, ld, targets, rows, classes, 0.0f, row_max, row_lse, row_loss, nullptr, 0, vec, s);
+  }
+}
+
+hipError_t launch_softmax_xent_bwd(const void* z, int64_t ld, const int32_t* targets,
+                                   const float* row_lse, const float* dloss, int64_t total_rows,
+                                   int64_t rows, int64_t classes, int act, void* dz,
+                                   int64_t ld_dz, bool vec, hipStream_t s) {
+  switch (act) {
+    case kF32: return bwd_typed<float>(z, ld, targets, row_lse, dloss, total_rows, rows, classes, dz, ld_dz, vec, s);
+    case kF16: return bwd_typed<_Float16>(z, ld, targets, row_lse, dloss, total_rows, rows, classes, dz, ld_dz, vec, s);
+    default: return bwd_typed<bf16>(z, ld, targets, row_lse, dloss, total_rows, rows, classes, dz, ld_dz, vec, s);
   }
 }
 

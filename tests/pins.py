@@ -339,6 +339,39 @@ def softmax_bwd_rows_sum_zero(impl):
     return float(np.max(np.abs(dx.sum(-1)))) / float(np.max(np.abs(dy)))
 
 
+def softmax_lse_vs_scipy(impl):
+    from scipy.special import logsumexp
+
+    g = _rng(21)
+    x = g.standard_normal((8, 45)) * 3
+    x[2] -= 900.0
+    x[5] += 700.0
+    return rel(impl.lse(x), logsumexp(x, axis=-1))
+
+
+def softmax_bwd_from_x_torch(impl):
+    """The rebuilt-y backward against torch fp64 autograd of softmax, batch 1 and 7."""
+    import torch
+
+    g = _rng(22)
+    err = 0.0
+    for R, C in [(1, 1), (1, 9), (7, 7), (7, 130)]:
+        x = g.standard_normal((R, C)) * 3
+        dy = g.standard_normal((R, C))
+        xt = torch.tensor(x, requires_grad=True)
+        torch.softmax(xt, dim=-1).backward(torch.tensor(dy))
+        err = max(err, rel(impl.bwd_from_x(dy, x), xt.grad.numpy()))
+    return err
+
+
+def softmax_bwd_from_x_fd(impl):
+    g = _rng(23)
+    x = g.standard_normal((3, 11)) * 2
+    dy = g.standard_normal((3, 11))
+    fx = fd_grad(lambda xx: float(np.sum(dy * np.exp(xx - impl.lse(xx)[:, None]))), x)
+    return rel(impl.bwd_from_x(dy, x), fx)
+
+
 # ----------------------------------------------------------------------------- softmax-xent
 
 def _xent_case(seed, R, C, sigma=2.0):
@@ -426,6 +459,37 @@ def xent_invalid_targets(impl):
     return max(rel(out["dz"][1], p[1]), rel(out["dz"][2], p[2])) if ok else np.inf
 
 
+def xent_split_vs_torch(impl):
+    """Split forward / backward against torch fp64 cross_entropy with an upstream
+    gradient other than 1 (batch 1 and 7)."""
+    import torch
+    import torch.nn.functional as F
+
+    err = 0.0
+    for R, C in [(1, 1), (1, 5), (7, 7), (7, 300)]:
+        z, t = _xent_case(80 + R + C, R, C)
+        zt = torch.tensor(z, requires_grad=True)
+        loss = F.cross_entropy(zt, torch.tensor(t), reduction="mean")
+        loss.backward(torch.tensor(-2.5, dtype=torch.float64))
+        f = impl.fwd(z, t)
+        err = max(err, abs(f["loss"] - loss.item()) / max(1.0, abs(loss.item())),
+                  rel(impl.bwd(z, t, -2.5), zt.grad.numpy()))
+    return err
+
+
+def xent_split_stats(impl):
+    """Forward statistics of the split form against scipy (lse) and numpy (max, loss rows)."""
+    from scipy.special import logsumexp
+
+    z, t = _xent_case(90, 6, 77)
+    z[1] -= 500.0
+    f = impl.fwd(z, t)
+    rows = np.arange(6)
+    return max(rel(f["row_lse"], logsumexp(z, axis=1)), rel(f["row_max"], z.max(axis=1)),
+               rel(f["row_loss"], logsumexp(z, axis=1) - z[rows, t]),
+               0.0 if ("dz" not in f and f["n_invalid"] == 0) else np.inf)
+
+
 PINS = {
     "weighted_sum": [
         ("fwd_vs_matmul", ws_fwd_vs_matmul, 1e-12),
@@ -454,6 +518,9 @@ PINS = {
         ("bwd_finite_differences", softmax_bwd_fd, 1e-9),
         ("bwd_vs_torch_autograd", softmax_bwd_torch, 1e-13),
         ("bwd_rows_sum_zero", softmax_bwd_rows_sum_zero, 1e-14),
+        ("lse_vs_scipy", softmax_lse_vs_scipy, 1e-14),
+        ("bwd_from_x_vs_torch", softmax_bwd_from_x_torch, 1e-13),
+        ("bwd_from_x_finite_differences", softmax_bwd_from_x_fd, 1e-9),
     ],
     "softmax_xent": [
         ("vs_torch_cross_entropy", xent_vs_torch, 1e-13),
@@ -462,5 +529,7 @@ PINS = {
         ("softmax_minus_onehot", xent_softmax_minus_onehot, 1e-13),
         ("special_cases", xent_special_cases, 1e-13),
         ("invalid_targets", xent_invalid_targets, 1e-13),
+        ("split_vs_torch", xent_split_vs_torch, 1e-13),
+        ("split_stats", xent_split_stats, 1e-14),
     ],
 }

@@ -179,6 +179,51 @@ def test_softmax_xent_rejections():
     assert _xent(rmax=0) == EINVAL
 
 
+def test_softmax_lse_rejections():
+    assert L.vjp_softmax_fwd_lse(P(A), 100, P(B), 100, None, 10, 100, 2, None) == EINVAL   # no row_lse
+    assert L.vjp_softmax_fwd_lse(P(A), 100, P(B), 100, P(A + 8), 10, 100, 2, None) == EALIAS
+    assert L.vjp_softmax_fwd_lse(P(A), 100, P(B), 100, P(B + 64), 10, 100, 2, None) == EALIAS
+    assert L.vjp_softmax_fwd_lse(P(A), 100, P(B), 100, P(C + 2), 10, 100, 2, None) == EALIGN
+    assert L.vjp_softmax_bwd_lse(P(A), 100, P(B), 100, None, P(C), 100, 10, 100, 2, None) == EINVAL
+    assert L.vjp_softmax_bwd_lse(P(A), 100, P(B), 100, P(D + 1), P(C), 100, 10, 100, 2, None) == EALIGN
+    assert L.vjp_softmax_bwd_lse(P(A), 100, P(B), 100, P(D), P(D + 16), 100, 10, 100, 2, None) == EALIAS
+    assert L.vjp_softmax_bwd_lse(P(A), 100, P(B), 100, P(D), P(B + 2), 100, 10, 100, 2, None) == EALIAS
+    # empty problems are accepted and launch nothing
+    assert L.vjp_softmax_fwd_lse(P(A), 100, None, 0, None, 0, 100, 2, None) == OK
+    assert L.vjp_softmax_bwd_lse(P(A), 100, P(B), 100, None, P(C), 100, 0, 100, 2, None) == OK
+
+
+def _xent_fwd(**kw):
+    a = dict(z=A, ld=1000, t=B, rows=10, C=1000, act=2, loss=C, rmax=C + 64, rlse=C + 128,
+             ninv=C + 256, ws=C + 512, wsb=40)
+    a.update(kw)
+    return L.vjp_softmax_xent_fwd(P(a["z"]), a["ld"], P(a["t"]), a["rows"], a["C"], a["act"],
+                                  P(a["loss"]), P(a["rmax"]), P(a["rlse"]), P(a["ninv"]),
+                                  P(a["ws"]), a["wsb"], None)
+
+
+def _xent_bwd(**kw):
+    a = dict(z=A, ld=1000, t=B, rlse=C, rows=10, C=1000, act=2, dloss=C + 64, dz=D, ldd=1000)
+    a.update(kw)
+    return L.vjp_softmax_xent_bwd(P(a["z"]), a["ld"], P(a["t"]), P(a["rlse"]), a["rows"], a["C"],
+                                  a["act"], P(a["dloss"]), P(a["dz"]), a["ldd"], None)
+
+
+def test_softmax_xent_split_rejections():
+    assert _xent_fwd(rlse=0) == EINVAL
+    assert _xent_fwd(wsb=39) == EWORKSPACE
+    assert _xent_fwd(rmax=C + 128 + 8) == EALIAS          # row_max over row_lse
+    assert _xent_fwd(C=0) == EINVAL
+    assert _xent_fwd(act=5) == EDTYPE
+    assert _xent_bwd(dloss=0) == EINVAL
+    assert _xent_bwd(dloss=C + 2) == EALIGN
+    assert _xent_bwd(dz=A + 2) == EALIAS                  # partial overlap with the logits
+    assert _xent_bwd(dz=A, ldd=1008) == EALIAS            # same base, other leading dimension
+    assert _xent_bwd(dz=C) == EALIAS                      # over row_lse
+    assert _xent_bwd(rlse=0) == EINVAL
+    assert _xent_bwd(rows=0) == OK                        # nothing to do, nothing launched
+
+
 def test_binding_host_guards():
     """The binding checks shapes, dtypes and devices before calling the C ABI."""
     import torch

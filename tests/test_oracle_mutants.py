@@ -113,6 +113,25 @@ def _xent_lse_without_max(z, t, grad_scale):
     return out
 
 
+def _sm_lse_no_max(x):
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore", divide="ignore"):
+        return np.log(np.sum(np.exp(x), axis=-1))
+
+
+def _sm_bwd_from_x_unnormalised(dy, x):
+    e = np.exp(np.asarray(x) - np.max(x, axis=-1, keepdims=True))
+    return sm.bwd(dy, e)
+
+
+def _xent_bwd_sum_not_mean(z, t, dloss):
+    return xe.fwd_bwd(z, t, float(dloss))["dz"]
+
+
+def _xent_bwd_ignores_dloss(z, t, dloss):
+    return xe.bwd(z, t, 1.0)
+
+
 MUTANTS = [
     ("weighted_sum", "bwd_no_batch_reduction", _ns(ws, bwd=_ws_bwd_no_batch_reduction)),
     ("weighted_sum", "bwd_transposed_reduction", _ns(ws, bwd=_ws_bwd_transposed)),
@@ -130,6 +149,10 @@ MUTANTS = [
     ("softmax_xent", "no_onehot", _ns(xe, fwd_bwd=_xent_no_onehot)),
     ("softmax_xent", "sum_not_mean", _ns(xe, fwd_bwd=_xent_sum_not_mean)),
     ("softmax_xent", "lse_wrong", _ns(xe, fwd_bwd=_xent_lse_without_max)),
+    ("softmax", "lse_without_max", _ns(sm, lse=_sm_lse_no_max)),
+    ("softmax", "bwd_from_x_unnormalised", _ns(sm, bwd_from_x=_sm_bwd_from_x_unnormalised)),
+    ("softmax_xent", "split_bwd_sum_not_mean", _ns(xe, bwd=_xent_bwd_sum_not_mean)),
+    ("softmax_xent", "split_bwd_ignores_dloss", _ns(xe, bwd=_xent_bwd_ignores_dloss)),
 ]
 
 
