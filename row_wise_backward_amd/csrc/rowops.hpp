@@ -188,9 +188,9 @@ constexpr int kStreamThreads = 256;
 
 // Combine per-thread online-softmax states (m, l) with l relative to m:
 // M = max m_i, L = sum_i l_i * 2^((m_i - M) log2 e), threads in index order
-// (wave butterflies, then waves in order).
-__device__ __forceinline__ void block_merge_ml(float& m, float& l, float* bm, float* bl) {
-  constexpr int W = kStreamThreads / kWave;
+// (wave butterflies, then the W waves in order).  Every thread receives (M, L).
+template <int W>
+__device__ __forceinline__ void block_merge_ml_w(float& m, float& l, float* bm, float* bl) {
   float M = wave_max(m);
   float contrib = (m == -__builtin_inff()) ? 0.0f : l * exp2_denorm_safe((m - M) * kLog2e);
   float Lw = wave_sum(contrib);
@@ -209,6 +209,10 @@ __device__ __forceinline__ void block_merge_ml(float& m, float& l, float* bm, fl
     Lg += (bm[k] == -__builtin_inff()) ? 0.0f : bl[k] * exp2_denorm_safe((bm[k] - Mg) * kLog2e);
   m = Mg;
   l = Lg;
+}
+
+__device__ __forceinline__ void block_merge_ml(float& m, float& l, float* bm, float* bl) {
+  block_merge_ml_w<kStreamThreads / kWave>(m, l, bm, bl);
 }
 
 // One element of an online softmax: fold x into the running (m, l).  An

@@ -285,8 +285,10 @@ hipError_t fwd_vec(const void* x, int64_t ld_x, void* y, int64_t ld_y, float* ls
   return hipGetLastError();
 }
 
-// Tiers of the backward (both variants): 8 waves x 1 vector for rows of 4096
-// 16-bit values measured fastest for the saved-y form.
+// Tiers of the backward.  Saved y: 8 waves x 1 vector for rows of 4096 16-bit
+// values measured fastest (127 us for 32768 x 4096 bf16).  Rebuilt y (two
+// exponentials per element): 4 waves x 2 vectors (129 us, against 169 us for
+// 8 waves x 1 vector), the forward's tiers.
 template <typename T, int VEC, bool FROM_LSE>
 hipError_t bwd_vec(const void* dy, int64_t ld_dy, const void* src, int64_t ld_src,
                    const float* lse, void* dx, int64_t ld_dx, int64_t rows, int64_t cols,
@@ -296,8 +298,13 @@ hipError_t bwd_vec(const void* dy, int64_t ld_dy, const void* src, int64_t ld_sr
   T* dp = static_cast<T*>(dx);
 #define VJP_SMB_TRY(W, K) \
   bwd_try<T, VEC, W, K, FROM_LSE>(gp, ld_dy, sp, ld_src, lse, dp, ld_dx, rows, cols, s)
-  if (!(VJP_SMB_TRY(1, 1) || VJP_SMB_TRY(2, 1) || VJP_SMB_TRY(4, 1) || VJP_SMB_TRY(8, 1) ||
-        VJP_SMB_TRY(8, 2) || VJP_SMB_TRY(8, 4) || VJP_SMB_TRY(8, 8)))
+  const bool done =
+      FROM_LSE ? (VJP_SMB_TRY(1, 2) || VJP_SMB_TRY(2, 2) || VJP_SMB_TRY(4, 2) ||
+                  VJP_SMB_TRY(8, 2) || VJP_SMB_TRY(8, 4) || VJP_SMB_TRY(8, 8))
+               : (VJP_SMB_TRY(1, 1) || VJP_SMB_TRY(2, 1) || VJP_SMB_TRY(4, 1) ||
+                  VJP_SMB_TRY(8, 1) || VJP_SMB_TRY(8, 2) || VJP_SMB_TRY(8, 4) ||
+                  VJP_SMB_TRY(8, 8));
+  if (!done)
     softmax_bwd_stream<T, VEC, FROM_LSE><<<unsigned(rows), kStreamThreads, 0, s>>>(
         gp, ld_dy, sp, ld_src, lse, dp, ld_dx, cols);
 #undef VJP_SMB_TRY
