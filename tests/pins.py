@@ -490,6 +490,124 @@ def xent_split_stats(impl):
                0.0 if ("dz" not in f and f["n_invalid"] == 0) else np.inf)
 
 
+# ----------------------------------------------------------------------------- norms
+
+def _norm_case(seed, R, D, scale=2.0):
+    g = _rng(seed)
+    x = g.standard_normal((R, D)) * scale + g.standard_normal((R, 1))
+    w = 1.0 + 0.3 * g.standard_normal(D)
+    b = 0.2 * g.standard_normal(D)
+    dy = g.standard_normal((R, D))
+    return x, w, b, dy
+
+
+def ln_fwd_vs_torch(impl):
+    import torch
+    import torch.nn.functional as F
+
+    x, w, b, _ = _norm_case(110, 7, 65)
+    y, mu, rstd = impl.layernorm_fwd(x, w, b, 1e-5)
+    ref = F.layer_norm(torch.tensor(x), (65,), torch.tensor(w), torch.tensor(b), 1e-5).numpy()
+    return max(rel(y, ref), rel(mu, x.mean(axis=1)), rel(rstd, 1.0 / np.sqrt(x.var(axis=1) + 1e-5)))
+
+
+def ln_bwd_vs_torch(impl):
+    """dx, dw, db against torch fp64 autograd of layer_norm, batch 1 and 7."""
+    import torch
+    import torch.nn.functional as F
+
+    err = 0.0
+    for R, D in [(1, 1), (1, 9), (7, 7), (7, 130)]:
+        x, w, b, dy = _norm_case(111 + R + D, R, D)
+        xt, wt, bt = (torch.tensor(a, requires_grad=True) for a in (x, w, b))
+        F.layer_norm(xt, (D,), wt, bt, 1e-5).backward(torch.tensor(dy))
+        dx, dw, db = impl.layernorm_bwd(dy, x, w, 1e-5)
+        err = max(err, rel(dx, xt.grad.numpy()) if D > 1 else float(np.max(np.abs(dx))),
+                  rel(dw, wt.grad.numpy()) if D > 1 else 0.0, rel(db, bt.grad.numpy()))
+    return err
+
+
+def ln_bwd_fd(impl):
+    """Finite differences of sum(dy * y) with respect to x, w and b."""
+    x, w, b, dy = _norm_case(112, 3, 6)
+    dx, dw, db = impl.layernorm_bwd(dy, x, w, 1e-3)
+    fx = fd_grad(lambda xx: float(np.sum(dy * impl.layernorm_fwd(xx, w, b, 1e-3)[0])), x)
+    fw = fd_grad(lambda ww: float(np.sum(dy * impl.layernorm_fwd(x, ww, b, 1e-3)[0])), w)
+    fb = fd_grad(lambda bb: float(np.sum(dy * impl.layernorm_fwd(x, w, bb, 1e-3)[0])), b)
+    return max(rel(dx, fx), rel(dw, fw), rel(db, fb))
+
+
+def ln_invariants(impl):
+    """Rows of dx sum to 0 (shift invariance) and, with eps -> 0, dx is orthogonal
+    to xhat (scale invariance); db = column sums of dy."""
+    x, w, b, dy = _norm_case(113, 5, 40)
+    dx, dw, db = impl.layernorm_bwd(dy, x, w, 1e-12)
+    mu, rstd = impl.layernorm_stats(x, 1e-12)
+    xhat = (x - mu[:, None]) * rstd[:, None]
+    scale = float(np.max(np.abs(dx)))
+    return max(float(np.max(np.abs(dx.sum(axis=1)))) / scale,
+               float(np.max(np.abs((dx * xhat).sum(axis=1)))) / scale / 40,
+               rel(db, np.array([math.fsum(dy[:, j]) for j in range(40)])))
+
+
+def ln_accumulate(impl):
+    x, w, b, dy = _norm_case(114, 4, 9)
+    g = _rng(114)
+    ow, ob = g.standard_normal(9), g.standard_normal(9)
+    _, a1, a2 = impl.layernorm_bwd(dy, x, w, 1e-5, dw_old=ow, db_old=ob)
+    _, b1, b2 = impl.layernorm_bwd(dy, x, w, 1e-5)
+    return max(rel(a1 - b1, ow), rel(a2 - b2, ob))
+
+
+def rms_fwd_vs_torch(impl):
+    import torch
+    import torch.nn.functional as F
+
+    x, w, _, _ = _norm_case(115, 7, 65)
+    y, rstd = impl.rmsnorm_fwd(x, w, 1e-6)
+    ref = F.rms_norm(torch.tensor(x), (65,), torch.tensor(w), 1e-6).numpy()
+    return max(rel(y, ref), rel(rstd, 1.0 / np.sqrt(np.mean(x * x, axis=1) + 1e-6)))
+
+
+def rms_bwd_vs_torch(impl):
+    import torch
+    import torch.nn.functional as F
+
+    err = 0.0
+    for R, D in [(1, 1), (1, 9), (7, 7), (7, 130)]:
+        x, w, _, dy = _norm_case(116 + R + D, R, D)
+        xt, wt = torch.tensor(x, requires_grad=True), torch.tensor(w, requires_grad=True)
+        F.rms_norm(xt, (D,), wt, 1e-6).backward(torch.tensor(dy))
+        dx, dw = impl.rmsnorm_bwd(dy, x, w, 1e-6)
+        # dx cancels (g - xhat c) almost exactly at D = 1: measure against |g rstd|
+        scale = float(np.max(np.abs(dy * w / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6))))
+        err = max(err, float(np.max(np.abs(dx - xt.grad.numpy()))) / scale, rel(dw, wt.grad.numpy()))
+    return err
+
+
+def rms_bwd_fd(impl):
+    x, w, _, dy = _norm_case(117, 3, 6)
+    dx, dw = impl.rmsnorm_bwd(dy, x, w, 1e-3)
+    fx = fd_grad(lambda xx: float(np.sum(dy * impl.rmsnorm_fwd(xx, w, 1e-3)[0])), x)
+    fw = fd_grad(lambda ww: float(np.sum(dy * impl.rmsnorm_fwd(x, ww, 1e-3)[0])), w)
+    return max(rel(dx, fx), rel(dw, fw))
+
+
+def rms_scale_invariance(impl):
+    """With eps -> 0, RMSNorm(a x) = RMSNorm(x) for a > 0, so dx . x = 0 per row."""
+    x, w, _, dy = _norm_case(118, 5, 33)
+    dx, _ = impl.rmsnorm_bwd(dy, x, w, 1e-14)
+    return float(np.max(np.abs((dx * x).sum(axis=1)))) / float(np.max(np.abs(dx)) * np.max(np.abs(x)) * 33)
+
+
+def rms_accumulate(impl):
+    x, w, _, dy = _norm_case(119, 4, 9)
+    ow = _rng(119).standard_normal(9)
+    _, a = impl.rmsnorm_bwd(dy, x, w, 1e-6, dw_old=ow)
+    _, b = impl.rmsnorm_bwd(dy, x, w, 1e-6)
+    return rel(a - b, ow)
+
+
 PINS = {
     "weighted_sum": [
         ("fwd_vs_matmul", ws_fwd_vs_matmul, 1e-12),
@@ -531,5 +649,17 @@ PINS = {
         ("invalid_targets", xent_invalid_targets, 1e-13),
         ("split_vs_torch", xent_split_vs_torch, 1e-13),
         ("split_stats", xent_split_stats, 1e-14),
+    ],
+    "norms": [
+        ("ln_fwd_vs_torch", ln_fwd_vs_torch, 1e-13),
+        ("ln_bwd_vs_torch_autograd", ln_bwd_vs_torch, 1e-12),
+        ("ln_bwd_finite_differences", ln_bwd_fd, 1e-8),
+        ("ln_invariants", ln_invariants, 1e-10),
+        ("ln_accumulate", ln_accumulate, 1e-13),
+        ("rms_fwd_vs_torch", rms_fwd_vs_torch, 1e-13),
+        ("rms_bwd_vs_torch_autograd", rms_bwd_vs_torch, 1e-12),
+        ("rms_bwd_finite_differences", rms_bwd_fd, 1e-8),
+        ("rms_scale_invariance", rms_scale_invariance, 1e-12),
+        ("rms_accumulate", rms_accumulate, 1e-13),
     ],
 }

@@ -237,3 +237,21 @@ def test_binding_host_guards():
         rwb._ld(torch.zeros(8, 4).t())                     # non-unit inner stride
     with pytest.raises(ValueError):
         rwb._expect(torch.zeros(3), (4,), None, torch.device("cpu"), "y")
+
+
+def test_autograd_layer_rejects_host_tensors():
+    """The autograd wrappers call the same guarded binding: CPU tensors never
+    reach a kernel, and there is no CPU fallback."""
+    import torch
+
+    from row_wise_backward_amd import autograd as ag
+
+    x = torch.zeros(4, 8, requires_grad=True)
+    with pytest.raises(ValueError):
+        ag.weighted_sum(x, torch.zeros(8))
+    with pytest.raises(ValueError):
+        ag.softmax(x)
+    with pytest.raises(ValueError):
+        ag.softmax_cross_entropy(x, torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        ag.softmax(x, save="nothing")

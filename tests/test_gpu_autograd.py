@@ -1,0 +1,153 @@
+"""torch.autograd.Function layer over libvjp on the GPU: gradients that the
+autograd engine delivers (arity, order, accumulation into .grad, inputs that
+need no gradient, non-contiguous inputs, chains of ops) against the CPU
+oracle.  Tolerances are the per-op rules of the parity tests, checked here
+on fp32 activations (16-bit cases are covered op by op elsewhere)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, to_host
+from oracle.compare import pointwise, reduced
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ag(gpu_lib):
+    from row_wise_backward_amd import autograd
+    return autograd
+
+
+def _t(a, dtype="f32", grad=True):
+    t = synth.to_torch(a, dtype, DEV).clone()
+    return t.requires_grad_(grad)
+
+
+def test_weighted_sum_grads_and_accumulation(ag):
+    n, d = 7, 33
+    x = synth.normal((n, d), 1.0, "f32", 300, 0)
+    w = synth.normal((d,), 1.0, "f32", 300, 1)
+    g = synth.normal((n,), 1.0, "f32", 300, 2)
+    xt, wt = _t(x), _t(w)
+    for rep in range(2):                       # the second pass accumulates into .grad
+        y = ag.weighted_sum(xt, wt)
+        y.backward(synth.to_torch(g, "f32", DEV))
+    gx, gw = oracle.weighted_sum.bwd(synth.to_f64(g, "f32"), synth.to_f64(x, "f32"), synth.to_f64(w, "f32"))
+    r1 = pointwise(to_host(xt.grad, "f32"), 2 * gx, "f32", name="x.grad")
+    r2 = reduced(to_host(wt.grad, "f32"), 2 * gw, name="w.grad")
+    print("   ", r1, "\n   ", r2)
+    assert r1.ok and r2.ok
+
+
+def test_weighted_sum_needs_input_grad_and_layout(ag):
+    """Only w needs a gradient; x is a non-contiguous view (every other column)."""
+    n, d = 9, 16
+    base = synth.normal((n, 2 * d), 1.0, "f32", 301, 0)
+    w = synth.normal((d,), 1.0, "f32", 301, 1)
+    xt = synth.to_torch(base, "f32", DEV)[:, ::2]
+    assert not xt.is_contiguous()
+    wt = _t(w)
+    ag.weighted_sum(xt, wt).sum().backward()
+    x64 = synth.to_f64(base, "f32")[:, ::2]
+    _, gw = oracle.weighted_sum.bwd(np.ones(n), x64, synth.to_f64(w, "f32"))
+    r = reduced(to_host(wt.grad, "f32"), gw, name="w.grad")
+    assert r.ok and xt.grad is None
+
+
+def test_weighted_sum_bf16_parameter_grad_dtype(ag):
+    x = _t(synth.normal((5, 8), 1.0, "bf16", 302, 0), "bf16")
+    w = _t(synth.normal((8,), 1.0, "bf16", 302, 1), "bf16")
+    ag.weighted_sum(x, w).float().sum().backward()
+    assert w.grad.dtype == torch.bfloat16 and x.grad.dtype == torch.bfloat16
+
+
+def test_scaled_silu_grads(ag):
+    x = synth.normal((4, 1000), 2.0, "f32", 303, 0)
+    g = synth.normal((4, 1000), 1.0, "f32", 303, 2)
+    xt = _t(x)
+    wt = torch.tensor([0.75], device=DEV, requires_grad=True)
+    y = ag.scaled_silu(xt, wt)
+    assert y.shape == (4, 1000)
+    y.backward(synth.to_torch(g, "f32", DEV))
+    dx, dw = oracle.scaled_silu.bwd(synth.to_f64(g, "f32"), synth.to_f64(x, "f32"), 0.75)
+    r1 = pointwise(to_host(xt.grad, "f32"), dx, "f32", name="x.grad")
+    r2 = reduced(to_host(wt.grad, "f32"), np.array([dw]), name="w.grad")
+    print("   ", r1, "\n   ", r2)
+    assert r1.ok and r2.ok and wt.grad.shape == (1,)
+
+
+@pytest.mark.parametrize("save", ["y", "lse"])
+def test_softmax_grads(ag, save):
+    x = synth.normal((2, 3, 257), 3.0, "f32", 304, 0)      # leading dims flattened into rows
+    g = synth.normal((2, 3, 257), 1.0, "f32", 304, 2)
+    xt = _t(x)
+    y = ag.softmax(xt, save=save)
+    y.backward(synth.to_torch(g, "f32", DEV))
+    x64, g64 = synth.to_f64(x, "f32").reshape(6, 257), synth.to_f64(g, "f32").reshape(6, 257)
+    y_ref = oracle.softmax.fwd(x64)
+    r0 = pointwise(to_host(y.detach(), "f32").reshape(6, 257), y_ref, "f32", name="y")
+    dx_ref = oracle.softmax.bwd_from_x(g64, x64)
+    s = np.sum(g64 * y_ref, axis=-1, keepdims=True)
+    S = np.abs(y_ref) * (np.abs(g64) + np.abs(s) + np.sum(np.abs(g64 * y_ref), axis=-1, keepdims=True))
+    r1 = pointwise(to_host(xt.grad, "f32").reshape(6, 257), dx_ref, "f32", S=S * 4, name="x.grad")
+    print("   ", r0, "\n   ", r1)
+    assert r0.ok and r1.ok
+
+
+def test_softmax_cross_entropy_grads(ag):
+    R, C = 7, 3000
+    z = synth.normal((R, C), 2.0, "f32", 305, 0)
+    t = synth.targets(R, C, 305)
+    zt = _t(z)
+    loss = ag.softmax_cross_entropy(zt, torch.from_numpy(t.astype(np.int64)).to(DEV))
+    assert loss.dim() == 0
+    (loss * -2.5).backward()                  # upstream gradient other than 1
+    z64 = synth.to_f64(z, "f32")
+    ref = oracle.softmax_xent.fwd(z64, t)
+    r0 = reduced(to_host(loss.detach().reshape(1), "f32"), np.array([ref["loss"]]), name="loss")
+    dz = oracle.softmax_xent.bwd(z64, t, -2.5)
+    p = np.exp(z64 - ref["row_lse"][:, None])
+    r1 = pointwise(to_host(zt.grad, "f32"), dz, "f32", S=2.5 / R * (p + 1) * 4, name="logits.grad")
+    print("   ", r0, "\n   ", r1)
+    assert r0.ok and r1.ok
+
+
+def test_chain_silu_into_cross_entropy(ag):
+    """loss = xent(scaled_silu(x, w), t): the gradient flows through both ops."""
+    R, C = 5, 700
+    x = synth.normal((R, C), 2.0, "f32", 306, 0)
+    t = synth.targets(R, C, 306)
+    xt = _t(x)
+    wt = torch.tensor([1.5], device=DEV, requires_grad=True)
+    loss = ag.softmax_cross_entropy(ag.scaled_silu(xt, wt), torch.from_numpy(t).to(DEV))
+    loss.backward()
+    x64 = synth.to_f64(x, "f32")
+    z = oracle.scaled_silu.fwd(x64, 1.5)
+    dz = oracle.softmax_xent.bwd(z, t, 1.0)
+    dx, dw = oracle.scaled_silu.bwd(dz, x64, 1.5)
+    r1 = reduced(to_host(xt.grad, "f32").reshape(-1), dx.reshape(-1), name="x.grad")
+    r2 = reduced(to_host(wt.grad, "f32"), np.array([dw]), name="w.grad")
+    print("   ", r1, "\n   ", r2)
+    assert r1.ok and r2.ok
+
+
+def test_chain_weighted_sum_into_softmax(ag):
+    """softmax over a [B, N] matrix of weighted sums: rows of x are grouped."""
+    B, N, d = 3, 50, 24
+    x = synth.normal((B * N, d), 1.0, "f32", 307, 0)
+    w = synth.normal((d,), 1.0, "f32", 307, 1)
+    g = synth.normal((B, N), 1.0, "f32", 307, 2)
+    xt, wt = _t(x), _t(w)
+    y = ag.softmax(ag.weighted_sum(xt, wt).reshape(B, N), save="lse")
+    y.backward(synth.to_torch(g, "f32", DEV))
+    x64, w64, g64 = synth.to_f64(x, "f32"), synth.to_f64(w, "f32"), synth.to_f64(g, "f32")
+    s = oracle.weighted_sum.fwd(x64, w64).reshape(B, N)
+    ds = oracle.softmax.bwd_from_x(g64, s).reshape(-1)
+    dx, dw = oracle.weighted_sum.bwd(ds, x64, w64)
+    r1 = reduced(to_host(xt.grad, "f32").reshape(-1), dx.reshape(-1), name="x.grad")
+    r2 = reduced(to_host(wt.grad, "f32"), dw, name="w.grad")
+    print("   ", r1, "\n   ", r2)
+    assert r1.ok and r2.ok

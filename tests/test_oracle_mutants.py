@@ -21,6 +21,7 @@ def _ns(mod, **over):
 
 
 ws, silu, sm, xe = oracle.weighted_sum, oracle.scaled_silu, oracle.softmax, oracle.softmax_xent
+nm = oracle.norms
 
 
 def _ws_bwd_no_batch_reduction(dy, x, w, grad_w_old=None):
@@ -132,6 +133,40 @@ def _xent_bwd_ignores_dloss(z, t, dloss):
     return xe.bwd(z, t, 1.0)
 
 
+def _ln_bwd_no_mean_term(dy, x, w, eps, dw_old=None, db_old=None):
+    dx, dw, db = nm.layernorm_bwd(dy, x, w, eps, dw_old, db_old)
+    g = np.asarray(dy) * np.asarray(w)
+    _, rstd = nm.layernorm_stats(x, eps)
+    return dx + rstd[:, None] * np.mean(g, axis=-1, keepdims=True), dw, db
+
+
+def _ln_bwd_dw_without_xhat(dy, x, w, eps, dw_old=None, db_old=None):
+    dx, _, db = nm.layernorm_bwd(dy, x, w, eps, dw_old, db_old)
+    return dx, np.sum(np.asarray(dy) * np.asarray(x), axis=0), db
+
+
+def _ln_unbiased_var(x, eps):
+    x = np.asarray(x, np.float64)
+    return np.mean(x, axis=-1), 1.0 / np.sqrt(np.var(x, axis=-1, ddof=1) + eps)
+
+
+def _ln_fwd_unbiased(x, w, b, eps):
+    mu, rstd = _ln_unbiased_var(x, eps)
+    return (np.asarray(x) - mu[:, None]) * rstd[:, None] * w + b, mu, rstd
+
+
+def _rms_bwd_no_projection(dy, x, w, eps, dw_old=None):
+    rstd = nm.rmsnorm_rstd(x, eps)
+    dx = rstd[:, None] * np.asarray(dy) * np.asarray(w)
+    return dx, nm.rmsnorm_bwd(dy, x, w, eps, dw_old)[1]
+
+
+def _rms_bwd_dw_per_row(dy, x, w, eps, dw_old=None):
+    dx, _ = nm.rmsnorm_bwd(dy, x, w, eps, dw_old)
+    xhat = np.asarray(x) * nm.rmsnorm_rstd(x, eps)[:, None]
+    return dx, (np.asarray(dy) * xhat)[0]
+
+
 MUTANTS = [
     ("weighted_sum", "bwd_no_batch_reduction", _ns(ws, bwd=_ws_bwd_no_batch_reduction)),
     ("weighted_sum", "bwd_transposed_reduction", _ns(ws, bwd=_ws_bwd_transposed)),
@@ -153,6 +188,11 @@ MUTANTS = [
     ("softmax", "bwd_from_x_unnormalised", _ns(sm, bwd_from_x=_sm_bwd_from_x_unnormalised)),
     ("softmax_xent", "split_bwd_sum_not_mean", _ns(xe, bwd=_xent_bwd_sum_not_mean)),
     ("softmax_xent", "split_bwd_ignores_dloss", _ns(xe, bwd=_xent_bwd_ignores_dloss)),
+    ("norms", "ln_bwd_no_mean_term", _ns(nm, layernorm_bwd=_ln_bwd_no_mean_term)),
+    ("norms", "ln_bwd_dw_without_xhat", _ns(nm, layernorm_bwd=_ln_bwd_dw_without_xhat)),
+    ("norms", "ln_unbiased_variance", _ns(nm, layernorm_fwd=_ln_fwd_unbiased, layernorm_stats=_ln_unbiased_var)),
+    ("norms", "rms_bwd_no_projection", _ns(nm, rmsnorm_bwd=_rms_bwd_no_projection)),
+    ("norms", "rms_bwd_dw_one_row", _ns(nm, rmsnorm_bwd=_rms_bwd_dw_per_row)),
 ]
 
 

@@ -10,6 +10,7 @@ IMPL = {
     "scaled_silu": oracle.scaled_silu,
     "softmax": oracle.softmax,
     "softmax_xent": oracle.softmax_xent,
+    "norms": oracle.norms,
 }
 
 CASES = [(op, name, fn, thr) for op, pins in PINS.items() for (name, fn, thr) in pins]
