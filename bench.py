@@ -21,7 +21,8 @@ largest share of the step; `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workloads on one host core.  `extras` times the
 save-the-statistics variants (softmax forward writing the row logsumexp and
 the backward rebuilding y from it; the split cross-entropy forward and
-backward) on the same inputs, after and outside the step.
+backward) and LayerNorm / RMSNorm forward and backward on the softmax
+workload's [32768, 4096] bf16 inputs, after and outside the step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -104,6 +105,22 @@ def bytes_xent_fwd(r, c, es=2):
 def bytes_xent_bwd(r, c, es=2):
     # logits read, dlogits written, targets and row_lse read, dloss read
     return 2 * r * c * es + 2 * r * 4 + 4
+
+
+def bytes_layernorm_fwd(r, c, es=2, ws=2):
+    return 2 * r * c * es + 2 * c * ws + 8 * r
+
+
+def bytes_layernorm_bwd(r, c, T, es=2, ws=2):
+    return 3 * r * c * es + c * ws + 8 * r + 2 * T * 2 * c * 4 + 8 * c
+
+
+def bytes_rmsnorm_fwd(r, c, es=2, ws=2):
+    return 2 * r * c * es + c * ws + 4 * r
+
+
+def bytes_rmsnorm_bwd(r, c, T, es=2, ws=2):
+    return 3 * r * c * es + c * ws + 4 * r + 2 * T * c * 4 + 4 * c
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -319,6 +336,18 @@ def main() -> int:
     mlse = torch.empty(r_m, dtype=torch.float32, device=dev)
     dz2 = torch.empty_like(z)
     dloss = torch.ones(1, dtype=torch.float32, device=dev)
+    # LayerNorm / RMSNorm on the softmax workload's shape (x = mx, dy = mg)
+    nw = synth.normal_device((c_m,), 0.1, "bf16", SOFTMAX.seed, 1, dev) + 1.0
+    nb = synth.normal_device((c_m,), 0.1, "bf16", SOFTMAX.seed, 3, dev)
+    nmean = torch.empty(r_m, dtype=torch.float32, device=dev)
+    nrstd = torch.empty(r_m, dtype=torch.float32, device=dev)
+    ndw = torch.empty(c_m, dtype=torch.float32, device=dev)
+    ndb = torch.empty(c_m, dtype=torch.float32, device=dev)
+    T_ln = rwb.vjp_layernorm_bwd_workspace_size(r_m, c_m) // (8 * c_m)
+    lnws = torch.empty(rwb.vjp_layernorm_bwd_workspace_size(r_m, c_m), dtype=torch.uint8, device=dev)
+    T_rms = rwb.vjp_rmsnorm_bwd_workspace_size(r_m, c_m) // (4 * c_m)
+    rmsws = torch.empty(rwb.vjp_rmsnorm_bwd_workspace_size(r_m, c_m), dtype=torch.uint8, device=dev)
+    F32 = ctypes.c_float
     extra_ops = [
         ("softmax_fwd_lse", L.vjp_softmax_fwd_lse,
          (P(mx), c_m, P(my), c_m, P(mlse), r_m, c_m, BF16, stream), bytes_softmax_fwd_lse(r_m, c_m),
@@ -332,6 +361,20 @@ def main() -> int:
         ("softmax_xent_bwd", L.vjp_softmax_xent_bwd,
          (P(z), c_x, P(tg), P(rlse), r_x, c_x, BF16, P(dloss), P(dz2), c_x, stream),
          bytes_xent_bwd(r_x, c_x), r_x * c_x),
+        ("layernorm_fwd", L.vjp_layernorm_fwd,
+         (P(mx), c_m, P(nw), P(nb), P(my), c_m, P(nmean), P(nrstd), r_m, c_m, F32(1e-5), BF16, BF16,
+          stream), bytes_layernorm_fwd(r_m, c_m), r_m * c_m),
+        ("layernorm_bwd", L.vjp_layernorm_bwd,
+         (P(mg), c_m, P(mx), c_m, P(nw), P(nmean), P(nrstd), P(mdx), c_m, P(ndw), P(ndb), 0, r_m, c_m,
+          F32(1e-5), BF16, BF16, P(lnws), lnws.numel(), stream),
+         bytes_layernorm_bwd(r_m, c_m, T_ln), r_m * c_m),
+        ("rmsnorm_fwd", L.vjp_rmsnorm_fwd,
+         (P(mx), c_m, P(nw), P(my), c_m, P(nrstd), r_m, c_m, F32(1e-6), BF16, BF16, stream),
+         bytes_rmsnorm_fwd(r_m, c_m), r_m * c_m),
+        ("rmsnorm_bwd", L.vjp_rmsnorm_bwd,
+         (P(mg), c_m, P(mx), c_m, P(nw), P(nrstd), P(mdx), c_m, P(ndw), 0, r_m, c_m, F32(1e-6), BF16,
+          BF16, P(rmsws), rmsws.numel(), stream),
+         bytes_rmsnorm_bwd(r_m, c_m, T_rms), r_m * c_m),
     ]
     n_extra = max(3, args.steps // 2)
     xevs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]

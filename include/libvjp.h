@@ -247,6 +247,58 @@ int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* targets,
                          const float* dloss, void* dlogits, int64_t ld_dlogits,
                          vjp_stream_t stream);
 
+/* ---------------------------------------------------------------- LayerNorm / RMSNorm
+ * Over the last dimension of x [rows, cols] (ld_x); w, b [cols] in w_dtype.
+ *   LayerNorm: mu = mean(x), rstd = 1 / sqrt(mean((x - mu)^2) + eps)
+ *              (biased variance, computed as the mean of squared deviations),
+ *              xhat = (x - mu) rstd, y = xhat w + b
+ *   RMSNorm:   rstd = 1 / sqrt(mean(x^2) + eps), xhat = x rstd, y = xhat w
+ * Backward, with g = dy w, a = mean(g) (LayerNorm only), c = mean(g xhat):
+ *   dx = rstd (g - a - xhat c),  dw = sum over rows of dy xhat (fp32),
+ *   db = sum over rows of dy (fp32, LayerNorm only).
+ * Source: "Backprop for kernel writers", the LayerNorm passage after 04 "The
+ * duality" (the backward collapses to two row scalars; the parameter
+ * gradients reduce over the batch axis) and section 07 (normalisation
+ * constants are worth saving: one float per row); "Backward in Triton",
+ * sections "Save vs recompute" and "The backward grid is not the forward
+ * grid" (RMSNorm's dw partials summed by a deterministic second pass).
+ * row_mean / row_rstd (fp32 [rows]) are optional outputs of the forward
+ * (NULL: not written) and optional inputs of the backward (NULL: recomputed
+ * from x with eps; LayerNorm takes both or neither).  eps must be finite and
+ * >= 0.  cols may not exceed vjp_norm_max_cols(act, aligned16) = 16384 for
+ * every dtype and alignment (a row lives in the registers of at most 1024
+ * lanes, 16 values each); wider rows are VJP_EINVAL.
+ * Backward stage 1: rows are dealt round-robin to tiles = min(1024, rows)
+ * workgroups; tile t holds rows t, t + tiles, ... and writes its fp32
+ * partial row P[t][0 .. cols) = sum dy xhat and, for LayerNorm,
+ * P[t][cols .. 2 cols) = sum dy (workspace layout, row width cols or
+ * 2 cols).  Stage 2 sums the partial rows in the order documented for
+ * vjp_weighted_sum_bwd (d = 2 cols for LayerNorm, split into dw and db).
+ * accumulate = 1 adds into dw (and db). */
+int64_t vjp_norm_max_cols(int act, int aligned16);
+
+size_t vjp_layernorm_bwd_workspace_size(int64_t rows, int64_t cols);
+size_t vjp_rmsnorm_bwd_workspace_size(int64_t rows, int64_t cols);
+
+int vjp_layernorm_fwd(const void* x, int64_t ld_x, const void* w, const void* b, void* y,
+                      int64_t ld_y, float* row_mean, float* row_rstd, int64_t rows,
+                      int64_t cols, float eps, int act, int w_dtype, vjp_stream_t stream);
+
+int vjp_layernorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* w,
+                      const float* row_mean, const float* row_rstd, void* dx, int64_t ld_dx,
+                      float* dw, float* db, int accumulate, int64_t rows, int64_t cols,
+                      float eps, int act, int w_dtype, void* workspace, size_t workspace_bytes,
+                      vjp_stream_t stream);
+
+int vjp_rmsnorm_fwd(const void* x, int64_t ld_x, const void* w, void* y, int64_t ld_y,
+                    float* row_rstd, int64_t rows, int64_t cols, float eps, int act,
+                    int w_dtype, vjp_stream_t stream);
+
+int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* w,
+                    const float* row_rstd, void* dx, int64_t ld_dx, float* dw, int accumulate,
+                    int64_t rows, int64_t cols, float eps, int act, int w_dtype,
+                    void* workspace, size_t workspace_bytes, vjp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,16 @@ _SIGS = {
     "vjp_softmax_xent_fwd": ([_vp, _i64, _vp, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                              _int),
     "vjp_softmax_xent_bwd": ([_vp, _i64, _vp, _vp, _i64, _i64, _int, _vp, _vp, _i64, _vp], _int),
+    "vjp_norm_max_cols": ([_int, _int], _i64),
+    "vjp_layernorm_bwd_workspace_size": ([_i64, _i64], _sz),
+    "vjp_rmsnorm_bwd_workspace_size": ([_i64, _i64], _sz),
+    "vjp_layernorm_fwd": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _f32, _int, _int,
+                           _vp], _int),
+    "vjp_layernorm_bwd": ([_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _int, _i64,
+                           _i64, _f32, _int, _int, _vp, _sz, _vp], _int),
+    "vjp_rmsnorm_fwd": ([_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _f32, _int, _int, _vp], _int),
+    "vjp_rmsnorm_bwd": ([_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _int, _i64, _i64, _f32,
+                         _int, _int, _vp, _sz, _vp], _int),
     "vjp_softmax_xent_fwd_bwd": ([_vp, _i64, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp,
                                   _i64, _vp, _vp, _sz, _vp], _int),
 }
@@ -383,3 +393,108 @@ def vjp_softmax_xent_bwd(logits, targets, row_lse, dloss, dlogits=None):
                                     _ptr(dlogits), _ld(dlogits), _stream(logits)),
            "vjp_softmax_xent_bwd")
     return dlogits
+
+
+# ----------------------------------------------------------------- LayerNorm / RMSNorm
+
+def vjp_norm_max_cols(dtype=torch.bfloat16, aligned16=True) -> int:
+    return int(lib.vjp_norm_max_cols(_DT[dtype], int(bool(aligned16))))
+
+
+def vjp_layernorm_bwd_workspace_size(rows: int, cols: int) -> int:
+    return int(lib.vjp_layernorm_bwd_workspace_size(rows, cols))
+
+
+def vjp_rmsnorm_bwd_workspace_size(rows: int, cols: int) -> int:
+    return int(lib.vjp_rmsnorm_bwd_workspace_size(rows, cols))
+
+
+def _stats(t, rows, dev, name):
+    if t is not None:
+        _expect(t, (rows,), torch.float32, dev, name)
+    return t
+
+
+def vjp_layernorm_fwd(x, w, b, eps=1e-5, y=None, row_mean=None, row_rstd=None, save_stats=True):
+    """(y, row_mean, row_rstd): LayerNorm over the last dim of x [rows, cols];
+    the statistics are fp32 [rows] (None when save_stats is False)."""
+    rows, cols = x.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    if save_stats:
+        row_mean = torch.empty(rows, dtype=torch.float32, device=dev) if row_mean is None else row_mean
+        row_rstd = torch.empty(rows, dtype=torch.float32, device=dev) if row_rstd is None else row_rstd
+    _expect(y, (rows, cols), x.dtype, dev, "y")
+    _expect(w, (cols,), None, dev, "w")
+    _expect(b, (cols,), w.dtype, dev, "b")
+    _stats(row_mean, rows, dev, "row_mean")
+    _stats(row_rstd, rows, dev, "row_rstd")
+    _check(lib.vjp_layernorm_fwd(_ptr(x), _ld(x), _ptr(_flat(w)), _ptr(_flat(b)), _ptr(y), _ld(y),
+                                 _ptr(row_mean), _ptr(row_rstd), rows, cols, float(eps), _dt(x),
+                                 _dt(w), _stream(x)), "vjp_layernorm_fwd")
+    return y, row_mean, row_rstd
+
+
+def vjp_layernorm_bwd(dy, x, w, row_mean=None, row_rstd=None, eps=1e-5, dx=None, dw=None, db=None,
+                      accumulate=False, workspace=None):
+    """(dx, dw, db); dw, db fp32 [cols].  Without saved statistics they are
+    recomputed from x."""
+    rows, cols = x.shape
+    dev = x.device
+    if dx is None:
+        dx = torch.empty_like(x)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dw = torch.empty(cols, **f32) if dw is None else dw
+    db = torch.empty(cols, **f32) if db is None else db
+    _expect(dy, (rows, cols), x.dtype, dev, "dy")
+    _expect(w, (cols,), None, dev, "w")
+    _expect(dx, (rows, cols), x.dtype, dev, "dx")
+    _expect(dw, (cols,), torch.float32, dev, "dw")
+    _expect(db, (cols,), torch.float32, dev, "db")
+    _stats(row_mean, rows, dev, "row_mean")
+    _stats(row_rstd, rows, dev, "row_rstd")
+    ws = _workspace(vjp_layernorm_bwd_workspace_size(rows, cols), x, workspace)
+    _check(lib.vjp_layernorm_bwd(_ptr(dy), _ld(dy), _ptr(x), _ld(x), _ptr(_flat(w)), _ptr(row_mean),
+                                 _ptr(row_rstd), _ptr(dx), _ld(dx), _ptr(dw), _ptr(db),
+                                 int(bool(accumulate)), rows, cols, float(eps), _dt(x), _dt(w),
+                                 _ptr(ws), _nbytes(ws), _stream(x)), "vjp_layernorm_bwd")
+    return dx, dw, db
+
+
+def vjp_rmsnorm_fwd(x, w, eps=1e-6, y=None, row_rstd=None, save_stats=True):
+    """(y, row_rstd): RMSNorm over the last dim of x [rows, cols]."""
+    rows, cols = x.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    if save_stats and row_rstd is None:
+        row_rstd = torch.empty(rows, dtype=torch.float32, device=dev)
+    _expect(y, (rows, cols), x.dtype, dev, "y")
+    _expect(w, (cols,), None, dev, "w")
+    _stats(row_rstd, rows, dev, "row_rstd")
+    _check(lib.vjp_rmsnorm_fwd(_ptr(x), _ld(x), _ptr(_flat(w)), _ptr(y), _ld(y), _ptr(row_rstd),
+                               rows, cols, float(eps), _dt(x), _dt(w), _stream(x)),
+           "vjp_rmsnorm_fwd")
+    return y, row_rstd
+
+
+def vjp_rmsnorm_bwd(dy, x, w, row_rstd=None, eps=1e-6, dx=None, dw=None, accumulate=False,
+                    workspace=None):
+    """(dx, dw); dw fp32 [cols]."""
+    rows, cols = x.shape
+    dev = x.device
+    if dx is None:
+        dx = torch.empty_like(x)
+    dw = torch.empty(cols, dtype=torch.float32, device=dev) if dw is None else dw
+    _expect(dy, (rows, cols), x.dtype, dev, "dy")
+    _expect(w, (cols,), None, dev, "w")
+    _expect(dx, (rows, cols), x.dtype, dev, "dx")
+    _expect(dw, (cols,), torch.float32, dev, "dw")
+    _stats(row_rstd, rows, dev, "row_rstd")
+    ws = _workspace(vjp_rmsnorm_bwd_workspace_size(rows, cols), x, workspace)
+    _check(lib.vjp_rmsnorm_bwd(_ptr(dy), _ld(dy), _ptr(x), _ld(x), _ptr(_flat(w)), _ptr(row_rstd),
+                               _ptr(dx), _ld(dx), _ptr(dw), int(bool(accumulate)), rows, cols,
+                               float(eps), _dt(x), _dt(w), _ptr(ws), _nbytes(ws), _stream(x)),
+           "vjp_rmsnorm_bwd")
+    return dx, dw

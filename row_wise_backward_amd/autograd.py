@@ -19,6 +19,7 @@ What is saved ("Backward in Triton", section "Save vs recompute";
 * scaled SiLU: x and w; sigmoid(x) is recomputed in the backward kernel;
 * softmax: y (save="y"), or x and the row logsumexp (save="lse": one fp32
   per row, y rebuilt on chip);
+* LayerNorm / RMSNorm: x, w and the row mean / rstd (one fp32 each per row);
 * softmax cross-entropy: the logits, the targets and the row logsumexp;
   the backward rebuilds p = exp(z - lse) and reads the upstream gradient
   from device memory (no host synchronisation).
@@ -32,12 +33,14 @@ from __future__ import annotations
 
 import torch
 
-from . import (vjp_scaled_silu_bwd, vjp_scaled_silu_fwd, vjp_softmax_bwd, vjp_softmax_bwd_lse,
+from . import (vjp_layernorm_bwd, vjp_layernorm_fwd, vjp_rmsnorm_bwd, vjp_rmsnorm_fwd,
+               vjp_scaled_silu_bwd, vjp_scaled_silu_fwd, vjp_softmax_bwd, vjp_softmax_bwd_lse,
                vjp_softmax_fwd, vjp_softmax_fwd_lse, vjp_softmax_xent_bwd, vjp_softmax_xent_fwd,
                vjp_weighted_sum_bwd, vjp_weighted_sum_fwd)
 
-__all__ = ["WeightedSum", "ScaledSiLU", "Softmax", "SoftmaxCrossEntropy", "weighted_sum",
-           "scaled_silu", "softmax", "softmax_cross_entropy"]
+__all__ = ["WeightedSum", "ScaledSiLU", "Softmax", "SoftmaxCrossEntropy", "LayerNorm", "RMSNorm",
+           "weighted_sum", "scaled_silu", "softmax", "softmax_cross_entropy", "layer_norm",
+           "rms_norm"]
 
 
 def _param_grad(g32: torch.Tensor, like: torch.Tensor) -> torch.Tensor:
@@ -141,6 +144,60 @@ class SoftmaxCrossEntropy(torch.autograd.Function):
             g = g.float()
         dz = vjp_softmax_xent_bwd(z, t, lse, g.contiguous())
         return dz, None
+
+
+class LayerNorm(torch.autograd.Function):
+    """LayerNorm over the last dimension with weight w and bias b."""
+
+    @staticmethod
+    def forward(ctx, x, w, b, eps=1e-5):
+        shape = x.shape
+        x2 = x.contiguous().reshape(-1, shape[-1])
+        w = w.contiguous()
+        y, mean, rstd = vjp_layernorm_fwd(x2, w, b.contiguous(), eps)
+        ctx.save_for_backward(x2, w, mean, rstd)
+        ctx.shape, ctx.eps, ctx.b_dtype = shape, eps, b.dtype
+        return y.reshape(shape)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x2, w, mean, rstd = ctx.saved_tensors
+        dx, dw, db = vjp_layernorm_bwd(dy.contiguous().reshape(x2.shape), x2, w, mean, rstd, ctx.eps)
+        return (dx.reshape(ctx.shape) if ctx.needs_input_grad[0] else None,
+                _param_grad(dw, w) if ctx.needs_input_grad[1] else None,
+                (db if ctx.b_dtype == torch.float32 else db.to(ctx.b_dtype))
+                if ctx.needs_input_grad[2] else None,
+                None)
+
+
+class RMSNorm(torch.autograd.Function):
+    """RMSNorm over the last dimension with weight w."""
+
+    @staticmethod
+    def forward(ctx, x, w, eps=1e-6):
+        shape = x.shape
+        x2 = x.contiguous().reshape(-1, shape[-1])
+        w = w.contiguous()
+        y, rstd = vjp_rmsnorm_fwd(x2, w, eps)
+        ctx.save_for_backward(x2, w, rstd)
+        ctx.shape, ctx.eps = shape, eps
+        return y.reshape(shape)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x2, w, rstd = ctx.saved_tensors
+        dx, dw = vjp_rmsnorm_bwd(dy.contiguous().reshape(x2.shape), x2, w, rstd, ctx.eps)
+        return (dx.reshape(ctx.shape) if ctx.needs_input_grad[0] else None,
+                _param_grad(dw, w) if ctx.needs_input_grad[1] else None,
+                None)
+
+
+def layer_norm(x, w, b, eps=1e-5):
+    return LayerNorm.apply(x, w, b, eps)
+
+
+def rms_norm(x, w, eps=1e-6):
+    return RMSNorm.apply(x, w, eps)
 
 
 def weighted_sum(x, w):

@@ -515,3 +515,159 @@ VJP_API int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* 
   }
   return ok();
 }
+
+// ------------------------------------------------------------------ LayerNorm / RMSNorm
+
+namespace {
+
+// Backward tiles: rows are dealt round-robin to at most kNormTiles workgroups.
+constexpr int64_t kNormTiles = 1024;
+
+int64_t norm_tiles(int64_t rows) { return rows < kNormTiles ? rows : kNormTiles; }
+
+bool eps_ok(float eps) { return eps >= 0.0f && eps < __builtin_inff(); }
+
+int norm_check_cols(int64_t rows, int64_t cols, int act, bool vec) {
+  if (rows > 0 && cols == 0) return fail(VJP_EINVAL, "normalisation over zero columns");
+  const int64_t lim = norm_max_cols(act, vec);
+  if (cols > lim)
+    return fail(VJP_EINVAL, "%lld columns exceed the limit of %lld", (long long)cols,
+                (long long)lim);
+  return VJP_OK;
+}
+
+int norm_fwd_impl(bool rms, const void* x, int64_t ld_x, const void* w, const void* b, void* y,
+                  int64_t ld_y, float* row_mean, float* row_rstd, int64_t rows, int64_t cols,
+                  float eps, int act, int w_dtype, vjp_stream_t stream) {
+  if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (rows < 0 || cols < 0) return fail(VJP_EINVAL, "negative size");
+  if (!eps_ok(eps)) return fail(VJP_EINVAL, "eps must be finite and >= 0");
+  const int es = dtype_size(act), ws = dtype_size(w_dtype);
+  VJP_TRY(check_matrix("x", x, rows, cols, ld_x, es));
+  VJP_TRY(check_matrix("y", y, rows, cols, ld_y, es));
+  VJP_TRY(check_vector("w", w, rows > 0 ? cols : 0, ws));
+  if (!rms) VJP_TRY(check_vector("b", b, rows > 0 ? cols : 0, ws));
+  if (row_mean) VJP_TRY(check_vector("row_mean", row_mean, rows, 4));
+  if (row_rstd) VJP_TRY(check_vector("row_rstd", row_rstd, rows, 4));
+  VJP_TRY(check_alias({span(y, mat_bytes(rows, cols, ld_y, es), "y"),
+                       span(row_mean, row_mean ? rows * 4 : 0, "row_mean"),
+                       span(row_rstd, row_rstd ? rows * 4 : 0, "row_rstd")},
+                      {span(x, mat_bytes(rows, cols, ld_x, es), "x"), span(w, cols * ws, "w"),
+                       span(rms ? nullptr : b, cols * ws, "b")}));
+  const bool vec = rows_vec_ok(x, ld_x, es) && rows_vec_ok(y, ld_y, es);
+  VJP_TRY(norm_check_cols(rows, cols, act, vec));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const int64_t nr = rows - r0 < kRowsPerLaunch ? rows - r0 : kRowsPerLaunch;
+    const hipError_t e = launch_norm_fwd(
+        rms, static_cast<const char*>(x) + r0 * ld_x * es, ld_x, w, b, w_dtype,
+        static_cast<char*>(y) + r0 * ld_y * es, ld_y, row_mean ? row_mean + r0 : nullptr,
+        row_rstd ? row_rstd + r0 : nullptr, nr, cols, eps, act, vec, s);
+    if (e != hipSuccess) return hip_status(e, rms ? "rmsnorm_fwd" : "layernorm_fwd");
+  }
+  return ok();
+}
+
+int norm_bwd_impl(bool rms, const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
+                  const void* w, const float* row_mean, const float* row_rstd, void* dx,
+                  int64_t ld_dx, float* dw, float* db, int accumulate, int64_t rows, int64_t cols,
+                  float eps, int act, int w_dtype, void* workspace, size_t workspace_bytes,
+                  vjp_stream_t stream) {
+  if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (rows < 0 || cols < 0) return fail(VJP_EINVAL, "negative size");
+  if (!eps_ok(eps)) return fail(VJP_EINVAL, "eps must be finite and >= 0");
+  if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
+  if (!rms && ((row_mean == nullptr) != (row_rstd == nullptr)))
+    return fail(VJP_EINVAL, "row_mean and row_rstd must both be given or both be NULL");
+  const int es = dtype_size(act), ws = dtype_size(w_dtype);
+  VJP_TRY(check_matrix("dy", dy, rows, cols, ld_dy, es));
+  VJP_TRY(check_matrix("x", x, rows, cols, ld_x, es));
+  VJP_TRY(check_matrix("dx", dx, rows, cols, ld_dx, es));
+  VJP_TRY(check_vector("w", w, rows > 0 ? cols : 0, ws));
+  VJP_TRY(check_vector("dw", dw, cols, 4));
+  if (!rms) VJP_TRY(check_vector("db", db, cols, 4));
+  if (row_rstd) VJP_TRY(check_vector("row_rstd", row_rstd, rows, 4));
+  if (row_mean) VJP_TRY(check_vector("row_mean", row_mean, rows, 4));
+  const size_t need = rms ? vjp_rmsnorm_bwd_workspace_size(rows, cols)
+                          : vjp_layernorm_bwd_workspace_size(rows, cols);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(VJP_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned(workspace, 4)) return fail(VJP_EALIGN, "workspace is not 4-byte aligned");
+  }
+  VJP_TRY(check_alias({span(dx, mat_bytes(rows, cols, ld_dx, es), "dx"), span(dw, cols * 4, "dw"),
+                       span(rms ? nullptr : db, cols * 4, "db"),
+                       span(workspace, int64_t(need), "workspace")},
+                      {span(dy, mat_bytes(rows, cols, ld_dy, es), "dy"),
+                       span(x, mat_bytes(rows, cols, ld_x, es), "x"), span(w, cols * ws, "w"),
+                       span(row_mean, row_mean ? rows * 4 : 0, "row_mean"),
+                       span(row_rstd, row_rstd ? rows * 4 : 0, "row_rstd")}));
+  const bool vec = rows_vec_ok(dy, ld_dy, es) && rows_vec_ok(x, ld_x, es) &&
+                   rows_vec_ok(dx, ld_dx, es);
+  VJP_TRY(norm_check_cols(rows, cols, act, vec));
+  if (cols == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = norm_tiles(rows);
+  float* P = static_cast<float*>(workspace);
+  if (T > 0) {
+    const hipError_t e = launch_norm_bwd_stage1(rms, dy, ld_dy, x, ld_x, w, w_dtype, row_mean,
+                                                row_rstd, dx, ld_dx, P, rows, cols, T, eps, act,
+                                                vec, s);
+    if (e != hipSuccess) return hip_status(e, rms ? "rmsnorm_bwd stage 1" : "layernorm_bwd stage 1");
+  }
+  return hip_status(rms ? launch_reduce_partials(P, T, cols, dw, accumulate, s)
+                        : launch_reduce_partials_split(P, T, 2 * cols, dw, db, cols, accumulate, s),
+                    rms ? "rmsnorm_bwd stage 2" : "layernorm_bwd stage 2");
+}
+
+}  // namespace
+
+VJP_API size_t vjp_layernorm_bwd_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return size_t(norm_tiles(rows)) * size_t(2 * cols) * sizeof(float);
+}
+
+VJP_API size_t vjp_rmsnorm_bwd_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return size_t(norm_tiles(rows)) * size_t(cols) * sizeof(float);
+}
+
+VJP_API int64_t vjp_norm_max_cols(int act, int aligned16) {
+  if (!dtype_ok(act)) return -1;
+  return norm_max_cols(act, aligned16 != 0);
+}
+
+VJP_API int vjp_layernorm_fwd(const void* x, int64_t ld_x, const void* w, const void* b, void* y,
+                              int64_t ld_y, float* row_mean, float* row_rstd, int64_t rows,
+                              int64_t cols, float eps, int act, int w_dtype,
+                              vjp_stream_t stream) {
+  return norm_fwd_impl(false, x, ld_x, w, b, y, ld_y, row_mean, row_rstd, rows, cols, eps, act,
+                       w_dtype, stream);
+}
+
+VJP_API int vjp_layernorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
+                              const void* w, const float* row_mean, const float* row_rstd,
+                              void* dx, int64_t ld_dx, float* dw, float* db, int accumulate,
+                              int64_t rows, int64_t cols, float eps, int act, int w_dtype,
+                              void* workspace, size_t workspace_bytes, vjp_stream_t stream) {
+  return norm_bwd_impl(false, dy, ld_dy, x, ld_x, w, row_mean, row_rstd, dx, ld_dx, dw, db,
+                       accumulate, rows, cols, eps, act, w_dtype, workspace, workspace_bytes,
+                       stream);
+}
+
+VJP_API int vjp_rmsnorm_fwd(const void* x, int64_t ld_x, const void* w, void* y, int64_t ld_y,
+                            float* row_rstd, int64_t rows, int64_t cols, float eps, int act,
+                            int w_dtype, vjp_stream_t stream) {
+  return norm_fwd_impl(true, x, ld_x, w, nullptr, y, ld_y, nullptr, row_rstd, rows, cols, eps,
+                       act, w_dtype, stream);
+}
+
+VJP_API int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
+                            const void* w, const float* row_rstd, void* dx, int64_t ld_dx,
+                            float* dw, int accumulate, int64_t rows, int64_t cols, float eps,
+                            int act, int w_dtype, void* workspace, size_t workspace_bytes,
+                            vjp_stream_t stream) {
+  return norm_bwd_impl(true, dy, ld_dy, x, ld_x, w, nullptr, row_rstd, dx, ld_dx, dw, nullptr,
+                       accumulate, rows, cols, eps, act, w_dtype, workspace, workspace_bytes,
+                       stream);
+}

@@ -218,4 +218,12 @@ __device__ __forceinline__ float sigmoid(float x) {
   return rcp_fast(1.0f + exp2_fast(-x * kLog2e));
 }
 
+// One element of a parameter vector stored as fp32, fp16 or bf16 (dt is the
+// library's dtype code: 0 fp32, 1 fp16, 2 bf16), widened to fp32.
+__device__ __forceinline__ float load_param_f32(const void* __restrict__ w, int64_t j, int dt) {
+  if (dt == 0) return static_cast<const float*>(w)[j];
+  if (dt == 1) return to_f32(static_cast<const _Float16*>(w)[j]);
+  return to_f32(static_cast<const bf16*>(w)[j]);
+}
+
 }  // namespace vjp

@@ -15,6 +15,10 @@ inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 // Stage 2: out[j] = (accumulate ? out[j] : 0) + fixed-order sum_t P[t * d + j].
 hipError_t launch_reduce_partials(const float* P, int64_t T, int64_t d, float* out,
                                   int accumulate, hipStream_t s);
+// As above with columns j >= split written to out2[j - split].
+hipError_t launch_reduce_partials_split(const float* P, int64_t T, int64_t d, float* out,
+                                        float* out2, int64_t split, int accumulate,
+                                        hipStream_t s);
 
 // Weighted sum.
 hipError_t launch_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
@@ -59,5 +63,21 @@ hipError_t launch_softmax_xent_bwd(const void* z, int64_t ld, const int32_t* tar
 hipError_t launch_xent_finalize(const float* row_loss, const int32_t* targets, int64_t rows,
                                 int64_t classes, float* loss, int32_t* n_invalid,
                                 hipStream_t s);
+
+// LayerNorm (rms = false) / RMSNorm (rms = true).  Rows wider than
+// norm_max_cols(act, vec) are not supported (hipErrorInvalidValue).
+int64_t norm_max_cols(int act, bool vec);
+hipError_t launch_norm_fwd(bool rms, const void* x, int64_t ld_x, const void* w, const void* b,
+                           int wdt, void* y, int64_t ld_y, float* row_mean, float* row_rstd,
+                           int64_t rows, int64_t cols, float eps, int act, bool vec,
+                           hipStream_t s);
+// Stage 1 of the backward: dx and the per-tile partials P[tiles][cols] (dw)
+// followed, for LayerNorm, by P[tiles][cols .. 2 cols) (db) in each row.
+// row_rstd (and row_mean) null: the statistics are recomputed from x.
+hipError_t launch_norm_bwd_stage1(bool rms, const void* dy, int64_t ld_dy, const void* x,
+                                  int64_t ld_x, const void* w, int wdt, const float* row_mean,
+                                  const float* row_rstd, void* dx, int64_t ld_dx, float* P,
+                                  int64_t rows, int64_t cols, int64_t tiles, float eps, int act,
+                                  bool vec, hipStream_t s);
 
 }  // namespace vjp

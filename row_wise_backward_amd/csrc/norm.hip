@@ -1,0 +1,415 @@
+// LayerNorm and RMSNorm over the last dimension: forward and backward.
+//
+// Source: "Backprop for kernel writers", the LayerNorm passage after 04 "The
+// duality" (every element of a row is coupled through its mean and variance,
+// yet the backward collapses to two row scalars; the parameter gradients
+// reduce over the batch axis and need cross-block accumulation) and section
+// 07 (save normalisation constants: one float per row).  "Backward in Triton
+// -- autograd.Function and the backward grid", sections "Save vs recompute"
+// (the rstd is a one-scalar-per-row statistic) and "The backward grid is not
+// the forward grid" (RMSNorm's dw: a length-d partial from every row, summed
+// by a second, deterministic pass).
+//
+//   LayerNorm: mu = mean(x), rstd = 1 / sqrt(mean((x - mu)^2) + eps),
+//              xhat = (x - mu) rstd, y = xhat w + b
+//   RMSNorm:   mu = 0,       rstd = 1 / sqrt(mean(x^2) + eps), y = xhat w
+//   backward:  g = dy w, a = mean(g) (LayerNorm only), c = mean(g xhat),
+//              dx = rstd (g - a - xhat c); dw = sum_rows dy xhat, db = sum_rows dy
+//
+// Forward: the resident row layout of rowops.hpp, the row read once; the
+// variance is the two-pass mean of squared deviations of the values held in
+// registers.  Backward: workgroup t owns the rows t, t + tiles, t + 2 tiles,
+// ... (a round-robin deal, so all workgroups stream neighbouring rows at the
+// same moment); for each row it loads x and dy into registers, forms the two
+// row scalars with one exchange, writes dx, and adds dy xhat (and dy) into
+// fp32 column partials that stay in its lanes' registers: every lane owns
+// fixed columns, so no cross-lane reduction is needed.  The tile's partial
+// rows go to P[t][0 .. cols) (dw) and P[t][cols .. 2 cols) (db), summed by
+// the fixed-order stage-2 kernel.
+#include "launch.hpp"
+#include "rowops.hpp"
+
+namespace vjp {
+
+namespace {
+
+// Loads the lane's K vectors of row `row` (padding reads 0).
+template <typename T, int VEC, int WAVES, int K>
+__device__ __forceinline__ void load_lane_row(const T* __restrict__ r, int64_t cols,
+                                              int64_t lane_col, Vec<T, VEC> (&v)[K]) {
+  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if (k * kStep < cols) load_row_vec<T, VEC>(r, k * kStep + lane_col, cols, zero_of<T>(), v[k]);
+}
+
+// Forward.  Workgroup g (WAVES waves) takes rows g, g + gridDim.x, ...; its
+// lanes keep w and b of their columns in registers for all of them, and the
+// next row is loaded while the current one is reduced and written.
+template <typename T, int VEC, int WAVES, int K, bool RMS>
+__global__ __launch_bounds__(WAVES * kWave) void norm_fwd_rows(
+    const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
+    const void* __restrict__ b, int wdt, T* __restrict__ y, int64_t ld_y,
+    float* __restrict__ row_mean, float* __restrict__ row_rstd, int64_t rows, int64_t cols,
+    float eps) {
+  __shared__ float buf[2][2][WAVES];   // [row parity][reduction]
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
+  const int64_t lane_col = (int64_t(wave) * kWave + lane) * VEC;
+  const float inv_cols = 1.0f / float(cols);
+
+  float wv[K][VEC], bv[RMS ? 1 : K][VEC];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t col = k * kStep + lane_col;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const bool in = col + i < cols;
+      wv[k][i] = in ? load_param_f32(w, col + i, wdt) : 0.0f;
+      if constexpr (!RMS) bv[k][i] = in ? load_param_f32(b, col + i, wdt) : 0.0f;
+    }
+  }
+
+  // Prefetch only while a lane holds at most 8 values of a row (wider rows
+  // would need more than the 128 registers a 1024-thread workgroup allows).
+  constexpr bool kPrefetch = K * VEC <= 8;
+  int64_t row = blockIdx.x;
+  Vec<T, VEC> cur[K], nxt[kPrefetch ? K : 1];
+  if (kPrefetch && row < rows) load_lane_row<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, cur);
+  for (int par = 0; row < rows; row += gridDim.x, par ^= 1) {
+    const int64_t next = row + gridDim.x;
+    if constexpr (kPrefetch) {
+      if (next < rows) load_lane_row<T, VEC, WAVES, K>(x + next * ld_x, cols, lane_col, nxt);
+    } else {
+      load_lane_row<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, cur);
+    }
+
+    float mean = 0.0f;
+    if constexpr (!RMS) {
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (k * kStep < cols)
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) s += to_f32(cur[k].v[i]);   // padding reads 0
+      mean = row_reduce_sum<WAVES>(s, buf[par][0]) * inv_cols;
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k * kStep < cols) {
+        const int64_t col = k * kStep + lane_col;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float d = to_f32(cur[k].v[i]) - mean;
+          if (col + i < cols) ss = fmaf(d, d, ss);
+        }
+      }
+    }
+    const float rstd =
+        1.0f / __builtin_sqrtf(row_reduce_sum<WAVES>(ss, buf[par][1]) * inv_cols + eps);
+    if (wave == 0 && lane == 0) {
+      if (row_mean != nullptr) row_mean[row] = mean;
+      if (row_rstd != nullptr) row_rstd[row] = rstd;
+    }
+
+    T* yr = y + row * ld_y;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k * kStep < cols) {
+        const int64_t col = k * kStep + lane_col;
+        if (col < cols) {
+          float o[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i)
+            o[i] = fmaf((to_f32(cur[k].v[i]) - mean) * rstd, wv[k][i], RMS ? 0.0f : bv[k][i]);
+          store_row_vec<T, VEC>(yr, col, cols, o);
+        }
+      }
+    }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) cur[k] = nxt[k];
+    }
+  }
+}
+
+template <typename T, int VEC, int WAVES, int K, bool RMS>
+__global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
+    const T* __restrict__ dy, int64_t ld_dy, const T* __restrict__ x, int64_t ld_x,
+    const void* __restrict__ w, int wdt, const float* __restrict__ row_mean,
+    const float* __restrict__ row_rstd, T* __restrict__ dx, int64_t ld_dx,
+    float* __restrict__ P, int64_t rows, int64_t cols, int64_t tiles, float eps) {
+  // Reduction slots, double-buffered by row parity: a wave may start the next
+  // row's exchange while a slower wave still reads this row's values.
+  __shared__ float buf[2][4][WAVES];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
+  const int64_t lane_col = (int64_t(wave) * kWave + lane) * VEC;
+  const float inv_cols = 1.0f / float(cols);
+  const int64_t tile = blockIdx.x;
+
+  float wv[K][VEC], pdw[K][VEC], pdb[RMS ? 1 : K][VEC];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t col = k * kStep + lane_col;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      wv[k][i] = (col + i < cols) ? load_param_f32(w, col + i, wdt) : 0.0f;
+      pdw[k][i] = 0.0f;
+      if constexpr (!RMS) pdb[k][i] = 0.0f;
+    }
+  }
+
+  // The next row of the tile is loaded while the current one is processed
+  // (while a lane holds at most 8 values of a row; wider rows load in turn).
+  constexpr bool kPrefetch = K * VEC <= 8;
+  constexpr int KN = kPrefetch ? K : 1;
+  Vec<T, VEC> rx[K], rg[K], nx[KN], ng[KN];
+  if (kPrefetch && tile < rows) {
+    load_lane_row<T, VEC, WAVES, K>(x + tile * ld_x, cols, lane_col, rx);
+    load_lane_row<T, VEC, WAVES, K>(dy + tile * ld_dy, cols, lane_col, rg);
+  }
+  int par = 0;
+  for (int64_t row = tile; row < rows; row += tiles, par ^= 1) {
+    const int64_t next = row + tiles;
+    if constexpr (kPrefetch) {
+      if (next < rows) {
+        load_lane_row<T, VEC, WAVES, KN>(x + next * ld_x, cols, lane_col, nx);
+        load_lane_row<T, VEC, WAVES, KN>(dy + next * ld_dy, cols, lane_col, ng);
+      }
+    } else {
+      load_lane_row<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, rx);
+      load_lane_row<T, VEC, WAVES, K>(dy + row * ld_dy, cols, lane_col, rg);
+    }
+    float mean = 0.0f, rstd;
+    if (row_rstd != nullptr) {          // saved statistics (uniform branch)
+      rstd = row_rstd[row];
+      if constexpr (!RMS) mean = row_mean[row];
+    } else {                            // recomputed from the row in registers
+      if constexpr (!RMS) {
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          if (k * kStep < cols)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) s += to_f32(rx[k].v[i]);
+        mean = row_reduce_sum<WAVES>(s, buf[par][2]) * inv_cols;
+      }
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if (k * kStep < cols) {
+          const int64_t col = k * kStep + lane_col;
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            const float d = to_f32(rx[k].v[i]) - mean;
+            if (col + i < cols) ss = fmaf(d, d, ss);
+          }
+        }
+      }
+      rstd = 1.0f / __builtin_sqrtf(row_reduce_sum<WAVES>(ss, buf[par][3]) * inv_cols + eps);
+    }
+    // Row scalars.  Padding has dy = 0 and w = 0, so g = 0 there.
+    float a = 0.0f, c = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k * kStep < cols) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float xh = (to_f32(rx[k].v[i]) - mean) * rstd;
+          const float g = to_f32(rg[k].v[i]) * wv[k][i];
+          if constexpr (!RMS) a += g;
+          c = fmaf(g, xh, c);
+        }
+      }
+    }
+    row_reduce_sum2<WAVES>(a, c, buf[par][0], buf[par][1]);
+    a *= inv_cols;
+    c *= inv_cols;
+    if constexpr (RMS) a = 0.0f;
+
+    T* dr = dx + row * ld_dx;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k * kStep < cols) {
+        const int64_t col = k * kStep + lane_col;
+        float o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float xh = (to_f32(rx[k].v[i]) - mean) * rstd;
+          const float gy = to_f32(rg[k].v[i]);
+          o[i] = rstd * (gy * wv[k][i] - a - xh * c);
+          pdw[k][i] = fmaf(gy, xh, pdw[k][i]);
+          if constexpr (!RMS) pdb[k][i] += gy;
+        }
+        if (col < cols) store_row_vec<T, VEC>(dr, col, cols, o);
+      }
+    }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int k = 0; k < KN; ++k) {
+        rx[k] = nx[k];
+        rg[k] = ng[k];
+      }
+    }
+  }
+
+  const int64_t pw = RMS ? cols : 2 * cols;   // partial row width
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t col = k * kStep + lane_col;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      if (col + i < cols) {
+        P[tile * pw + col + i] = pdw[k][i];
+        if constexpr (!RMS) P[tile * pw + cols + col + i] = pdb[k][i];
+      }
+    }
+  }
+}
+
+// Launch tiers, smallest first: (waves per row, vectors per lane).  The first
+// tier whose capacity WAVES * 64 * K * VEC holds the row is used.  A lane
+// holds at most 16 elements of a row (the backward keeps w and the dw / db
+// partials of its columns in fp32 registers besides x and dy), so rows of
+// up to 16 waves * 64 lanes * 16 = 16384 columns are supported.
+constexpr int kLaneElems = 16;
+// Forward grid: enough workgroups for 8192 waves (32 per CU), each looping
+// over its rows.
+constexpr int64_t kFwdWaves = 8192;
+
+template <typename T, int VEC, int WAVES, int K, bool RMS>
+bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, T* yp,
+             int64_t ld_y, float* mean, float* rstd, int64_t rows, int64_t cols, float eps,
+             hipStream_t s) {
+  if constexpr (K * VEC > kLaneElems) {
+    return false;
+  } else {
+    if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
+    const int64_t g = rows < kFwdWaves / WAVES ? rows : kFwdWaves / WAVES;
+    norm_fwd_rows<T, VEC, WAVES, K, RMS><<<unsigned(g), WAVES * kWave, 0, s>>>(
+        xp, ld_x, w, b, wdt, yp, ld_y, mean, rstd, rows, cols, eps);
+    return true;
+  }
+}
+
+template <typename T, int VEC, int WAVES, int K, bool RMS>
+bool bwd_try(const T* gp, int64_t ld_dy, const T* xp, int64_t ld_x, const void* w, int wdt,
+             const float* mean, const float* rstd, T* dp, int64_t ld_dx, float* P, int64_t rows,
+             int64_t cols, int64_t tiles, float eps, hipStream_t s) {
+  if constexpr (K * VEC > kLaneElems) {
+    return false;
+  } else {
+    if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
+    norm_bwd_tile<T, VEC, WAVES, K, RMS><<<unsigned(tiles), WAVES * kWave, 0, s>>>(
+        gp, ld_dy, xp, ld_x, w, wdt, mean, rstd, dp, ld_dx, P, rows, cols, tiles, eps);
+    return true;
+  }
+}
+
+template <typename T, int VEC, bool RMS>
+hipError_t fwd_vec(const void* x, int64_t ld_x, const void* w, const void* b, int wdt, void* y,
+                   int64_t ld_y, float* mean, float* rstd, int64_t rows, int64_t cols, float eps,
+                   hipStream_t s) {
+  const T* xp = static_cast<const T*>(x);
+  T* yp = static_cast<T*>(y);
+#define VJP_NF_TRY(W, K) \
+  fwd_try<T, VEC, W, K, RMS>(xp, ld_x, w, b, wdt, yp, ld_y, mean, rstd, rows, cols, eps, s)
+  const bool done = VJP_NF_TRY(1, 2) || VJP_NF_TRY(2, 2) || VJP_NF_TRY(4, 2) ||
+                    VJP_NF_TRY(8, 2) || VJP_NF_TRY(16, 2) || VJP_NF_TRY(16, 4) ||
+                    VJP_NF_TRY(16, 8) || VJP_NF_TRY(16, 16);
+#undef VJP_NF_TRY
+  return done ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+template <typename T, int VEC, bool RMS>
+hipError_t bwd_vec(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* w,
+                   int wdt, const float* mean, const float* rstd, void* dx, int64_t ld_dx,
+                   float* P, int64_t rows, int64_t cols, int64_t tiles, float eps,
+                   hipStream_t s) {
+  const T* gp = static_cast<const T*>(dy);
+  const T* xp = static_cast<const T*>(x);
+  T* dp = static_cast<T*>(dx);
+#define VJP_NB_TRY(W, K)                                                                  \
+  bwd_try<T, VEC, W, K, RMS>(gp, ld_dy, xp, ld_x, w, wdt, mean, rstd, dp, ld_dx, P, rows, \
+                             cols, tiles, eps, s)
+  const bool done = VJP_NB_TRY(1, 1) || VJP_NB_TRY(2, 1) || VJP_NB_TRY(4, 1) ||
+                    VJP_NB_TRY(8, 1) || VJP_NB_TRY(16, 1) || VJP_NB_TRY(16, 2) ||
+                    VJP_NB_TRY(16, 4) || VJP_NB_TRY(16, 8) || VJP_NB_TRY(16, 16);
+#undef VJP_NB_TRY
+  return done ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+template <typename T, bool RMS>
+hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, const void* b, int wdt, void* y,
+                     int64_t ld_y, float* mean, float* rstd, int64_t rows, int64_t cols,
+                     float eps, bool vec, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  return vec ? fwd_vec<T, V, RMS>(x, ld_x, w, b, wdt, y, ld_y, mean, rstd, rows, cols, eps, s)
+             : fwd_vec<T, 1, RMS>(x, ld_x, w, b, wdt, y, ld_y, mean, rstd, rows, cols, eps, s);
+}
+
+template <typename T, bool RMS>
+hipError_t bwd_typed(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* w,
+                     int wdt, const float* mean, const float* rstd, void* dx, int64_t ld_dx,
+                     float* P, int64_t rows, int64_t cols, int64_t tiles, float eps, bool vec,
+                     hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  return vec ? bwd_vec<T, V, RMS>(dy, ld_dy, x, ld_x, w, wdt, mean, rstd, dx, ld_dx, P, rows,
+                                  cols, tiles, eps, s)
+             : bwd_vec<T, 1, RMS>(dy, ld_dy, x, ld_x, w, wdt, mean, rstd, dx, ld_dx, P, rows,
+                                  cols, tiles, eps, s);
+}
+
+}  // namespace
+
+int64_t norm_max_cols(int, bool) { return int64_t(16) * kWave * kLaneElems; }
+
+hipError_t launch_norm_fwd(bool rms, const void* x, int64_t ld_x, const void* w, const void* b,
+                           int wdt, void* y, int64_t ld_y, float* row_mean, float* row_rstd,
+                           int64_t rows, int64_t cols, float eps, int act, bool vec,
+                           hipStream_t s) {
+#define VJP_NF(T, R) \
+  fwd_typed<T, R>(x, ld_x, w, b, wdt, y, ld_y, row_mean, row_rstd, rows, cols, eps, vec, s)
+  if (rms) {
+    switch (act) {
+      case kF32: return VJP_NF(float, true);
+      case kF16: return VJP_NF(_Float16, true);
+      default: return VJP_NF(bf16, true);
+    }
+  }
+  switch (act) {
+    case kF32: return VJP_NF(float, false);
+    case kF16: return VJP_NF(_Float16, false);
+    default: return VJP_NF(bf16, false);
+  }
+#undef VJP_NF
+}
+
+hipError_t launch_norm_bwd_stage1(bool rms, const void* dy, int64_t ld_dy, const void* x,
+                                  int64_t ld_x, const void* w, int wdt, const float* row_mean,
+                                  const float* row_rstd, void* dx, int64_t ld_dx, float* P,
+                                  int64_t rows, int64_t cols, int64_t tiles, float eps, int act,
+                                  bool vec, hipStream_t s) {
+#define VJP_NB(T, R)                                                                          \
+  bwd_typed<T, R>(dy, ld_dy, x, ld_x, w, wdt, row_mean, row_rstd, dx, ld_dx, P, rows, cols, \
+                  tiles, eps, vec, s)
+  if (rms) {
+    switch (act) {
+      case kF32: return VJP_NB(float, true);
+      case kF16: return VJP_NB(_Float16, true);
+      default: return VJP_NB(bf16, true);
+    }
+  }
+  switch (act) {
+    case kF32: return VJP_NB(float, false);
+    case kF16: return VJP_NB(_Float16, false);
+    default: return VJP_NB(bf16, false);
+  }
+#undef VJP_NB
+}
+
+}  // namespace vjp

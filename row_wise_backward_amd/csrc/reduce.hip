@@ -35,9 +35,12 @@ constexpr int kColsPerBlock = 4 * kColLanes;            // 32
 
 // VEC4: d % 4 == 0 and P 16-byte aligned, so a lane's four columns are one
 // aligned 16-byte load (all four in range or none).
+// Column j of the sum goes to out[j] for j < split and to out2[j - split]
+// otherwise (two parameter gradients from one partials buffer).
 template <bool VEC4>
 __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
-    const float* __restrict__ P, int64_t T, int64_t d, float* __restrict__ out, int accumulate) {
+    const float* __restrict__ P, int64_t T, int64_t d, float* __restrict__ out,
+    float* __restrict__ out2, int64_t split, int accumulate) {
   __shared__ float4 red[kRowLanes][kColLanes];
   const int c = threadIdx.x % kColLanes;
   const int r = threadIdx.x / kColLanes;
@@ -83,8 +86,12 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(
     const float4 s = red[0][c];
     const float sv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (j + k < d) out[j + k] = accumulate ? out[j + k] + sv[k] : sv[k];
+    for (int k = 0; k < 4; ++k) {
+      if (j + k < d) {
+        float* o = j + k < split ? out + (j + k) : out2 + (j + k - split);
+        *o = accumulate ? *o + sv[k] : sv[k];
+      }
+    }
   }
 }
 
@@ -110,16 +117,22 @@ __global__ __launch_bounds__(kScalarThreads) void reduce_scalar_kernel(
 
 hipError_t launch_reduce_partials(const float* P, int64_t T, int64_t d, float* out,
                                   int accumulate, hipStream_t s) {
-  if (d == 1) {
+  return launch_reduce_partials_split(P, T, d, out, nullptr, d, accumulate, s);
+}
+
+hipError_t launch_reduce_partials_split(const float* P, int64_t T, int64_t d, float* out,
+                                        float* out2, int64_t split, int accumulate,
+                                        hipStream_t s) {
+  if (d == 1 && split >= 1) {
     reduce_scalar_kernel<<<1, kScalarThreads, 0, s>>>(P, T, out, accumulate);
     return hipGetLastError();
   }
   const dim3 grid(unsigned((d + kColsPerBlock - 1) / kColsPerBlock)), block(kReduceThreads);
   const bool vec4 = d % 4 == 0 && reinterpret_cast<uintptr_t>(P) % 16 == 0;
   if (vec4)
-    reduce_partials_kernel<true><<<grid, block, 0, s>>>(P, T, d, out, accumulate);
+    reduce_partials_kernel<true><<<grid, block, 0, s>>>(P, T, d, out, out2, split, accumulate);
   else
-    reduce_partials_kernel<false><<<grid, block, 0, s>>>(P, T, d, out, accumulate);
+    reduce_partials_kernel<false><<<grid, block, 0, s>>>(P, T, d, out, out2, split, accumulate);
   return hipGetLastError();
 }
 

@@ -80,6 +80,27 @@ __device__ __forceinline__ float row_reduce_sum(float v, float* buf) {
   return v;
 }
 
+// Two sums of a row in one exchange (one barrier): waves combined in order.
+template <int WAVES>
+__device__ __forceinline__ void row_reduce_sum2(float& a, float& b, float* bufa, float* bufb) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if constexpr (WAVES > 1) {
+    if ((threadIdx.x % kWave) == 0) {
+      bufa[threadIdx.x / kWave] = a;
+      bufb[threadIdx.x / kWave] = b;
+    }
+    __syncthreads();
+    a = bufa[0];
+    b = bufb[0];
+#pragma unroll
+    for (int k = 1; k < WAVES; ++k) {
+      a += bufa[k];
+      b += bufb[k];
+    }
+  }
+}
+
 // 2^t without flushing subnormal results: v_exp_f32 is only trusted for
 // results >= 2^-126, below that the argument is shifted up by 64 and the
 // result scaled back (an exact power-of-two scaling, one rounding).

@@ -255,3 +255,46 @@ def test_autograd_layer_rejects_host_tensors():
         ag.softmax_cross_entropy(x, torch.zeros(4, dtype=torch.int64))
     with pytest.raises(ValueError):
         ag.softmax(x, save="nothing")
+
+
+def _ln_fwd(**kw):
+    a = dict(x=A, ld=64, w=B, b=B + 0x1000, y=C, ldy=64, mean=D, rstd=D + 0x1000, rows=10, cols=64,
+             eps=1e-5, act=2, wdt=2)
+    a.update(kw)
+    return L.vjp_layernorm_fwd(P(a["x"]), a["ld"], P(a["w"]), P(a["b"]), P(a["y"]), a["ldy"],
+                               P(a["mean"]), P(a["rstd"]), a["rows"], a["cols"],
+                               ctypes.c_float(a["eps"]), a["act"], a["wdt"], None)
+
+
+def _ln_bwd(**kw):
+    a = dict(dy=A, x=B, w=C, mean=D, rstd=D + 0x1000, dx=D + 0x100000, dw=D + 0x200000,
+             db=D + 0x201000, acc=0, rows=10, cols=64, eps=1e-5, act=2, wdt=2, ws=D + 0x300000,
+             wsb=10 * 128 * 4)
+    a.update(kw)
+    return L.vjp_layernorm_bwd(P(a["dy"]), 64, P(a["x"]), 64, P(a["w"]), P(a["mean"]), P(a["rstd"]),
+                               P(a["dx"]), 64, P(a["dw"]), P(a["db"]), a["acc"], a["rows"], a["cols"],
+                               ctypes.c_float(a["eps"]), a["act"], a["wdt"], P(a["ws"]), a["wsb"], None)
+
+
+def test_norm_queries_and_rejections():
+    assert rwb.vjp_norm_max_cols() == 16384
+    assert L.vjp_norm_max_cols(0, 0) == 16384 and L.vjp_norm_max_cols(9, 1) == -1
+    # round-robin tiles: min(1024, rows) partial rows of 2 cols (LayerNorm) or cols (RMSNorm)
+    assert rwb.vjp_layernorm_bwd_workspace_size(10, 64) == 10 * 128 * 4
+    assert rwb.vjp_layernorm_bwd_workspace_size(32768, 4096) == 1024 * 8192 * 4
+    assert rwb.vjp_rmsnorm_bwd_workspace_size(5000, 100) == 1024 * 100 * 4
+    assert _ln_fwd(eps=-1.0) == EINVAL
+    assert _ln_fwd(eps=float("inf")) == EINVAL
+    assert _ln_fwd(cols=16385, ld=16385, ldy=16385) == EINVAL        # wider than the resident limit
+    assert "16384" in rwb.vjp_last_error()
+    assert _ln_fwd(cols=0, ld=0, ldy=0) == EINVAL
+    assert _ln_fwd(b=0) == EINVAL
+    assert _ln_fwd(y=A + 64) == EALIAS
+    assert _ln_fwd(rstd=D + 4) == EALIAS                             # rstd over mean
+    assert _ln_fwd(act=4) == EDTYPE
+    assert _ln_bwd(wsb=10 * 128 * 4 - 1) == EWORKSPACE
+    assert _ln_bwd(mean=0) == EINVAL                                 # mean without rstd
+    assert _ln_bwd(acc=3) == EINVAL
+    assert _ln_bwd(db=D + 0x200000 + 8) == EALIAS                    # db over dw
+    assert _ln_bwd(dx=B + 2) == EALIAS
+    assert L.vjp_rmsnorm_fwd(P(A), 64, P(B), P(A + 2), 64, None, 10, 64, ctypes.c_float(1e-6), 2, 2, None) == EALIAS

@@ -72,8 +72,11 @@ def test_scaled_silu_grads(ag):
     y = ag.scaled_silu(xt, wt)
     assert y.shape == (4, 1000)
     y.backward(synth.to_torch(g, "f32", DEV))
-    dx, dw = oracle.scaled_silu.bwd(synth.to_f64(g, "f32"), synth.to_f64(x, "f32"), 0.75)
-    r1 = pointwise(to_host(xt.grad, "f32"), dx, "f32", name="x.grad")
+    x64, g64 = synth.to_f64(x, "f32"), synth.to_f64(g, "f32")
+    dx, dw = oracle.scaled_silu.bwd(g64, x64, 0.75)
+    s = oracle.scaled_silu.sigmoid(x64)
+    S = np.abs(g64 * 0.75) * (s + np.abs(x64) * s)   # s + x s (1 - s) cancels near x = -1.28
+    r1 = pointwise(to_host(xt.grad, "f32"), dx, "f32", S=S, name="x.grad")
     r2 = reduced(to_host(wt.grad, "f32"), np.array([dw]), name="w.grad")
     print("   ", r1, "\n   ", r2)
     assert r1.ok and r2.ok and wt.grad.shape == (1,)
@@ -151,3 +154,29 @@ def test_chain_weighted_sum_into_softmax(ag):
     r2 = reduced(to_host(wt.grad, "f32"), dw, name="w.grad")
     print("   ", r1, "\n   ", r2)
     assert r1.ok and r2.ok
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_norm_grads(ag, kind):
+    x = synth.normal((2, 5, 300), 1.0, "f32", 308, 0)
+    g = synth.normal((2, 5, 300), 1.0, "f32", 308, 2)
+    rng = np.random.default_rng(308)
+    w = (1 + 0.1 * rng.standard_normal(300)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(300)).astype(np.float32)
+    xt, wt, bt = _t(x), _t(w), _t(b)
+    y = ag.layer_norm(xt, wt, bt) if kind == "ln" else ag.rms_norm(xt, wt)
+    y.backward(synth.to_torch(g, "f32", DEV))
+    x64, g64 = synth.to_f64(x, "f32").reshape(10, 300), synth.to_f64(g, "f32").reshape(10, 300)
+    if kind == "ln":
+        dx, dw, db = oracle.norms.layernorm_bwd(g64, x64, w.astype(np.float64), 1e-5)
+        r3 = reduced(to_host(bt.grad, "f32"), db, name="b.grad")
+    else:
+        dx, dw = oracle.norms.rmsnorm_bwd(g64, x64, w.astype(np.float64), 1e-6)
+        r3 = None
+        assert bt.grad is None
+    r1 = reduced(to_host(xt.grad, "f32").reshape(-1), dx.reshape(-1), name="x.grad")
+    r2 = reduced(to_host(wt.grad, "f32"), dw, name="w.grad")
+    for r in (r1, r2, r3):
+        if r is not None:
+            print("   ", r)
+    assert r1.ok and r2.ok and (r3 is None or r3.ok)
