@@ -268,7 +268,7 @@ int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* targets,
  * >= 0.  cols may not exceed vjp_norm_max_cols(act, aligned16) = 16384 for
  * every dtype and alignment (a row lives in the registers of at most 1024
  * lanes, 16 values each); wider rows are VJP_EINVAL.
- * Backward stage 1: rows are dealt round-robin to tiles = min(1024, rows)
+ * Backward stage 1: rows are dealt round-robin to tiles = min(512, rows)
  * workgroups; tile t holds rows t, t + tiles, ... and writes its fp32
  * partial row P[t][0 .. cols) = sum dy xhat and, for LayerNorm,
  * P[t][cols .. 2 cols) = sum dy (workspace layout, row width cols or

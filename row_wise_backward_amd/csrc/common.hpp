@@ -218,6 +218,16 @@ __device__ __forceinline__ float sigmoid(float x) {
   return rcp_fast(1.0f + exp2_fast(-x * kLog2e));
 }
 
+// Workgroup barrier that orders LDS accesses only.  The kernels exchange only
+// LDS data across their barriers, so global loads (a prefetched next row) and
+// stores (the previous row's output) issued before it stay in flight instead
+// of being drained as a full __syncthreads() would.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // One element of a parameter vector stored as fp32, fp16 or bf16 (dt is the
 // library's dtype code: 0 fp32, 1 fp16, 2 bf16), widened to fp32.
 __device__ __forceinline__ float load_param_f32(const void* __restrict__ w, int64_t j, int dt) {

@@ -16,9 +16,9 @@
 //   backward:  g = dy w, a = mean(g) (LayerNorm only), c = mean(g xhat),
 //              dx = rstd (g - a - xhat c); dw = sum_rows dy xhat, db = sum_rows dy
 //
-// Forward: the resident row layout of rowops.hpp, the row read once; the
-// variance is the two-pass mean of squared deviations of the values held in
-// registers.  Backward: workgroup t owns the rows t, t + tiles, t + 2 tiles,
+// Forward: one row per workgroup in the resident row layout of rowops.hpp,
+// the row read once; the variance is the two-pass mean of squared deviations
+// of the values held in registers.  Backward: workgroup t owns the rows t, t + tiles, t + 2 tiles,
 // ... (a round-robin deal, so all workgroups stream neighbouring rows at the
 // same moment); for each row it loads x and dy into registers, forms the two
 // row scalars with one exchange, writes dx, and adds dy xhat (and dy) into
@@ -43,94 +43,107 @@ __device__ __forceinline__ void load_lane_row(const T* __restrict__ r, int64_t c
     if (k * kStep < cols) load_row_vec<T, VEC>(r, k * kStep + lane_col, cols, zero_of<T>(), v[k]);
 }
 
-// Forward.  Workgroup g (WAVES waves) takes rows g, g + gridDim.x, ...; its
-// lanes keep w and b of their columns in registers for all of them, and the
-// next row is loaded while the current one is reduced and written.
+// VEC consecutive parameter values starting at column col, widened to fp32.
+// pvec: the parameter vectors are 16-byte aligned, so a full vector is one
+// aligned access of VEC * element-size bytes; otherwise, and at the ragged
+// end of the row, element by element (zero past cols).
+template <typename P, int VEC>
+__device__ __forceinline__ void params_as_f32(const P* __restrict__ p, float (&o)[VEC]) {
+  const Vec<P, VEC> v = *reinterpret_cast<const Vec<P, VEC>*>(p);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) o[i] = to_f32(v.v[i]);
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_params_vec(const void* __restrict__ w, int64_t col,
+                                                int64_t cols, int wdt, bool pvec,
+                                                float (&o)[VEC]) {
+  if (pvec && col + VEC <= cols) {
+    if (wdt == kF32) {
+      params_as_f32<float, VEC>(static_cast<const float*>(w) + col, o);
+    } else if (wdt == kF16) {
+      params_as_f32<_Float16, VEC>(static_cast<const _Float16*>(w) + col, o);
+    } else {
+      params_as_f32<bf16, VEC>(static_cast<const bf16*>(w) + col, o);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) o[i] = (col + i < cols) ? load_param_f32(w, col + i, wdt) : 0.0f;
+}
+
+// Forward: one row per workgroup (four rows per 256-thread workgroup when a
+// wave holds a row), the resident layout of rowops.hpp, w and b read with
+// vector loads (they stay in L2: every row reads the same values).
 template <typename T, int VEC, int WAVES, int K, bool RMS>
-__global__ __launch_bounds__(WAVES * kWave) void norm_fwd_rows(
+__global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
     const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
-    const void* __restrict__ b, int wdt, T* __restrict__ y, int64_t ld_y,
+    const void* __restrict__ b, int wdt, bool pvec, T* __restrict__ y, int64_t ld_y,
     float* __restrict__ row_mean, float* __restrict__ row_rstd, int64_t rows, int64_t cols,
     float eps) {
-  __shared__ float buf[2][2][WAVES];   // [row parity][reduction]
+  __shared__ float buf[2][WAVES];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
+  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
+                                 : int64_t(blockIdx.x);
+  const int wv = WAVES == 1 ? 0 : wave;
+  if (WAVES == 1 && row >= rows) return;
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
-  const int64_t lane_col = (int64_t(wave) * kWave + lane) * VEC;
+  const int64_t lane_col = (int64_t(wv) * kWave + lane) * VEC;
   const float inv_cols = 1.0f / float(cols);
 
-  float wv[K][VEC], bv[RMS ? 1 : K][VEC];
+  Vec<T, VEC> raw[K];
+  load_lane_row<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, raw);
+  float pw[K][VEC], pb[RMS ? 1 : K][VEC];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int64_t col = k * kStep + lane_col;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-      const bool in = col + i < cols;
-      wv[k][i] = in ? load_param_f32(w, col + i, wdt) : 0.0f;
-      if constexpr (!RMS) bv[k][i] = in ? load_param_f32(b, col + i, wdt) : 0.0f;
+    if (k * kStep < cols) {
+      load_params_vec<VEC>(w, k * kStep + lane_col, cols, wdt, pvec, pw[k]);
+      if constexpr (!RMS) load_params_vec<VEC>(b, k * kStep + lane_col, cols, wdt, pvec, pb[k]);
     }
   }
 
-  // Prefetch only while a lane holds at most 8 values of a row (wider rows
-  // would need more than the 128 registers a 1024-thread workgroup allows).
-  constexpr bool kPrefetch = K * VEC <= 8;
-  int64_t row = blockIdx.x;
-  Vec<T, VEC> cur[K], nxt[kPrefetch ? K : 1];
-  if (kPrefetch && row < rows) load_lane_row<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, cur);
-  for (int par = 0; row < rows; row += gridDim.x, par ^= 1) {
-    const int64_t next = row + gridDim.x;
-    if constexpr (kPrefetch) {
-      if (next < rows) load_lane_row<T, VEC, WAVES, K>(x + next * ld_x, cols, lane_col, nxt);
-    } else {
-      load_lane_row<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, cur);
-    }
-
-    float mean = 0.0f;
-    if constexpr (!RMS) {
-      float s = 0.0f;
+  float mean = 0.0f;
+  if constexpr (!RMS) {
+    float s = 0.0f;
 #pragma unroll
-      for (int k = 0; k < K; ++k)
-        if (k * kStep < cols)
+    for (int k = 0; k < K; ++k)
+      if (k * kStep < cols)
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) s += to_f32(cur[k].v[i]);   // padding reads 0
-      mean = row_reduce_sum<WAVES>(s, buf[par][0]) * inv_cols;
-    }
-    float ss = 0.0f;
+        for (int i = 0; i < VEC; ++i) s += to_f32(raw[k].v[i]);   // padding reads 0
+    mean = row_reduce_sum<WAVES>(s, buf[0]) * inv_cols;
+  }
+  float ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (k * kStep < cols) {
-        const int64_t col = k * kStep + lane_col;
+  for (int k = 0; k < K; ++k) {
+    if (k * kStep < cols) {
+      const int64_t col = k * kStep + lane_col;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float d = to_f32(cur[k].v[i]) - mean;
-          if (col + i < cols) ss = fmaf(d, d, ss);
-        }
+      for (int i = 0; i < VEC; ++i) {
+        const float d = to_f32(raw[k].v[i]) - mean;
+        if (col + i < cols) ss = fmaf(d, d, ss);
       }
     }
-    const float rstd =
-        1.0f / __builtin_sqrtf(row_reduce_sum<WAVES>(ss, buf[par][1]) * inv_cols + eps);
-    if (wave == 0 && lane == 0) {
-      if (row_mean != nullptr) row_mean[row] = mean;
-      if (row_rstd != nullptr) row_rstd[row] = rstd;
-    }
+  }
+  const float rstd =
+      1.0f / __builtin_sqrtf(row_reduce_sum<WAVES>(ss, buf[1]) * inv_cols + eps);
+  if (wv == 0 && lane == 0) {
+    if (row_mean != nullptr) row_mean[row] = mean;
+    if (row_rstd != nullptr) row_rstd[row] = rstd;
+  }
 
-    T* yr = y + row * ld_y;
+  T* yr = y + row * ld_y;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (k * kStep < cols) {
-        const int64_t col = k * kStep + lane_col;
-        if (col < cols) {
-          float o[VEC];
+  for (int k = 0; k < K; ++k) {
+    if (k * kStep < cols) {
+      const int64_t col = k * kStep + lane_col;
+      if (col < cols) {
+        float o[VEC];
 #pragma unroll
-          for (int i = 0; i < VEC; ++i)
-            o[i] = fmaf((to_f32(cur[k].v[i]) - mean) * rstd, wv[k][i], RMS ? 0.0f : bv[k][i]);
-          store_row_vec<T, VEC>(yr, col, cols, o);
-        }
+        for (int i = 0; i < VEC; ++i)
+          o[i] = fmaf((to_f32(raw[k].v[i]) - mean) * rstd, pw[k][i], RMS ? 0.0f : pb[k][i]);
+        store_row_vec<T, VEC>(yr, col, cols, o);
       }
-    }
-    if constexpr (kPrefetch) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) cur[k] = nxt[k];
     }
   }
 }
@@ -277,21 +290,22 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
 // partials of its columns in fp32 registers besides x and dy), so rows of
 // up to 16 waves * 64 lanes * 16 = 16384 columns are supported.
 constexpr int kLaneElems = 16;
-// Forward grid: enough workgroups for 8192 waves (32 per CU), each looping
-// over its rows.
-constexpr int64_t kFwdWaves = 8192;
+// Forward measured on MI355X for 32768 x 4096 bf16: one workgroup per row
+// with vector parameter loads (95 us) beats workgroups that loop over rows
+// with the parameters held in registers (127 us).
 
 template <typename T, int VEC, int WAVES, int K, bool RMS>
-bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, T* yp,
+bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, bool pvec, T* yp,
              int64_t ld_y, float* mean, float* rstd, int64_t rows, int64_t cols, float eps,
              hipStream_t s) {
   if constexpr (K * VEC > kLaneElems) {
     return false;
   } else {
     if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
-    const int64_t g = rows < kFwdWaves / WAVES ? rows : kFwdWaves / WAVES;
-    norm_fwd_rows<T, VEC, WAVES, K, RMS><<<unsigned(g), WAVES * kWave, 0, s>>>(
-        xp, ld_x, w, b, wdt, yp, ld_y, mean, rstd, rows, cols, eps);
+    const unsigned grid =
+        unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
+    norm_fwd_resident<T, VEC, WAVES, K, RMS><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+        xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps);
     return true;
   }
 }
@@ -311,13 +325,13 @@ bool bwd_try(const T* gp, int64_t ld_dy, const T* xp, int64_t ld_x, const void* 
 }
 
 template <typename T, int VEC, bool RMS>
-hipError_t fwd_vec(const void* x, int64_t ld_x, const void* w, const void* b, int wdt, void* y,
-                   int64_t ld_y, float* mean, float* rstd, int64_t rows, int64_t cols, float eps,
-                   hipStream_t s) {
+hipError_t fwd_vec(const void* x, int64_t ld_x, const void* w, const void* b, int wdt, bool pvec,
+                   void* y, int64_t ld_y, float* mean, float* rstd, int64_t rows, int64_t cols,
+                   float eps, hipStream_t s) {
   const T* xp = static_cast<const T*>(x);
   T* yp = static_cast<T*>(y);
 #define VJP_NF_TRY(W, K) \
-  fwd_try<T, VEC, W, K, RMS>(xp, ld_x, w, b, wdt, yp, ld_y, mean, rstd, rows, cols, eps, s)
+  fwd_try<T, VEC, W, K, RMS>(xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps, s)
   const bool done = VJP_NF_TRY(1, 2) || VJP_NF_TRY(2, 2) || VJP_NF_TRY(4, 2) ||
                     VJP_NF_TRY(8, 2) || VJP_NF_TRY(16, 2) || VJP_NF_TRY(16, 4) ||
                     VJP_NF_TRY(16, 8) || VJP_NF_TRY(16, 16);
@@ -348,8 +362,10 @@ hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, const void* b, 
                      int64_t ld_y, float* mean, float* rstd, int64_t rows, int64_t cols,
                      float eps, bool vec, hipStream_t s) {
   constexpr int V = 16 / sizeof(T);
-  return vec ? fwd_vec<T, V, RMS>(x, ld_x, w, b, wdt, y, ld_y, mean, rstd, rows, cols, eps, s)
-             : fwd_vec<T, 1, RMS>(x, ld_x, w, b, wdt, y, ld_y, mean, rstd, rows, cols, eps, s);
+  const bool pvec = reinterpret_cast<uintptr_t>(w) % 16 == 0 &&
+                    (RMS || reinterpret_cast<uintptr_t>(b) % 16 == 0);
+  return vec ? fwd_vec<T, V, RMS>(x, ld_x, w, b, wdt, pvec, y, ld_y, mean, rstd, rows, cols, eps, s)
+             : fwd_vec<T, 1, RMS>(x, ld_x, w, b, wdt, pvec, y, ld_y, mean, rstd, rows, cols, eps, s);
 }
 
 template <typename T, bool RMS>

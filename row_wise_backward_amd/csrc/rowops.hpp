@@ -59,7 +59,7 @@ __device__ __forceinline__ float row_reduce_max(float v, float* buf) {
   v = wave_max(v);
   if constexpr (WAVES > 1) {
     if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
-    __syncthreads();
+    lds_barrier();
     v = buf[0];
 #pragma unroll
     for (int k = 1; k < WAVES; ++k) v = fmaxf(v, buf[k]);
@@ -72,7 +72,7 @@ __device__ __forceinline__ float row_reduce_sum(float v, float* buf) {
   v = wave_sum(v);
   if constexpr (WAVES > 1) {
     if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
-    __syncthreads();
+    lds_barrier();
     v = buf[0];
 #pragma unroll
     for (int k = 1; k < WAVES; ++k) v += buf[k];
@@ -90,7 +90,7 @@ __device__ __forceinline__ void row_reduce_sum2(float& a, float& b, float* bufa,
       bufa[threadIdx.x / kWave] = a;
       bufb[threadIdx.x / kWave] = b;
     }
-    __syncthreads();
+    lds_barrier();
     a = bufa[0];
     b = bufb[0];
 #pragma unroll
@@ -215,12 +215,12 @@ __device__ __forceinline__ void block_merge_ml_w(float& m, float& l, float* bm, 
   float M = wave_max(m);
   float contrib = (m == -__builtin_inff()) ? 0.0f : l * exp2_denorm_safe((m - M) * kLog2e);
   float Lw = wave_sum(contrib);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x % kWave) == 0) {
     bm[threadIdx.x / kWave] = M;
     bl[threadIdx.x / kWave] = Lw;
   }
-  __syncthreads();
+  lds_barrier();
   float Mg = bm[0];
 #pragma unroll
   for (int k = 1; k < W; ++k) Mg = fmaxf(Mg, bm[k]);
@@ -250,9 +250,9 @@ __device__ __forceinline__ void online_step(float x, float& m, float& l) {
 template <int W>
 __device__ __forceinline__ float block_sum_stream(float v, float* buf) {
   v = wave_sum(v);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x % kWave) == 0) buf[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   float s = buf[0];
 #pragma unroll
   for (int k = 1; k < W; ++k) s += buf[k];

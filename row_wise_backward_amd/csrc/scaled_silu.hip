@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void silu_bwd_kernel(
   }
   acc = wave_sum(acc);
   if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = acc;
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x == 0) {
     float s = red[0];
 #pragma unroll

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
 #pragma unroll
       for (int i = 0; i < VEC; ++i) red[wave][c * VEC + i] = acc[i];
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0 && sub == 0) {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
         if (col + i < d) P[tile * d + col + i] = s;
       }
     }
-    __syncthreads();   // red is reused by the next tile of this workgroup
+    lds_barrier();   // red is reused by the next tile of this workgroup
   }
 }
 

@@ -279,10 +279,10 @@ def _ln_bwd(**kw):
 def test_norm_queries_and_rejections():
     assert rwb.vjp_norm_max_cols() == 16384
     assert L.vjp_norm_max_cols(0, 0) == 16384 and L.vjp_norm_max_cols(9, 1) == -1
-    # round-robin tiles: min(1024, rows) partial rows of 2 cols (LayerNorm) or cols (RMSNorm)
+    # round-robin tiles: min(512, rows) partial rows of 2 cols (LayerNorm) or cols (RMSNorm)
     assert rwb.vjp_layernorm_bwd_workspace_size(10, 64) == 10 * 128 * 4
-    assert rwb.vjp_layernorm_bwd_workspace_size(32768, 4096) == 1024 * 8192 * 4
-    assert rwb.vjp_rmsnorm_bwd_workspace_size(5000, 100) == 1024 * 100 * 4
+    assert rwb.vjp_layernorm_bwd_workspace_size(32768, 4096) == 512 * 8192 * 4
+    assert rwb.vjp_rmsnorm_bwd_workspace_size(5000, 100) == 512 * 100 * 4
     assert _ln_fwd(eps=-1.0) == EINVAL
     assert _ln_fwd(eps=float("inf")) == EINVAL
     assert _ln_fwd(cols=16385, ld=16385, ldy=16385) == EINVAL        # wider than the resident limit

@@ -87,8 +87,15 @@ def _inputs(rows, cols, act, wdt, seed, shift=0.0):
     return x, w, b, dy
 
 
+def _param_dev(a, dtype, offset):
+    """A device copy of a parameter vector starting `offset` elements into its buffer."""
+    buf = torch.zeros(a.size + offset, dtype=synth.torch_dtype(dtype), device=DEV)
+    buf[offset:] = to_dev(a, dtype)
+    return buf[offset:]
+
+
 def run_case(rwb, kind, rows, cols, act, wdt, seed, ld=None, offset=0, saved=True,
-             accumulate=False, eps=None, shift=0.0):
+             accumulate=False, eps=None, shift=0.0, param_offset=0):
     rms = kind == "rms"
     eps = (1e-6 if rms else 1e-5) if eps is None else eps
     print(f"\n[{kind}] rows={rows} cols={cols} act={act} w={wdt} ld={ld} off={offset} "
@@ -97,7 +104,7 @@ def run_case(rwb, kind, rows, cols, act, wdt, seed, ld=None, offset=0, saved=Tru
     x64, w64, b64, dy64 = (synth.to_f64(x, act), synth.to_f64(w, wdt), synth.to_f64(b, wdt),
                            synth.to_f64(dy, act))
     xd, dyd = padded(x, act, ld, offset), padded(dy, act, ld, offset)
-    wd, bd = to_dev(w, wdt), to_dev(b, wdt)
+    wd, bd = _param_dev(w, wdt, param_offset), _param_dev(b, wdt, param_offset)
     y, _ = empty_padded(rows, cols, act, ld, offset)
     mean_g, rstd_g = Guarded(rows, torch.float32), Guarded(rows, torch.float32)
     if rms:
@@ -177,6 +184,13 @@ def test_recomputed_stats_and_accumulate(gpu_lib, kind, rows, cols):
 def test_layouts(gpu_lib, kind, cols, layout):
     ld, off = (cols + 8, 0) if layout == "padded_ld" else (cols + 1, 1)
     run_case(gpu_lib, kind, 5, cols, "bf16", "bf16", seed=420 + cols, ld=ld, offset=off)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_unaligned_parameters(gpu_lib, kind, wdt):
+    """w and b one element into their buffers: element-wise parameter loads."""
+    run_case(gpu_lib, kind, 9, 1000, "bf16", wdt, seed=425, param_offset=1)
 
 
 def test_batch1_and_batch7(gpu_lib):
