@@ -44,13 +44,21 @@ PEAK_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_softmax_xent_bf16_16384x32000.json")
 
 
-def source_digest() -> str:
-    """Hash of every kernel source, so stored counter readings expire when a kernel changes."""
+# Sources that define the fused cross-entropy kernels (the op with the largest
+# share of the step) and the build flags: stored counter readings for it expire
+# when any of them changes.
+XENT_SOURCES = ("softmax_xent.hip", "reduce.hip", "rowops.hpp", "common.hpp", "launch.hpp")
+
+
+def source_digest(files=XENT_SOURCES) -> str:
+    """Hash of the named kernel sources and of the build script."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "row_wise_backward_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    paths = [os.path.join(csrc, f) for f in files]
+    paths.append(os.path.join(ROOT, "row_wise_backward_amd", "build.py"))
+    for path in paths:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
