@@ -9,8 +9,8 @@ computes, written from the definitions on the source pages:
   (row-wise weighted sum, two-stage grad_w reduction);
 * "Backprop for kernel writers" (the VJP contract, the softmax collapse,
   the fused softmax-cross-entropy, logsumexp statistics, LayerNorm's
-  two-row-scalar backward; RMSNorm's dw reduction from "Backward in
-  Triton").
+  two-row-scalar backward, the scatter-add backward of a gather; RMSNorm's
+  dw reduction from "Backward in Triton").
 
 Every function takes and returns float64 arrays and computes the plain
 definition of its result; there is no tiling, fusion or reordering beyond
@@ -27,4 +27,4 @@ its formula (finite differences, brute-force Jacobians, library routines,
 invariants, special cases, the weighted-sum page's worked tiling example,
 exhaustive rounding enumeration).  No function is "parity unpinned".
 """
-from . import norms, rounding, scaled_silu, softmax, softmax_xent, weighted_sum  # noqa: F401
+from . import gather, norms, rounding, scaled_silu, softmax, softmax_xent, weighted_sum  # noqa: F401

@@ -608,6 +608,89 @@ def rms_accumulate(impl):
     return rel(a - b, ow)
 
 
+# ----------------------------------------------------------------------------- gather / scatter-add
+
+def _gather_case(seed, M, V, D, dup=True):
+    g = _rng(seed)
+    x = g.standard_normal((V, D))
+    idx = g.integers(0, max(1, V // 3) if dup else V, size=M) if dup else g.permutation(V)[:M]
+    dy = g.standard_normal((M, D))
+    return x, idx, dy
+
+
+def gather_fwd_vs_take(impl):
+    x, idx, _ = _gather_case(130, 50, 20, 7)
+    return rel(impl.fwd(x, idx), np.take(x, idx, axis=0))
+
+
+def gather_bwd_vs_add_at(impl):
+    """numpy's unbuffered scatter-add, batch 1 and 7 and a longer case."""
+    err = 0.0
+    for M, V, D in [(1, 3, 4), (7, 5, 3), (200, 30, 9)]:
+        x, idx, dy = _gather_case(131 + M, M, V, D)
+        ref = np.zeros((V, D))
+        np.add.at(ref, idx, dy)
+        dx, n_inv = impl.bwd(dy, idx, V)
+        err = max(err, rel(dx, ref) if np.any(ref) else float(np.max(np.abs(dx))), float(n_inv))
+    return err
+
+
+def gather_bwd_one_hot_matmul(impl):
+    """dx = O^T dy with O[m, v] = [idx[m] = v], the Jacobian of the gather."""
+    x, idx, dy = _gather_case(132, 40, 12, 5)
+    O = np.zeros((40, 12))
+    O[np.arange(40), idx] = 1.0
+    return rel(impl.bwd(dy, idx, 12)[0], O.T @ dy)
+
+
+def gather_bwd_fd(impl):
+    x, idx, dy = _gather_case(133, 9, 6, 3)
+    dx, _ = impl.bwd(dy, idx, 6)
+    fx = fd_grad(lambda xx: float(np.sum(dy * impl.fwd(xx, idx))), x)
+    return rel(dx, fx)
+
+
+def gather_conservation(impl):
+    """Every upstream row lands in exactly one table row: column sums agree, rows
+    never selected stay zero; distinct indices reduce to a plain scatter."""
+    x, idx, dy = _gather_case(134, 100, 40, 6)
+    dx, _ = impl.bwd(dy, idx, 40)
+    unused = np.setdiff1d(np.arange(40), idx)
+    e1 = rel(dx.sum(axis=0), np.array([math.fsum(dy[:, j]) for j in range(6)]))
+    e2 = float(np.max(np.abs(dx[unused]))) if unused.size else 0.0
+    x, idx2, dy2 = _gather_case(135, 15, 40, 6, dup=False)
+    dx2, _ = impl.bwd(dy2, idx2, 40)
+    return max(e1, e2, rel(dx2[idx2], dy2))
+
+
+def gather_invalid_and_order(impl):
+    """A hand-worked case: idx = [3, 1, 3, 0, 1, 3, -1, 5], V = 5.  Rows 6 and 7
+    are invalid (counted, no contribution, zero output row); the stable order by
+    index is 0 (m = 3), 1 (m = 1, 4), 3 (m = 0, 2, 5), then the invalid m = 6, 7."""
+    idx = np.array([3, 1, 3, 0, 1, 3, -1, 5])
+    V, D = 5, 2
+    dy = np.arange(16, dtype=np.float64).reshape(8, 2) + 1.0
+    dx, n_inv = impl.bwd(dy, idx, V)
+    want = np.zeros((V, D))
+    want[0] = dy[3]
+    want[1] = dy[1] + dy[4]
+    want[3] = dy[0] + dy[2] + dy[5]
+    order_ok = list(impl.sorted_order(idx, V)) == [3, 1, 4, 0, 2, 5, 6, 7]
+    counts_ok = list(impl.counts(idx, V)) == [1, 2, 0, 3, 0]
+    y = impl.fwd(np.ones((V, D)), idx)
+    fwd_ok = bool(np.all(y[6:] == 0) and np.all(y[:6] == 1))
+    ok = order_ok and counts_ok and fwd_ok and n_inv == 2
+    return rel(dx, want) if ok else np.inf
+
+
+def gather_accumulate(impl):
+    x, idx, dy = _gather_case(136, 30, 10, 4)
+    old = _rng(136).standard_normal((10, 4))
+    a, _ = impl.bwd(dy, idx, 10, dx_old=old)
+    b, _ = impl.bwd(dy, idx, 10)
+    return rel(a - b, old)
+
+
 PINS = {
     "weighted_sum": [
         ("fwd_vs_matmul", ws_fwd_vs_matmul, 1e-12),
@@ -661,5 +744,14 @@ PINS = {
         ("rms_bwd_finite_differences", rms_bwd_fd, 1e-8),
         ("rms_scale_invariance", rms_scale_invariance, 1e-12),
         ("rms_accumulate", rms_accumulate, 1e-13),
+    ],
+    "gather": [
+        ("fwd_vs_take", gather_fwd_vs_take, 0.0),
+        ("bwd_vs_add_at", gather_bwd_vs_add_at, 1e-15),
+        ("bwd_one_hot_matmul", gather_bwd_one_hot_matmul, 1e-14),
+        ("bwd_finite_differences", gather_bwd_fd, 1e-9),
+        ("conservation_and_distinct", gather_conservation, 1e-14),
+        ("invalid_and_order", gather_invalid_and_order, 0.0),
+        ("accumulate", gather_accumulate, 1e-14),
     ],
 }

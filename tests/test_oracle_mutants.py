@@ -22,6 +22,7 @@ def _ns(mod, **over):
 
 ws, silu, sm, xe = oracle.weighted_sum, oracle.scaled_silu, oracle.softmax, oracle.softmax_xent
 nm = oracle.norms
+ga = oracle.gather
 
 
 def _ws_bwd_no_batch_reduction(dy, x, w, grad_w_old=None):
@@ -167,6 +168,26 @@ def _rms_bwd_dw_per_row(dy, x, w, eps, dw_old=None):
     return dx, (np.asarray(dy) * xhat)[0]
 
 
+def _ga_plain_scatter(dy, idx, V, dx_old=None):
+    dy = np.asarray(dy, np.float64)
+    idx = np.asarray(idx)
+    dx = np.zeros((V, dy.shape[1])) if dx_old is None else np.array(dx_old, np.float64)
+    ok = (idx >= 0) & (idx < V)
+    dx[idx[ok]] = dy[ok]                          # last write wins: duplicates dropped
+    return dx, int(np.count_nonzero(~ok))
+
+
+def _ga_order_descending_ties(idx, V):
+    idx = np.asarray(idx, np.int64)
+    key = np.where(ga.valid_mask(idx, V), idx, V)
+    return np.lexsort((-np.arange(idx.size), key))
+
+
+def _ga_fwd_wraps_invalid(x, idx):
+    x = np.asarray(x, np.float64)
+    return x[np.asarray(idx) % x.shape[0]]
+
+
 MUTANTS = [
     ("weighted_sum", "bwd_no_batch_reduction", _ns(ws, bwd=_ws_bwd_no_batch_reduction)),
     ("weighted_sum", "bwd_transposed_reduction", _ns(ws, bwd=_ws_bwd_transposed)),
@@ -193,6 +214,9 @@ MUTANTS = [
     ("norms", "ln_unbiased_variance", _ns(nm, layernorm_fwd=_ln_fwd_unbiased, layernorm_stats=_ln_unbiased_var)),
     ("norms", "rms_bwd_no_projection", _ns(nm, rmsnorm_bwd=_rms_bwd_no_projection)),
     ("norms", "rms_bwd_dw_one_row", _ns(nm, rmsnorm_bwd=_rms_bwd_dw_per_row)),
+    ("gather", "bwd_plain_scatter", _ns(ga, bwd=_ga_plain_scatter)),
+    ("gather", "order_descending_ties", _ns(ga, sorted_order=_ga_order_descending_ties)),
+    ("gather", "fwd_wraps_invalid", _ns(ga, fwd=_ga_fwd_wraps_invalid)),
 ]
 
 

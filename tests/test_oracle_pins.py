@@ -11,6 +11,7 @@ IMPL = {
     "softmax": oracle.softmax,
     "softmax_xent": oracle.softmax_xent,
     "norms": oracle.norms,
+    "gather": oracle.gather,
 }
 
 CASES = [(op, name, fn, thr) for op, pins in PINS.items() for (name, fn, thr) in pins]
