@@ -21,8 +21,10 @@ largest share of the step; `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workloads on one host core.  `extras` times the
 save-the-statistics variants (softmax forward writing the row logsumexp and
 the backward rebuilding y from it; the split cross-entropy forward and
-backward) and LayerNorm / RMSNorm forward and backward on the softmax
-workload's [32768, 4096] bf16 inputs, after and outside the step.
+backward), LayerNorm / RMSNorm forward and backward on the softmax
+workload's [32768, 4096] bf16 inputs, and the embedding gather with its
+deterministic scatter-add backward (16384 Zipf token ids, 32000 x 4096
+table), after and outside the step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -47,7 +49,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_softmax_xent_bf16_16384x3
 # Sources that define the fused cross-entropy kernels (the op with the largest
 # share of the step) and the build flags: stored counter readings for it expire
 # when any of them changes.
-XENT_SOURCES = ("softmax_xent.hip", "reduce.hip", "rowops.hpp", "common.hpp", "launch.hpp")
+XENT_SOURCES = ("softmax_xent.hip", "reduce.hip", "rowops.hpp", "common.hpp")
 
 
 def source_digest(files=XENT_SOURCES) -> str:
@@ -129,6 +131,16 @@ def bytes_rmsnorm_fwd(r, c, es=2, ws=2):
 
 def bytes_rmsnorm_bwd(r, c, T, es=2, ws=2):
     return 3 * r * c * es + c * ws + 4 * r + 2 * T * c * 4 + 4 * c
+
+
+def bytes_gather_fwd(M, D, es=2):
+    # each output row reads its table row once; indices read
+    return 2 * M * D * es + 4 * M
+
+
+def bytes_gather_bwd(M, V, D, es=2):
+    # dy read once, every fp32 gradient row written once, indices read
+    return M * D * es + V * D * 4 + 4 * M
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -356,6 +368,18 @@ def main() -> int:
     T_rms = rwb.vjp_rmsnorm_bwd_workspace_size(r_m, c_m) // (4 * c_m)
     rmsws = torch.empty(rwb.vjp_rmsnorm_bwd_workspace_size(r_m, c_m), dtype=torch.uint8, device=dev)
     F32 = ctypes.c_float
+    # Embedding lookup and its scatter-add backward (Zipf token ids)
+    from synth.workloads import EMBED
+    e_M, e_D = EMBED.shape
+    e_V = EMBED.extra["V"]
+    e_idx = torch.from_numpy(synth.zipf_indices(e_M, e_V, EMBED.seed, EMBED.extra["zipf_a"])).to(dev)
+    e_tab = synth.normal_device((e_V, e_D), 1.0, "bf16", EMBED.seed, 0, dev)
+    e_y = torch.empty((e_M, e_D), dtype=torch.bfloat16, device=dev)
+    e_dy = synth.normal_device((e_M, e_D), 1.0, "bf16", EMBED.seed, 2, dev)
+    e_dt = torch.empty((e_V, e_D), dtype=torch.float32, device=dev)
+    e_ninv = torch.empty(1, dtype=torch.int32, device=dev)
+    e_ws = torch.empty(rwb.vjp_gather_rows_bwd_workspace_size(e_M, e_V, e_D), dtype=torch.uint8,
+                       device=dev)
     extra_ops = [
         ("softmax_fwd_lse", L.vjp_softmax_fwd_lse,
          (P(mx), c_m, P(my), c_m, P(mlse), r_m, c_m, BF16, stream), bytes_softmax_fwd_lse(r_m, c_m),
@@ -379,6 +403,13 @@ def main() -> int:
         ("rmsnorm_fwd", L.vjp_rmsnorm_fwd,
          (P(mx), c_m, P(nw), P(my), c_m, P(nrstd), r_m, c_m, F32(1e-6), BF16, BF16, stream),
          bytes_rmsnorm_fwd(r_m, c_m), r_m * c_m),
+        ("gather_rows_fwd", L.vjp_gather_rows_fwd,
+         (P(e_tab), e_D, e_V, e_D, P(e_idx), e_M, P(e_y), e_D, BF16, stream),
+         bytes_gather_fwd(e_M, e_D), e_M * e_D),
+        ("gather_rows_bwd", L.vjp_gather_rows_bwd,
+         (P(e_dy), e_D, P(e_idx), e_M, e_V, e_D, P(e_dt), e_D, 0, P(e_ninv), BF16, P(e_ws),
+          e_ws.numel(), stream),
+         bytes_gather_bwd(e_M, e_V, e_D), e_M * e_D),
         ("rmsnorm_bwd", L.vjp_rmsnorm_bwd,
          (P(mg), c_m, P(mx), c_m, P(nw), P(nrstd), P(mdx), c_m, P(ndw), 0, r_m, c_m, F32(1e-6), BF16,
           BF16, P(rmsws), rmsws.numel(), stream),

@@ -299,6 +299,40 @@ int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, 
                     int64_t rows, int64_t cols, float eps, int act, int w_dtype,
                     void* workspace, size_t workspace_bytes, vjp_stream_t stream);
 
+/* ---------------------------------------------------------------- gather / scatter-add
+ * Row gather (embedding lookup): y[m, :] = table[idx[m], :] for m < M;
+ * table [V, D] (ld_t), idx [M] int32, y [M, D] (ld_y), all activations in
+ * `act`.  An index outside [0, V) selects nothing: its y row is zero.
+ * Backward, a scatter-add: dtable[v, :] = sum over m with idx[m] = v of
+ * dy[m, :], fp32 [V, D] (ld_dt); rows never selected are 0 (or unchanged with
+ * accumulate = 1); invalid indices contribute nothing and are counted in
+ * *n_invalid (optional).
+ * Source: "Backprop for kernel writers", section 06 "Top-k & routing"
+ * (selection sends gradient only to the selected slots; repeated indices
+ * must all be summed, and atomic adds make the result order-dependent) and
+ * section 04 "The duality" (a value read by many outputs sums their
+ * gradients).
+ * Deterministic order: the indices are sorted stably (invalid last); a table
+ * row selected at most 32 times sums its contributions in increasing m; a
+ * row selected more often sums them in consecutive chunks of 32 (in
+ * increasing m within a chunk) and then the chunk sums in order; all in
+ * fp32, no float atomics, results bitwise reproducible.
+ * Workspace (16-byte aligned): int32 sorted keys [M] at offset 0 (invalid
+ * indices as V) and the positions m in sorted order [M] right after them,
+ * then sort buffers, a digit table, run bounds, chunk bookkeeping and fp32
+ * chunk sums; size from vjp_gather_rows_bwd_workspace_size.  M and V must be
+ * below 2^31 - 1. */
+size_t vjp_gather_rows_bwd_workspace_size(int64_t M, int64_t V, int64_t D);
+
+int vjp_gather_rows_fwd(const void* table, int64_t ld_t, int64_t V, int64_t D,
+                        const int32_t* idx, int64_t M, void* y, int64_t ld_y, int act,
+                        vjp_stream_t stream);
+
+int vjp_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M, int64_t V,
+                        int64_t D, float* dtable, int64_t ld_dt, int accumulate,
+                        int32_t* n_invalid, int act, void* workspace, size_t workspace_bytes,
+                        vjp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,10 @@ _SIGS = {
                              _int),
     "vjp_softmax_xent_bwd": ([_vp, _i64, _vp, _vp, _i64, _i64, _int, _vp, _vp, _i64, _vp], _int),
     "vjp_norm_max_cols": ([_int, _int], _i64),
+    "vjp_gather_rows_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
+    "vjp_gather_rows_fwd": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp], _int),
+    "vjp_gather_rows_bwd": ([_vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _int, _vp, _int, _vp, _sz,
+                             _vp], _int),
     "vjp_layernorm_bwd_workspace_size": ([_i64, _i64], _sz),
     "vjp_rmsnorm_bwd_workspace_size": ([_i64, _i64], _sz),
     "vjp_layernorm_fwd": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _f32, _int, _int,
@@ -498,3 +502,42 @@ def vjp_rmsnorm_bwd(dy, x, w, row_rstd=None, eps=1e-6, dx=None, dw=None, accumul
                                float(eps), _dt(x), _dt(w), _ptr(ws), _nbytes(ws), _stream(x)),
            "vjp_rmsnorm_bwd")
     return dx, dw
+
+
+# ----------------------------------------------------------------- gather / scatter-add
+
+def vjp_gather_rows_bwd_workspace_size(M: int, V: int, D: int) -> int:
+    return int(lib.vjp_gather_rows_bwd_workspace_size(M, V, D))
+
+
+def vjp_gather_rows_fwd(table, idx, y=None):
+    """y[m] = table[idx[m]] (zero row for an index outside [0, V))."""
+    V, D = table.shape
+    M = idx.numel()
+    if y is None:
+        y = torch.empty((M, D), dtype=table.dtype, device=table.device)
+    _expect(idx, (M,), torch.int32, table.device, "idx")
+    _expect(y, (M, D), table.dtype, table.device, "y")
+    _check(lib.vjp_gather_rows_fwd(_ptr(table), _ld(table), V, D, _ptr(_flat(idx)), M, _ptr(y),
+                                   _ld(y), _dt(table), _stream(table)), "vjp_gather_rows_fwd")
+    return y
+
+
+def vjp_gather_rows_bwd(dy, idx, V, dtable=None, accumulate=False, n_invalid=None,
+                        count_invalid=True, workspace=None):
+    """(dtable fp32 [V, D], n_invalid int32 [1] or None): the scatter-add of dy rows."""
+    M, D = dy.shape
+    dev = dy.device
+    if dtable is None:
+        dtable = torch.empty((V, D), dtype=torch.float32, device=dev)
+    if count_invalid and n_invalid is None:
+        n_invalid = torch.empty(1, dtype=torch.int32, device=dev)
+    _expect(idx, (M,), torch.int32, dev, "idx")
+    _expect(dtable, (V, D), torch.float32, dev, "dtable")
+    if n_invalid is not None:
+        _expect(n_invalid, (1,), torch.int32, dev, "n_invalid")
+    ws = _workspace(vjp_gather_rows_bwd_workspace_size(M, V, D), dy, workspace)
+    _check(lib.vjp_gather_rows_bwd(_ptr(dy), _ld(dy), _ptr(_flat(idx)), M, V, D, _ptr(dtable),
+                                   _ld(dtable), int(bool(accumulate)), _ptr(n_invalid), _dt(dy),
+                                   _ptr(ws), _nbytes(ws), _stream(dy)), "vjp_gather_rows_bwd")
+    return dtable, n_invalid

@@ -673,3 +673,58 @@ VJP_API int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_
                        accumulate, rows, cols, eps, act, w_dtype, workspace, workspace_bytes,
                        stream);
 }
+
+// ------------------------------------------------------------------ gather / scatter-add
+
+VJP_API size_t vjp_gather_rows_bwd_workspace_size(int64_t M, int64_t V, int64_t D) {
+  if (M < 0 || V < 0 || D < 0) return 0;
+  return size_t(gather_workspace_ints(M, V, D)) * sizeof(int32_t);
+}
+
+VJP_API int vjp_gather_rows_fwd(const void* table, int64_t ld_t, int64_t V, int64_t D,
+                                const int32_t* idx, int64_t M, void* y, int64_t ld_y, int act,
+                                vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (V < 0 || D < 0 || M < 0) return fail(VJP_EINVAL, "negative size");
+  if (M > INT32_MAX || V >= INT32_MAX) return fail(VJP_EINVAL, "M or V beyond int32");
+  const int es = dtype_size(act);
+  VJP_TRY(check_matrix("table", table, V, D, ld_t, es));
+  VJP_TRY(check_vector("idx", idx, M, 4));
+  VJP_TRY(check_matrix("y", y, M, D, ld_y, es));
+  VJP_TRY(check_alias({span(y, mat_bytes(M, D, ld_y, es), "y")},
+                      {span(table, mat_bytes(V, D, ld_t, es), "table"), span(idx, M * 4, "idx")}));
+  if (M == 0 || D == 0) return ok();
+  const bool vec = rows_vec_ok(table, ld_t, es) && rows_vec_ok(y, ld_y, es);
+  return hip_status(launch_gather_rows_fwd(table, ld_t, idx, M, V, D, y, ld_y, act, vec,
+                                           static_cast<hipStream_t>(stream)),
+                    "gather_rows_fwd");
+}
+
+VJP_API int vjp_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M,
+                                int64_t V, int64_t D, float* dtable, int64_t ld_dt,
+                                int accumulate, int32_t* n_invalid, int act, void* workspace,
+                                size_t workspace_bytes, vjp_stream_t stream) {
+  if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
+  if (V < 0 || D < 0 || M < 0) return fail(VJP_EINVAL, "negative size");
+  if (M > INT32_MAX || V >= INT32_MAX) return fail(VJP_EINVAL, "M or V beyond int32");
+  if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
+  const int es = dtype_size(act);
+  VJP_TRY(check_matrix("dy", dy, M, D, ld_dy, es));
+  VJP_TRY(check_vector("idx", idx, M, 4));
+  VJP_TRY(check_matrix("dtable", dtable, V, D, ld_dt, 4));
+  if (n_invalid && !aligned(n_invalid, 4)) return fail(VJP_EALIGN, "n_invalid is not 4-byte aligned");
+  const size_t need = vjp_gather_rows_bwd_workspace_size(M, V, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(VJP_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(VJP_EALIGN, "workspace is not 16-byte aligned");
+  VJP_TRY(check_alias({span(dtable, mat_bytes(V, D, ld_dt, 4), "dtable"),
+                       span(n_invalid, n_invalid ? 4 : 0, "n_invalid"),
+                       span(workspace, int64_t(need), "workspace")},
+                      {span(dy, mat_bytes(M, D, ld_dy, es), "dy"), span(idx, M * 4, "idx")}));
+  const bool vec = rows_vec_ok(dy, ld_dy, es);
+  const bool pvec = aligned(dtable, 16) && ld_dt % 4 == 0;
+  return hip_status(launch_gather_rows_bwd(dy, ld_dy, idx, M, V, D, dtable, ld_dt, accumulate,
+                                           n_invalid, static_cast<int32_t*>(workspace), act, vec,
+                                           pvec, static_cast<hipStream_t>(stream)),
+                    "gather_rows_bwd");
+}

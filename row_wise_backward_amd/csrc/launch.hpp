@@ -80,4 +80,17 @@ hipError_t launch_norm_bwd_stage1(bool rms, const void* dy, int64_t ld_dy, const
                                   int64_t rows, int64_t cols, int64_t tiles, float eps, int act,
                                   bool vec, hipStream_t s);
 
+// Row gather and its scatter-add backward.  The backward's workspace holds
+// gather_workspace_ints(M, V, D) 4-byte values, sorted keys [M] first and the
+// sorted positions [M] next (layout in gather.hip).
+int gather_sort_passes(int64_t V);
+int64_t gather_workspace_ints(int64_t M, int64_t V, int64_t D);
+hipError_t launch_gather_rows_fwd(const void* x, int64_t ld_x, const int32_t* idx, int64_t M,
+                                  int64_t V, int64_t D, void* y, int64_t ld_y, int act, bool vec,
+                                  hipStream_t s);
+hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M,
+                                  int64_t V, int64_t D, float* dt, int64_t ld_dt, int accumulate,
+                                  int32_t* n_invalid, int32_t* ws, int act, bool vec, bool pvec,
+                                  hipStream_t s);
+
 }  // namespace vjp

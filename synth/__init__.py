@@ -59,6 +59,19 @@ def targets(rows: int, classes: int, seed: int, stream: int = STREAM_TARGETS) ->
     return rng(seed, stream).integers(0, classes, size=rows, dtype=np.int64).astype(np.int32)
 
 
+STREAM_INDEX = 4
+
+
+def zipf_indices(M: int, V: int, seed: int, a: float = 1.2, stream: int = STREAM_INDEX) -> np.ndarray:
+    """M int32 row indices in [0, V) with a Zipf(a) rank distribution (a few
+    rows drawn very often, as token ids in text are); ranks are mapped to rows
+    through a seeded permutation so frequent rows are spread over the table."""
+    g = rng(seed, stream)
+    ranks = np.minimum(g.zipf(a, size=M), V) - 1
+    perm = g.permutation(V) if V > 0 else np.zeros(0, np.int64)
+    return perm[ranks].astype(np.int32) if V > 0 else np.zeros(M, np.int32)
+
+
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     """Exact value of every stored element as float64."""
     if dtype == "f32":

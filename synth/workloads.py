@@ -12,7 +12,7 @@ from dataclasses import dataclass, field
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str                 # "weighted_sum" | "scaled_silu" | "softmax" | "softmax_xent"
+    op: str                 # "weighted_sum" | "scaled_silu" | "softmax" | "softmax_xent" | "gather_rows"
     dtype: str              # activation storage dtype
     shape: tuple            # x / logits shape
     seed: int
@@ -36,5 +36,10 @@ SOFTMAX = Workload("softmax_bf16_32768x4096", "softmax", "bf16", (32768, 4096), 
 XENT = Workload("softmax_xent_bf16_16384x32000", "softmax_xent", "bf16", (16384, 32000), 1004,
                 sigma_x=2.0, extra={"grad_scale": 1.0 / 16384})
 
-ALL = (WS_SMALL, SILU_16M, WS_LARGE, SOFTMAX, XENT)
+# Embedding lookup (gather) and its scatter-add backward: 16384 tokens with
+# Zipf(1.2) ids over a 32000-row table of 4096-wide bf16 rows.
+EMBED = Workload("gather_rows_bf16_16384x32000x4096", "gather_rows", "bf16", (16384, 4096), 1005,
+                 sigma_x=1.0, extra={"V": 32000, "zipf_a": 1.2})
+
+ALL = (WS_SMALL, SILU_16M, WS_LARGE, SOFTMAX, XENT, EMBED)
 BY_NAME = {w.name: w for w in ALL}

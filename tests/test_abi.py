@@ -298,3 +298,27 @@ def test_norm_queries_and_rejections():
     assert _ln_bwd(db=D + 0x200000 + 8) == EALIAS                    # db over dw
     assert _ln_bwd(dx=B + 2) == EALIAS
     assert L.vjp_rmsnorm_fwd(P(A), 64, P(B), P(A + 2), 64, None, 10, 64, ctypes.c_float(1e-6), 2, 2, None) == EALIAS
+
+
+def test_gather_queries_and_rejections():
+    n = rwb.vjp_gather_rows_bwd_workspace_size(1000, 50, 64)
+    assert n > 0 and n % 4 == 0
+    assert rwb.vjp_gather_rows_bwd_workspace_size(-1, 5, 5) == 0
+    fwd = lambda **k: L.vjp_gather_rows_fwd(P(k.get("t", A)), k.get("ldt", 64), k.get("V", 10), 64,
+                                            P(k.get("idx", B)), k.get("M", 20), P(k.get("y", C)),
+                                            64, k.get("act", 2), None)
+    assert fwd(y=A + 128) == EALIAS
+    assert fwd(ldt=63) == EINVAL
+    assert fwd(idx=B + 2) == EALIGN
+    assert fwd(act=7) == EDTYPE
+    assert fwd(V=1 << 31) == EINVAL
+    assert fwd(M=0) == OK                                   # nothing to do
+    bwd = lambda **k: L.vjp_gather_rows_bwd(P(A), 64, P(B), 20, 10, 64, P(k.get("dt", C)), 64,
+                                            k.get("acc", 0), P(k.get("ninv", None)), 2,
+                                            P(k.get("ws", D)), k.get("wsb", 1 << 20), None)
+    assert bwd(wsb=16) == EWORKSPACE
+    assert bwd(ws=D + 4) == EALIGN                          # 16-byte alignment required
+    assert bwd(dt=A + 64) == EALIAS
+    assert bwd(acc=5) == EINVAL
+    assert bwd(ninv=C + 2) == EALIGN
+    assert bwd(ninv=D + 8) == EALIAS                        # count inside the workspace
