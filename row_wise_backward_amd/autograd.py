@@ -20,6 +20,8 @@ What is saved ("Backward in Triton", section "Save vs recompute";
 * softmax: y (save="y"), or x and the row logsumexp (save="lse": one fp32
   per row, y rebuilt on chip);
 * LayerNorm / RMSNorm: x, w and the row mean / rstd (one fp32 each per row);
+* row gather (embedding lookup): the indices only; the backward is the
+  deterministic scatter-add of dy into the table's rows;
 * softmax cross-entropy: the logits, the targets and the row logsumexp;
   the backward rebuilds p = exp(z - lse) and reads the upstream gradient
   from device memory (no host synchronisation).
@@ -33,14 +35,15 @@ from __future__ import annotations
 
 import torch
 
-from . import (vjp_layernorm_bwd, vjp_layernorm_fwd, vjp_rmsnorm_bwd, vjp_rmsnorm_fwd,
+from . import (vjp_gather_rows_bwd, vjp_gather_rows_fwd, vjp_layernorm_bwd, vjp_layernorm_fwd,
+               vjp_rmsnorm_bwd, vjp_rmsnorm_fwd,
                vjp_scaled_silu_bwd, vjp_scaled_silu_fwd, vjp_softmax_bwd, vjp_softmax_bwd_lse,
                vjp_softmax_fwd, vjp_softmax_fwd_lse, vjp_softmax_xent_bwd, vjp_softmax_xent_fwd,
                vjp_weighted_sum_bwd, vjp_weighted_sum_fwd)
 
 __all__ = ["WeightedSum", "ScaledSiLU", "Softmax", "SoftmaxCrossEntropy", "LayerNorm", "RMSNorm",
-           "weighted_sum", "scaled_silu", "softmax", "softmax_cross_entropy", "layer_norm",
-           "rms_norm"]
+           "GatherRows", "weighted_sum", "scaled_silu", "softmax", "softmax_cross_entropy",
+           "layer_norm", "rms_norm", "gather_rows"]
 
 
 def _param_grad(g32: torch.Tensor, like: torch.Tensor) -> torch.Tensor:
@@ -190,6 +193,32 @@ class RMSNorm(torch.autograd.Function):
         return (dx.reshape(ctx.shape) if ctx.needs_input_grad[0] else None,
                 _param_grad(dw, w) if ctx.needs_input_grad[1] else None,
                 None)
+
+
+class GatherRows(torch.autograd.Function):
+    """y[m] = table[idx[m]] (embedding lookup); idx integer indices of any shape."""
+
+    @staticmethod
+    def forward(ctx, table, idx):
+        t = table.contiguous()
+        i = idx.contiguous().reshape(-1)
+        if i.dtype != torch.int32:
+            i = i.to(torch.int32)
+        y = vjp_gather_rows_fwd(t, i)
+        ctx.save_for_backward(i)
+        ctx.V, ctx.dtype, ctx.out_shape = t.shape[0], t.dtype, (*idx.shape, t.shape[1])
+        return y.reshape(ctx.out_shape)
+
+    @staticmethod
+    def backward(ctx, dy):
+        (i,) = ctx.saved_tensors
+        dt, _ = vjp_gather_rows_bwd(dy.contiguous().reshape(i.numel(), -1), i, ctx.V,
+                                    count_invalid=False)
+        return (dt if ctx.dtype == torch.float32 else dt.to(ctx.dtype)), None
+
+
+def gather_rows(table, idx):
+    return GatherRows.apply(table, idx)
 
 
 def layer_norm(x, w, b, eps=1e-5):

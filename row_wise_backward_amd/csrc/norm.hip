@@ -72,28 +72,34 @@ __device__ __forceinline__ void load_params_vec(const void* __restrict__ w, int6
   for (int i = 0; i < VEC; ++i) o[i] = (col + i < cols) ? load_param_f32(w, col + i, wdt) : 0.0f;
 }
 
-// Forward: one row per workgroup (four rows per 256-thread workgroup when a
-// wave holds a row), the resident layout of rowops.hpp, w and b read with
-// vector loads (they stay in L2: every row reads the same values).
-template <typename T, int VEC, int WAVES, int K, bool RMS>
+// Forward: RB consecutive rows per workgroup of WAVES waves (WAVES = 1: one
+// wave per row, four rows per 256-thread workgroup, RB = 1), the resident
+// layout of rowops.hpp, every row read once and all RB rows loaded before any
+// is reduced; w and b read once per workgroup with vector loads (they stay in
+// L2: every workgroup reads the same values), the RB means and then the RB
+// variances exchanged together.
+template <typename T, int VEC, int WAVES, int K, bool RMS, int RB>
 __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
     const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
     const void* __restrict__ b, int wdt, bool pvec, T* __restrict__ y, int64_t ld_y,
     float* __restrict__ row_mean, float* __restrict__ row_rstd, int64_t rows, int64_t cols,
     float eps) {
-  __shared__ float buf[2][WAVES];
+  static_assert(WAVES > 1 || RB == 1, "one-wave rows take one row per wave");
+  __shared__ float buf[2][RB][WAVES];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
-                                 : int64_t(blockIdx.x);
+  const int64_t row0 = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
+                                  : int64_t(blockIdx.x) * RB;
   const int wv = WAVES == 1 ? 0 : wave;
-  if (WAVES == 1 && row >= rows) return;
+  if (WAVES == 1 && row0 >= rows) return;
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
   const int64_t lane_col = (int64_t(wv) * kWave + lane) * VEC;
   const float inv_cols = 1.0f / float(cols);
 
-  Vec<T, VEC> raw[K];
-  load_lane_row<T, VEC, WAVES, K>(x + row * ld_x, cols, lane_col, raw);
+  Vec<T, VEC> raw[RB][K];
+#pragma unroll
+  for (int q = 0; q < RB; ++q)
+    if (row0 + q < rows) load_lane_row<T, VEC, WAVES, K>(x + (row0 + q) * ld_x, cols, lane_col, raw[q]);
   float pw[K][VEC], pb[RMS ? 1 : K][VEC];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -103,46 +109,64 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
     }
   }
 
-  float mean = 0.0f;
+  float mean[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q) mean[q] = 0.0f;
   if constexpr (!RMS) {
-    float s = 0.0f;
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      if (k * kStep < cols)
+    for (int q = 0; q < RB; ++q) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s += to_f32(raw[k].v[i]);   // padding reads 0
-    mean = row_reduce_sum<WAVES>(s, buf[0]) * inv_cols;
+      for (int k = 0; k < K; ++k)
+        if (k * kStep < cols)
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) mean[q] += to_f32(raw[q][k].v[i]);   // padding reads 0
+    }
+    row_reduce_sum_n<WAVES, RB>(mean, buf[0]);
+#pragma unroll
+    for (int q = 0; q < RB; ++q) mean[q] *= inv_cols;
   }
-  float ss = 0.0f;
+  float rstd[RB];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if (k * kStep < cols) {
-      const int64_t col = k * kStep + lane_col;
+  for (int q = 0; q < RB; ++q) {
+    float ss = 0.0f;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const float d = to_f32(raw[k].v[i]) - mean;
-        if (col + i < cols) ss = fmaf(d, d, ss);
+    for (int k = 0; k < K; ++k) {
+      if (k * kStep < cols) {
+        const int64_t col = k * kStep + lane_col;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float d = to_f32(raw[q][k].v[i]) - mean[q];
+          if (col + i < cols) ss = fmaf(d, d, ss);
+        }
       }
     }
+    rstd[q] = ss;
   }
-  const float rstd =
-      1.0f / __builtin_sqrtf(row_reduce_sum<WAVES>(ss, buf[1]) * inv_cols + eps);
-  if (wv == 0 && lane == 0) {
-    if (row_mean != nullptr) row_mean[row] = mean;
-    if (row_rstd != nullptr) row_rstd[row] = rstd;
-  }
+  row_reduce_sum_n<WAVES, RB>(rstd, buf[1]);
+#pragma unroll
+  for (int q = 0; q < RB; ++q) rstd[q] = 1.0f / __builtin_sqrtf(rstd[q] * inv_cols + eps);
 
-  T* yr = y + row * ld_y;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if (k * kStep < cols) {
-      const int64_t col = k * kStep + lane_col;
-      if (col < cols) {
-        float o[VEC];
+  for (int q = 0; q < RB; ++q) {
+    const int64_t row = row0 + q;
+    if (row >= rows) break;
+    if (wv == 0 && lane == 0) {
+      if (row_mean != nullptr) row_mean[row] = mean[q];
+      if (row_rstd != nullptr) row_rstd[row] = rstd[q];
+    }
+    T* yr = y + row * ld_y;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i)
-          o[i] = fmaf((to_f32(raw[k].v[i]) - mean) * rstd, pw[k][i], RMS ? 0.0f : pb[k][i]);
-        store_row_vec<T, VEC>(yr, col, cols, o);
+    for (int k = 0; k < K; ++k) {
+      if (k * kStep < cols) {
+        const int64_t col = k * kStep + lane_col;
+        if (col < cols) {
+          float o[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i)
+            o[i] = fmaf((to_f32(raw[q][k].v[i]) - mean[q]) * rstd[q], pw[k][i],
+                        RMS ? 0.0f : pb[k][i]);
+          store_row_vec<T, VEC>(yr, col, cols, o);
+        }
       }
     }
   }
@@ -290,9 +314,11 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
 // partials of its columns in fp32 registers besides x and dy), so rows of
 // up to 16 waves * 64 lanes * 16 = 16384 columns are supported.
 constexpr int kLaneElems = 16;
-// Forward measured on MI355X for 32768 x 4096 bf16: one workgroup per row
-// with vector parameter loads (95 us) beats workgroups that loop over rows
-// with the parameters held in registers (127 us).
+// Forward measured on MI355X for 32768 x 4096 bf16: one row per workgroup
+// with vector parameter loads (RMSNorm 92 us, LayerNorm 108-117 us) beats
+// workgroups that loop over rows with the parameters held in registers
+// (127 us) and matches two or four rows per workgroup (108-156 us).
+constexpr int kFwdRowsPerBlock = 1;
 
 template <typename T, int VEC, int WAVES, int K, bool RMS>
 bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, bool pvec, T* yp,
@@ -302,9 +328,10 @@ bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, b
     return false;
   } else {
     if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
-    const unsigned grid =
-        unsigned((rows + rows_per_block<WAVES>() - 1) / rows_per_block<WAVES>());
-    norm_fwd_resident<T, VEC, WAVES, K, RMS><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+    constexpr int RB = WAVES == 1 ? 1 : kFwdRowsPerBlock;
+    const int64_t per = WAVES == 1 ? rows_per_block<1>() : RB;
+    const unsigned grid = unsigned((rows + per - 1) / per);
+    norm_fwd_resident<T, VEC, WAVES, K, RMS, RB><<<grid, row_block_threads<WAVES>(), 0, s>>>(
         xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps);
     return true;
   }

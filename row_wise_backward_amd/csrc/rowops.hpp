@@ -101,6 +101,27 @@ __device__ __forceinline__ void row_reduce_sum2(float& a, float& b, float* bufa,
   }
 }
 
+// N sums of a row (or of N rows owned by the same waves) in one exchange.
+template <int WAVES, int N>
+__device__ __forceinline__ void row_reduce_sum_n(float (&v)[N], float (*buf)[WAVES]) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) v[n] = wave_sum(v[n]);
+  if constexpr (WAVES > 1) {
+    if ((threadIdx.x % kWave) == 0) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) buf[n][threadIdx.x / kWave] = v[n];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float t = buf[n][0];
+#pragma unroll
+      for (int k = 1; k < WAVES; ++k) t += buf[n][k];
+      v[n] = t;
+    }
+  }
+}
+
 // 2^t without flushing subnormal results: v_exp_f32 is only trusted for
 // results >= 2^-126, below that the argument is shifted up by 64 and the
 // result scaled back (an exact power-of-two scaling, one rounding).

@@ -180,3 +180,23 @@ def test_norm_grads(ag, kind):
         if r is not None:
             print("   ", r)
     assert r1.ok and r2.ok and (r3 is None or r3.ok)
+
+
+def test_gather_rows_grads(ag):
+    """Embedding lookup with repeated ids ([2, 50] index tensor), two backward
+    passes accumulating into table.grad."""
+    V, D = 40, 24
+    table = synth.normal((V, D), 1.0, "f32", 309, 0)
+    idx = synth.zipf_indices(100, V, 309)
+    g = synth.normal((100, D), 1.0, "f32", 309, 2)
+    tt = _t(table)
+    it = torch.from_numpy(idx.astype(np.int64)).to(DEV).reshape(2, 50)
+    for _ in range(2):
+        y = ag.gather_rows(tt, it)
+        assert y.shape == (2, 50, D)
+        y.backward(synth.to_torch(g, "f32", DEV).reshape(2, 50, D))
+    dt, _ = oracle.gather.bwd(synth.to_f64(g, "f32"), idx, V)
+    S, _ = oracle.gather.bwd(np.abs(synth.to_f64(g, "f32")), idx, V)
+    r = pointwise(to_host(tt.grad, "f32"), 2 * dt, "f32", S=2 * S, name="table.grad")
+    print("   ", r)
+    assert r.ok
