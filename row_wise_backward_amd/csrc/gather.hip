@@ -172,7 +172,8 @@ __global__ __launch_bounds__(256) void segment_bounds(const int32_t* __restrict_
 // chunks of kRun positions.  Every long run has more than kRun positions, so
 // it has fewer than len / 16 chunks, and all chunks together fewer than M / 16.
 // (Measured on MI355X for 16384 Zipf ids into 32000 x 4096: 32-position runs
-// 218 us for the whole backward, 64-position runs 330 us.)
+// 218 us for the whole backward; 64-position runs with the chunk counts
+// folded into a strided scan, 330 us.)
 constexpr int kRun = 32;
 
 // acc[i] += dy[pos[j], col + i] for j = j0 .. j1 - 1 in order, U rows in flight.
