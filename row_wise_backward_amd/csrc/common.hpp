@@ -38,6 +38,17 @@ template <typename T, int N> struct alignas(sizeof(T) * N) Vec {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x8_t __attribute__((ext_vector_type(8)));
+
+// The vector of 32-bit words (or the one narrower word) with the bytes of a
+// Vec<T, N>.
+template <int kBytes> struct WordVec;
+template <> struct WordVec<32> { using type = u32x8_t; };
+template <> struct WordVec<16> { using type = u32x4_t; };
+template <> struct WordVec<8> { using type = u32x2_t; };
+template <> struct WordVec<4> { using type = unsigned; };
+template <> struct WordVec<2> { using type = unsigned short; };
+template <typename T, int N> using words_t = typename WordVec<sizeof(T) * N>::type;
 
 // Streaming accesses: data read or written exactly once by the kernel are
 // moved with the nontemporal hint, which on gfx950 lets a 128-bit load stream
@@ -85,6 +96,39 @@ __device__ __forceinline__ void store_f32(T* __restrict__ p, const float (&in)[N
 #pragma unroll
   for (int i = 0; i < N; ++i) r.v[i] = from_f32<T>(in[i]);
   store_stream<T, N>(p, r);
+}
+
+// Loads split in two so that several vectors of a lane are in flight at
+// once.  issue_vec starts one streaming vector load of the N elements at p
+// when all of them lie below `avail` elements from p, and otherwise leaves w
+// as it is; fix_vec completes such a vector element by element (elements at
+// or past avail read as `fill`; avail may be zero or negative).  A caller
+// issues all of its vectors, fixes them, and only then views them as
+// elements (as_vec).  Both steps work on whole 32-bit words for the sake of
+// the code the compiler emits: where a value loaded in one arm of a branch
+// merges with another, any work the merge needs on the loaded data (a copy,
+// or the split of a word into 16-bit elements) waits for the load right
+// where it is issued, and the loads of a lane then run one at a time.
+template <typename T, int N>
+__device__ __forceinline__ void issue_vec(const T* __restrict__ p, int64_t avail,
+                                          words_t<T, N>& w) {
+  if (avail >= N) w = __builtin_nontemporal_load(reinterpret_cast<const words_t<T, N>*>(p));
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void fix_vec(const T* __restrict__ p, int64_t avail, T fill,
+                                        words_t<T, N>& w) {
+  if (avail < N) {
+    Vec<T, N> t;
+#pragma unroll
+    for (int i = 0; i < N; ++i) t.v[i] = (i < avail) ? p[i] : fill;
+    w = __builtin_bit_cast(words_t<T, N>, t);
+  }
+}
+
+template <typename T, int N>
+__device__ __forceinline__ Vec<T, N> as_vec(const words_t<T, N>& w) {
+  return __builtin_bit_cast(Vec<T, N>, w);
 }
 
 // Guarded variants for the ragged end of a row or array: a full vector when

@@ -33,43 +33,61 @@ namespace vjp {
 
 namespace {
 
-// Loads the lane's K vectors of row `row` (padding reads 0).
+// Loads the lane's K vectors of row `row` (padding reads 0), all in flight
+// together.
 template <typename T, int VEC, int WAVES, int K>
 __device__ __forceinline__ void load_lane_row(const T* __restrict__ r, int64_t cols,
                                               int64_t lane_col, Vec<T, VEC> (&v)[K]) {
-  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
-#pragma unroll
-  for (int k = 0; k < K; ++k)
-    if (k * kStep < cols) load_row_vec<T, VEC>(r, k * kStep + lane_col, cols, zero_of<T>(), v[k]);
+  load_row_resident<T, VEC, WAVES, K>(r, cols, lane_col, zero_of<T>(), v);
 }
 
-// VEC consecutive parameter values starting at column col, widened to fp32.
-// pvec: the parameter vectors are 16-byte aligned, so a full vector is one
-// aligned access of VEC * element-size bytes; otherwise, and at the ragged
-// end of the row, element by element (zero past cols).
-template <typename P, int VEC>
-__device__ __forceinline__ void params_as_f32(const P* __restrict__ p, float (&o)[VEC]) {
-  const Vec<P, VEC> v = *reinterpret_cast<const Vec<P, VEC>*>(p);
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) o[i] = to_f32(v.v[i]);
+// VEC consecutive parameter values starting at column col, in two phases
+// like issue_vec / fix_vec: issue_params starts the load (one aligned vector
+// of VEC elements of the parameter dtype) when the parameter vectors are
+// 16-byte aligned (pvec) and the VEC columns lie inside the row;
+// params_f32 widens the loaded values to fp32, or loads a ragged or
+// unaligned vector element by element (zero past cols).  The dtype is a
+// launch-wide value, so its branches are uniform.
+template <int VEC>
+struct ParamVec {
+  words_t<float, VEC> f;      // fp32 parameters
+  words_t<uint16_t, VEC> h;   // fp16 / bf16 parameters
+};
+
+template <int VEC>
+__device__ __forceinline__ void issue_params(const void* __restrict__ p, int64_t col, int64_t cols,
+                                             int wdt, bool pvec, ParamVec<VEC>& r) {
+  if (pvec && col + VEC <= cols) {
+    if (wdt == kF32)
+      r.f = *reinterpret_cast<const words_t<float, VEC>*>(static_cast<const float*>(p) + col);
+    else
+      r.h = *reinterpret_cast<const words_t<uint16_t, VEC>*>(static_cast<const uint16_t*>(p) + col);
+  }
 }
 
 template <int VEC>
-__device__ __forceinline__ void load_params_vec(const void* __restrict__ w, int64_t col,
-                                                int64_t cols, int wdt, bool pvec,
-                                                float (&o)[VEC]) {
+__device__ __forceinline__ void params_f32(const void* __restrict__ p, int64_t col, int64_t cols,
+                                           int wdt, bool pvec, const ParamVec<VEC>& r,
+                                           float (&o)[VEC]) {
   if (pvec && col + VEC <= cols) {
     if (wdt == kF32) {
-      params_as_f32<float, VEC>(static_cast<const float*>(w) + col, o);
-    } else if (wdt == kF16) {
-      params_as_f32<_Float16, VEC>(static_cast<const _Float16*>(w) + col, o);
+      const Vec<float, VEC> f = __builtin_bit_cast(Vec<float, VEC>, r.f);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = f.v[i];
     } else {
-      params_as_f32<bf16, VEC>(static_cast<const bf16*>(w) + col, o);
+      const Vec<uint16_t, VEC> h = __builtin_bit_cast(Vec<uint16_t, VEC>, r.h);
+      if (wdt == kF16) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = to_f32(__builtin_bit_cast(_Float16, h.v[i]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = to_f32(bf16{h.v[i]});
+      }
     }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) o[i] = (col + i < cols) ? load_param_f32(w, col + i, wdt) : 0.0f;
+  for (int i = 0; i < VEC; ++i) o[i] = (col + i < cols) ? load_param_f32(p, col + i, wdt) : 0.0f;
 }
 
 // Forward: RB consecutive rows per workgroup of WAVES waves (WAVES = 1: one
@@ -96,6 +114,14 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
   const int64_t lane_col = (int64_t(wv) * kWave + lane) * VEC;
   const float inv_cols = 1.0f / float(cols);
 
+  // Every load of the parameters and rows is issued before the first wait
+  // (the parameters first: they are L2 hits and arrive before the rows).
+  ParamVec<VEC> rw[K], rb[RMS ? 1 : K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    issue_params<VEC>(w, k * kStep + lane_col, cols, wdt, pvec, rw[k]);
+    if constexpr (!RMS) issue_params<VEC>(b, k * kStep + lane_col, cols, wdt, pvec, rb[k]);
+  }
   Vec<T, VEC> raw[RB][K];
 #pragma unroll
   for (int q = 0; q < RB; ++q)
@@ -103,10 +129,8 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
   float pw[K][VEC], pb[RMS ? 1 : K][VEC];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    if (k * kStep < cols) {
-      load_params_vec<VEC>(w, k * kStep + lane_col, cols, wdt, pvec, pw[k]);
-      if constexpr (!RMS) load_params_vec<VEC>(b, k * kStep + lane_col, cols, wdt, pvec, pb[k]);
-    }
+    params_f32<VEC>(w, k * kStep + lane_col, cols, wdt, pvec, rw[k], pw[k]);
+    if constexpr (!RMS) params_f32<VEC>(b, k * kStep + lane_col, cols, wdt, pvec, rb[k], pb[k]);
   }
 
   float mean[RB];

@@ -34,13 +34,33 @@ template <typename T> __device__ __forceinline__ T zero_of() { return T{}; }
 template <typename T, int VEC>
 __device__ __forceinline__ bool load_row_vec(const T* __restrict__ row, int64_t col, int64_t cols,
                                              T fill, Vec<T, VEC>& r) {
-  if (col + VEC <= cols) {
-    r = load_stream<T, VEC>(row + col);
-    return true;
+  words_t<T, VEC> w;
+  issue_vec<T, VEC>(row + col, cols - col, w);
+  fix_vec<T, VEC>(row + col, cols - col, fill, w);
+  r = as_vec<T, VEC>(w);
+  return col + VEC <= cols;
+}
+
+// Loads the lane's K vectors of a row in the resident layout, all K loads
+// issued before any is completed or used; elements at or beyond `cols`
+// (including vectors wholly past the end) read as `fill`.
+template <typename T, int VEC, int WAVES, int K>
+__device__ __forceinline__ void load_row_resident(const T* __restrict__ row, int64_t cols,
+                                                  int64_t lane_col, T fill, Vec<T, VEC> (&r)[K]) {
+  constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
+  words_t<T, VEC> w[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t col = k * kStep + lane_col;
+    issue_vec<T, VEC>(row + col, cols - col, w[k]);
   }
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) r.v[i] = (col + i < cols) ? row[col + i] : fill;
-  return false;
+  for (int k = 0; k < K; ++k) {
+    const int64_t col = k * kStep + lane_col;
+    fix_vec<T, VEC>(row + col, cols - col, fill, w[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) r[k] = as_vec<T, VEC>(w[k]);
 }
 
 // Store vector `col` of a row, dropping elements at or beyond `cols`.
@@ -150,36 +170,37 @@ __device__ __forceinline__ void exp_vec(const Vec<T, VEC>& r, float m, bool safe
 // Row logsumexp from the row max m and the row sum l of exp(x - m).
 __device__ __forceinline__ float row_lse_of(float m, float l) { return m + log2_fast(l) * kLn2; }
 
-// Loads the lane's K vectors of a row (padding reads as -inf) and returns the
-// lane's max over its elements and min over its valid elements.
+// The lane's max over its K vectors (padding read as -inf) and min over its
+// valid elements.
 template <typename T, int VEC, int WAVES, int K>
-__device__ __forceinline__ void load_row_minmax(const T* __restrict__ row, int64_t cols,
-                                                int64_t lane_col, Vec<T, VEC> (&raw)[K],
-                                                float& mx, float& mn) {
+__device__ __forceinline__ void lane_minmax(const Vec<T, VEC> (&raw)[K], int64_t cols,
+                                            int64_t lane_col, float& mx, float& mn) {
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
   mx = -__builtin_inff();
   mn = __builtin_inff();
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (k * kStep < cols) {
-      const int64_t col = k * kStep + lane_col;
-      if (load_row_vec<T, VEC>(row, col, cols, neg_inf_of<T>(), raw[k])) {
+      const int64_t rem = cols - (k * kStep + lane_col);
+      const int nv = rem >= VEC ? VEC : (rem > 0 ? int(rem) : 0);   // valid elements
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float f = to_f32(raw[k].v[i]);
-          mx = fmaxf(mx, f);
-          mn = fminf(mn, f);
-        }
-      } else {  // ragged end of the row: padding counts for neither max nor min
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float f = to_f32(raw[k].v[i]);
-          mx = fmaxf(mx, f);
-          mn = fminf(mn, col + i < cols ? f : __builtin_inff());
-        }
+      for (int i = 0; i < VEC; ++i) {
+        const float f = to_f32(raw[k].v[i]);
+        mx = fmaxf(mx, f);   // padding is -inf
+        mn = fminf(mn, i < nv ? f : __builtin_inff());
       }
     }
   }
+}
+
+// Loads the lane's K vectors of a row (padding reads as -inf) and returns the
+// lane's max over its elements and min over its valid elements.
+template <typename T, int VEC, int WAVES, int K>
+__device__ __forceinline__ void load_row_minmax(const T* __restrict__ row, int64_t cols,
+                                                int64_t lane_col, Vec<T, VEC> (&raw)[K],
+                                                float& mx, float& mn) {
+  load_row_resident<T, VEC, WAVES, K>(row, cols, lane_col, neg_inf_of<T>(), raw);
+  lane_minmax<T, VEC, WAVES, K>(raw, cols, lane_col, mx, mn);
 }
 
 // Register barrier on a loaded vector: the compiler must treat its contents

@@ -119,19 +119,14 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void softmax_bwd_reside
   Vec<T, VEC> rg[K], ry[K];
   float L = 0.0f;
   bool safe = false;
+  // x padding = -inf (y = 0 there), y padding = 0
+  load_row_resident<T, VEC, WAVES, K>(sr, cols, lane_col, FROM_LSE ? neg_inf_of<T>() : zero_of<T>(), ry);
+  load_row_resident<T, VEC, WAVES, K>(gr, cols, lane_col, zero_of<T>(), rg);
   if constexpr (FROM_LSE) {
     float mx, mn;
-    load_row_minmax<T, VEC, WAVES, K>(sr, cols, lane_col, ry, mx, mn);   // padding = -inf
+    lane_minmax<T, VEC, WAVES, K>(ry, cols, lane_col, mx, mn);
     L = row_lse[row];
     safe = needs_denorm_exp(mn, L);
-  }
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if (k * kStep < cols) {
-      const int64_t col = k * kStep + lane_col;
-      load_row_vec<T, VEC>(gr, col, cols, zero_of<T>(), rg[k]);
-      if constexpr (!FROM_LSE) load_row_vec<T, VEC>(sr, col, cols, zero_of<T>(), ry[k]);
-    }
   }
   float s = 0.0f;
 #pragma unroll

@@ -57,12 +57,15 @@ __global__ __launch_bounds__(NT) void xent_bwd_kernel(
   T* dr = dz + row * ld_dz;
   constexpr int64_t kChunk = int64_t(NT) * VEC;
   const int64_t c0 = int64_t(blockIdx.y) * kChunk * U + int64_t(threadIdx.x) * VEC;
+  words_t<T, VEC> w[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) issue_vec<T, VEC>(zr + c0 + u * kChunk, C - (c0 + u * kChunk), w[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    fix_vec<T, VEC>(zr + c0 + u * kChunk, C - (c0 + u * kChunk), neg_inf_of<T>(), w[u]);
   Vec<T, VEC> r[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t col = c0 + u * kChunk;
-    if (col < C) load_row_vec<T, VEC>(zr, col, C, neg_inf_of<T>(), r[u]);
-  }
+  for (int u = 0; u < U; ++u) r[u] = as_vec<T, VEC>(w[u]);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t col = c0 + u * kChunk;

@@ -44,62 +44,75 @@ __device__ __forceinline__ void load_params(const void* __restrict__ w, int64_t 
   for (int i = 0; i < VEC; ++i) out[i] = (col + i < d) ? load_param(w, col + i, dt) : 0.0f;
 }
 
-// Forward.  The row loop is uniform across the wave (lanes past the end of
-// the block carry zeros), so the per-row DPP reductions always see every lane.
-template <typename T, int VEC, int U>
+// Forward.  The rows are cut into chunks of U workgroup steps (U * 4 G
+// rows); workgroup g takes chunks g, g + gridDim.x, ..., so at any moment the
+// workgroups stream neighbouring chunks.  The row loop is uniform across the
+// wave (lanes past the last row carry zeros), so the per-row DPP reductions
+// always see every lane.  WIDE: rows wider than 64 * VEC elements, whose
+// further column chunks are looped over (a separate instantiation, so that
+// the common case holds fewer registers).
+template <typename T, int VEC, int U, bool WIDE>
 __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ x, int64_t ld,
                                                           const void* __restrict__ w, int wdt,
                                                           T* __restrict__ y, int64_t n, int64_t d,
-                                                          int L, int64_t rows_per_block) {
+                                                          int L) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int G = kWave / L;
   const int sub = lane / L;
   const int c = lane % L;
   const int64_t cw = int64_t(L) * VEC;                 // columns per chunk
-  const int64_t row_beg = int64_t(blockIdx.x) * rows_per_block;
-  const int64_t row_end = min(row_beg + rows_per_block, n);
   const int64_t step = int64_t(kWavesPerBlock) * G;    // rows per workgroup step
+  const int64_t row_end = n;
 
   float w0[VEC];
   load_params<VEC>(w, int64_t(c) * VEC, d, wdt, w0);
 
-  for (int64_t wbase = row_beg + int64_t(wave) * G; wbase < row_end; wbase += U * step) {
-    float xv[U][VEC];
+  for (int64_t q = blockIdx.x; q * U * step < n; q += gridDim.x) {
+    const int64_t wbase = q * U * step + int64_t(wave) * G;
+    // All U loads in flight before the first is used (rows past the end of
+    // the block have nothing available and read as zeros).
+    const int64_t col = int64_t(c) * VEC;
+    words_t<T, VEC> xw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t row = wbase + sub + u * step;
-      const int64_t col = int64_t(c) * VEC;
-      if (row < row_end)
-        load_f32_tail<T, VEC>(x + row * ld + col, d - col, 0.0f, xv[u]);
-      else
+      issue_vec<T, VEC>(x + row * ld + col, row < row_end ? d - col : 0, xw[u]);
+    }
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) xv[u][i] = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = wbase + sub + u * step;
+      fix_vec<T, VEC>(x + row * ld + col, row < row_end ? d - col : 0, T{}, xw[u]);
     }
     float acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const Vec<T, VEC> xv = as_vec<T, VEC>(xw[u]);
       float a = 0.0f;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) a = fmaf(xv[u][i], w0[i], a);
+      for (int i = 0; i < VEC; ++i) a = fmaf(to_f32(xv.v[i]), w0[i], a);
       acc[u] = a;
     }
     // Remaining column chunks (rows wider than 64 * VEC elements).
-    for (int64_t col0 = cw; col0 < d; col0 += cw) {
-      const int64_t col = col0 + int64_t(c) * VEC;
-      float wk[VEC];
-      load_params<VEC>(w, col, d, wdt, wk);
+    for (int64_t col0 = cw; WIDE && col0 < d; col0 += cw) {
+      const int64_t colk = col0 + int64_t(c) * VEC;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t row = wbase + sub + u * step;
-        float xk[VEC];
-        if (row < row_end)
-          load_f32_tail<T, VEC>(x + row * ld + col, d - col, 0.0f, xk);
-        else
+        issue_vec<T, VEC>(x + row * ld + colk, row < row_end ? d - colk : 0, xw[u]);
+      }
+      float wk[VEC];
+      load_params<VEC>(w, colk, d, wdt, wk);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) xk[i] = 0.0f;
+      for (int u = 0; u < U; ++u) {
+        const int64_t row = wbase + sub + u * step;
+        fix_vec<T, VEC>(x + row * ld + colk, row < row_end ? d - colk : 0, T{}, xw[u]);
+      }
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[u] = fmaf(xk[i], wk[i], acc[u]);
+      for (int u = 0; u < U; ++u) {
+        const Vec<T, VEC> xk = as_vec<T, VEC>(xw[u]);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[u] = fmaf(to_f32(xk.v[i]), wk[i], acc[u]);
       }
     }
 #pragma unroll
@@ -211,12 +224,12 @@ int lanes_per_row(int64_t d, int vec) {
 }
 
 // Launch shapes (measured on MI355X for 1048576 x 256 bf16): the forward
-// loads one row group per lane per step and gives each workgroup enough steps
-// that about 2048 workgroups cover the rows; the backward loads one row group
-// per step (46 VGPRs, eight workgroups per CU).
-constexpr int kFwdUnroll = 1;
-constexpr int64_t kFwdTargetBlocks = 2048;
-constexpr int64_t kFwdMaxSteps = 64;
+// keeps four row groups per lane in flight, in chunks dealt to at most 8192
+// workgroups (86 us; contiguous blocks of 512 rows per workgroup with one
+// row group per step, 89.5 us); the backward loads one row group per step
+// (46 VGPRs, eight workgroups per CU).
+constexpr int kFwdUnroll = 4;
+constexpr int64_t kFwdMaxGrid = 8192;
 constexpr int kBwdUnroll = 1;
 constexpr int64_t kBwdMaxGrid = int64_t(1) << 20;   // workgroups loop over tiles beyond this
 
@@ -226,17 +239,20 @@ hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, int wdt, void* 
   constexpr int V = 16 / sizeof(T);
   const int v = vec ? V : 1;
   const int L = lanes_per_row(d, v);
-  const int64_t rows_per_step = int64_t(kWavesPerBlock) * (kWave / L) * kFwdUnroll;
-  int64_t steps = (n + rows_per_step * kFwdTargetBlocks - 1) / (rows_per_step * kFwdTargetBlocks);
-  steps = steps < 1 ? 1 : (steps > kFwdMaxSteps ? kFwdMaxSteps : steps);
-  const int64_t rows_per_block = rows_per_step * steps;
-  const dim3 grid(unsigned((n + rows_per_block - 1) / rows_per_block));
-  if (vec)
-    ws_fwd_kernel<T, V, kFwdUnroll><<<grid, kThreads, 0, s>>>(
-        static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(y), n, d, L, rows_per_block);
+  const int64_t rows_per_chunk = int64_t(kWavesPerBlock) * (kWave / L) * kFwdUnroll;
+  const int64_t chunks = (n + rows_per_chunk - 1) / rows_per_chunk;
+  const dim3 grid(unsigned(chunks < kFwdMaxGrid ? chunks : kFwdMaxGrid));
+  const bool wide = d > int64_t(kWave) * v;
+  const T* xp = static_cast<const T*>(x);
+  T* yp = static_cast<T*>(y);
+  if (vec && wide)
+    ws_fwd_kernel<T, V, kFwdUnroll, true><<<grid, kThreads, 0, s>>>(xp, ld_x, w, wdt, yp, n, d, L);
+  else if (vec)
+    ws_fwd_kernel<T, V, kFwdUnroll, false><<<grid, kThreads, 0, s>>>(xp, ld_x, w, wdt, yp, n, d, L);
+  else if (wide)
+    ws_fwd_kernel<T, 1, kFwdUnroll, true><<<grid, kThreads, 0, s>>>(xp, ld_x, w, wdt, yp, n, d, L);
   else
-    ws_fwd_kernel<T, 1, kFwdUnroll><<<grid, kThreads, 0, s>>>(
-        static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(y), n, d, L, rows_per_block);
+    ws_fwd_kernel<T, 1, kFwdUnroll, false><<<grid, kThreads, 0, s>>>(xp, ld_x, w, wdt, yp, n, d, L);
   return hipGetLastError();
 }
 
