@@ -29,6 +29,13 @@
 // block in four rounds of 256 (thread order within a round, rounds in
 // order), ranking equal digits within a wave with eight ballots and across
 // waves and rounds with counts in LDS.
+//
+// For M <= 16384 the same plan takes three launches instead of a dozen: one
+// kernel per radix pass (each block counts the digits of all M keys itself
+// instead of reading a scanned table) and one workgroup for the run bounds,
+// the chunks and a list of the selected rows; step 4 then runs from that
+// list, with the rows never selected zero-filled by other workgroups at the
+// same time.  The arrays and every result bit are the same on both paths.
 #include "launch.hpp"
 #include "common.hpp"
 
@@ -169,12 +176,252 @@ __global__ __launch_bounds__(256) void segment_bounds(const int32_t* __restrict_
 }
 
 // Runs of at most kRun sorted positions are summed directly; longer runs in
-// chunks of kRun positions.  Every long run has more than kRun positions, so
+// chunks of kRun positions (a run of len positions has ceil(len / kRun)).  Every long run has more than kRun positions, so
 // it has fewer than len / 16 chunks, and all chunks together fewer than M / 16.
 // (Measured on MI355X for 16384 Zipf ids into 32000 x 4096: 32-position runs
 // 218 us for the whole backward; 64-position runs with the chunk counts
 // folded into a strided scan, 330 us.)
 constexpr int kRun = 32;
+
+// Plans for 0 < M <= kPlanMaxM take three launches: one kernel per radix
+// pass, in which every block counts the digits of all M keys itself (the
+// keys are L2 resident), so that it knows both where each digit starts and
+// how many keys of each digit the blocks before it hold, and then places its
+// own 1024 keys exactly as radix_downsweep does; and one workgroup that
+// writes the run bounds, chunk offsets and chunk owners.  The arrays are the
+// same, bit for bit, as those of the separate kernels above.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kPlanRounds = 16;
+constexpr int64_t kPlanMaxM = int64_t(kPlanThreads) * kPlanRounds;
+
+// Exclusive prefix of v over a workgroup of W waves in thread order; `total`
+// gets the sum.  wsum: W ints of LDS (LDS barriers only).
+template <int W>
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum,
+                                                        int32_t& total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int32_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = x;
+  lds_barrier();
+  int32_t pre = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const int32_t t = wsum[w];
+    if (w < wave) pre += t;
+    total += t;
+  }
+  lds_barrier();   // wsum is free again
+  return pre + x - v;
+}
+
+// Keys read per thread per step of the digit count (loads in flight).
+constexpr int kCountUnroll = 16;
+
+// zero / nzero: the first pass also zero-fills the run bounds (2 (V + 1)
+// entries) and the invalid count for the plan_tail kernel that follows.  The
+// workgroup exchanges data only through LDS (its sorted keys are read by the
+// next kernel), so its barriers leave the global stores in flight.
+// FIRST: the pass reads the raw indices (position = m), otherwise the
+// previous pass's keys and positions.  Loads are unconditional (indices past
+// the end are clamped to M - 1 and their values discarded), so that a
+// thread's loads are all in flight together.
+template <bool FIRST>
+__global__ __launch_bounds__(kSortThreads) void radix_pass_fused(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ keys_in,
+    const int32_t* __restrict__ vals_in, int64_t M, int64_t V, int shift,
+    int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int32_t* __restrict__ zero,
+    int64_t nzero, int32_t* __restrict__ n_invalid) {
+  // Digit counts in four copies (by lane mod 4): keys concentrated on a few
+  // digits then collide on one LDS address four times less often.
+  __shared__ int32_t all[4][kDigits], before[4][kDigits], base[kDigits];
+  __shared__ int32_t wave_cnt[kSortWaves][kDigits];
+  __shared__ int32_t wsum[kSortWaves];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int64_t b = blockIdx.x;
+  const int64_t lo = b * kSortBlock;
+  if (zero != nullptr) {
+    for (int64_t i = b * kSortThreads + threadIdx.x; i < nzero; i += int64_t(gridDim.x) * kSortThreads)
+      zero[i] = 0;
+    if (b == 0 && threadIdx.x == 0 && n_invalid != nullptr) *n_invalid = 0;
+  }
+  // This block's keys, all four rounds in flight.
+  const int32_t* __restrict__ src = FIRST ? idx : keys_in;
+  int32_t key[kSortRounds], val[kSortRounds];
+#pragma unroll
+  for (int r = 0; r < kSortRounds; ++r) {
+    const int64_t j = lo + r * kSortThreads + threadIdx.x;
+    const int64_t jj = j < M ? j : M - 1;
+    key[r] = src[jj];
+    val[r] = FIRST ? int32_t(jj) : vals_in[jj];
+  }
+#pragma unroll
+  for (int r = 0; r < kSortRounds; ++r)
+    if (FIRST) key[r] = (key[r] >= 0 && int64_t(key[r]) < V) ? key[r] : int32_t(V);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    all[c][threadIdx.x] = 0;
+    before[c][threadIdx.x] = 0;
+  }
+  lds_barrier();
+  // Digit counts of all keys and of the keys before this block (integer
+  // atomics: exact), kCountUnroll loads in flight per thread.
+  for (int64_t j0 = threadIdx.x; j0 < M; j0 += int64_t(kCountUnroll) * kSortThreads) {
+    int32_t k[kCountUnroll];
+#pragma unroll
+    for (int u = 0; u < kCountUnroll; ++u) {
+      const int64_t j = j0 + int64_t(u) * kSortThreads;
+      k[u] = src[j < M ? j : M - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kCountUnroll; ++u) {
+      const int64_t j = j0 + int64_t(u) * kSortThreads;
+      if (j >= M) break;
+      const int32_t kv = FIRST ? ((k[u] >= 0 && int64_t(k[u]) < V) ? k[u] : int32_t(V)) : k[u];
+      const int d = int((uint32_t(kv) >> shift) & (kDigits - 1));
+      atomicAdd(&all[lane & 3][d], 1);
+      if (j < lo) atomicAdd(&before[lane & 3][d], 1);
+    }
+  }
+  lds_barrier();
+  int32_t tot;
+  const int32_t n_all = all[0][threadIdx.x] + all[1][threadIdx.x] + all[2][threadIdx.x] +
+                        all[3][threadIdx.x];
+  const int32_t n_before = before[0][threadIdx.x] + before[1][threadIdx.x] +
+                           before[2][threadIdx.x] + before[3][threadIdx.x];
+  base[threadIdx.x] = block_exclusive_scan<kSortWaves>(n_all, wsum, tot) + n_before;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+#pragma unroll
+  for (int r = 0; r < kSortRounds; ++r) {
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) wave_cnt[w][threadIdx.x] = 0;
+    lds_barrier();
+    const int64_t j = lo + r * kSortThreads + threadIdx.x;
+    const bool in = j < M;
+    const int32_t k = key[r], v = val[r];
+    // Lanes past the end carry digit 256 (bit 8), which matches no real digit.
+    const int d = in ? int((uint32_t(k) >> shift) & (kDigits - 1)) : kDigits;
+    uint64_t same = ~uint64_t(0);
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+      const bool on = (d >> bit) & 1;
+      const uint64_t m = __ballot(on);
+      same &= on ? m : ~m;
+    }
+    const int rank = __popcll(same & below);
+    if (in && rank == 0) wave_cnt[wave][d] = __popcll(same);
+    lds_barrier();
+    if (in) {
+      int32_t pre = base[d];
+      for (int w = 0; w < wave; ++w) pre += wave_cnt[w][d];
+      keys_out[pre + rank] = k;
+      vals_out[pre + rank] = v;
+    }
+    lds_barrier();
+    int32_t add = 0;
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) add += wave_cnt[w][threadIdx.x];
+    base[threadIdx.x] += add;
+    lds_barrier();
+  }
+}
+
+// Run bounds, invalid count, chunk offsets, chunk owners and the list of
+// selected rows (in key order, with its length in *n_rows) from the sorted
+// keys, in one workgroup (M <= kPlanMaxM; the bounds and the invalid count
+// arrive zero-filled).  Thread t takes the sorted positions [16 t, 16 t +
+// 16); a run that starts there ends at the next run start, found in the
+// thread's own positions or, past them, as the smallest first run start of
+// the threads after it (a suffix minimum over the workgroup).  The workgroup
+// exchanges data only through LDS; its global writes are never read back.
+__global__ __launch_bounds__(kPlanThreads) void plan_tail(
+    const int32_t* __restrict__ sk, int64_t M, int64_t V, int32_t* __restrict__ seg_begin,
+    int32_t* __restrict__ seg_end, int32_t* __restrict__ chunk_off, int32_t* __restrict__ owner,
+    int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid) {
+  __shared__ int32_t wmin[kPlanWaves];
+  __shared__ int32_t wsum[kPlanWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int32_t M32 = int32_t(M);
+  // Loads are unconditional (indices clamped into [0, M)), values past the
+  // end replaced afterwards, so a thread's loads are in flight together.
+  const int64_t j0 = int64_t(tid) * kPlanRounds;
+  auto clampj = [M](int64_t j) { return j < 0 ? int64_t(0) : (j < M ? j : M - 1); };
+  int32_t prev = sk[clampj(j0 - 1)];
+  int32_t kk[kPlanRounds];
+#pragma unroll
+  for (int i = 0; i < kPlanRounds; ++i) kk[i] = sk[clampj(j0 + i)];
+  // Run starts among my positions, and the first of them (M if none).
+  bool st[kPlanRounds];
+  int32_t first = M32;
+#pragma unroll
+  for (int i = 0; i < kPlanRounds; ++i) {
+    const int64_t j = j0 + i;
+    st[i] = j < M && (j == 0 || (i == 0 ? prev : kk[i - 1]) != kk[i]);
+    if (st[i] && first == M32) first = int32_t(j);
+  }
+  // Smallest first run start over the threads after me.
+  int32_t x = first;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_down(x, o, kWave);
+    if (lane + o < kWave) x = min(x, y);
+  }
+  if (lane == 0) wmin[wave] = x;   // minimum over the wave
+  lds_barrier();
+  int32_t next = __shfl_down(x, 1, kWave);
+  if (lane == kWave - 1) next = M32;
+  for (int w = wave + 1; w < kPlanWaves; ++w) next = min(next, wmin[w]);
+  // Each run starting here: its bounds, its chunks, and whether it is a row.
+  int32_t end[kPlanRounds], nch[kPlanRounds];
+#pragma unroll
+  for (int i = kPlanRounds - 1; i >= 0; --i) {
+    end[i] = next;
+    if (st[i]) next = int32_t(j0 + i);
+  }
+  int32_t my_chunks = 0, my_rows = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanRounds; ++i) {
+    nch[i] = 0;
+    if (!st[i]) continue;
+    const int32_t j = int32_t(j0 + i);
+    seg_begin[kk[i]] = j;
+    seg_end[kk[i]] = end[i];
+    if (int64_t(kk[i]) == V) {
+      if (n_invalid != nullptr) *n_invalid = M32 - j;
+      continue;
+    }
+    const int32_t len = end[i] - j;
+    nch[i] = len > kRun ? (len + kRun - 1) / kRun : 0;
+    my_chunks += nch[i];
+    my_rows += 1;
+  }
+  int32_t total_chunks, total_rows;
+  int32_t q = block_exclusive_scan<kPlanWaves>(my_chunks, wsum, total_chunks);
+  int32_t r = block_exclusive_scan<kPlanWaves>(my_rows, wsum, total_rows);
+#pragma unroll
+  for (int i = 0; i < kPlanRounds; ++i) {
+    if (!st[i] || int64_t(kk[i]) == V) continue;
+    rows[r++] = kk[i];
+    if (nch[i] > 0) {
+      chunk_off[kk[i]] = q;
+      for (int32_t c = 0; c < nch[i]; ++c) owner[q + c] = kk[i];
+      q += nch[i];
+    }
+  }
+  if (tid == 0) {
+    chunk_off[V] = total_chunks;
+    *n_rows = total_rows;
+  }
+}
 
 // acc[i] += dy[pos[j], col + i] for j = j0 .. j1 - 1 in order, U rows in flight.
 template <typename T, int VEC, int U>
@@ -197,6 +444,32 @@ __device__ __forceinline__ void sum_dy_rows(const T* __restrict__ dy, int64_t ld
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] += r[u][i];
+  }
+}
+
+// The same sums for lanes whose VEC columns lie inside the row (left >=
+// VEC): the U loads of a step are unconditional (positions past j1 - 1 read
+// the row at pos[j1 - 1] again and add zeros, as sum_dy_rows adds zeros), so
+// they are all in flight together.  Bitwise the same results.
+template <typename T, int VEC, int U>
+__device__ __forceinline__ void sum_dy_rows_full(const T* __restrict__ dy, int64_t ld_dy,
+                                                 const int32_t* __restrict__ pos, int32_t j0,
+                                                 int32_t j1, int64_t col, float (&acc)[VEC]) {
+  for (int32_t j = j0; j < j1; j += U) {
+    words_t<T, VEC> w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t p = pos[j + u < j1 ? j + u : j1 - 1];
+      w[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const words_t<T, VEC>*>(dy + int64_t(p) * ld_dy + col));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const Vec<T, VEC> r = as_vec<T, VEC>(w[u]);
+      const bool in = j + u < j1;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] += in ? to_f32(r.v[i]) : 0.0f;
+    }
   }
 }
 
@@ -237,7 +510,10 @@ __global__ __launch_bounds__(kSortThreads) void chunk_sums(
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
-  sum_dy_rows<T, VEC, U>(dy, ld_dy, sorted_pos, j0, j1, col, left, acc);
+  if (left >= VEC)
+    sum_dy_rows_full<T, VEC, U>(dy, ld_dy, sorted_pos, j0, j1, col, acc);
+  else
+    sum_dy_rows<T, VEC, U>(dy, ld_dy, sorted_pos, j0, j1, col, left, acc);
   float* out = Q + q * ldq + col;   // rows of ldq (a multiple of 4) floats, 16-byte aligned
   if (left >= VEC && VEC % 4 == 0) {
 #pragma unroll
@@ -254,28 +530,30 @@ __global__ __launch_bounds__(kSortThreads) void chunk_sums(
   }
 }
 
-// Stage B: workgroup (v, c) forms the gradient of table row v for chunk c of
-// the columns and writes (or adds into) it.  PVEC: the gradient rows are
-// 16-byte aligned, so each lane's VEC fp32 values go out as 16-byte stores.
+// Stage B for table row v and the VEC columns of this lane at col (left =
+// D - col > 0): the gradient row, written (or added into dt).  PVEC: the
+// gradient rows are 16-byte aligned, so each lane's VEC fp32 values go out
+// as 16-byte stores.
 template <typename T, int VEC, int U, bool PVEC>
-__global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
-    const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
-    const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
-    const int32_t* __restrict__ chunk_off, const float* __restrict__ Q, int64_t ldq, int64_t D,
-    float* __restrict__ dt, int64_t ld_dt, int accumulate) {
-  const int64_t v = blockIdx.x;
-  const int64_t col = int64_t(blockIdx.y) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
+__device__ __forceinline__ void row_gradient(
+    int64_t v, int64_t col, const T* __restrict__ dy, int64_t ld_dy,
+    const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ seg_begin,
+    const int32_t* __restrict__ seg_end, const int32_t* __restrict__ chunk_off,
+    const float* __restrict__ Q, int64_t ldq, int64_t D, float* __restrict__ dt, int64_t ld_dt,
+    int accumulate) {
   const int64_t left = D - col;
-  if (left <= 0) return;
   const int32_t beg = seg_begin[v], end = seg_end[v];
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
   if (end - beg <= kRun) {
-    sum_dy_rows<T, VEC, U>(dy, ld_dy, sorted_pos, beg, end, col, left, acc);
+    if (left >= VEC)
+      sum_dy_rows_full<T, VEC, U>(dy, ld_dy, sorted_pos, beg, end, col, acc);
+    else
+      sum_dy_rows<T, VEC, U>(dy, ld_dy, sorted_pos, beg, end, col, left, acc);
   } else {
     // The chunk partials of the run, U rows in flight, added in chunk order.
-    const int32_t q0 = chunk_off[v], q1 = chunk_off[v + 1];
+    const int32_t q0 = chunk_off[v], q1 = q0 + (end - beg + kRun - 1) / kRun;
     for (int32_t q = q0; q < q1; q += U) {
       float r[U][VEC];
 #pragma unroll
@@ -317,6 +595,68 @@ __global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
       if (i < left) out[i] = accumulate ? out[i] + acc[i] : acc[i];
+  }
+}
+
+// Stage B over every table row: workgroup (v, c) writes (or adds into) the
+// gradient of row v for chunk c of the columns; rows never selected get
+// zeros (or stay unchanged).
+template <typename T, int VEC, int U, bool PVEC>
+__global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
+    const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
+    const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
+    const int32_t* __restrict__ chunk_off, const float* __restrict__ Q, int64_t ldq, int64_t D,
+    float* __restrict__ dt, int64_t ld_dt, int accumulate) {
+  const int64_t col = int64_t(blockIdx.y) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
+  if (col >= D) return;
+  row_gradient<T, VEC, U, PVEC>(blockIdx.x, col, dy, ld_dy, sorted_pos, seg_begin, seg_end,
+                                chunk_off, Q, ldq, D, dt, ld_dt, accumulate);
+}
+
+// Stage B from the list of selected rows (plans of M <= kPlanMaxM).  When
+// writing (not accumulating) the even workgroups loop over the (listed row,
+// column chunk) pairs and the odd ones write zeros to the rows never
+// selected (a run of length zero), so that the latency-bound sums and the
+// bandwidth-bound zero rows run side by side; when accumulating every
+// workgroup takes listed pairs and the other rows are left as they are.
+// Needs gridDim.x >= 2.  (Measured on MI355X for 16384 Zipf ids into
+// 32000 x 4096: 106 us with 32768 workgroups; the pairs first and the zero
+// rows after them in every workgroup, 132 us; one workgroup per table row
+// and column chunk, 128 us.)
+template <typename T, int VEC, int U, bool PVEC>
+__global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
+    const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
+    const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
+    const int32_t* __restrict__ chunk_off, const float* __restrict__ Q, int64_t ldq, int64_t D,
+    int64_t V, const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows, int64_t cb,
+    float* __restrict__ dt, int64_t ld_dt, int accumulate) {
+  const int64_t b = blockIdx.x;
+  if (accumulate || b % 2 == 0) {
+    const int64_t me = accumulate ? b : b / 2;
+    const int64_t stride = accumulate ? int64_t(gridDim.x) : int64_t(gridDim.x + 1) / 2;
+    const int64_t items = int64_t(*n_rows) * cb;
+    for (int64_t it = me; it < items; it += stride) {
+      const int64_t col = (it % cb) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
+      if (col < D)
+        row_gradient<T, VEC, U, PVEC>(rows[it / cb], col, dy, ld_dy, sorted_pos, seg_begin,
+                                      seg_end, chunk_off, Q, ldq, D, dt, ld_dt, accumulate);
+    }
+    return;
+  }
+  const int64_t stride = int64_t(gridDim.x) / 2;
+  for (int64_t v = b / 2; v < V; v += stride) {
+    if (seg_end[v] != seg_begin[v]) continue;   // a selected row (uniform)
+    float* out = dt + v * ld_dt;
+    for (int64_t col = int64_t(threadIdx.x) * VEC; col < D; col += int64_t(kSortThreads) * VEC) {
+      if (PVEC && D - col >= VEC && VEC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC; i += 4) store_stream<float, 4>(out + col + i, Vec<float, 4>{});
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+          if (col + i < D) out[col + i] = 0.0f;
+      }
+    }
   }
 }
 
@@ -365,11 +705,17 @@ hipError_t fwd_typed(const void* x, int64_t ld_x, const int32_t* idx, int64_t M,
 // Rows summed per step of the backward (loads in flight per lane).
 constexpr int kScatterUnroll = 8;
 
+// Workgroups of the listed-rows stage B (each loops over its items).
+constexpr int64_t kListedGrid = 32768;
+
+// rows / n_rows: the list of selected rows (then stage B runs from the list),
+// or null (stage B over every table row).
 template <typename T>
 hipError_t scatter_typed(const void* dy, int64_t ld_dy, const int32_t* pos, const int32_t* beg,
                          const int32_t* end, const int32_t* chunk_off, const int32_t* owner,
-                         float* Q, int64_t ldq, int64_t nq_max, int64_t V, int64_t D, float* dt,
-                         int64_t ld_dt, int accumulate, bool vec, bool pvec, hipStream_t s) {
+                         float* Q, int64_t ldq, int64_t nq_max, int64_t V, int64_t D,
+                         const int32_t* rows, const int32_t* n_rows, float* dt, int64_t ld_dt,
+                         int accumulate, bool vec, bool pvec, hipStream_t s) {
   // Four columns per lane: each lane's fp32 results are one 16-byte store,
   // so a wave's stores cover 1 KB contiguously (eight 16-bit columns per lane
   // would leave every store instruction writing half of each 32-byte span).
@@ -387,6 +733,22 @@ hipError_t scatter_typed(const void* dy, int64_t ld_dy, const int32_t* pos, cons
     else
       chunk_sums<T, 1, U><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end, chunk_off, owner,
                                                       V, D, Q, ldq);
+  }
+  if (rows != nullptr) {
+    const int64_t want = 2 * V * int64_t(cb);
+    const unsigned gl = unsigned(want < 2 ? 2 : (want < kListedGrid ? want : kListedGrid));
+#define VJP_LISTED(VV, PV)                                                                      \
+  scatter_listed_rows<T, VV, U, PV><<<gl, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end,      \
+                                                                chunk_off, Q, ldq, D, V, rows, \
+                                                                n_rows, cb, dt, ld_dt, accumulate)
+    if (vec && pvec)
+      VJP_LISTED(V4, true);
+    else if (vec)
+      VJP_LISTED(V4, false);
+    else
+      VJP_LISTED(1, false);
+#undef VJP_LISTED
+    return hipGetLastError();
   }
   const dim3 gb(unsigned(V), cb);
   if (vec && pvec)
@@ -427,34 +789,13 @@ int64_t gather_workspace_ints(int64_t M, int64_t V, int64_t D) {
   return gather_ws_q_offset(M, V) + gather_max_chunks(M) * ((D + 3) / 4 * 4);
 }
 
-hipError_t launch_gather_rows_fwd(const void* x, int64_t ld_x, const int32_t* idx, int64_t M,
-                                  int64_t V, int64_t D, void* y, int64_t ld_y, int act, bool vec,
-                                  hipStream_t s) {
-  switch (act) {
-    case kF32: return fwd_typed<float>(x, ld_x, idx, M, V, D, y, ld_y, vec, s);
-    case kF16: return fwd_typed<_Float16>(x, ld_x, idx, M, V, D, y, ld_y, vec, s);
-    default: return fwd_typed<bf16>(x, ld_x, idx, M, V, D, y, ld_y, vec, s);
-  }
-}
-
-hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M,
-                                  int64_t V, int64_t D, float* dt, int64_t ld_dt, int accumulate,
-                                  int32_t* n_invalid, int32_t* ws, int act, bool vec, bool pvec,
-                                  hipStream_t s) {
-  const int64_t nb = (M + kSortBlock - 1) / kSortBlock;
-  int32_t* sk = ws;                 // sorted keys
-  int32_t* sv = ws + M;             // sorted positions
-  int32_t* ak = ws + 2 * M;
-  int32_t* av = ws + 3 * M;
-  int32_t* bk = ws + 4 * M;
-  int32_t* bv = ws + 5 * M;
-  int32_t* hist = ws + 6 * M;
-  int32_t* seg_begin = hist + int64_t(kDigits) * nb;
-  int32_t* seg_end = seg_begin + (V + 1);
-  int32_t* chunk_off = seg_end + (V + 1);
-  int32_t* owner = chunk_off + (V + 1);
-  const int64_t ldq = (D + 3) / 4 * 4;
-  float* Q = reinterpret_cast<float*>(ws + gather_ws_q_offset(M, V));
+// The plan for any M: radix passes of three kernels each, then the run
+// bounds, chunk counts, their scan and the chunk owners as separate kernels.
+static hipError_t plan_multi(const int32_t* idx, int64_t M, int64_t V, int64_t D, int32_t* sk,
+                             int32_t* sv, int32_t* ak, int32_t* av, int32_t* bk, int32_t* bv,
+                             int32_t* hist, int64_t nb, int32_t* seg_begin, int32_t* seg_end,
+                             int32_t* chunk_off, int32_t* owner, int32_t* n_invalid,
+                             hipStream_t s) {
   hipError_t e;
   if (M > 0) {
     const int passes = gather_sort_passes(V);
@@ -485,11 +826,74 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
   count_chunks<<<gv, 256, 0, s>>>(seg_begin, seg_end, V, chunk_off);
   scan_exclusive<<<1, kScanThreads, 0, s>>>(chunk_off, V + 1);
   chunk_owners<<<gv, 256, 0, s>>>(chunk_off, V, owner);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows_fwd(const void* x, int64_t ld_x, const int32_t* idx, int64_t M,
+                                  int64_t V, int64_t D, void* y, int64_t ld_y, int act, bool vec,
+                                  hipStream_t s) {
+  switch (act) {
+    case kF32: return fwd_typed<float>(x, ld_x, idx, M, V, D, y, ld_y, vec, s);
+    case kF16: return fwd_typed<_Float16>(x, ld_x, idx, M, V, D, y, ld_y, vec, s);
+    default: return fwd_typed<bf16>(x, ld_x, idx, M, V, D, y, ld_y, vec, s);
+  }
+}
+
+hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M,
+                                  int64_t V, int64_t D, float* dt, int64_t ld_dt, int accumulate,
+                                  int32_t* n_invalid, int32_t* ws, int act, bool vec, bool pvec,
+                                  hipStream_t s) {
+  const int64_t nb = (M + kSortBlock - 1) / kSortBlock;
+  int32_t* sk = ws;                 // sorted keys
+  int32_t* sv = ws + M;             // sorted positions
+  int32_t* ak = ws + 2 * M;
+  int32_t* av = ws + 3 * M;
+  int32_t* bk = ws + 4 * M;
+  int32_t* bv = ws + 5 * M;
+  int32_t* hist = ws + 6 * M;
+  int32_t* seg_begin = hist + int64_t(kDigits) * nb;
+  int32_t* seg_end = seg_begin + (V + 1);
+  int32_t* chunk_off = seg_end + (V + 1);
+  int32_t* owner = chunk_off + (V + 1);
+  const int64_t ldq = (D + 3) / 4 * 4;
+  float* Q = reinterpret_cast<float*>(ws + gather_ws_q_offset(M, V));
+  // Plans of M <= kPlanMaxM also list the selected rows: the list reuses the
+  // sort's spare key buffer, its length the digit table's first entry.
+  int32_t* rows = bk;
+  int32_t* n_rows = hist;
+  hipError_t e;
+  if (M > 0 && M <= kPlanMaxM) {
+    const int passes = gather_sort_passes(V);
+    const int32_t* ik = nullptr;
+    const int32_t* iv = nullptr;
+    for (int p = 0; p < passes; ++p) {
+      int32_t* ok = p == passes - 1 ? sk : (p % 2 == 0 ? ak : bk);
+      int32_t* ov = p == passes - 1 ? sv : (p % 2 == 0 ? av : bv);
+      if (p == 0)
+        radix_pass_fused<true><<<unsigned(nb), kSortThreads, 0, s>>>(
+            idx, ik, iv, M, V, 8 * p, ok, ov, seg_begin, 2 * (V + 1), n_invalid);
+      else
+        radix_pass_fused<false><<<unsigned(nb), kSortThreads, 0, s>>>(
+            idx, ik, iv, M, V, 8 * p, ok, ov, nullptr, 0, nullptr);
+      ik = ok;
+      iv = ov;
+    }
+    plan_tail<<<1, kPlanThreads, 0, s>>>(sk, M, V, seg_begin, seg_end, chunk_off, owner,
+                                         rows, n_rows, n_invalid);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (V == 0 || D == 0) return hipSuccess;
+  } else {
+    if ((e = plan_multi(idx, M, V, D, sk, sv, ak, av, bk, bv, hist, nb, seg_begin, seg_end,
+                        chunk_off, owner, n_invalid, s)) != hipSuccess ||
+        V == 0 || D == 0)
+      return e;
+  }
   const int64_t nq_max = M > kRun ? gather_max_chunks(M) : 0;
-#define VJP_SC(T)                                                                          \
-  scatter_typed<T>(dy, ld_dy, sv, seg_begin, seg_end, chunk_off, owner, Q, ldq, nq_max, V, D, \
-                   dt, ld_dt, accumulate, vec, pvec, s)
+  const bool listed = M > 0 && M <= kPlanMaxM;
+#define VJP_SC(T)                                                                            \
+  scatter_typed<T>(dy, ld_dy, sv, seg_begin, seg_end, chunk_off, owner, Q, ldq, nq_max, V, D,   \
+                   listed ? rows : nullptr, listed ? n_rows : nullptr, dt, ld_dt, accumulate, \
+                   vec, pvec, s)
   switch (act) {
     case kF32: return VJP_SC(float);
     case kF16: return VJP_SC(_Float16);
