@@ -16,6 +16,9 @@ struct bf16 {
   uint16_t bits;
 };
 
+template <typename T> inline constexpr bool is_bf16 = false;
+template <> inline constexpr bool is_bf16<bf16> = true;
+
 // ------------------------------------------------------------------ conversions
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(_Float16 v) { return static_cast<float>(v); }

@@ -165,7 +165,10 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
     if (k * kStep < C) {
       const int64_t col = k * kStep + lane_col;
       if (col < C) {
-        if (uint64_t(t - col) < uint64_t(VEC)) {  // the lane holding z_t writes the row loss
+        // The lane holding z_t writes the row loss (an invalid target past the
+        // last column can fall in the last vector's padding: the NaN written
+        // above stands).
+        if (valid && uint64_t(t - col) < uint64_t(VEC)) {
 #pragma unroll
           for (int i = 0; i < VEC; ++i)
             if (col + i == t) row_loss[row] = lse - to_f32(raw[k].v[i]);
@@ -232,11 +235,13 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream(
 
 // Launch tiers, smallest first, as for the softmax forward: (waves per row,
 // vectors per lane, keep the exponentials).  Measured on MI355X: rows of
-// 32000 16-bit logits run best as 8 waves x 8 vectors recomputing the
-// exponentials (54 VGPRs, four rows in flight per CU).  The statistics-only
-// form never keeps the exponentials (an online max / sum folding each vector
-// as it arrives measured slower: 217 us against 189 us for the read of
-// 16384 x 32000 bf16).
+// 32000 16-bit logits run best recomputing the exponentials; keeping them in
+// fp32 VGPRs cuts the waves per SIMD from 5 to 3 (484-498 us against 364 us),
+// and keeping them rounded to bf16 in place of the stored row did not help
+// either (the exponentials are not what limits this kernel).  The
+// statistics-only form never keeps the exponentials (an online max / sum
+// folding each vector as it arrives measured slower: 217 us against 189 us
+// for the read of 16384 x 32000 bf16).
 template <typename T, int VEC, int WAVES, int K, bool KEEP, bool GRAD>
 bool resident_try(const T* zp, int64_t ld, const int32_t* tg, int64_t rows, int64_t C,
                   float scale, float* rmax, float* rlse, float* rloss, T* dp, int64_t ld_dz,
@@ -257,8 +262,15 @@ hipError_t run_vec(const void* z, int64_t ld, const int32_t* tg, int64_t rows, i
 
 #define VJP_XENT_TRY(W, K, KEEP) \
   resident_try<T, VEC, W, K, KEEP, GRAD>(zp, ld, tg, rows, C, scale, rmax, rlse, rloss, dp, ld_dz, s)
-  if (!(VJP_XENT_TRY(1, 2, true) || VJP_XENT_TRY(2, 2, true) || VJP_XENT_TRY(4, 2, true) ||
-        VJP_XENT_TRY(8, 2, true) || VJP_XENT_TRY(8, 4, false) || VJP_XENT_TRY(8, 8, false)))
+  // Rows up to 8 waves x 8 vectors: with the gradient as 16 waves x 4 vectors
+  // (measured on MI355X for 16384 x 32000 bf16: 358-361 us against 364-365
+  // us), statistics only as 8 waves x 8 vectors (159 us against 184 us).
+  // (Each try launches when its capacity holds the row, so the widest tier
+  // is tried only after the narrower ones.)
+  bool done = VJP_XENT_TRY(1, 2, true) || VJP_XENT_TRY(2, 2, true) || VJP_XENT_TRY(4, 2, true) ||
+              VJP_XENT_TRY(8, 2, true) || VJP_XENT_TRY(8, 4, false);
+  if (!done) done = GRAD ? VJP_XENT_TRY(16, 4, false) : VJP_XENT_TRY(8, 8, false);
+  if (!done)
     xent_stream<T, VEC, GRAD><<<unsigned(rows), kStreamThreads, 0, s>>>(
         zp, ld, tg, C, scale, rmax, rlse, rloss, dp, ld_dz);
 #undef VJP_XENT_TRY

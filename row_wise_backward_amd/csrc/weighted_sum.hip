@@ -166,29 +166,33 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
       const T* __restrict__ xp = x + (r0 + my_row) * ld_x + col;
       T* __restrict__ dp = dx + (r0 + my_row) * ld_dx + col;
       for (int base = 0; base < nrows; base += U * wg_rows) {
-        Vec<T, VEC> xr[U];   // rows stay in storage type until used
-        float g[U];
+        // Rows stay in storage type until used; all U row loads (and the dy
+        // values, read at a clamped row and zeroed past the end) are in
+        // flight before the first is used.
+        words_t<T, VEC> xw[U];
+        T gr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int r = base + u * wg_rows + my_row;
-          if (r < nrows) {
-            g[u] = to_f32(gw[r]);
-            xr[u] = load_raw_tail<T, VEC>(xp + u * xstep, cols_left);
-          } else {
-            g[u] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) xr[u].v[i] = T{};
-          }
+          gr[u] = gw[r < nrows ? r : nrows - 1];
+          issue_vec<T, VEC>(xp + u * xstep, r < nrows ? cols_left : 0, xw[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int r = base + u * wg_rows + my_row;
+          fix_vec<T, VEC>(xp + u * xstep, r < nrows ? cols_left : 0, T{}, xw[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int r = base + u * wg_rows + my_row;
+          const float g = r < nrows ? to_f32(gr[u]) : 0.0f;
+          const Vec<T, VEC> xr = as_vec<T, VEC>(xw[u]);
           float gx[VEC];
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) gx[i] = g[u] * wr[i];
+          for (int i = 0; i < VEC; ++i) gx[i] = g * wr[i];
           if (r < nrows && cols_left > 0) store_f32_tail<T, VEC>(dp + u * dstep, cols_left, gx);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[i] = fmaf(to_f32(xr[u].v[i]), g[u], acc[i]);
+          for (int i = 0; i < VEC; ++i) acc[i] = fmaf(to_f32(xr.v[i]), g, acc[i]);
         }
         xp += U * xstep;
         dp += U * dstep;

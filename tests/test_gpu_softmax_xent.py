@@ -95,6 +95,14 @@ def test_invalid_targets(gpu_lib):
     run_case(gpu_lib, 6, 300, "bf16", seed=98, targets=[3, -1, 300, 0, 299, 2 ** 31 - 1])
 
 
+@pytest.mark.parametrize("act,C", [("bf16", 300), ("f16", 300), ("f32", 301)])
+def test_invalid_target_in_last_vector_padding(gpu_lib, act, C):
+    """Rows padded to 304 elements take the vector path with C not a multiple of
+    the vector width: targets C and 303 fall in the last vector's padding.  They
+    are the only invalid targets, so the row losses and the mean must be NaN."""
+    run_case(gpu_lib, 4, C, act, seed=96, ld=304, targets=[3, C, 0, 303])
+
+
 def test_batch1_and_batch7(gpu_lib):
     run_case(gpu_lib, 1, 32000, "bf16", seed=99)
     run_case(gpu_lib, 7, 32000, "bf16", seed=99)

@@ -121,6 +121,11 @@ def test_invalid_targets(gpu_lib):
     run_case(gpu_lib, 6, 300, "bf16", seed=203, targets=[3, -1, 300, 0, 299, 2 ** 31 - 1])
 
 
+@pytest.mark.parametrize("act,C", [("bf16", 300), ("f32", 301)])
+def test_invalid_target_in_last_vector_padding(gpu_lib, act, C):
+    run_case(gpu_lib, 4, C, act, seed=204, ld=304, targets=[3, C, 0, 303])
+
+
 def test_batch1_and_batch7(gpu_lib):
     run_case(gpu_lib, 1, 32000, "bf16", seed=205)
     run_case(gpu_lib, 7, 32000, "bf16", seed=205)
