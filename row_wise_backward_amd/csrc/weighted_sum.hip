@@ -124,18 +124,30 @@ __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ 
   }
 }
 
-// Backward stage 1.  Rows are cut into blocks of block_rows rows; tile t
-// holds blocks t, t + tiles, t + 2 tiles, ... (with tiles = number of blocks
-// this is one contiguous block per tile).  Workgroup (g, cb) takes tiles g,
-// g + gridDim.x, ... and column block cb.  Each lane accumulates VEC fp32
-// partials over its rows in increasing row order; the lanes holding the same
-// columns are combined by a butterfly and the four waves through LDS in wave
-// order, and the tile's partial row is written to P[t][.].
+// Backward stage 1.  grad_x = dy (x) w needs no x, so it is written by its
+// own workgroups while others read x for grad_w: workgroups g < readers
+// form the partials, the rest write grad_x, side by side, so a pure read
+// stream and a pure write stream share HBM (measured on MI355X for
+// 1048576 x 256 bf16, old and new in one process: 185-188 us with 512
+// readers and 32768 writers on two boxes, against 205 us on one and 186 us
+// on the other with every workgroup reading x and writing its grad_x rows).
+//
+// Readers.  Rows are cut into blocks of block_rows rows; tile t holds blocks
+// t, t + tiles, t + 2 tiles, ... (with tiles = number of blocks this is one
+// contiguous block per tile).  Reader (g, cb) takes tiles g, g + readers,
+// ... and column block cb.  Each lane accumulates VEC fp32 partials over its
+// rows in increasing row order; the lanes holding the same columns are
+// combined by a butterfly and the four waves through LDS in wave order, and
+// the tile's partial row is written to P[t][.].
+//
+// Writers.  Writer (h, cb) writes grad_x for the row groups h, h + writers,
+// ... (4 G consecutive rows each) and column block cb: grad_x[i, j] =
+// dy[i] w[j], one fp32 product rounded once.
 template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
     int wdt, T* __restrict__ dx, int64_t ld_dx, float* __restrict__ P, int64_t n, int64_t d,
-    int L, int block_rows, int64_t tiles) {
+    int L, int block_rows, int64_t tiles, int64_t readers) {
   __shared__ float red[kWavesPerBlock][kWave * VEC];
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform per wave
@@ -145,18 +157,32 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
   const int64_t col0 = int64_t(blockIdx.y) * L * VEC;
   const int64_t col = col0 + int64_t(c) * VEC;
   const int64_t cols_left = d - col;
+  if (int64_t(blockIdx.x) >= readers) {
+    float wr[VEC];
+    load_params<VEC>(w, col, d, wdt, wr);
+    const int64_t me = int64_t(blockIdx.x) - readers, writers = int64_t(gridDim.x) - readers;
+    const int64_t group = int64_t(kWavesPerBlock) * G;
+    for (int64_t r0 = me * group; r0 < n; r0 += writers * group) {
+      const int64_t row = r0 + int64_t(wave) * G + sub;
+      if (row < n && cols_left > 0) {
+        const float g = to_f32(dy[row]);
+        float gx[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) gx[i] = g * wr[i];
+        store_f32_tail<T, VEC>(dx + row * ld_dx + col, cols_left, gx);
+      }
+    }
+    return;
+  }
   // The four waves interleave: one workgroup step covers 4 G consecutive rows
   // (wave w takes rows w G .. w G + G - 1 of it, one per L-lane group), so a
   // workgroup streams one contiguous window of a block.  Row indices are
   // relative to the block; loop bounds are uniform across the wave.
   const int wg_rows = kWavesPerBlock * G;
   const int my_row = wave * G + sub;
-  const int64_t xstep = int64_t(wg_rows) * ld_x, dstep = int64_t(wg_rows) * ld_dx;
+  const int64_t xstep = int64_t(wg_rows) * ld_x;
 
-  float wr[VEC];
-  load_params<VEC>(w, col, d, wdt, wr);
-
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += readers) {
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
@@ -164,7 +190,6 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
       const int nrows = int(min(int64_t(block_rows), n - r0));
       const T* __restrict__ gw = dy + r0;
       const T* __restrict__ xp = x + (r0 + my_row) * ld_x + col;
-      T* __restrict__ dp = dx + (r0 + my_row) * ld_dx + col;
       for (int base = 0; base < nrows; base += U * wg_rows) {
         // Rows stay in storage type until used; all U row loads (and the dy
         // values, read at a clamped row and zeroed past the end) are in
@@ -187,15 +212,10 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
           const int r = base + u * wg_rows + my_row;
           const float g = r < nrows ? to_f32(gr[u]) : 0.0f;
           const Vec<T, VEC> xr = as_vec<T, VEC>(xw[u]);
-          float gx[VEC];
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) gx[i] = g * wr[i];
-          if (r < nrows && cols_left > 0) store_f32_tail<T, VEC>(dp + u * dstep, cols_left, gx);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) acc[i] = fmaf(to_f32(xr.v[i]), g, acc[i]);
         }
         xp += U * xstep;
-        dp += U * dstep;
       }
     }
 
@@ -230,12 +250,15 @@ int lanes_per_row(int64_t d, int vec) {
 // Launch shapes (measured on MI355X for 1048576 x 256 bf16): the forward
 // keeps four row groups per lane in flight, in chunks dealt to at most 8192
 // workgroups (86 us; contiguous blocks of 512 rows per workgroup with one
-// row group per step, 89.5 us); the backward loads one row group per step
-// (46 VGPRs, eight workgroups per CU).
+// row group per step, 89.5 us); the backward keeps four row groups per lane
+// in flight in up to 512 reader workgroups (which loop over the tiles beyond
+// that; one row group: 235 us, two: 188 us, four: 185 us) beside up to
+// 32768 writer workgroups (four row groups each at this size).
 constexpr int kFwdUnroll = 4;
 constexpr int64_t kFwdMaxGrid = 8192;
-constexpr int kBwdUnroll = 1;
-constexpr int64_t kBwdMaxGrid = int64_t(1) << 20;   // workgroups loop over tiles beyond this
+constexpr int kBwdUnroll = 4;
+constexpr int64_t kBwdReaders = 512;
+constexpr int64_t kBwdWriters = 32768;
 
 template <typename T>
 hipError_t fwd_typed(const void* x, int64_t ld_x, const void* w, int wdt, void* y, int64_t n,
@@ -268,15 +291,19 @@ hipError_t bwd_typed(const void* dy, const void* x, int64_t ld_x, const void* w,
   const int v = vec ? V : 1;
   const int L = lanes_per_row(d, v);
   const int64_t cw = int64_t(L) * v;
-  const dim3 grid(unsigned(tiles < kBwdMaxGrid ? tiles : kBwdMaxGrid), unsigned((d + cw - 1) / cw));
+  const int64_t readers = tiles < kBwdReaders ? tiles : kBwdReaders;
+  const int64_t groups = (n + int64_t(kWavesPerBlock) * (kWave / L) - 1) /
+                         (int64_t(kWavesPerBlock) * (kWave / L));
+  const int64_t writers = groups < kBwdWriters ? groups : kBwdWriters;
+  const dim3 grid(unsigned(readers + writers), unsigned((d + cw - 1) / cw));
   if (vec)
     ws_bwd_kernel<T, V, kBwdUnroll><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
-        ld_dx, P, n, d, L, block_rows, tiles);
+        ld_dx, P, n, d, L, block_rows, tiles, readers);
   else
     ws_bwd_kernel<T, 1, kBwdUnroll><<<grid, kThreads, 0, s>>>(
         static_cast<const T*>(dy), static_cast<const T*>(x), ld_x, w, wdt, static_cast<T*>(dx),
-        ld_dx, P, n, d, L, block_rows, tiles);
+        ld_dx, P, n, d, L, block_rows, tiles, readers);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 """Row and tile counts past the per-launch limits: more than 2^20 rows (the
 row ops launch in chunks of 2^20 rows) and more than 2^20 tiles (the
-weighted-sum backward's workgroups then loop over tiles).  Narrow rows keep
+weighted-sum backward's reader workgroups loop over the tiles).  Narrow rows keep
 the inputs small; outputs are compared with the oracle at the bars of the
 per-op suites (full reductions over all rows, the rest on sampled rows that
 include both sides of each chunk boundary)."""
@@ -26,7 +26,7 @@ def _sample(n, seed):
 
 
 def test_weighted_sum_more_tiles_than_workgroups(gpu_lib):
-    """One-row tiles over 2^20 + 3 rows: 2^20 + 3 tiles for 2^20 workgroups."""
+    """One-row tiles over 2^20 + 3 rows: 2^20 + 3 tiles for 512 reader workgroups."""
     n, d = BIG, 2
     print(f"\n[weighted_sum tiles>2^20] n={n} d={d} rows_per_tile=1", flush=True)
     x = synth.normal((n, d), 1.0, "f32", 700, synth.STREAM_X)
