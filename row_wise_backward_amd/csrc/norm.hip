@@ -26,6 +26,8 @@
 // fixed columns, so no cross-lane reduction is needed.  The tile's partial
 // rows go to P[t][0 .. cols) (dw) and P[t][cols .. 2 cols) (db), summed by
 // the fixed-order stage-2 kernel.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "rowops.hpp"
 
@@ -43,39 +45,34 @@ __device__ __forceinline__ void load_lane_row(const T* __restrict__ r, int64_t c
 
 // VEC consecutive parameter values starting at column col, in two phases
 // like issue_vec / fix_vec: issue_params starts the load (one aligned vector
-// of VEC elements of the parameter dtype) when the parameter vectors are
-// 16-byte aligned (pvec) and the VEC columns lie inside the row;
-// params_f32 widens the loaded values to fp32, or loads a ragged or
-// unaligned vector element by element (zero past cols).  The dtype is a
-// launch-wide value, so its branches are uniform.
-template <int VEC>
-struct ParamVec {
-  words_t<float, VEC> f;      // fp32 parameters
-  words_t<uint16_t, VEC> h;   // fp16 / bf16 parameters
-};
+// of VEC elements, PB bytes each: 4 for fp32, 2 for fp16 / bf16) when the
+// parameter vectors are 16-byte aligned (pvec) and the VEC columns lie inside
+// the row; params_f32 widens the loaded values to fp32, or loads a ragged or
+// unaligned vector element by element (zero past cols).  The loaded values
+// stay packed in their own width until they are used.  fp16 against bf16 is
+// a launch-wide value, so its branch is uniform.
+template <int VEC, int PB>
+using param_words_t =
+    typename std::conditional<PB == 4, words_t<float, VEC>, words_t<uint16_t, VEC>>::type;
 
-template <int VEC>
+template <int VEC, int PB>
 __device__ __forceinline__ void issue_params(const void* __restrict__ p, int64_t col, int64_t cols,
-                                             int wdt, bool pvec, ParamVec<VEC>& r) {
-  if (pvec && col + VEC <= cols) {
-    if (wdt == kF32)
-      r.f = *reinterpret_cast<const words_t<float, VEC>*>(static_cast<const float*>(p) + col);
-    else
-      r.h = *reinterpret_cast<const words_t<uint16_t, VEC>*>(static_cast<const uint16_t*>(p) + col);
-  }
+                                             bool pvec, param_words_t<VEC, PB>& r) {
+  if (pvec && col + VEC <= cols)
+    r = *reinterpret_cast<const param_words_t<VEC, PB>*>(static_cast<const char*>(p) + col * PB);
 }
 
-template <int VEC>
+template <int VEC, int PB>
 __device__ __forceinline__ void params_f32(const void* __restrict__ p, int64_t col, int64_t cols,
-                                           int wdt, bool pvec, const ParamVec<VEC>& r,
+                                           int wdt, bool pvec, const param_words_t<VEC, PB>& r,
                                            float (&o)[VEC]) {
   if (pvec && col + VEC <= cols) {
-    if (wdt == kF32) {
-      const Vec<float, VEC> f = __builtin_bit_cast(Vec<float, VEC>, r.f);
+    if constexpr (PB == 4) {
+      const Vec<float, VEC> f = __builtin_bit_cast(Vec<float, VEC>, r);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = f.v[i];
     } else {
-      const Vec<uint16_t, VEC> h = __builtin_bit_cast(Vec<uint16_t, VEC>, r.h);
+      const Vec<uint16_t, VEC> h = __builtin_bit_cast(Vec<uint16_t, VEC>, r);
       if (wdt == kF16) {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o[i] = to_f32(__builtin_bit_cast(_Float16, h.v[i]));
@@ -96,7 +93,7 @@ __device__ __forceinline__ void params_f32(const void* __restrict__ p, int64_t c
 // is reduced; w and b read once per workgroup with vector loads (they stay in
 // L2: every workgroup reads the same values), the RB means and then the RB
 // variances exchanged together.
-template <typename T, int VEC, int WAVES, int K, bool RMS, int RB>
+template <typename T, int VEC, int WAVES, int K, bool RMS, int RB, int PB>
 __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
     const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
     const void* __restrict__ b, int wdt, bool pvec, T* __restrict__ y, int64_t ld_y,
@@ -116,22 +113,16 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
 
   // Every load of the parameters and rows is issued before the first wait
   // (the parameters first: they are L2 hits and arrive before the rows).
-  ParamVec<VEC> rw[K], rb[RMS ? 1 : K];
+  param_words_t<VEC, PB> rw[K], rb[RMS ? 1 : K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    issue_params<VEC>(w, k * kStep + lane_col, cols, wdt, pvec, rw[k]);
-    if constexpr (!RMS) issue_params<VEC>(b, k * kStep + lane_col, cols, wdt, pvec, rb[k]);
+    issue_params<VEC, PB>(w, k * kStep + lane_col, cols, pvec, rw[k]);
+    if constexpr (!RMS) issue_params<VEC, PB>(b, k * kStep + lane_col, cols, pvec, rb[k]);
   }
   Vec<T, VEC> raw[RB][K];
 #pragma unroll
   for (int q = 0; q < RB; ++q)
     if (row0 + q < rows) load_lane_row<T, VEC, WAVES, K>(x + (row0 + q) * ld_x, cols, lane_col, raw[q]);
-  float pw[K][VEC], pb[RMS ? 1 : K][VEC];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    params_f32<VEC>(w, k * kStep + lane_col, cols, wdt, pvec, rw[k], pw[k]);
-    if constexpr (!RMS) params_f32<VEC>(b, k * kStep + lane_col, cols, wdt, pvec, rb[k], pb[k]);
-  }
 
   float mean[RB];
 #pragma unroll
@@ -184,11 +175,13 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
       if (k * kStep < cols) {
         const int64_t col = k * kStep + lane_col;
         if (col < cols) {
+          float pw[VEC], pb[VEC];   // widened here: packed until now
+          params_f32<VEC, PB>(w, col, cols, wdt, pvec, rw[k], pw);
+          if constexpr (!RMS) params_f32<VEC, PB>(b, col, cols, wdt, pvec, rb[k], pb);
           float o[VEC];
 #pragma unroll
           for (int i = 0; i < VEC; ++i)
-            o[i] = fmaf((to_f32(raw[q][k].v[i]) - mean[q]) * rstd[q], pw[k][i],
-                        RMS ? 0.0f : pb[k][i]);
+            o[i] = fmaf((to_f32(raw[q][k].v[i]) - mean[q]) * rstd[q], pw[i], RMS ? 0.0f : pb[i]);
           store_row_vec<T, VEC>(yr, col, cols, o);
         }
       }
@@ -355,8 +348,12 @@ bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, b
     constexpr int RB = WAVES == 1 ? 1 : kFwdRowsPerBlock;
     const int64_t per = WAVES == 1 ? rows_per_block<1>() : RB;
     const unsigned grid = unsigned((rows + per - 1) / per);
-    norm_fwd_resident<T, VEC, WAVES, K, RMS, RB><<<grid, row_block_threads<WAVES>(), 0, s>>>(
-        xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps);
+    if (wdt == kF32)
+      norm_fwd_resident<T, VEC, WAVES, K, RMS, RB, 4><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+          xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps);
+    else
+      norm_fwd_resident<T, VEC, WAVES, K, RMS, RB, 2><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+          xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps);
     return true;
   }
 }
