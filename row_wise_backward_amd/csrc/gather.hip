@@ -34,8 +34,9 @@
 // kernel per radix pass (each block counts the digits of all M keys itself
 // instead of reading a scanned table) and one workgroup for the run bounds,
 // the chunks and a list of the selected rows; step 4 then runs from that
-// list, with the rows never selected zero-filled by other workgroups at the
-// same time.  The arrays and every result bit are the same on both paths.
+// list.  The rows never selected are zero-filled by extra workgroups of the
+// plan's own launches, which otherwise leave most of the chip idle.  The
+// arrays and every result bit are the same on both paths.
 #include "launch.hpp"
 #include "common.hpp"
 
@@ -224,6 +225,103 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wsum
 // Keys read per thread per step of the digit count (loads in flight).
 constexpr int kCountUnroll = 16;
 
+// Zero rows beside the plan.  The plan kernels run on a few CUs; extra
+// workgroups of the same launches write the zeros of the table rows no index
+// selects (when the gradient is written, not added into).  Each such
+// workgroup takes `rows` consecutive table rows of the launch's share
+// [r0, r1), finds which of them are selected by reading all M indices itself
+// (so it needs nothing from the plan), and writes zeros to the others.  The
+// rows it writes are disjoint from those the listed-rows kernel writes
+// later, so the two never touch the same bytes.
+struct FillShare {
+  int64_t r0, r1;               // table rows of this launch
+  int64_t rows;                 // rows per fill workgroup (<= kFillMaxRows)
+  int64_t groups;               // fill workgroups of this launch (0: none)
+  const int32_t* idx;           // the M indices
+  int64_t M, D;
+  float* dt;                    // the gradient table
+  int64_t ld_dt;
+  bool pvec;                    // gradient rows 16-byte aligned
+};
+constexpr int64_t kFillMaxRows = 1024;
+constexpr int64_t kFillBytes = int64_t(128) << 10;       // zeros per fill workgroup (target)
+// Zeros beside the plan launches, at most: about what each launch writes in
+// the time of its own work.  (Measured on MI355X for 16384 Zipf ids into
+// 32000 x 4096: 162 us for the backward, against 172 us with every zero row
+// written by the listed-rows kernel and 172 us with 192 / 128 MB beside the
+// second pass / plan_tail.)
+constexpr int64_t kFillFirstPassBytes = int64_t(64) << 20;
+constexpr int64_t kFillPassBytes = int64_t(128) << 20;
+constexpr int64_t kFillTailBytes = int64_t(96) << 20;
+constexpr int kFillUnroll = 16;
+
+// Zeros to one fp32 row of D values, by the whole workgroup.
+template <int THREADS>
+__device__ __forceinline__ void zero_row(float* __restrict__ out, int64_t D, bool pvec) {
+  for (int64_t col = int64_t(threadIdx.x) * 4; col < D; col += int64_t(THREADS) * 4) {
+    if (pvec && col + 4 <= D) {
+      store_stream<float, 4>(out + col, Vec<float, 4>{});
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (col + i < D) out[col + i] = 0.0f;
+    }
+  }
+}
+
+// sel: kFillMaxRows / 32 words of LDS.
+template <int THREADS>
+__device__ void zero_unselected_rows(const FillShare& fs, int64_t f, uint32_t* sel) {
+  const int32_t* __restrict__ idx = fs.idx;
+  const int64_t M = fs.M, D = fs.D, ld_dt = fs.ld_dt;
+  float* __restrict__ dt = fs.dt;
+  const bool pvec = fs.pvec;
+  const int64_t a = fs.r0 + f * fs.rows;
+  const int64_t e = a + fs.rows < fs.r1 ? a + fs.rows : fs.r1;
+  if (a >= e) return;   // uniform
+  const int n = int(e - a);
+  for (int i = threadIdx.x; i < (n + 31) / 32; i += THREADS) sel[i] = 0;
+  lds_barrier();
+  // Mark the selected rows (integer LDS atomics), kFillUnroll loads in
+  // flight per thread (positions past the end read index M - 1 again):
+  // groups of four indices when the array is 16-byte aligned, else single.
+  auto mark = [&](int32_t k) {
+    const int64_t d = int64_t(k) - a;
+    if (d >= 0 && d < n) atomicOr(&sel[d >> 5], 1u << (d & 31));
+  };
+  if (reinterpret_cast<uintptr_t>(idx) % 16 == 0) {
+    const int64_t M4 = M / 4;
+    const Vec<int32_t, 4>* idx4 = reinterpret_cast<const Vec<int32_t, 4>*>(idx);
+    for (int64_t j0 = threadIdx.x; j0 < M4; j0 += int64_t(kFillUnroll) * THREADS) {
+      Vec<int32_t, 4> k[kFillUnroll];
+#pragma unroll
+      for (int u = 0; u < kFillUnroll; ++u) {
+        const int64_t j = j0 + int64_t(u) * THREADS;
+        k[u] = idx4[j < M4 ? j : M4 - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kFillUnroll; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mark(k[u].v[i]);
+    }
+    for (int64_t j = 4 * M4 + threadIdx.x; j < M; j += THREADS) mark(idx[j]);
+  } else {
+    for (int64_t j0 = threadIdx.x; j0 < M; j0 += int64_t(kFillUnroll) * THREADS) {
+      int32_t k[kFillUnroll];
+#pragma unroll
+      for (int u = 0; u < kFillUnroll; ++u) {
+        const int64_t j = j0 + int64_t(u) * THREADS;
+        k[u] = idx[j < M ? j : M - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kFillUnroll; ++u) mark(k[u]);
+    }
+  }
+  lds_barrier();
+  for (int r = 0; r < n; ++r)
+    if (!((sel[r >> 5] >> (r & 31)) & 1u)) zero_row<THREADS>(dt + (a + r) * ld_dt, D, pvec);
+}
+
 // zero / nzero: the first pass also zero-fills the run bounds (2 (V + 1)
 // entries) and the invalid count for the plan_tail kernel that follows.  The
 // workgroup exchanges data only through LDS (its sorted keys are read by the
@@ -237,18 +335,24 @@ __global__ __launch_bounds__(kSortThreads) void radix_pass_fused(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ keys_in,
     const int32_t* __restrict__ vals_in, int64_t M, int64_t V, int shift,
     int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int32_t* __restrict__ zero,
-    int64_t nzero, int32_t* __restrict__ n_invalid) {
+    int64_t nzero, int32_t* __restrict__ n_invalid, FillShare fs) {
   // Digit counts in four copies (by lane mod 4): keys concentrated on a few
   // digits then collide on one LDS address four times less often.
   __shared__ int32_t all[4][kDigits], before[4][kDigits], base[kDigits];
   __shared__ int32_t wave_cnt[kSortWaves][kDigits];
   __shared__ int32_t wsum[kSortWaves];
+  static_assert(4 * kDigits >= kFillMaxRows / 32, "fill bitmap fits in all[][]");
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int64_t b = blockIdx.x;
+  const int64_t nb = (M + kSortBlock - 1) / kSortBlock;   // the sort's own workgroups
+  if (b >= nb) {
+    zero_unselected_rows<kSortThreads>(fs, b - nb, reinterpret_cast<uint32_t*>(&all[0][0]));
+    return;
+  }
   const int64_t lo = b * kSortBlock;
   if (zero != nullptr) {
-    for (int64_t i = b * kSortThreads + threadIdx.x; i < nzero; i += int64_t(gridDim.x) * kSortThreads)
+    for (int64_t i = b * kSortThreads + threadIdx.x; i < nzero; i += nb * kSortThreads)
       zero[i] = 0;
     if (b == 0 && threadIdx.x == 0 && n_invalid != nullptr) *n_invalid = 0;
   }
@@ -344,9 +448,15 @@ __global__ __launch_bounds__(kSortThreads) void radix_pass_fused(
 __global__ __launch_bounds__(kPlanThreads) void plan_tail(
     const int32_t* __restrict__ sk, int64_t M, int64_t V, int32_t* __restrict__ seg_begin,
     int32_t* __restrict__ seg_end, int32_t* __restrict__ chunk_off, int32_t* __restrict__ owner,
-    int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid) {
+    int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid,
+    FillShare fs) {
   __shared__ int32_t wmin[kPlanWaves];
   __shared__ int32_t wsum[kPlanWaves];
+  __shared__ uint32_t sel[kFillMaxRows / 32];
+  if (blockIdx.x > 0) {   // the plan is workgroup 0; the others write zero rows
+    zero_unselected_rows<kPlanThreads>(fs, int64_t(blockIdx.x) - 1, sel);
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
@@ -614,26 +724,27 @@ __global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
 }
 
 // Stage B from the list of selected rows (plans of M <= kPlanMaxM).  When
-// writing (not accumulating) the even workgroups loop over the (listed row,
-// column chunk) pairs and the odd ones write zeros to the rows never
-// selected (a run of length zero), so that the latency-bound sums and the
-// bandwidth-bound zero rows run side by side; when accumulating every
-// workgroup takes listed pairs and the other rows are left as they are.
-// Needs gridDim.x >= 2.  (Measured on MI355X for 16384 Zipf ids into
-// 32000 x 4096: 106 us with 32768 workgroups; the pairs first and the zero
-// rows after them in every workgroup, 132 us; one workgroup per table row
-// and column chunk, 128 us.)
+// the share fs holds rows to zero-fill (writing, not accumulating), the even
+// workgroups loop over the (listed row, column chunk) pairs and the odd ones
+// write zeros to the share's rows never selected (an empty run), so that the
+// latency-bound sums and the bandwidth-bound zero rows run side by side; the
+// rows before the share were zero-filled beside the plan.  Otherwise every
+// workgroup takes listed pairs.  Needs gridDim.x >= 2.  (Measured on MI355X
+// for 16384 Zipf ids into 32000 x 4096, all zero rows here: 99-106 us with
+// 32768 workgroups; the pairs first and the zero rows after them in every
+// workgroup, 132 us; one workgroup per table row and column chunk, 128 us.)
 template <typename T, int VEC, int U, bool PVEC>
 __global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
     const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
     const int32_t* __restrict__ chunk_off, const float* __restrict__ Q, int64_t ldq, int64_t D,
-    int64_t V, const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows, int64_t cb,
-    float* __restrict__ dt, int64_t ld_dt, int accumulate) {
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows, int64_t cb,
+    float* __restrict__ dt, int64_t ld_dt, int accumulate, FillShare fs) {
   const int64_t b = blockIdx.x;
-  if (accumulate || b % 2 == 0) {
-    const int64_t me = accumulate ? b : b / 2;
-    const int64_t stride = accumulate ? int64_t(gridDim.x) : int64_t(gridDim.x + 1) / 2;
+  const bool split = fs.r1 > fs.r0;
+  if (!split || b % 2 == 0) {
+    const int64_t me = split ? b / 2 : b;
+    const int64_t stride = split ? int64_t(gridDim.x + 1) / 2 : int64_t(gridDim.x);
     const int64_t items = int64_t(*n_rows) * cb;
     for (int64_t it = me; it < items; it += stride) {
       const int64_t col = (it % cb) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
@@ -644,20 +755,8 @@ __global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
     return;
   }
   const int64_t stride = int64_t(gridDim.x) / 2;
-  for (int64_t v = b / 2; v < V; v += stride) {
-    if (seg_end[v] != seg_begin[v]) continue;   // a selected row (uniform)
-    float* out = dt + v * ld_dt;
-    for (int64_t col = int64_t(threadIdx.x) * VEC; col < D; col += int64_t(kSortThreads) * VEC) {
-      if (PVEC && D - col >= VEC && VEC % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < VEC; i += 4) store_stream<float, 4>(out + col + i, Vec<float, 4>{});
-      } else {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i)
-          if (col + i < D) out[col + i] = 0.0f;
-      }
-    }
-  }
+  for (int64_t v = fs.r0 + b / 2; v < fs.r1; v += stride)
+    if (seg_end[v] == seg_begin[v]) zero_row<kSortThreads>(dt + v * ld_dt, D, PVEC);   // uniform
 }
 
 // Forward: workgroup (m, c) copies the columns of chunk c of x[idx[m]] to
@@ -715,7 +814,8 @@ hipError_t scatter_typed(const void* dy, int64_t ld_dy, const int32_t* pos, cons
                          const int32_t* end, const int32_t* chunk_off, const int32_t* owner,
                          float* Q, int64_t ldq, int64_t nq_max, int64_t V, int64_t D,
                          const int32_t* rows, const int32_t* n_rows, float* dt, int64_t ld_dt,
-                         int accumulate, bool vec, bool pvec, hipStream_t s) {
+                         int accumulate, bool vec, bool pvec, const FillShare& fill_listed,
+                         hipStream_t s) {
   // Four columns per lane: each lane's fp32 results are one 16-byte store,
   // so a wave's stores cover 1 KB contiguously (eight 16-bit columns per lane
   // would leave every store instruction writing half of each 32-byte span).
@@ -738,9 +838,9 @@ hipError_t scatter_typed(const void* dy, int64_t ld_dy, const int32_t* pos, cons
     const int64_t want = 2 * V * int64_t(cb);
     const unsigned gl = unsigned(want < 2 ? 2 : (want < kListedGrid ? want : kListedGrid));
 #define VJP_LISTED(VV, PV)                                                                      \
-  scatter_listed_rows<T, VV, U, PV><<<gl, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end,      \
-                                                                chunk_off, Q, ldq, D, V, rows, \
-                                                                n_rows, cb, dt, ld_dt, accumulate)
+  scatter_listed_rows<T, VV, U, PV><<<gl, kSortThreads, 0, s>>>(                              \
+      g, ld_dy, pos, beg, end, chunk_off, Q, ldq, D, rows, n_rows, cb, dt, ld_dt, accumulate,   \
+      fill_listed)
     if (vec && pvec)
       VJP_LISTED(V4, true);
     else if (vec)
@@ -862,24 +962,51 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
   int32_t* rows = bk;
   int32_t* n_rows = hist;
   hipError_t e;
-  if (M > 0 && M <= kPlanMaxM) {
-    const int passes = gather_sort_passes(V);
+  const int64_t nq_max = M > kRun ? gather_max_chunks(M) : 0;
+  const bool listed = M > 0 && M <= kPlanMaxM;
+  // Zero rows beside the plan: when writing, each radix pass and plan_tail
+  // take up to a fixed number of bytes of the zero rows, in order of rows,
+  // and the listed-rows kernel the rest.  A FillShare with r0 = r1 fills
+  // nothing.
+  const int passes = listed ? gather_sort_passes(V) : 0;
+  const bool fill_rows = listed && !accumulate && V > 0 && D > 0;
+  int64_t per = (kFillBytes / 4 + D - 1) / (D > 0 ? D : 1);
+  per = per < 1 ? 1 : (per > kFillMaxRows ? kFillMaxRows : per);
+  int64_t cursor = 0;   // next unassigned row
+  // bytes: the most zeros this launch takes (-1: all the rest); wide: its
+  // workgroups have kPlanThreads threads, and take four times the rows.
+  auto share = [&](int64_t bytes, bool wide) {
+    const int64_t rows = wide ? (4 * per < kFillMaxRows ? 4 * per : kFillMaxRows) : per;
+    FillShare f{cursor, cursor, rows, 0, idx, M, D, dt, ld_dt, pvec};
+    if (fill_rows) {
+      const int64_t budget = bytes < 0 ? V : (bytes / 4 + D - 1) / D;
+      f.r1 = V - cursor < budget ? V : cursor + budget;
+      f.groups = (f.r1 - f.r0 + rows - 1) / rows;
+      cursor = f.r1;
+    }
+    return f;
+  };
+  if (listed) {
     const int32_t* ik = nullptr;
     const int32_t* iv = nullptr;
     for (int p = 0; p < passes; ++p) {
       int32_t* ok = p == passes - 1 ? sk : (p % 2 == 0 ? ak : bk);
       int32_t* ov = p == passes - 1 ? sv : (p % 2 == 0 ? av : bv);
+      const FillShare f = share(p == 0 ? kFillFirstPassBytes : kFillPassBytes, false);
+      const unsigned grid = unsigned(nb + f.groups);
       if (p == 0)
-        radix_pass_fused<true><<<unsigned(nb), kSortThreads, 0, s>>>(
-            idx, ik, iv, M, V, 8 * p, ok, ov, seg_begin, 2 * (V + 1), n_invalid);
+        radix_pass_fused<true><<<grid, kSortThreads, 0, s>>>(
+            idx, ik, iv, M, V, 8 * p, ok, ov, seg_begin, 2 * (V + 1), n_invalid, f);
       else
-        radix_pass_fused<false><<<unsigned(nb), kSortThreads, 0, s>>>(
-            idx, ik, iv, M, V, 8 * p, ok, ov, nullptr, 0, nullptr);
+        radix_pass_fused<false><<<grid, kSortThreads, 0, s>>>(
+            idx, ik, iv, M, V, 8 * p, ok, ov, nullptr, 0, nullptr, f);
       ik = ok;
       iv = ov;
     }
-    plan_tail<<<1, kPlanThreads, 0, s>>>(sk, M, V, seg_begin, seg_end, chunk_off, owner,
-                                         rows, n_rows, n_invalid);
+    const FillShare f = share(kFillTailBytes, true);
+    plan_tail<<<unsigned(1 + f.groups), kPlanThreads, 0, s>>>(sk, M, V, seg_begin, seg_end,
+                                                             chunk_off, owner, rows, n_rows,
+                                                             n_invalid, f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (V == 0 || D == 0) return hipSuccess;
   } else {
@@ -888,12 +1015,11 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
         V == 0 || D == 0)
       return e;
   }
-  const int64_t nq_max = M > kRun ? gather_max_chunks(M) : 0;
-  const bool listed = M > 0 && M <= kPlanMaxM;
+  const FillShare fl = share(-1, false);   // the listed-rows kernel: the rest
 #define VJP_SC(T)                                                                            \
   scatter_typed<T>(dy, ld_dy, sv, seg_begin, seg_end, chunk_off, owner, Q, ldq, nq_max, V, D,   \
                    listed ? rows : nullptr, listed ? n_rows : nullptr, dt, ld_dt, accumulate, \
-                   vec, pvec, s)
+                   vec, pvec, fl, s)
   switch (act) {
     case kF32: return VJP_SC(float);
     case kF16: return VJP_SC(_Float16);
