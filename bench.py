@@ -19,10 +19,7 @@ time over K steps whose only instrumentation is one pair of HIP events
 around the `roofline` op (the op with the largest share of the step), on the
 stream the kernels are launched on; its `achieved` comes from those events.
 The per-op breakdown (`per_op`) comes from a separate pass with events around
-every op (those records slow each op slightly).  `copy_ceiling` times a plain
-device-to-device copy of as many bytes as the roofline op moves (half read,
-half written) in the same process: the practical ceiling for a kernel that
-reads and writes its bytes once.  `cpu_baseline` times the fp64 CPU oracle on a
+every op (those records slow each op slightly).  `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workloads on one host core.  `extras` times the
 save-the-statistics variants (softmax forward writing the row logsumexp and
 the backward rebuilding y from it; the split cross-entropy forward and
@@ -464,23 +461,6 @@ def main() -> int:
                        "elements_per_s": round(nelem / (ms * 1e-3), 1)})
     print(f"[bench] timed the statistics-saving variants ({n_extra} rounds)", file=sys.stderr, flush=True)
 
-    # Copy ceiling: a device-to-device copy (hipMemcpyAsync through torch) of
-    # as many bytes as the roofline op moves, half read and half written,
-    # timed in the same process.
-    half = dom["bytes"] // 2
-    ca = torch.empty(half, dtype=torch.uint8, device=dev)
-    cb = torch.empty_like(ca)
-    cevs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(6)]
-    for e in cevs:                        # the first copy is a warmup
-        e[0].record()
-        cb.copy_(ca)
-        e[1].record()
-    torch.cuda.synchronize()
-    ms_copy = sum(e[0].elapsed_time(e[1]) for e in cevs[1:]) / (len(cevs) - 1)
-    copy_gbs = 2 * half / (ms_copy * 1e-3) / 1e9
-    del ca, cb
-
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -518,13 +498,6 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(dom["GB/s"] / PEAK_GBS, 4),
             "traffic": traffic,
-        },
-        "copy_ceiling": {
-            "GB/s": round(copy_gbs, 1),
-            "bytes": 2 * half,
-            "kind": "device-to-device copy (torch copy_ -> hipMemcpyAsync) of the roofline "
-                    "op's bytes, half read and half written, same process",
-            "roofline_frac_of_copy": round(dom["GB/s"] / copy_gbs, 4),
         },
         "cpu_baseline": None,
     }
