@@ -133,6 +133,14 @@ def test_deterministic(gpu_lib):
     assert torch.equal(a, b)
 
 
+def test_zero_rows_across_every_launch(gpu_lib):
+    """A 70000 x 2048 fp32 gradient table (573 MB; three radix passes): its
+    never-selected rows are zero-filled partly beside each plan launch and
+    partly by the listed-rows kernel.  The table starts as NaN, so a row
+    that no launch writes fails the comparison."""
+    run_case(gpu_lib, 16384, 70000, 2048, "bf16", seed=515, kind="uniform")
+
+
 def test_full_size(gpu_lib):
     """16384 Zipf(1.2) token ids over a 32000 x 4096 bf16 table: y and every
     gradient row against the oracle."""
