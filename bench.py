@@ -19,7 +19,12 @@ time over K steps whose only instrumentation is one pair of HIP events
 around the `roofline` op (the op with the largest share of the step), on the
 stream the kernels are launched on; its `achieved` comes from those events.
 The per-op breakdown (`per_op`) comes from a separate pass with events around
-every op (those records slow each op slightly).  `cpu_baseline` times the fp64 CPU oracle on a
+every op (those records slow each op slightly); `pairs` sums it per forward +
+backward pair.  `copy_ceiling` times the library's streaming copy
+(vjp_copy) of as many bytes as the roofline op moves, half read and half
+written, in the same process: the rate at which this GPU reads and writes
+each byte once, which no kernel that moves its bytes once can beat by much;
+`frac_of_copy` compares against it.  `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workloads on one host core.  `extras` times the
 save-the-statistics variants (softmax forward writing the row logsumexp and
 the backward rebuilding y from it; the split cross-entropy forward and
@@ -45,6 +50,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd achieved HBM GB/s and % of MI355X peak; elements/s per op"
 PEAK_GBS = 8000.0          # MI355X HBM3E, published
+# Forward + backward pairs of the step (the fused cross-entropy is its own pair).
+PAIRS = [("weighted_sum", ("weighted_sum_fwd", "weighted_sum_bwd")),
+         ("scaled_silu", ("scaled_silu_fwd", "scaled_silu_bwd")),
+         ("softmax", ("softmax_fwd", "softmax_bwd")),
+         ("softmax_xent", ("softmax_xent_fwd_bwd",))]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_softmax_xent_bf16_16384x32000.json")
 
 
@@ -461,6 +471,36 @@ def main() -> int:
                        "elements_per_s": round(nelem / (ms * 1e-3), 1)})
     print(f"[bench] timed the statistics-saving variants ({n_extra} rounds)", file=sys.stderr, flush=True)
 
+    # Copy ceiling: vjp_copy (16-byte nontemporal loads and stores) of as many
+    # bytes as the roofline op moves, half read and half written, in this
+    # process: the rate at which this GPU reads and writes each byte once.
+    half = dom["bytes"] // 32 * 16
+    ca = torch.empty(half, dtype=torch.uint8, device=dev)
+    cb = torch.empty_like(ca)
+    cevs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(6)]
+    for e in cevs:                        # the first copy is a warmup
+        e[0].record()
+        st = L.vjp_copy(P(ca), P(cb), half, stream)
+        if st != 0:
+            raise RuntimeError(f"vjp_copy: status {st} ({rwb.vjp_last_error()})")
+        e[1].record()
+    torch.cuda.synchronize()
+    ms_copy = sum(e[0].elapsed_time(e[1]) for e in cevs[1:]) / (len(cevs) - 1)
+    copy_gbs = 2 * half / (ms_copy * 1e-3) / 1e9
+    del ca, cb
+
+    # Forward + backward pairs (from the per-op pass).
+    by_name = {o["op"]: o for o in per_op}
+    pairs = []
+    for pname, members in PAIRS:
+        ms = sum(by_name[m]["ms"] for m in members)
+        nbytes = sum(by_name[m]["bytes"] for m in members)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        pairs.append({"op": pname, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
+                      "frac_of_peak": round(gbs / PEAK_GBS, 4),
+                      "frac_of_copy": round(gbs / copy_gbs, 4)})
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -488,6 +528,7 @@ def main() -> int:
             "frac_of_peak": round(value / PEAK_GBS, 4),
         },
         "per_op": per_op,
+        "pairs": pairs,
         "per_op_timing": "separate pass, HIP events around every op (not the timed steps)",
         "extras": extras,
         "roofline": {
@@ -498,6 +539,12 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(dom["GB/s"] / PEAK_GBS, 4),
             "traffic": traffic,
+        },
+        "copy_ceiling": {
+            "GB/s": round(copy_gbs, 1),
+            "bytes": 2 * half,
+            "kernel": "vjp_copy (16-byte nontemporal loads and stores), same process",
+            "roofline_frac_of_copy": round(dom["GB/s"] / copy_gbs, 4),
         },
         "cpu_baseline": None,
     }

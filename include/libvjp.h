@@ -88,6 +88,14 @@ const char* vjp_status_string(int status);
 /* Text of the calling thread's last error ("" if none). */
 const char* vjp_last_error(void);
 
+/* Streaming device copy of `bytes` bytes from src to dst (device pointers,
+ * any alignment; 16-byte aligned pointers take 16-byte nontemporal accesses).
+ * Not an operation of the method: it is the measurement reference, the rate
+ * at which this chip reads and writes each byte once, against which the
+ * kernels below are judged (each of them moves its bytes once as well).
+ * bytes = 0 is valid; overlapping ranges give VJP_EALIAS. */
+int vjp_copy(const void* src, void* dst, int64_t bytes, vjp_stream_t stream);
+
 /* ---------------------------------------------------------------- weighted sum
  * y[i] = sum_j x[i, j] * w[j];  x [n_rows, d] (ld_x), w [d], y [n_rows].
  * Backward: grad_x[i, j] = dy[i] * w[j]   (elementwise map, same shape as x)

@@ -40,6 +40,7 @@ _SIGS = {
     "vjp_version": ([], _int),
     "vjp_status_string": ([_int], ctypes.c_char_p),
     "vjp_last_error": ([], ctypes.c_char_p),
+    "vjp_copy": ([_vp, _vp, _i64, _vp], _int),
     "vjp_weighted_sum_fwd": ([_vp, _i64, _vp, _vp, _i64, _i64, _int, _int, _vp], _int),
     "vjp_weighted_sum_tiling": ([_i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], ctypes.c_int),
     "vjp_weighted_sum_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
@@ -165,6 +166,18 @@ def vjp_status_string(status: int) -> str:
 
 def vjp_last_error() -> str:
     return lib.vjp_last_error().decode()
+
+
+def vjp_copy(src, dst):
+    """Copy the bytes of contiguous src into contiguous dst (same byte size,
+    same device): the streaming copy the kernels are measured against."""
+    n = _nbytes(_flat(src))
+    if _nbytes(_flat(dst)) != n:
+        raise ValueError(f"dst holds {_nbytes(dst)} bytes, src {n}")
+    if dst.device != src.device:
+        raise ValueError("src and dst must be on the same device")
+    _check(lib.vjp_copy(_ptr(src), _ptr(dst), n, _stream(src)), "vjp_copy")
+    return dst
 
 
 # ----------------------------------------------------------------- weighted sum

@@ -156,6 +156,14 @@ VJP_API const char* vjp_status_string(int status) {
 
 VJP_API const char* vjp_last_error(void) { return g_err; }
 
+VJP_API int vjp_copy(const void* src, void* dst, int64_t bytes, vjp_stream_t stream) {
+  if (bytes < 0) return fail(VJP_EINVAL, "negative size");
+  if (bytes == 0) return ok();
+  if (!src || !dst) return fail(VJP_EINVAL, "NULL pointer");
+  VJP_TRY(check_alias({span(dst, bytes, "dst")}, {span(src, bytes, "src")}));
+  return hip_status(launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "copy");
+}
+
 // ------------------------------------------------------------------ weighted sum
 
 VJP_API int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,

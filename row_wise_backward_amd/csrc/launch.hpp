@@ -20,6 +20,9 @@ hipError_t launch_reduce_partials_split(const float* P, int64_t T, int64_t d, fl
                                         float* out2, int64_t split, int accumulate,
                                         hipStream_t s);
 
+// Streaming device copy of `bytes` bytes (the measurement reference).
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 // Weighted sum.
 hipError_t launch_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
                                    int64_t n, int64_t d, int act, int wdt, bool vec,

@@ -322,3 +322,12 @@ def test_gather_queries_and_rejections():
     assert bwd(acc=5) == EINVAL
     assert bwd(ninv=C + 2) == EALIGN
     assert bwd(ninv=D + 8) == EALIAS                        # count inside the workspace
+
+
+def test_copy_rejections():
+    assert L.vjp_copy(P(A), P(B), -1, None) == EINVAL
+    assert L.vjp_copy(None, P(B), 16, None) == EINVAL
+    assert L.vjp_copy(P(A), None, 16, None) == EINVAL
+    assert L.vjp_copy(P(A), P(A + 8), 16, None) == EALIAS      # overlapping ranges
+    assert L.vjp_copy(P(A + 8), P(A), 16, None) == EALIAS
+    assert L.vjp_copy(None, None, 0, None) == OK               # nothing to do
