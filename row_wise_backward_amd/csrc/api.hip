@@ -171,6 +171,7 @@ VJP_API int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, voi
                                  vjp_stream_t stream) {
   if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n_rows < 0 || d < 0) return fail(VJP_EINVAL, "negative size");
+  if (n_rows > kMaxElems || d > kMaxElems) return fail(VJP_EINVAL, "size too large");
   const int es = dtype_size(act), ws = dtype_size(w_dtype);
   VJP_TRY(check_matrix("x", x, n_rows, d, ld_x, es));
   VJP_TRY(check_vector("w", w, d, ws));
@@ -208,6 +209,7 @@ VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, co
                                  vjp_stream_t stream) {
   if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n_rows < 0 || d < 0 || rows_per_tile < 0) return fail(VJP_EINVAL, "negative size");
+  if (n_rows > kMaxElems || d > kMaxElems) return fail(VJP_EINVAL, "size too large");
   if (rows_per_tile > kMaxRowsPerTile) return fail(VJP_EINVAL, "rows_per_tile above 2^30");
   if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
   const int es = dtype_size(act), ws = dtype_size(w_dtype);

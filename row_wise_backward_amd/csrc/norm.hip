@@ -331,11 +331,15 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
 // partials of its columns in fp32 registers besides x and dy), so rows of
 // up to 16 waves * 64 lanes * 16 = 16384 columns are supported.
 constexpr int kLaneElems = 16;
-// Forward measured on MI355X for 32768 x 4096 bf16: one row per workgroup
-// with vector parameter loads (RMSNorm 92 us, LayerNorm 108-117 us) beats
-// workgroups that loop over rows with the parameters held in registers
-// (127 us) and matches two or four rows per workgroup (108-156 us).
-constexpr int kFwdRowsPerBlock = 1;
+// Rows per workgroup of the forward with 16-bit parameters (rows of 2 to 16
+// waves with at most two vectors per lane; wider rows would hold too many
+// registers).  Measured on MI355X for 32768 x 4096 bf16 with bf16
+// parameters: LayerNorm 101 us with one row per workgroup, 97 us with two
+// (w and b read once per two rows), 111 us with four; RMSNorm 90 us with
+// one, 91 us with two.  Workgroups that loop over rows with the parameters
+// held in registers measured 127 us.  (The bias loads cost LayerNorm 11 us:
+// 89-90 us without them.)
+template <bool RMS> constexpr int kFwdRowsPerBlock = RMS ? 1 : 2;
 
 template <typename T, int VEC, int WAVES, int K, bool RMS>
 bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, bool pvec, T* yp,
@@ -345,14 +349,18 @@ bool fwd_try(const T* xp, int64_t ld_x, const void* w, const void* b, int wdt, b
     return false;
   } else {
     if (int64_t(WAVES) * kWave * K * VEC < cols) return false;
-    constexpr int RB = WAVES == 1 ? 1 : kFwdRowsPerBlock;
-    const int64_t per = WAVES == 1 ? rows_per_block<1>() : RB;
-    const unsigned grid = unsigned((rows + per - 1) / per);
+    // fp32 parameters stay at one row per workgroup (two rows would take
+    // 96-107 VGPRs).
+    constexpr int RB2 = (WAVES == 1 || K > 2) ? 1 : kFwdRowsPerBlock<RMS>;
+    auto grid = [&](int rb) {
+      const int64_t per = WAVES == 1 ? rows_per_block<1>() : rb;
+      return unsigned((rows + per - 1) / per);
+    };
     if (wdt == kF32)
-      norm_fwd_resident<T, VEC, WAVES, K, RMS, RB, 4><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+      norm_fwd_resident<T, VEC, WAVES, K, RMS, 1, 4><<<grid(1), row_block_threads<WAVES>(), 0, s>>>(
           xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps);
     else
-      norm_fwd_resident<T, VEC, WAVES, K, RMS, RB, 2><<<grid, row_block_threads<WAVES>(), 0, s>>>(
+      norm_fwd_resident<T, VEC, WAVES, K, RMS, RB2, 2><<<grid(RB2), row_block_threads<WAVES>(), 0, s>>>(
           xp, ld_x, w, b, wdt, pvec, yp, ld_y, mean, rstd, rows, cols, eps);
     return true;
   }

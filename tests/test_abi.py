@@ -108,6 +108,7 @@ def test_weighted_sum_fwd_rejections():
     assert _ws_fwd(y=A + 64) == EALIAS                    # y inside x
     assert _ws_fwd(y=B + 8) == EALIAS                     # y inside w
     assert "overlaps" in rwb.vjp_last_error()
+    assert _ws_fwd(n=1 << 62, d=0, ld=0) == EINVAL        # no byte count can overflow
 
 
 def _ws_bwd(**kw):

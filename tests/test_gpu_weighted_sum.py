@@ -134,6 +134,17 @@ def test_empty_batch(gpu_lib):
     assert bool((dw == 0.0).all())
 
 
+def test_zero_width_rows(gpu_lib):
+    """d = 0: every y is an empty sum (0), grad_x and grad_w are empty."""
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
+    w = torch.empty(0, dtype=torch.bfloat16, device=DEV)
+    y = torch.full((5,), 7.0, dtype=torch.bfloat16, device=DEV)
+    gpu_lib.vjp_weighted_sum_fwd(x, w, y=y)
+    dx, dw = gpu_lib.vjp_weighted_sum_bwd(torch.ones(5, dtype=torch.bfloat16, device=DEV), x, w)
+    torch.cuda.synchronize()
+    assert bool((y == 0).all()) and dx.shape == (5, 0) and dw.shape == (0,)
+
+
 def test_large_batch_full_size(gpu_lib):
     """The 1,048,576 x 256 bf16 workload in the benchmark's launch configuration:
     grad_w and every tile partial in full, y and grad_x on sampled rows."""
