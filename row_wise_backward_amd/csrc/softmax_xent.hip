@@ -238,7 +238,11 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream(
 // 32000 16-bit logits run best recomputing the exponentials; keeping them in
 // fp32 VGPRs cuts the waves per SIMD from 5 to 3 (484-498 us against 364 us),
 // and keeping them rounded to bf16 in place of the stored row did not help
-// either (the exponentials are not what limits this kernel).  The
+// either (the exponentials are not what limits this kernel), nor did one
+// workgroup exchange per row instead of two (each wave's max and sum merged
+// online: 360-373 us against 359-361 us), nor a persistent kernel staging its
+// next row in LDS by direct loads while computing the current one (446-490
+// us); a plain copy of the same bytes takes 344-351 us.  The
 // statistics-only form never keeps the exponentials (an online max / sum
 // folding each vector as it arrives measured slower: 217 us against 189 us
 // for the read of 16384 x 32000 bf16).
