@@ -209,7 +209,7 @@ def cpu_baseline(scale: float = 1.0, min_seconds: float = 10.0):
     return {
         "value": round(total_bytes / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": 1 if limiter is not None else os.cpu_count(),   # BLAS threads unlimited without it
         "kind": "oracle",
         "sample": (f"fwd+bwd of scaled_silu n={n_silu}, weighted_sum {n_ws}x256, softmax "
                    f"{r_sm}x4096, softmax_xent {r_xe}x32000 (same distributions and seeds), "
