@@ -21,7 +21,7 @@ import test_gpu_softmax_xent_split as txs
 import test_gpu_weighted_sum as tw
 
 pytestmark = pytest.mark.gpu
-N_CASES = 32
+N_CASES = 96
 ACTS = ["f32", "f16", "bf16"]
 
 
