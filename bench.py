@@ -20,7 +20,9 @@ around the `roofline` op (the op with the largest share of the step), on the
 stream the kernels are launched on; its `achieved` comes from those events.
 The per-op breakdown (`per_op`) comes from a separate pass with events around
 every op (those records slow each op slightly); `pairs` sums it per forward +
-backward pair.  `copy_ceiling` times the library's streaming copy
+backward pair.  `per_op_cold` / `pairs_cold` time each op alone after 1 GiB
+of writes that evict L2 and the 256 MB Infinity Cache (no op finds its
+inputs, or an earlier op's pending write-back, in a cache).  `copy_ceiling` times the library's streaming copy
 (vjp_copy) of as many bytes as the roofline op moves, half read and half
 written, in the same process: the rate at which this GPU reads and writes
 each byte once, which no kernel that moves its bytes once can beat by much;
@@ -361,7 +363,32 @@ def main() -> int:
                        "frac_of_peak": round(gbs / PEAK_GBS, 4),
                        "elements_per_s": round(nelem / (ms * 1e-3), 1)})
     i_dom = max(range(len(ops)), key=lambda i: per_op[i]["ms"])
-    print(f"[bench] per-op pass done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    # Cold per-op pass: before every op, 1 GiB of writes evicts L2 and the
+    # 256 MB Infinity Cache, so no op finds its inputs, or the write-back of
+    # an earlier op's outputs, in a cache.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    n_cold = max(3, args.steps // 2)
+    cold_evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                 for _ in ops] for _ in range(n_cold)]
+    for k in range(n_cold):
+        for i, (name, fn, a, _, _) in enumerate(ops):
+            flush.fill_(k % 251)
+            cold_evs[k][i][0].record()
+            st = fn(*a)
+            if st != 0:
+                raise RuntimeError(f"{name}: status {st} ({rwb.vjp_last_error()})")
+            cold_evs[k][i][1].record()
+    torch.cuda.synchronize()
+    del flush
+    per_op_cold = []
+    for i, (name, _, _, nbytes, nelem) in enumerate(ops):
+        ms = sum(cold_evs[k][i][0].elapsed_time(cold_evs[k][i][1]) for k in range(n_cold)) / n_cold
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        per_op_cold.append({"op": name, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
+                            "frac_of_peak": round(gbs / PEAK_GBS, 4),
+                            "elements_per_s": round(nelem / (ms * 1e-3), 1)})
+    print(f"[bench] per-op passes done; timing {args.steps} steps", file=sys.stderr, flush=True)
 
     # The timed region: K steps with HIP events around the roofline kernel only
     # (on its launch stream), bracketed by device synchronisations.
@@ -490,16 +517,21 @@ def main() -> int:
     copy_gbs = 2 * half / (ms_copy * 1e-3) / 1e9
     del ca, cb
 
-    # Forward + backward pairs (from the per-op pass).
-    by_name = {o["op"]: o for o in per_op}
-    pairs = []
-    for pname, members in PAIRS:
-        ms = sum(by_name[m]["ms"] for m in members)
-        nbytes = sum(by_name[m]["bytes"] for m in members)
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        pairs.append({"op": pname, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
-                      "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                      "frac_of_copy": round(gbs / copy_gbs, 4)})
+    # Forward + backward pairs (from the per-op passes).
+    def pair_figures(rows):
+        by_name = {o["op"]: o for o in rows}
+        out = []
+        for pname, members in PAIRS:
+            ms = sum(by_name[m]["ms"] for m in members)
+            nbytes = sum(by_name[m]["bytes"] for m in members)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out.append({"op": pname, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
+                        "frac_of_peak": round(gbs / PEAK_GBS, 4),
+                        "frac_of_copy": round(gbs / copy_gbs, 4)})
+        return out
+
+    pairs = pair_figures(per_op)
+    pairs_cold = pair_figures(per_op_cold)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -530,6 +562,9 @@ def main() -> int:
         "per_op": per_op,
         "pairs": pairs,
         "per_op_timing": "separate pass, HIP events around every op (not the timed steps)",
+        "per_op_cold": per_op_cold,
+        "pairs_cold": pairs_cold,
+        "per_op_cold_timing": "each op alone after 1 GiB of writes that evict L2 and the Infinity Cache",
         "extras": extras,
         "roofline": {
             "kernel": dom["op"],
