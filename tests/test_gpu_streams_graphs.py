@@ -154,3 +154,51 @@ def test_graph_capture_replays_bitwise(gpu_lib):
             st.out[k].fill_(1 + rep)
         graph.replay()
         _same(refs[seed], st.snapshot())
+
+
+def test_graph_scatter_add_zero_rows_across_launches(gpu_lib):
+    """A 40000 x 2048 fp32 gradient table (328 MB): its never-selected rows are
+    zero-filled partly beside each plan launch and partly by the listed-rows
+    kernel.  Captured once, replayed with new indices and dy (the table
+    poisoned between replays), every replay equals the eager result bit for
+    bit."""
+    M, V, D = 6000, 40000, 2048
+    idx = torch.empty(M, dtype=torch.int32, device=DEV)
+    dy = torch.empty((M, D), dtype=BF16, device=DEV)
+    dt = torch.empty((V, D), dtype=F32, device=DEV)
+    ninv = torch.empty(1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(gpu_lib.vjp_gather_rows_bwd_workspace_size(M, V, D), dtype=torch.uint8,
+                     device=DEV)
+
+    def load(seed):
+        idx.copy_(torch.from_numpy(synth.zipf_indices(M, V, seed)).to(DEV))
+        dy.copy_(synth.normal_device((M, D), 1.0, "bf16", seed, 0, DEV))
+
+    def run():
+        gpu_lib.vjp_gather_rows_bwd(dy, idx, V, dtable=dt, n_invalid=ninv, workspace=ws)
+
+    refs = {}
+    for seed in (31, 32):
+        load(seed)
+        dt.fill_(float("nan"))
+        run()
+        torch.cuda.synchronize()
+        refs[seed] = dt.clone()
+        assert not torch.isnan(refs[seed]).any()
+    load(31)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for seed in (32, 31, 32):
+        load(seed)
+        dt.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dt.view(torch.int32), refs[seed].view(torch.int32)), seed
