@@ -40,9 +40,11 @@ def _compare(out_gpu, z64, t, scale, act, rows_idx=None, ws_rows=None, name="xen
     return ref, reps
 
 
-def run_case(rwb, rows, C, act, seed, sigma=2.0, ld=None, offset=0, targets=None, scale=None):
+def run_case(rwb, rows, C, act, seed, sigma=2.0, ld=None, offset=0, targets=None, scale=None,
+             z=None):
     print(f"\n[softmax_xent] rows={rows} C={C} act={act} ld={ld} off={offset}", flush=True)
-    z = synth.normal((rows, C), sigma, act, seed, synth.STREAM_X)
+    if z is None:
+        z = synth.normal((rows, C), sigma, act, seed, synth.STREAM_X)
     t = synth.targets(rows, C, seed) if targets is None else np.asarray(targets, np.int32)
     z64 = synth.to_f64(z, act)
     scale = 1.0 / rows if scale is None else scale
@@ -67,6 +69,21 @@ def run_case(rwb, rows, C, act, seed, sigma=2.0, ld=None, offset=0, targets=None
     for r in reps:
         print("   ", r, flush=True)
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+
+
+def spread_rows(C, act, seed):
+    """Rows whose logits span 100 to 200 natural-log units: the smallest
+    probabilities, and the gradients scale * p, fall in the subnormal range
+    of fp32 / bf16 (no flush to zero on any path), beside a normal row."""
+    g = np.random.default_rng(seed)
+    z = np.empty((5, C), np.float32)
+    z[0] = np.linspace(-100.0, 0.0, C)
+    z[1] = np.linspace(-140.0, 10.0, C)
+    z[2] = np.linspace(-90.0, -80.0, C)
+    z[2, C // 2] = 0.0
+    z[3] = g.standard_normal(C) * 2
+    z[4] = np.linspace(-200.0, 0.0, C)
+    return synth.f32_to_storage(g.permutation(z, axis=1), act)
 
 
 COLS16 = [1, 2, 7, 1000, 4095, 4096, 32000, 32768, 40000, 70000]
@@ -160,3 +177,9 @@ def test_full_size(gpu_lib):
     for r in reps:
         print("   ", r, flush=True)
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+
+
+@pytest.mark.parametrize("C", [1000, 32000, 40000])
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+def test_subnormal_probabilities(gpu_lib, C, act):
+    run_case(gpu_lib, 5, C, act, seed=120 + C, z=spread_rows(C, act, 120 + C))

@@ -52,10 +52,11 @@ def _dz_tols(z64, t, L32, dloss, act):
 
 
 def run_case(rwb, rows, C, act, seed, sigma=2.0, ld=None, offset=0, targets=None, dloss=1.0,
-             in_place=False):
+             in_place=False, z=None):
     print(f"\n[xent split] rows={rows} C={C} act={act} ld={ld} off={offset} dloss={dloss} "
           f"in_place={in_place}", flush=True)
-    z = synth.normal((rows, C), sigma, act, seed, synth.STREAM_X)
+    if z is None:
+        z = synth.normal((rows, C), sigma, act, seed, synth.STREAM_X)
     t = synth.targets(rows, C, seed) if targets is None else np.asarray(targets, np.int32)
     z64 = synth.to_f64(z, act)
     zd = padded(z, act, ld, offset)
@@ -84,6 +85,21 @@ def run_case(rwb, rows, C, act, seed, sigma=2.0, ld=None, offset=0, targets=None
     for r in reps:
         print("   ", r, flush=True)
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+
+
+def spread_rows(C, act, seed):
+    """Rows whose logits span 100 to 200 natural-log units: the smallest
+    probabilities, and the gradients scale * p, fall in the subnormal range
+    of fp32 / bf16 (no flush to zero on any path), beside a normal row."""
+    g = np.random.default_rng(seed)
+    z = np.empty((5, C), np.float32)
+    z[0] = np.linspace(-100.0, 0.0, C)
+    z[1] = np.linspace(-140.0, 10.0, C)
+    z[2] = np.linspace(-90.0, -80.0, C)
+    z[2, C // 2] = 0.0
+    z[3] = g.standard_normal(C) * 2
+    z[4] = np.linspace(-200.0, 0.0, C)
+    return synth.f32_to_storage(g.permutation(z, axis=1), act)
 
 
 COLS16 = [1, 2, 7, 1000, 4095, 4096, 32000, 32768, 40000, 70000]
@@ -204,3 +220,9 @@ def test_full_size(gpu_lib):
     for r in reps:
         print("   ", r, flush=True)
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+
+
+@pytest.mark.parametrize("C", [1000, 32000, 40000])
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+def test_subnormal_probabilities(gpu_lib, C, act):
+    run_case(gpu_lib, 5, C, act, seed=220 + C, z=spread_rows(C, act, 220 + C))
