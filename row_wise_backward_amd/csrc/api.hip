@@ -531,8 +531,10 @@ VJP_API int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* 
 namespace {
 
 // Backward tiles: rows are dealt round-robin to at most kNormTiles workgroups.
-// Measured on MI355X for 32768 x 4096 bf16: 512 tiles (two 8-wave workgroups
-// per CU) 164 us, 1024 tiles 179 us, 2048 tiles 205 us.
+// Measured on MI355X for 32768 x 4096 bf16 (LayerNorm / RMSNorm, one process):
+// 512 tiles of 8 waves x 1 vector per lane (two workgroups per CU)
+// 143-154 / 132-133 us; 256, 768, 1024 and 1536 tiles 151-198 / 140-198 us;
+// 4 waves x 2 vectors 155-176 / 141-153 us; 16 waves 189-207 us.
 constexpr int64_t kNormTiles = 512;
 
 int64_t norm_tiles(int64_t rows) { return rows < kNormTiles ? rows : kNormTiles; }
