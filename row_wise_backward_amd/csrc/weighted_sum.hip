@@ -124,6 +124,11 @@ __global__ __launch_bounds__(kThreads) void ws_fwd_kernel(const T* __restrict__ 
   }
 }
 
+// Row groups per step of a grad_x writer workgroup (their dy values loaded
+// together: 182-185 us against 184-192 us one group at a time, 1048576 x 256
+// bf16 with 32768 writers, one process).
+constexpr int kWriterUnroll = 4;
+
 // Backward stage 1.  grad_x = dy (x) w needs no x, so it is written by its
 // own workgroups while others read x for grad_w: workgroups g < readers
 // form the partials, the rest write grad_x, side by side, so a pure read
@@ -161,15 +166,26 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
     float wr[VEC];
     load_params<VEC>(w, col, d, wdt, wr);
     const int64_t me = int64_t(blockIdx.x) - readers, writers = int64_t(gridDim.x) - readers;
+    // kWriterUnroll row groups per step: their dy values are loaded together
+    // (rows past the end read dy[n - 1] and store nothing).
     const int64_t group = int64_t(kWavesPerBlock) * G;
-    for (int64_t r0 = me * group; r0 < n; r0 += writers * group) {
-      const int64_t row = r0 + int64_t(wave) * G + sub;
-      if (row < n && cols_left > 0) {
-        const float g = to_f32(dy[row]);
-        float gx[VEC];
+    for (int64_t r0 = me * group; r0 < n; r0 += kWriterUnroll * writers * group) {
+      T gv[kWriterUnroll];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) gx[i] = g * wr[i];
-        store_f32_tail<T, VEC>(dx + row * ld_dx + col, cols_left, gx);
+      for (int u = 0; u < kWriterUnroll; ++u) {
+        const int64_t row = r0 + u * writers * group + int64_t(wave) * G + sub;
+        gv[u] = dy[row < n ? row : n - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kWriterUnroll; ++u) {
+        const int64_t row = r0 + u * writers * group + int64_t(wave) * G + sub;
+        if (row < n && cols_left > 0) {
+          const float g = to_f32(gv[u]);
+          float gx[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) gx[i] = g * wr[i];
+          store_f32_tail<T, VEC>(dx + row * ld_dx + col, cols_left, gx);
+        }
       }
     }
     return;
