@@ -263,3 +263,55 @@ def test_training_steps_against_oracle_chain(ag):
     for r in reps:
         print("   ", r, flush=True)
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+
+
+def test_training_steps_norm_softmax_weighted_sum(ag):
+    """Five SGD steps through LayerNorm -> softmax (saving the row logsumexp)
+    -> weighted sum under a mean squared error against fixed targets r,
+    against the same steps chained by hand through the oracle in fp64: the
+    losses and the LayerNorm weight and bias and the weighted-sum weights
+    agree to 1e-4 (relative L2)."""
+    B, D, lr, eps = 64, 96, 0.5, 1e-5
+    g = np.random.default_rng(4343)
+    X = g.standard_normal((B, D)) * 2 + 0.5
+    r = g.standard_normal(B)
+    p64 = {"w": 1 + 0.1 * g.standard_normal(D), "b": 0.1 * g.standard_normal(D),
+           "v": g.standard_normal(D)}
+    params = {k: torch.tensor(v, dtype=torch.float32, device=DEV, requires_grad=True)
+              for k, v in p64.items()}
+    Xd = torch.tensor(X, dtype=torch.float32, device=DEV)
+    X32 = Xd.cpu().numpy().astype(np.float64)   # the oracle sees the same fp32 input
+    rd = torch.tensor(r, dtype=torch.float32, device=DEV)
+    r32 = rd.cpu().numpy().astype(np.float64)
+    gpu_losses, ref_losses = [], []
+    for _ in range(5):
+        for t in params.values():
+            t.grad = None
+        h = ag.layer_norm(Xd, params["w"], params["b"], eps)
+        p = ag.softmax(h, save="lse")
+        y = ag.weighted_sum(p, params["v"])
+        loss = ((y - rd) ** 2).mean()
+        loss.backward()
+        gpu_losses.append(float(loss.item()))
+        with torch.no_grad():
+            for t in params.values():
+                t -= lr * t.grad
+        P = {k: v.astype(np.float64) for k, v in p64.items()}
+        h64, _, _ = oracle.norms.layernorm_fwd(X32, P["w"], P["b"], eps)
+        y_sm = oracle.softmax.fwd(h64)
+        y64 = oracle.weighted_sum.fwd(y_sm, P["v"])
+        ref_losses.append(float(np.mean((y64 - r32) ** 2)))
+        dp, dv = oracle.weighted_sum.bwd(2.0 * (y64 - r32) / B, y_sm, P["v"])
+        dh = oracle.softmax.bwd(dp, y_sm)
+        _, dw, db = oracle.norms.layernorm_bwd(dh, X32, P["w"], eps)
+        grads = {"w": dw, "b": db, "v": dv}
+        p64 = {k: P[k] - lr * grads[k] for k in P}
+    print("\n    losses gpu", np.round(gpu_losses, 6), "\n    losses ref", np.round(ref_losses, 6),
+          flush=True)
+    assert ref_losses[-1] < ref_losses[0]
+    reps = [reduced(np.array(gpu_losses), np.array(ref_losses), name="losses")]
+    for k in p64:
+        reps.append(reduced(params[k].detach().cpu().numpy().astype(np.float64), p64[k], name=k))
+    for r_ in reps:
+        print("   ", r_, flush=True)
+    assert all(r_.ok for r_ in reps), [str(r_) for r_ in reps if not r_.ok]
