@@ -82,7 +82,7 @@ def test_worked_tiling_case(gpu_lib):
 
 
 SHAPES = [(1, 1), (7, 7), (7, 64), (1, 256), (333, 256), (1000, 100), (257, 600), (64, 1030),
-          (2049, 33)]
+          (2049, 33), (9, 8193), (3, 50001)]
 DTYPES = [("f32", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32"),
           ("f32", "bf16")]
 
