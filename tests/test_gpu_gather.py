@@ -80,7 +80,7 @@ def run_case(rwb, M, V, D, act, seed, kind="zipf", ld=None, offset=0, accumulate
 # separate kernels: both sides of the boundary are covered.
 CASES = [(1, 1, 1), (7, 5, 3), (1000, 37, 64), (2048, 300, 2049), (5000, 32000, 100),
          (3000, 70000, 40), (4097, 1, 16), (16384, 3000, 48), (16385, 3000, 48),
-         (40000, 70000, 24)]
+         (40000, 70000, 24), (50, 20, 70001)]
 
 
 @pytest.mark.parametrize("M,V,D", CASES)
