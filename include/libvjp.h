@@ -138,7 +138,7 @@ size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d, int64_t ro
  * s = 64, 32, ..., 1; finally dw[j] = v[0] (or dw[j] + v[0]).  For d = 1 the
  * order of vjp_scaled_silu_bwd's dw applies.  Within a tile each partial is
  * accumulated in fp32 in an order fixed by the tiling, so the whole result is
- * bitwise reproducible. */
+ * bitwise reproducible.  d at most 4194240 (VJP_EINVAL beyond). */
 int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
                          void* dx, int64_t ld_dx, float* dw, int accumulate,
                          int64_t n_rows, int64_t d, int64_t rows_per_tile,
@@ -333,7 +333,7 @@ int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, 
  * indices as V) and the positions m in sorted order [M] right after them,
  * then sort buffers, a digit table, run bounds, chunk bookkeeping and fp32
  * chunk sums; size from vjp_gather_rows_bwd_workspace_size.  M and V must be
- * below 2^31 - 1. */
+ * below 2^31 - 1, D at most 16776960. */
 size_t vjp_gather_rows_bwd_workspace_size(int64_t M, int64_t V, int64_t D);
 
 int vjp_gather_rows_fwd(const void* table, int64_t ld_t, int64_t V, int64_t D,

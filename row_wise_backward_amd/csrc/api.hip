@@ -38,6 +38,12 @@ int hip_status(hipError_t e, const char* what) {
 
 // Sizes beyond this are rejected so that no element offset can overflow int64.
 constexpr int64_t kMaxElems = int64_t(1) << 46;
+// Widest rows of the ops whose launches put column blocks in the second grid
+// dimension (at most 65535 blocks): the weighted-sum backward (blocks of 64
+// columns in its narrowest form) and the row gather / scatter-add (blocks of
+// 256 columns).
+constexpr int64_t kWsMaxCols = int64_t(65535) * 64;
+constexpr int64_t kGatherMaxCols = int64_t(65535) * 256;
 // Rows per launch of the row kernels (keeps every grid far below 2^31 threads).
 constexpr int64_t kRowsPerLaunch = int64_t(1) << 20;
 
@@ -210,6 +216,7 @@ VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, co
   if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n_rows < 0 || d < 0 || rows_per_tile < 0) return fail(VJP_EINVAL, "negative size");
   if (n_rows > kMaxElems || d > kMaxElems) return fail(VJP_EINVAL, "size too large");
+  if (d > kWsMaxCols) return fail(VJP_EINVAL, "d above %lld", (long long)kWsMaxCols);
   if (rows_per_tile > kMaxRowsPerTile) return fail(VJP_EINVAL, "rows_per_tile above 2^30");
   if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
   const int es = dtype_size(act), ws = dtype_size(w_dtype);
@@ -699,6 +706,7 @@ VJP_API int vjp_gather_rows_fwd(const void* table, int64_t ld_t, int64_t V, int6
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (V < 0 || D < 0 || M < 0) return fail(VJP_EINVAL, "negative size");
   if (M > INT32_MAX || V >= INT32_MAX) return fail(VJP_EINVAL, "M or V beyond int32");
+  if (D > kGatherMaxCols) return fail(VJP_EINVAL, "D above %lld", (long long)kGatherMaxCols);
   const int es = dtype_size(act);
   VJP_TRY(check_matrix("table", table, V, D, ld_t, es));
   VJP_TRY(check_vector("idx", idx, M, 4));
@@ -719,6 +727,7 @@ VJP_API int vjp_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* id
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (V < 0 || D < 0 || M < 0) return fail(VJP_EINVAL, "negative size");
   if (M > INT32_MAX || V >= INT32_MAX) return fail(VJP_EINVAL, "M or V beyond int32");
+  if (D > kGatherMaxCols) return fail(VJP_EINVAL, "D above %lld", (long long)kGatherMaxCols);
   if (accumulate != 0 && accumulate != 1) return fail(VJP_EINVAL, "accumulate must be 0 or 1");
   const int es = dtype_size(act);
   VJP_TRY(check_matrix("dy", dy, M, D, ld_dy, es));

@@ -118,18 +118,25 @@ __global__ __launch_bounds__(kThreads) void silu_bwd_kernel(
 constexpr int kFwdUnroll = 8;
 constexpr int kBwdUnroll = 2;
 
+// Elements per forward launch (a multiple of every elements-per-workgroup
+// value, so chunks keep the 16-byte alignment of vectorised pointers).
+constexpr int64_t kFwdLaunchElems = int64_t(1) << 30;
+
 template <typename T>
 hipError_t fwd_typed(const void* x, const float* w, void* y, int64_t n, bool vec,
                      hipStream_t s) {
   constexpr int V = 16 / sizeof(T);
   const int64_t epb = int64_t(kThreads) * (vec ? V : 1) * kFwdUnroll;
-  const dim3 grid(unsigned((n + epb - 1) / epb));
-  if (vec)
-    silu_fwd_kernel<T, V, kFwdUnroll><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), w,
-                                                    static_cast<T*>(y), n, epb);
-  else
-    silu_fwd_kernel<T, 1, kFwdUnroll><<<grid, kThreads, 0, s>>>(static_cast<const T*>(x), w,
-                                                    static_cast<T*>(y), n, epb);
+  for (int64_t off = 0; off < n; off += kFwdLaunchElems) {
+    const int64_t m = n - off < kFwdLaunchElems ? n - off : kFwdLaunchElems;
+    const dim3 grid(unsigned((m + epb - 1) / epb));
+    const T* xp = static_cast<const T*>(x) + off;
+    T* yp = static_cast<T*>(y) + off;
+    if (vec)
+      silu_fwd_kernel<T, V, kFwdUnroll><<<grid, kThreads, 0, s>>>(xp, w, yp, m, epb);
+    else
+      silu_fwd_kernel<T, 1, kFwdUnroll><<<grid, kThreads, 0, s>>>(xp, w, yp, m, epb);
+  }
   return hipGetLastError();
 }
 

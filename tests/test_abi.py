@@ -109,6 +109,8 @@ def test_weighted_sum_fwd_rejections():
     assert _ws_fwd(y=B + 8) == EALIAS                     # y inside w
     assert "overlaps" in rwb.vjp_last_error()
     assert _ws_fwd(n=1 << 62, d=0, ld=0) == EINVAL        # no byte count can overflow
+    assert _ws_bwd(n=1, d=65535 * 64 + 1, ld=65535 * 64 + 1, ldd=65535 * 64 + 1) == EINVAL
+    assert "d above" in rwb.vjp_last_error()
 
 
 def _ws_bwd(**kw):
@@ -313,6 +315,8 @@ def test_gather_queries_and_rejections():
     assert fwd(idx=B + 2) == EALIGN
     assert fwd(act=7) == EDTYPE
     assert fwd(V=1 << 31) == EINVAL
+    assert L.vjp_gather_rows_fwd(P(A), 1 << 24, 1, (1 << 24), P(B), 1, P(C), 1 << 24, 2,
+                                 None) == EINVAL                   # D above 65535 * 256
     assert fwd(M=0) == OK                                   # nothing to do
     bwd = lambda **k: L.vjp_gather_rows_bwd(P(A), 64, P(B), 20, 10, 64, P(k.get("dt", C)), 64,
                                             k.get("acc", 0), P(k.get("ninv", None)), 2,

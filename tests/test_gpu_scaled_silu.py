@@ -117,3 +117,27 @@ def test_full_size(gpu_lib, n):
     x = synth.normal((n,), c.sigma_x, c.dtype, c.seed, synth.STREAM_X)
     dy = synth.normal((n,), c.sigma_dy, c.dtype, c.seed, synth.STREAM_DY)
     check(gpu_lib, x, dy, c.w_value, c.dtype, name="scaled_silu full")
+
+
+def test_forward_past_one_launch(gpu_lib):
+    """n = 2^30 + 4099 fp16 elements: the forward runs as two launches of at
+    most 2^30 elements; y is compared with the oracle on every element of a
+    window around the boundary, at both ends, and on 100000 random positions."""
+    n = (1 << 30) + 4099
+    print(f"\n[scaled_silu forward past one launch] n={n}", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(777)
+    x = torch.randn(n, generator=gen, device=DEV, dtype=torch.float32).mul_(2.0).to(torch.float16)
+    w = torch.tensor([0.75], dtype=torch.float32, device=DEV)
+    y = gpu_lib.vjp_scaled_silu_fwd(x, w)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(777)
+    b = 1 << 30
+    pos = np.concatenate([np.arange(0, 4096), np.arange(b - 8192, n), np.arange(n - 4096, n),
+                          g.integers(0, n, size=100000)])
+    pos_d = torch.from_numpy(pos).to(DEV)
+    x64 = synth.to_f64(to_host(x[pos_d], "f16"), "f16")
+    ref = sl.fwd(x64, 0.75)
+    rep = pointwise(to_host(y[pos_d], "f16"), ref, "f16", name="y")
+    print("   ", rep, flush=True)
+    assert rep.ok
+    del x, y
