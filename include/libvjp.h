@@ -248,7 +248,8 @@ int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32_t* targ
  * synchronisation), divided by rows in fp32.  Rows with an invalid target
  * get no one-hot term.  dlogits may be the logits buffer itself (same
  * pointer and leading dimension: computed in place); any other overlap is
- * VJP_EALIAS. */
+ * VJP_EALIAS.  classes at most 268431360 (65535 blocks of 4096 columns),
+ * else VJP_EINVAL. */
 int vjp_softmax_xent_fwd(const void* logits, int64_t ld, const int32_t* targets, int64_t rows,
                          int64_t classes, int act, float* loss, float* row_max, float* row_lse,
                          int32_t* n_invalid, void* workspace, size_t workspace_bytes,

@@ -44,6 +44,10 @@ constexpr int64_t kMaxElems = int64_t(1) << 46;
 // 256 columns).
 constexpr int64_t kWsMaxCols = int64_t(65535) * 64;
 constexpr int64_t kGatherMaxCols = int64_t(65535) * 256;
+// Widest rows of the split cross-entropy backward, which also puts column
+// blocks in the second grid dimension: 4096 columns a block when its rows are
+// not 16-byte aligned (1024 threads x 4 elements).
+constexpr int64_t kXentBwdMaxClasses = int64_t(65535) * 4096;
 // Rows per launch of the row kernels (keeps every grid far below 2^31 threads).
 constexpr int64_t kRowsPerLaunch = int64_t(1) << 20;
 
@@ -504,7 +508,8 @@ VJP_API int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* 
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (rows < 0 || classes < 0) return fail(VJP_EINVAL, "negative size");
   if (classes == 0) return fail(VJP_EINVAL, "cross-entropy over zero classes");
-  if (classes > INT32_MAX) return fail(VJP_EINVAL, "classes beyond int32 targets");
+  if (classes > kXentBwdMaxClasses)
+    return fail(VJP_EINVAL, "classes above %lld", (long long)kXentBwdMaxClasses);
   const int es = dtype_size(act);
   VJP_TRY(check_matrix("logits", logits, rows, classes, ld, es));
   VJP_TRY(check_vector("targets", targets, rows, 4));

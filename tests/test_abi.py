@@ -225,6 +225,9 @@ def test_softmax_xent_split_rejections():
     assert _xent_bwd(dz=C) == EALIAS                      # over row_lse
     assert _xent_bwd(rlse=0) == EINVAL
     assert _xent_bwd(rows=0) == OK                        # nothing to do, nothing launched
+    wide = 65535 * 4096                                   # 65535 column blocks of 4096
+    assert _xent_bwd(rows=0, C=wide, ld=wide, ldd=wide) == OK
+    assert _xent_bwd(rows=0, C=wide + 1, ld=wide + 1, ldd=wide + 1) == EINVAL
 
 
 def test_binding_host_guards():
