@@ -26,7 +26,8 @@ inputs, or an earlier op's pending write-back, in a cache).  `copy_ceiling` time
 (vjp_copy) of as many bytes as the roofline op moves, half read and half
 written, in the same process: the rate at which this GPU reads and writes
 each byte once, which no kernel that moves its bytes once can beat by much;
-`frac_of_copy` compares against it.  `cpu_baseline` times the fp64 CPU oracle on a
+`frac_of_copy` compares against it; `frac_of_matched_copy` compares each
+pair with copies of each of its ops' own byte counts, one launch per op.  `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same workloads on one host core.  `extras` times the
 save-the-statistics variants (softmax forward writing the row logsumexp and
 the backward rebuilding y from it; the split cross-entropy forward and
@@ -515,7 +516,29 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_copy = sum(e[0].elapsed_time(e[1]) for e in cevs[1:]) / (len(cevs) - 1)
     copy_gbs = 2 * half / (ms_copy * 1e-3) / 1e9
-    del ca, cb
+
+    # Size-matched copies: a copy of each op's own byte count (half read, half
+    # written) in its own launch, so that a small op is compared with a copy
+    # that pays the same launch and ramp costs.  Successive copies move
+    # through the buffers, so a small copy does not find its source in a cache.
+    copy_ms_cache = {}
+
+    def copy_ms(nbytes):
+        n = min(nbytes // 32 * 16, half)
+        if n not in copy_ms_cache:
+            evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                   for _ in range(6)]
+            for k, e in enumerate(evs):
+                off = (k * n) % (half - n + 16) // 16 * 16
+                e[0].record()
+                st = L.vjp_copy(ctypes.c_void_p(ca.data_ptr() + off),
+                               ctypes.c_void_p(cb.data_ptr() + off), n, stream)
+                if st != 0:
+                    raise RuntimeError(f"vjp_copy: status {st} ({rwb.vjp_last_error()})")
+                e[1].record()
+            torch.cuda.synchronize()
+            copy_ms_cache[n] = sum(e[0].elapsed_time(e[1]) for e in evs[1:]) / (len(evs) - 1)
+        return copy_ms_cache[n]
 
     # Forward + backward pairs (from the per-op passes).
     def pair_figures(rows):
@@ -525,13 +548,17 @@ def main() -> int:
             ms = sum(by_name[m]["ms"] for m in members)
             nbytes = sum(by_name[m]["bytes"] for m in members)
             gbs = nbytes / (ms * 1e-3) / 1e9
+            ms_matched = sum(copy_ms(by_name[m]["bytes"]) for m in members)
             out.append({"op": pname, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
                         "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                        "frac_of_copy": round(gbs / copy_gbs, 4)})
+                        "frac_of_copy": round(gbs / copy_gbs, 4),
+                        "matched_copy_ms": round(ms_matched, 5),
+                        "frac_of_matched_copy": round(ms_matched / ms, 4)})
         return out
 
     pairs = pair_figures(per_op)
     pairs_cold = pair_figures(per_op_cold)
+    del ca, cb
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
