@@ -1,0 +1,48 @@
+"""Host-side pieces of bench.py: the one-GPU guard, the byte models and the
+CPU oracle baseline (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""          # no JSON line for an unsupported run
+
+
+@pytest.mark.parametrize("es", [2, 4])
+def test_byte_models_count_each_tensor_once(es):
+    # Every model is at least the bytes of the tensors the op must read and
+    # write once, and at most that plus its small fp32 side arrays.
+    r, c = 16384, 32000
+    big = 2 * r * c * es                            # logits read + dlogits written
+    assert big <= bench.bytes_xent(r, c, es) <= big + 64 * r
+    assert r * c * es <= bench.bytes_xent_fwd(r, c, es) <= r * c * es + 64 * r
+    assert big <= bench.bytes_xent_bwd(r, c, es) <= big + 64 * r
+    assert bench.bytes_softmax_fwd(r, c, es) == 2 * r * c * es
+    assert bench.bytes_softmax_bwd(r, c, es) == 3 * r * c * es
+    n, d, T = 1 << 20, 256, 2048
+    base = 2 * n * d * es                           # x read, grad_x written
+    wsb = bench.bytes_weighted_sum_bwd(n, d, T, es, es)
+    assert base + 2 * T * d * 4 <= wsb <= base + 2 * T * d * 4 + 8 * n + 8 * d
+    M, V, D = 65536, 128000, 1024
+    assert bench.bytes_gather_bwd(M, V, D, es) == M * D * es + V * D * 4 + 4 * M
+
+
+def test_cpu_baseline_small_sample():
+    out = bench.cpu_baseline(scale=0.01, min_seconds=0.0)
+    assert out["kind"] == "oracle" and out["unit"] == "GB/s"
+    assert out["value"] > 0 and out["cores"] >= 1
+    assert "repetitions" in out["sample"]
+    json.dumps(out)                                  # serialisable into the bench line
