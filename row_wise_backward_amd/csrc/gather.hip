@@ -248,8 +248,9 @@ constexpr int64_t kFillBytes = int64_t(128) << 10;       // zeros per fill workg
 // Zeros beside the plan launches, at most: about what each launch writes in
 // the time of its own work.  (Measured on MI355X for 16384 Zipf ids into
 // 32000 x 4096: 162 us for the backward, against 172 us with every zero row
-// written by the listed-rows kernel and 172 us with 192 / 128 MB beside the
-// second pass / plan_tail.)
+// written by the listed-rows kernel, 172 us with 192 / 128 MB beside the
+// second pass / plan_tail, and 182 us with 96 MB more beside the chunk sums
+// of long runs, whose own work streams dy.)
 constexpr int64_t kFillFirstPassBytes = int64_t(64) << 20;
 constexpr int64_t kFillPassBytes = int64_t(128) << 20;
 constexpr int64_t kFillTailBytes = int64_t(96) << 20;
