@@ -139,6 +139,8 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
     row_reduce_sum_n<WAVES, RB>(mean, buf[0]);
 #pragma unroll
     for (int q = 0; q < RB; ++q) mean[q] *= inv_cols;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) fence_row<T, VEC, K>(raw[q]);   // convert again below
   }
   float rstd[RB];
 #pragma unroll
@@ -160,6 +162,8 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void norm_fwd_resident(
   row_reduce_sum_n<WAVES, RB>(rstd, buf[1]);
 #pragma unroll
   for (int q = 0; q < RB; ++q) rstd[q] = 1.0f / __builtin_sqrtf(rstd[q] * inv_cols + eps);
+#pragma unroll
+  for (int q = 0; q < RB; ++q) fence_row<T, VEC, K>(raw[q]);
 
 #pragma unroll
   for (int q = 0; q < RB; ++q) {
@@ -338,7 +342,10 @@ constexpr int kLaneElems = 16;
 // (w and b read once per two rows), 111 us with four; RMSNorm 90 us with
 // one, 91 us with two.  Workgroups that loop over rows with the parameters
 // held in registers measured 127 us.  (The bias loads cost LayerNorm 11 us:
-// 89-90 us without them.)
+// 89-90 us without them.)  Those figures predate the register fences between
+// the phases of the forward: with them LayerNorm's two-row form holds 64
+// VGPRs instead of 80 (eight waves per SIMD instead of six) and took 96 us.
+// The same fences in the backward raised its VGPRs and were left out.
 template <bool RMS> constexpr int kFwdRowsPerBlock = RMS ? 1 : 2;
 
 template <typename T, int VEC, int WAVES, int K, bool RMS>
