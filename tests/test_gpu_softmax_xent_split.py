@@ -37,18 +37,21 @@ def _check_fwd(out, ws_rows, z64, t, has_max=True):
     return ref, reps
 
 
-def _dz_tols(z64, t, L32, dloss, act):
-    R, C = z64.shape
-    scale = dloss / R
-    p = np.exp(z64 - xe.fwd(z64, t)["row_lse"][:, None])
-    onehot = np.zeros_like(p)
-    valid = (t >= 0) & (t < C)
-    onehot[np.arange(R)[valid], t[valid]] = 1.0
-    a = (z64 - L32[:, None]) * np.log2(np.e)
+def _dz_tols_at(z_cols, cols, t, lse64, L32, scale):
+    """Scale S and floor F of dlogits at columns `cols` (z_cols = z[:, cols])
+    given the exact row lse and the fp32 lse the kernel was handed."""
+    p = np.exp(z_cols - lse64[:, None])
+    onehot = (np.asarray(cols)[None, :] == np.asarray(t)[:, None]).astype(np.float64)
+    a = (z_cols - L32[:, None]) * np.log2(np.e)
     delta = 4 * U32 * (2 + np.abs(a) + np.abs(L32)[:, None])
     S = np.abs(scale) * (p + onehot) * np.maximum(1.0, (delta + 8 * U32) / 1e-5)
     F = 16 * U32 * np.abs(scale) * onehot + np.abs(scale) * p * delta
     return S, F
+
+
+def _dz_tols(z64, t, L32, dloss, act):
+    R, C = z64.shape
+    return _dz_tols_at(z64, np.arange(C), t, xe.fwd(z64, t)["row_lse"], L32, dloss / R)
 
 
 def run_case(rwb, rows, C, act, seed, sigma=2.0, ld=None, offset=0, targets=None, dloss=1.0,
@@ -226,3 +229,30 @@ def test_full_size(gpu_lib):
 @pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
 def test_subnormal_probabilities(gpu_lib, C, act):
     run_case(gpu_lib, 5, C, act, seed=220 + C, z=spread_rows(C, act, 220 + C))
+
+
+def test_widest_rows_unaligned(gpu_lib):
+    """One row of 268431360 bf16 classes (the widest the split backward takes:
+    65535 column blocks of 4096) starting 2 bytes past a 16-byte boundary, so
+    the one-element-per-load form runs with every column block of the launch.
+    dlogits on sampled columns (every block's first and last column, the
+    target, random ones) against the oracle run on the whole row."""
+    C = 65535 * 4096
+    t = np.array([C - 3], np.int32)
+    print(f"\n[xent split widest] C={C}", flush=True)
+    z = synth.normal((1, C), 2.0, "bf16", 911, synth.STREAM_X)
+    zd = padded(z, "bf16", offset=1)
+    z64 = synth.to_f64(z, "bf16")
+    ref = xe.fwd_bwd(z64, t, 1.0)                 # one row: scale = dloss / rows = 1
+    L32 = ref["row_lse"].astype(np.float32)
+    dz = gpu_lib.vjp_softmax_xent_bwd(zd, torch.from_numpy(t).to(DEV), torch.from_numpy(L32).to(DEV),
+                                      torch.ones(1, device=DEV))
+    starts = np.arange(0, C, 4096)
+    cols = np.unique(np.concatenate([starts, starts + 4095, t,
+                                     np.random.default_rng(5).integers(0, C, 200000)]))
+    got = to_host(dz, "bf16")[:, cols]
+    del dz, zd
+    S, F = _dz_tols_at(z64[:, cols], cols, t, ref["row_lse"], L32, 1.0)
+    r = pointwise(got, ref["dz"][:, cols], "bf16", S=S, floor=F, name="dlogits(sampled)")
+    print("   ", r, flush=True)
+    assert r.ok, str(r)
