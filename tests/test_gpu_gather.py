@@ -159,3 +159,10 @@ def test_full_size(gpu_lib):
     r = pointwise(to_host(dt, "f32"), dt_ref, "f32", S=S, name="dtable")
     print("   ", r, flush=True)
     assert r.ok and int(n.item()) == n_inv == 0
+
+
+def test_widest_rows_unaligned(gpu_lib):
+    """D = 16776960, the widest the gather and scatter-add take: 65535 column
+    blocks of 256 in the one-element-per-load form (rows 2 bytes past a
+    16-byte boundary), forward and backward."""
+    run_case(gpu_lib, 3, 2, 65535 * 256, "bf16", 978, kind="uniform", offset=1)

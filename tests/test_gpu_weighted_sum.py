@@ -191,3 +191,9 @@ def test_large_batch_full_size(gpu_lib):
     assert r_y.ok and r_dx.ok and r_P.ok and r_dw.ok
     # determinism: two calls, bitwise identical
     assert torch.equal(dw, dw2) and torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+
+
+def test_widest_rows_unaligned(gpu_lib):
+    """d = 4194240, the widest the backward takes: 65535 column blocks of 64
+    in its one-element-per-load form (rows 2 bytes past a 16-byte boundary)."""
+    run_case(gpu_lib, 3, 65535 * 64, "bf16", "bf16", 977, offset=1)
