@@ -344,8 +344,10 @@ constexpr int kLaneElems = 16;
 // held in registers measured 127 us.  (The bias loads cost LayerNorm 11 us:
 // 89-90 us without them.)  Those figures predate the register fences between
 // the phases of the forward: with them LayerNorm's two-row form holds 64
-// VGPRs instead of 80 (eight waves per SIMD instead of six) and took 96 us.
-// The same fences in the backward raised its VGPRs and were left out.
+// VGPRs instead of 80 (eight waves per SIMD instead of six) and took 96 us;
+// RMSNorm with two rows (47 VGPRs) took 92 us against 90 us with one, and
+// LayerNorm with four rows needs 90 VGPRs.  The same fences in the backward
+// raised its VGPRs and were left out.
 template <bool RMS> constexpr int kFwdRowsPerBlock = RMS ? 1 : 2;
 
 template <typename T, int VEC, int WAVES, int K, bool RMS>
