@@ -223,6 +223,9 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
 
   // The next row of the tile is loaded while the current one is processed
   // (while a lane holds at most 8 values of a row; wider rows load in turn).
+  // Without it LayerNorm's backward holds 69 VGPRs instead of 79 (seven
+  // waves per SIMD instead of six) and measured the same, 153 us against
+  // 152-158 us at 32768 x 4096 bf16.
   constexpr bool kPrefetch = K * VEC <= 8;
   constexpr int KN = kPrefetch ? K : 1;
   Vec<T, VEC> rx[K], rg[K], nx[KN], ng[KN];
