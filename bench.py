@@ -159,64 +159,151 @@ def bytes_gather_bwd(M, V, D, es=2):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
+# The fp64 CPU oracle timed on the host's cores.  The sample's inputs are
+# drawn once and written to memory-mapped files; worker processes (started
+# fresh, BLAS and OpenMP limited to one thread each) load them and run the
+# oracle's forward and backward over chunks of rows or elements.  The
+# chunking only spreads the work: every chunk calls the oracle functions as
+# they are.  The one-core leg is the same with one worker.
 
-def cpu_baseline(scale: float = 1.0, min_seconds: float = 10.0):
-    """The oracle (fp64 numpy, one thread) on a bounded sample of each workload."""
+_CPU = {}   # the memory-mapped sample, per worker process
+
+
+def _cpu_worker_init(folder):
     import numpy as np
 
+    for name in ("silu_x", "silu_g", "ws_x", "ws_w", "ws_g", "sm_x", "sm_g", "xe_z", "xe_t"):
+        _CPU[name] = np.load(os.path.join(folder, name + ".npy"), mmap_mode="r")
+
+
+def _cpu_task(task):
+    """One chunk of the sample through the oracle: (op, lo, hi) rows or elements."""
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
-    except Exception:  # pragma: no cover
-        limiter = None
-    n_silu = int((1 << 23) * scale)
-    n_ws = int(131072 * scale)
-    r_sm = int(4096 * scale)
-    r_xe = int(1024 * scale)
-    # inputs first (not timed), then the oracle: decode to fp64, forward, backward
-    x = synth.normal((n_silu,), 2.0, "f16", 1001, 0)
-    g = synth.normal((n_silu,), 1.0, "f16", 1001, 2)
-    xw = synth.normal((n_ws, 256), 1.0, "bf16", 1002, 0)
-    ww = synth.normal((256,), 0.1, "bf16", 1002, 1)
-    gw = synth.normal((n_ws,), 1.0, "bf16", 1002, 2)
-    xs = synth.normal((r_sm, 4096), 3.0, "bf16", 1003, 0)
-    gs = synth.normal((r_sm, 4096), 1.0, "bf16", 1003, 2)
-    z = synth.normal((r_xe, 32000), 2.0, "bf16", 1004, 0)
-    t = synth.targets(r_xe, 32000, 1004)
-    total_bytes = (bytes_silu_fwd(n_silu) + bytes_silu_bwd(n_silu, 1)
-                   + bytes_weighted_sum_fwd(n_ws, 256) + bytes_weighted_sum_bwd(n_ws, 256, 1)
-                   + bytes_softmax_fwd(r_sm, 4096) + bytes_softmax_bwd(r_sm, 4096)
-                   + bytes_xent(r_xe, 32000))
-    # the whole sample is repeated until at least `min_seconds` of CPU work is timed
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        x64, g64 = synth.to_f64(x, "f16"), synth.to_f64(g, "f16")
+
+    op, lo, hi = task
+    c = _CPU
+    if op == "silu":
+        x64, g64 = synth.to_f64(c["silu_x"][lo:hi], "f16"), synth.to_f64(c["silu_g"][lo:hi], "f16")
         oracle.scaled_silu.fwd(x64, 0.75)
         oracle.scaled_silu.bwd(g64, x64, 0.75)
-        xw64, ww64, gw64 = synth.to_f64(xw, "bf16"), synth.to_f64(ww, "bf16"), synth.to_f64(gw, "bf16")
-        oracle.weighted_sum.fwd(xw64, ww64)
-        oracle.weighted_sum.bwd(gw64, xw64, ww64)
-        ys = oracle.softmax.fwd(synth.to_f64(xs, "bf16"))
-        oracle.softmax.bwd(synth.to_f64(gs, "bf16"), ys)
-        oracle.softmax_xent.fwd_bwd(synth.to_f64(z, "bf16"), t, 1.0 / 16384)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    total_bytes *= reps
-    if limiter is not None and hasattr(limiter, "unregister"):
-        limiter.unregister()
+    elif op == "ws":
+        x64, w64 = synth.to_f64(c["ws_x"][lo:hi], "bf16"), synth.to_f64(c["ws_w"], "bf16")
+        g64 = synth.to_f64(c["ws_g"][lo:hi], "bf16")
+        oracle.weighted_sum.fwd(x64, w64)
+        oracle.weighted_sum.bwd(g64, x64, w64)
+    elif op == "softmax":
+        y = oracle.softmax.fwd(synth.to_f64(c["sm_x"][lo:hi], "bf16"))
+        oracle.softmax.bwd(synth.to_f64(c["sm_g"][lo:hi], "bf16"), y)
+    elif op == "xent":
+        oracle.softmax_xent.fwd_bwd(synth.to_f64(c["xe_z"][lo:hi], "bf16"),
+                                    np_array(c["xe_t"][lo:hi]), 1.0 / 16384)
+    return hi - lo
+
+
+def np_array(a):
+    import numpy as np
+
+    return np.array(a)
+
+
+def cpu_cores() -> int:
+    """Cores this process may run on, at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(scale: float = 1.0, min_seconds: float = 10.0, cores: int | None = None):
+    """The oracle (fp64 numpy) on a bounded sample of each workload: on all
+    cores (one worker process per core) and on one core."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    import synth
+
+    n_silu = max(1 << 16, int((1 << 23) * scale))
+    n_ws = max(1024, int(131072 * scale))
+    r_sm = max(64, int(4096 * scale))
+    r_xe = max(16, int(1024 * scale))
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    folder = tempfile.mkdtemp(prefix="vjp_oracle_", dir=shm)
+    try:
+        arrays = {
+            "silu_x": synth.normal((n_silu,), 2.0, "f16", 1001, 0),
+            "silu_g": synth.normal((n_silu,), 1.0, "f16", 1001, 2),
+            "ws_x": synth.normal((n_ws, 256), 1.0, "bf16", 1002, 0),
+            "ws_w": synth.normal((256,), 0.1, "bf16", 1002, 1),
+            "ws_g": synth.normal((n_ws,), 1.0, "bf16", 1002, 2),
+            "sm_x": synth.normal((r_sm, 4096), 3.0, "bf16", 1003, 0),
+            "sm_g": synth.normal((r_sm, 4096), 1.0, "bf16", 1003, 2),
+            "xe_z": synth.normal((r_xe, 32000), 2.0, "bf16", 1004, 0),
+            "xe_t": synth.targets(r_xe, 32000, 1004),
+        }
+        for name, a in arrays.items():
+            np.save(os.path.join(folder, name + ".npy"), a)
+        del arrays
+        sample_bytes = (bytes_silu_fwd(n_silu) + bytes_silu_bwd(n_silu, 1)
+                        + bytes_weighted_sum_fwd(n_ws, 256) + bytes_weighted_sum_bwd(n_ws, 256, 1)
+                        + bytes_softmax_fwd(r_sm, 4096) + bytes_softmax_bwd(r_sm, 4096)
+                        + bytes_xent(r_xe, 32000))
+        tasks = ([("silu", i, min(i + (1 << 19), n_silu)) for i in range(0, n_silu, 1 << 19)]
+                 + [("ws", i, min(i + 8192, n_ws)) for i in range(0, n_ws, 8192)]
+                 + [("softmax", i, min(i + 256, r_sm)) for i in range(0, r_sm, 256)]
+                 + [("xent", i, min(i + 64, r_xe)) for i in range(0, r_xe, 64)])
+        # big chunks first, so the last ones to finish are small
+        tasks.sort(key=lambda t: -(t[2] - t[1]) * {"silu": 1, "ws": 256, "softmax": 4096,
+                                                   "xent": 32000}[t[0]])
+
+        def timed(n_workers):
+            saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                    "MKL_NUM_THREADS")}
+            for k in saved:
+                os.environ[k] = "1"
+            try:
+                ctx = mp.get_context("spawn")
+                with ctx.Pool(n_workers, initializer=_cpu_worker_init, initargs=(folder,)) as pool:
+                    # warm up (imports, file maps); every wait is bounded
+                    pool.map_async(_cpu_task, [("silu", 0, 1)] * n_workers, chunksize=1).get(300)
+                    reps = 0
+                    t0 = time.perf_counter()
+                    while True:
+                        pool.map_async(_cpu_task, tasks, chunksize=1).get(600)
+                        reps += 1
+                        dt = time.perf_counter() - t0
+                        if dt >= min_seconds:
+                            break
+            finally:
+                for k, v in saved.items():
+                    if v is None:
+                        os.environ.pop(k, None)
+                    else:
+                        os.environ[k] = v
+            return sample_bytes * reps / dt / 1e9, reps, dt
+
+        n = cores or cpu_cores()
+        v_all, reps_all, dt_all = timed(n)
+        v_one, reps_one, dt_one = timed(1)
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    sample = (f"fwd+bwd of scaled_silu n={n_silu}, weighted_sum {n_ws}x256, softmax {r_sm}x4096, "
+              f"softmax_xent {r_xe}x32000 (the workloads' distributions and seeds; "
+              f"{sample_bytes / 1e9:.3f} GB of algorithmic bytes: {scale:g} x 1/2, 1/8, 1/8 and "
+              f"1/16 of the four workloads), fp64 numpy with input decode, in "
+              f"{len(tasks)} chunks of rows or elements")
     return {
-        "value": round(total_bytes / dt / 1e9, 4),
+        "value": round(v_all, 4),
         "unit": "GB/s",
-        "cores": 1 if limiter is not None else os.cpu_count(),   # BLAS threads unlimited without it
+        "cores": n,
         "kind": "oracle",
-        "sample": (f"fwd+bwd of scaled_silu n={n_silu}, weighted_sum {n_ws}x256, softmax "
-                   f"{r_sm}x4096, softmax_xent {r_xe}x32000 (same distributions and seeds), "
-                   f"fp64 numpy, input decode included; {reps} repetitions, {dt:.1f} s"),
+        "sample": sample + f"; {n} worker processes, {reps_all} passes in {dt_all:.1f} s",
+        "one_core": {"value": round(v_one, 4), "unit": "GB/s", "cores": 1,
+                     "timing": f"one worker process, {reps_one} passes in {dt_one:.1f} s"},
     }
 
 

@@ -67,6 +67,8 @@ extern "C" {
 
 #define VJP_VERSION 1
 
+/* Storage dtype of activations (act) and parameters (w_dtype).  Passed as
+   this int-sized enum; a value outside it returns VJP_EDTYPE. */
 typedef enum { VJP_F32 = 0, VJP_F16 = 1, VJP_BF16 = 2 } vjp_dtype_t;
 
 typedef enum {
@@ -96,6 +98,14 @@ const char* vjp_last_error(void);
  * bytes = 0 is valid; overlapping ranges give VJP_EALIAS. */
 int vjp_copy(const void* src, void* dst, int64_t bytes, vjp_stream_t stream);
 
+/* vjp_copy with its launch shape given: vectors_per_lane 16-byte vectors in
+ * flight per lane (1, 2, 4 or 8; vjp_copy uses 4) and a grid of at most
+ * max_workgroups workgroups of 256 lanes looping over the data (vjp_copy:
+ * 32768).  For sweeps of the copy reference over launch shapes; other values
+ * give VJP_EINVAL.  Same pointers, alignment and aliasing rules as vjp_copy. */
+int vjp_copy_shaped(const void* src, void* dst, int64_t bytes, int vectors_per_lane,
+                    int64_t max_workgroups, vjp_stream_t stream);
+
 /* ---------------------------------------------------------------- weighted sum
  * y[i] = sum_j x[i, j] * w[j];  x [n_rows, d] (ld_x), w [d], y [n_rows].
  * Backward: grad_x[i, j] = dy[i] * w[j]   (elementwise map, same shape as x)
@@ -107,7 +117,7 @@ int vjp_copy(const void* src, void* dst, int64_t bytes, vjp_stream_t stream);
 
 /* x, y, dy, dx in `act`; w in `w_dtype`.  y has n_rows elements in `act`. */
 int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
-                         int64_t n_rows, int64_t d, int act, int w_dtype,
+                         int64_t n_rows, int64_t d, vjp_dtype_t act, vjp_dtype_t w_dtype,
                          vjp_stream_t stream);
 
 /* Row tiling of the backward's stage 1.  The rows are cut into blocks of
@@ -142,7 +152,7 @@ size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d, int64_t ro
 int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
                          void* dx, int64_t ld_dx, float* dw, int accumulate,
                          int64_t n_rows, int64_t d, int64_t rows_per_tile,
-                         int act, int w_dtype, void* workspace, size_t workspace_bytes,
+                         vjp_dtype_t act, vjp_dtype_t w_dtype, void* workspace, size_t workspace_bytes,
                          vjp_stream_t stream);
 
 /* ---------------------------------------------------------------- scaled SiLU
@@ -157,7 +167,7 @@ int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void
  * single-cell atomic add of per-block partials is replaced by the two-stage
  * reduction described above.
  */
-int vjp_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, int act,
+int vjp_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, vjp_dtype_t act,
                         vjp_stream_t stream);
 
 /* Elements per dw tile: max(2048, 2048 * ceil(ceil(n / 4096) / 2048)), a
@@ -175,7 +185,7 @@ size_t vjp_scaled_silu_bwd_workspace_size(int64_t n);
  * (neighbour swap, pair swap, half-row mirror, row mirror, then 16-lane rows
  * (0 + 1) + (2 + 3)); the sixteen wave sums added in wave order. */
 int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx, float* dw,
-                        int accumulate, int64_t n, int act, void* workspace,
+                        int accumulate, int64_t n, vjp_dtype_t act, void* workspace,
                         size_t workspace_bytes, vjp_stream_t stream);
 
 /* ---------------------------------------------------------------- row softmax
@@ -187,10 +197,10 @@ int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx,
  * memory; the max shift adds no backward term).
  */
 int vjp_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
-                    int64_t cols, int act, vjp_stream_t stream);
+                    int64_t cols, vjp_dtype_t act, vjp_stream_t stream);
 
 int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, void* dx,
-                    int64_t ld_dx, int64_t rows, int64_t cols, int act, vjp_stream_t stream);
+                    int64_t ld_dx, int64_t rows, int64_t cols, vjp_dtype_t act, vjp_stream_t stream);
 
 /* Save-the-statistics form ("Backprop for kernel writers", the softmax
  * section after 04: y can be recomputed from the saved max and logsumexp;
@@ -203,11 +213,11 @@ int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y, 
  * rebuilt in fp32 as exp(x - L) (never rounded to the storage type), then
  * dx = y (dy - s), s = sum_j dy_j y_j.  Reads dy and x, writes dx. */
 int vjp_softmax_fwd_lse(const void* x, int64_t ld_x, void* y, int64_t ld_y, float* row_lse,
-                        int64_t rows, int64_t cols, int act, vjp_stream_t stream);
+                        int64_t rows, int64_t cols, vjp_dtype_t act, vjp_stream_t stream);
 
 int vjp_softmax_bwd_lse(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
                         const float* row_lse, void* dx, int64_t ld_dx, int64_t rows,
-                        int64_t cols, int act, vjp_stream_t stream);
+                        int64_t cols, vjp_dtype_t act, vjp_stream_t stream);
 
 /* ---------------------------------------------------------------- softmax + cross-entropy
  * Fused forward and backward of the mean cross-entropy of a row softmax:
@@ -231,7 +241,7 @@ int vjp_softmax_bwd_lse(const void* dy, int64_t ld_dy, const void* x, int64_t ld
 size_t vjp_softmax_xent_workspace_size(int64_t rows);
 
 int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32_t* targets,
-                             int64_t rows, int64_t classes, int act, float grad_scale,
+                             int64_t rows, int64_t classes, vjp_dtype_t act, float grad_scale,
                              float* loss, float* row_max, float* row_lse, void* dlogits,
                              int64_t ld_dlogits, int32_t* n_invalid, void* workspace,
                              size_t workspace_bytes, vjp_stream_t stream);
@@ -251,12 +261,12 @@ int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32_t* targ
  * VJP_EALIAS.  classes at most 268431360 (65535 blocks of 4096 columns),
  * else VJP_EINVAL. */
 int vjp_softmax_xent_fwd(const void* logits, int64_t ld, const int32_t* targets, int64_t rows,
-                         int64_t classes, int act, float* loss, float* row_max, float* row_lse,
+                         int64_t classes, vjp_dtype_t act, float* loss, float* row_max, float* row_lse,
                          int32_t* n_invalid, void* workspace, size_t workspace_bytes,
                          vjp_stream_t stream);
 
 int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* targets,
-                         const float* row_lse, int64_t rows, int64_t classes, int act,
+                         const float* row_lse, int64_t rows, int64_t classes, vjp_dtype_t act,
                          const float* dloss, void* dlogits, int64_t ld_dlogits,
                          vjp_stream_t stream);
 
@@ -288,28 +298,28 @@ int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* targets,
  * 2 cols).  Stage 2 sums the partial rows in the order documented for
  * vjp_weighted_sum_bwd (d = 2 cols for LayerNorm, split into dw and db).
  * accumulate = 1 adds into dw (and db). */
-int64_t vjp_norm_max_cols(int act, int aligned16);
+int64_t vjp_norm_max_cols(vjp_dtype_t act, int aligned16);
 
 size_t vjp_layernorm_bwd_workspace_size(int64_t rows, int64_t cols);
 size_t vjp_rmsnorm_bwd_workspace_size(int64_t rows, int64_t cols);
 
 int vjp_layernorm_fwd(const void* x, int64_t ld_x, const void* w, const void* b, void* y,
                       int64_t ld_y, float* row_mean, float* row_rstd, int64_t rows,
-                      int64_t cols, float eps, int act, int w_dtype, vjp_stream_t stream);
+                      int64_t cols, float eps, vjp_dtype_t act, vjp_dtype_t w_dtype, vjp_stream_t stream);
 
 int vjp_layernorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* w,
                       const float* row_mean, const float* row_rstd, void* dx, int64_t ld_dx,
                       float* dw, float* db, int accumulate, int64_t rows, int64_t cols,
-                      float eps, int act, int w_dtype, void* workspace, size_t workspace_bytes,
+                      float eps, vjp_dtype_t act, vjp_dtype_t w_dtype, void* workspace, size_t workspace_bytes,
                       vjp_stream_t stream);
 
 int vjp_rmsnorm_fwd(const void* x, int64_t ld_x, const void* w, void* y, int64_t ld_y,
-                    float* row_rstd, int64_t rows, int64_t cols, float eps, int act,
-                    int w_dtype, vjp_stream_t stream);
+                    float* row_rstd, int64_t rows, int64_t cols, float eps, vjp_dtype_t act,
+                    vjp_dtype_t w_dtype, vjp_stream_t stream);
 
 int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, const void* w,
                     const float* row_rstd, void* dx, int64_t ld_dx, float* dw, int accumulate,
-                    int64_t rows, int64_t cols, float eps, int act, int w_dtype,
+                    int64_t rows, int64_t cols, float eps, vjp_dtype_t act, vjp_dtype_t w_dtype,
                     void* workspace, size_t workspace_bytes, vjp_stream_t stream);
 
 /* ---------------------------------------------------------------- gather / scatter-add
@@ -338,12 +348,12 @@ int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x, 
 size_t vjp_gather_rows_bwd_workspace_size(int64_t M, int64_t V, int64_t D);
 
 int vjp_gather_rows_fwd(const void* table, int64_t ld_t, int64_t V, int64_t D,
-                        const int32_t* idx, int64_t M, void* y, int64_t ld_y, int act,
+                        const int32_t* idx, int64_t M, void* y, int64_t ld_y, vjp_dtype_t act,
                         vjp_stream_t stream);
 
 int vjp_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M, int64_t V,
                         int64_t D, float* dtable, int64_t ld_dt, int accumulate,
-                        int32_t* n_invalid, int act, void* workspace, size_t workspace_bytes,
+                        int32_t* n_invalid, vjp_dtype_t act, void* workspace, size_t workspace_bytes,
                         vjp_stream_t stream);
 
 #ifdef __cplusplus

@@ -41,6 +41,7 @@ _SIGS = {
     "vjp_status_string": ([_int], ctypes.c_char_p),
     "vjp_last_error": ([], ctypes.c_char_p),
     "vjp_copy": ([_vp, _vp, _i64, _vp], _int),
+    "vjp_copy_shaped": ([_vp, _vp, _i64, _int, _i64, _vp], _int),
     "vjp_weighted_sum_fwd": ([_vp, _i64, _vp, _vp, _i64, _i64, _int, _int, _vp], _int),
     "vjp_weighted_sum_tiling": ([_i64, _i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], ctypes.c_int),
     "vjp_weighted_sum_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
@@ -177,6 +178,18 @@ def vjp_copy(src, dst):
     if dst.device != src.device:
         raise ValueError("src and dst must be on the same device")
     _check(lib.vjp_copy(_ptr(src), _ptr(dst), n, _stream(src)), "vjp_copy")
+    return dst
+
+
+def vjp_copy_shaped(src, dst, vectors_per_lane=4, max_workgroups=32768):
+    """vjp_copy with its launch shape given (for sweeps of the copy reference)."""
+    n = _nbytes(_flat(src))
+    if _nbytes(_flat(dst)) != n:
+        raise ValueError(f"dst holds {_nbytes(dst)} bytes, src {n}")
+    if dst.device != src.device:
+        raise ValueError("src and dst must be on the same device")
+    _check(lib.vjp_copy_shaped(_ptr(src), _ptr(dst), n, int(vectors_per_lane), int(max_workgroups),
+                               _stream(src)), "vjp_copy_shaped")
     return dst
 
 

@@ -174,10 +174,26 @@ VJP_API int vjp_copy(const void* src, void* dst, int64_t bytes, vjp_stream_t str
   return hip_status(launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "copy");
 }
 
+VJP_API int vjp_copy_shaped(const void* src, void* dst, int64_t bytes, int vectors_per_lane,
+                            int64_t max_workgroups, vjp_stream_t stream) {
+  if (bytes < 0) return fail(VJP_EINVAL, "negative size");
+  if (vectors_per_lane != 1 && vectors_per_lane != 2 && vectors_per_lane != 4 &&
+      vectors_per_lane != 8)
+    return fail(VJP_EINVAL, "vectors_per_lane must be 1, 2, 4 or 8");
+  if (max_workgroups < 1 || max_workgroups > (int64_t(1) << 31) - 1)
+    return fail(VJP_EINVAL, "max_workgroups must be in [1, 2^31 - 1]");
+  if (bytes == 0) return ok();
+  if (!src || !dst) return fail(VJP_EINVAL, "NULL pointer");
+  VJP_TRY(check_alias({span(dst, bytes, "dst")}, {span(src, bytes, "src")}));
+  return hip_status(launch_copy_shaped(src, dst, bytes, vectors_per_lane, max_workgroups,
+                                       static_cast<hipStream_t>(stream)),
+                    "copy");
+}
+
 // ------------------------------------------------------------------ weighted sum
 
 VJP_API int vjp_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,
-                                 int64_t n_rows, int64_t d, int act, int w_dtype,
+                                 int64_t n_rows, int64_t d, vjp_dtype_t act, vjp_dtype_t w_dtype,
                                  vjp_stream_t stream) {
   if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n_rows < 0 || d < 0) return fail(VJP_EINVAL, "negative size");
@@ -214,8 +230,8 @@ VJP_API size_t vjp_weighted_sum_bwd_workspace_size(int64_t n_rows, int64_t d,
 
 VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, const void* w,
                                  void* dx, int64_t ld_dx, float* dw, int accumulate,
-                                 int64_t n_rows, int64_t d, int64_t rows_per_tile, int act,
-                                 int w_dtype, void* workspace, size_t workspace_bytes,
+                                 int64_t n_rows, int64_t d, int64_t rows_per_tile, vjp_dtype_t act,
+                                 vjp_dtype_t w_dtype, void* workspace, size_t workspace_bytes,
                                  vjp_stream_t stream) {
   if (!dtype_ok(act) || !dtype_ok(w_dtype)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n_rows < 0 || d < 0 || rows_per_tile < 0) return fail(VJP_EINVAL, "negative size");
@@ -256,7 +272,7 @@ VJP_API int vjp_weighted_sum_bwd(const void* dy, const void* x, int64_t ld_x, co
 
 // ------------------------------------------------------------------ scaled SiLU
 
-VJP_API int vjp_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, int act,
+VJP_API int vjp_scaled_silu_fwd(const void* x, const float* w, void* y, int64_t n, vjp_dtype_t act,
                                 vjp_stream_t stream) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n < 0) return fail(VJP_EINVAL, "negative size");
@@ -284,7 +300,7 @@ VJP_API size_t vjp_scaled_silu_bwd_workspace_size(int64_t n) {
 }
 
 VJP_API int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx,
-                                float* dw, int accumulate, int64_t n, int act, void* workspace,
+                                float* dw, int accumulate, int64_t n, vjp_dtype_t act, void* workspace,
                                 size_t workspace_bytes, vjp_stream_t stream) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n < 0) return fail(VJP_EINVAL, "negative size");
@@ -381,18 +397,18 @@ int softmax_bwd_impl(const void* dy, int64_t ld_dy, const void* src, int64_t ld_
 }  // namespace
 
 VJP_API int vjp_softmax_fwd(const void* x, int64_t ld_x, void* y, int64_t ld_y, int64_t rows,
-                            int64_t cols, int act, vjp_stream_t stream) {
+                            int64_t cols, vjp_dtype_t act, vjp_stream_t stream) {
   return softmax_fwd_impl(x, ld_x, y, ld_y, nullptr, rows, cols, act, stream);
 }
 
 VJP_API int vjp_softmax_bwd(const void* dy, int64_t ld_dy, const void* y, int64_t ld_y,
-                            void* dx, int64_t ld_dx, int64_t rows, int64_t cols, int act,
+                            void* dx, int64_t ld_dx, int64_t rows, int64_t cols, vjp_dtype_t act,
                             vjp_stream_t stream) {
   return softmax_bwd_impl(dy, ld_dy, y, ld_y, nullptr, dx, ld_dx, rows, cols, act, stream);
 }
 
 VJP_API int vjp_softmax_fwd_lse(const void* x, int64_t ld_x, void* y, int64_t ld_y,
-                                float* row_lse, int64_t rows, int64_t cols, int act,
+                                float* row_lse, int64_t rows, int64_t cols, vjp_dtype_t act,
                                 vjp_stream_t stream) {
   if (row_lse == nullptr && rows > 0) return fail(VJP_EINVAL, "row_lse is null");
   if (y == nullptr) ld_y = cols;   // ignored
@@ -402,7 +418,7 @@ VJP_API int vjp_softmax_fwd_lse(const void* x, int64_t ld_x, void* y, int64_t ld
 
 VJP_API int vjp_softmax_bwd_lse(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
                                 const float* row_lse, void* dx, int64_t ld_dx, int64_t rows,
-                                int64_t cols, int act, vjp_stream_t stream) {
+                                int64_t cols, vjp_dtype_t act, vjp_stream_t stream) {
   if (row_lse == nullptr && rows > 0) return fail(VJP_EINVAL, "row_lse is null");
   if (row_lse != nullptr && !aligned(row_lse, 4)) return fail(VJP_EALIGN, "row_lse is not 4-byte aligned");
   if (rows == 0) return softmax_bwd_impl(dy, ld_dy, x, ld_x, nullptr, dx, ld_dx, 0, cols, act, stream);
@@ -416,7 +432,7 @@ VJP_API size_t vjp_softmax_xent_workspace_size(int64_t rows) {
 }
 
 VJP_API int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32_t* targets,
-                                     int64_t rows, int64_t classes, int act, float grad_scale,
+                                     int64_t rows, int64_t classes, vjp_dtype_t act, float grad_scale,
                                      float* loss, float* row_max, float* row_lse, void* dlogits,
                                      int64_t ld_dlogits, int32_t* n_invalid, void* workspace,
                                      size_t workspace_bytes, vjp_stream_t stream) {
@@ -461,7 +477,7 @@ VJP_API int vjp_softmax_xent_fwd_bwd(const void* logits, int64_t ld, const int32
 }
 
 VJP_API int vjp_softmax_xent_fwd(const void* logits, int64_t ld, const int32_t* targets,
-                                 int64_t rows, int64_t classes, int act, float* loss,
+                                 int64_t rows, int64_t classes, vjp_dtype_t act, float* loss,
                                  float* row_max, float* row_lse, int32_t* n_invalid,
                                  void* workspace, size_t workspace_bytes, vjp_stream_t stream) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
@@ -502,7 +518,7 @@ VJP_API int vjp_softmax_xent_fwd(const void* logits, int64_t ld, const int32_t* 
 }
 
 VJP_API int vjp_softmax_xent_bwd(const void* logits, int64_t ld, const int32_t* targets,
-                                 const float* row_lse, int64_t rows, int64_t classes, int act,
+                                 const float* row_lse, int64_t rows, int64_t classes, vjp_dtype_t act,
                                  const float* dloss, void* dlogits, int64_t ld_dlogits,
                                  vjp_stream_t stream) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
@@ -658,14 +674,14 @@ VJP_API size_t vjp_rmsnorm_bwd_workspace_size(int64_t rows, int64_t cols) {
   return size_t(norm_tiles(rows)) * size_t(cols) * sizeof(float);
 }
 
-VJP_API int64_t vjp_norm_max_cols(int act, int aligned16) {
+VJP_API int64_t vjp_norm_max_cols(vjp_dtype_t act, int aligned16) {
   if (!dtype_ok(act)) return -1;
   return norm_max_cols(act, aligned16 != 0);
 }
 
 VJP_API int vjp_layernorm_fwd(const void* x, int64_t ld_x, const void* w, const void* b, void* y,
                               int64_t ld_y, float* row_mean, float* row_rstd, int64_t rows,
-                              int64_t cols, float eps, int act, int w_dtype,
+                              int64_t cols, float eps, vjp_dtype_t act, vjp_dtype_t w_dtype,
                               vjp_stream_t stream) {
   return norm_fwd_impl(false, x, ld_x, w, b, y, ld_y, row_mean, row_rstd, rows, cols, eps, act,
                        w_dtype, stream);
@@ -674,7 +690,7 @@ VJP_API int vjp_layernorm_fwd(const void* x, int64_t ld_x, const void* w, const 
 VJP_API int vjp_layernorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
                               const void* w, const float* row_mean, const float* row_rstd,
                               void* dx, int64_t ld_dx, float* dw, float* db, int accumulate,
-                              int64_t rows, int64_t cols, float eps, int act, int w_dtype,
+                              int64_t rows, int64_t cols, float eps, vjp_dtype_t act, vjp_dtype_t w_dtype,
                               void* workspace, size_t workspace_bytes, vjp_stream_t stream) {
   return norm_bwd_impl(false, dy, ld_dy, x, ld_x, w, row_mean, row_rstd, dx, ld_dx, dw, db,
                        accumulate, rows, cols, eps, act, w_dtype, workspace, workspace_bytes,
@@ -682,8 +698,8 @@ VJP_API int vjp_layernorm_bwd(const void* dy, int64_t ld_dy, const void* x, int6
 }
 
 VJP_API int vjp_rmsnorm_fwd(const void* x, int64_t ld_x, const void* w, void* y, int64_t ld_y,
-                            float* row_rstd, int64_t rows, int64_t cols, float eps, int act,
-                            int w_dtype, vjp_stream_t stream) {
+                            float* row_rstd, int64_t rows, int64_t cols, float eps, vjp_dtype_t act,
+                            vjp_dtype_t w_dtype, vjp_stream_t stream) {
   return norm_fwd_impl(true, x, ld_x, w, nullptr, y, ld_y, nullptr, row_rstd, rows, cols, eps,
                        act, w_dtype, stream);
 }
@@ -691,7 +707,7 @@ VJP_API int vjp_rmsnorm_fwd(const void* x, int64_t ld_x, const void* w, void* y,
 VJP_API int vjp_rmsnorm_bwd(const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
                             const void* w, const float* row_rstd, void* dx, int64_t ld_dx,
                             float* dw, int accumulate, int64_t rows, int64_t cols, float eps,
-                            int act, int w_dtype, void* workspace, size_t workspace_bytes,
+                            vjp_dtype_t act, vjp_dtype_t w_dtype, void* workspace, size_t workspace_bytes,
                             vjp_stream_t stream) {
   return norm_bwd_impl(true, dy, ld_dy, x, ld_x, w, nullptr, row_rstd, dx, ld_dx, dw, nullptr,
                        accumulate, rows, cols, eps, act, w_dtype, workspace, workspace_bytes,
@@ -706,7 +722,7 @@ VJP_API size_t vjp_gather_rows_bwd_workspace_size(int64_t M, int64_t V, int64_t 
 }
 
 VJP_API int vjp_gather_rows_fwd(const void* table, int64_t ld_t, int64_t V, int64_t D,
-                                const int32_t* idx, int64_t M, void* y, int64_t ld_y, int act,
+                                const int32_t* idx, int64_t M, void* y, int64_t ld_y, vjp_dtype_t act,
                                 vjp_stream_t stream) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (V < 0 || D < 0 || M < 0) return fail(VJP_EINVAL, "negative size");
@@ -727,7 +743,7 @@ VJP_API int vjp_gather_rows_fwd(const void* table, int64_t ld_t, int64_t V, int6
 
 VJP_API int vjp_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M,
                                 int64_t V, int64_t D, float* dtable, int64_t ld_dt,
-                                int accumulate, int32_t* n_invalid, int act, void* workspace,
+                                int accumulate, int32_t* n_invalid, vjp_dtype_t act, void* workspace,
                                 size_t workspace_bytes, vjp_stream_t stream) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (V < 0 || D < 0 || M < 0) return fail(VJP_EINVAL, "negative size");

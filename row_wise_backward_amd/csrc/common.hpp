@@ -253,7 +253,7 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // ------------------------------------------------------------------ math
-// exp(x) as 2^(x * log2 e) on the hardware exp2; sigmoid as 1 / (1 + e^-x).
+// exp(x) as 2^(x * log2 e) on the hardware exp2.
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -261,8 +261,40 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 
-__device__ __forceinline__ float sigmoid(float x) {
-  return rcp_fast(1.0f + exp2_fast(-x * kLog2e));
+// sigmoid(x) as s * k, evaluated without overflow and without flushing
+// results below 2^-126 (x < -87.3, where sigmoid(x) is an fp32 subnormal
+// that bf16 and fp32 outputs such as w x sigmoid(x) can still hold).  With
+// e = 2^(-|x| log2 e) = exp(-|x|) <= 1: sigmoid(x) = 1 / (1 + e) for x >= 0
+// and e / (1 + e) for x < 0, so neither form can overflow.  Where e itself
+// would be subnormal (x < 0 only), it is formed as 2^(t + 64) and k = 2^-64
+// carries the scale: products formed from s stay normal and round once when
+// finally multiplied by k.  k = 1 elsewhere (a multiply by k is then exact).
+struct ScaledSigmoid {
+  float s;
+  float k;
+};
+
+__device__ __forceinline__ ScaledSigmoid sigmoid_scaled(float x) {
+  const float t = -__builtin_fabsf(x) * kLog2e;
+  const bool tiny = x < 0.0f && t < -126.0f;
+  const float e = exp2_fast(tiny ? t + 64.0f : t);
+  const float r = rcp_fast(1.0f + (tiny ? 0.0f : e));
+  return {x >= 0.0f ? r : e * r, tiny ? 5.421010862427522e-20f /* 2^-64 */ : 1.0f};
+}
+
+// The sigmoid a kernel with storage type T needs.  fp16 values and results
+// are zero below 2^-24 in magnitude: where 1 / (1 + 2^(-x log2 e)) underflows
+// or overflows (x < -87), every fp16 result formed from it (w x s, dy w s
+// (1 + x (1 - s))) is +-0 either way, so the two-operation form serves, with
+// k = 1.  bf16 and fp32 results reach down to 2^-133 and 2^-149 and take the
+// scaled form.
+template <typename T>
+__device__ __forceinline__ ScaledSigmoid sigmoid_for(float x) {
+  if constexpr (sizeof(T) == 2 && !is_bf16<T>) {
+    return {rcp_fast(1.0f + exp2_fast(-x * kLog2e)), 1.0f};
+  } else {
+    return sigmoid_scaled(x);
+  }
 }
 
 // Workgroup barrier that orders LDS accesses only.  The kernels exchange only

@@ -20,8 +20,11 @@ hipError_t launch_reduce_partials_split(const float* P, int64_t T, int64_t d, fl
                                         float* out2, int64_t split, int accumulate,
                                         hipStream_t s);
 
-// Streaming device copy of `bytes` bytes (the measurement reference).
+// Streaming device copy of `bytes` bytes (the measurement reference), with
+// its launch shape (vectors in flight per lane: 1, 2, 4 or 8; grid bound).
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+hipError_t launch_copy_shaped(const void* src, void* dst, int64_t bytes, int vectors_per_lane,
+                              int64_t max_groups, hipStream_t s);
 
 // Weighted sum.
 hipError_t launch_weighted_sum_fwd(const void* x, int64_t ld_x, const void* w, void* y,

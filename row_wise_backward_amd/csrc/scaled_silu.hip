@@ -11,8 +11,11 @@
 //
 // gfx950 mapping: flat elementwise stream, 16-byte accesses (8 x fp16/bf16,
 // 4 x fp32) per lane, 256-thread workgroups, kUnroll vectors per lane
-// issued before any is used.  sigmoid(x) = 1 / (1 + 2^(-x log2 e)) on v_exp_f32 and
-// v_rcp_f32 (both accurate to about 1 ulp in fp32).  The scalar w is read
+// issued before any is used.  sigmoid(x) from e = 2^(-|x| log2 e) on v_exp_f32
+// and v_rcp_f32 (both accurate to about 1 ulp in fp32): 1 / (1 + e) for
+// x >= 0, e / (1 + e) for x < 0, so nothing overflows, with a 2^64 scale
+// carried through where sigmoid(x) is an fp32 subnormal (fp16 storage, whose
+// results there are +-0, takes 1 / (1 + 2^(-x log2 e))).  The scalar w is read
 // from device memory by every workgroup (no host synchronisation).
 #include "common.hpp"
 #include "launch.hpp"
@@ -49,7 +52,8 @@ __global__ __launch_bounds__(kThreads) void silu_fwd_kernel(const T* __restrict_
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           const float xf = to_f32(xv.v[i]);
-          yv[i] = wv * xf * sigmoid(xf);
+          const ScaledSigmoid sg = sigmoid_for<T>(xf);
+          yv[i] = (wv * xf * sg.s) * sg.k;
         }
         store_f32_tail<T, VEC>(y + i0, end - i0, yv);
       }
@@ -92,10 +96,12 @@ __global__ __launch_bounds__(kThreads) void silu_bwd_kernel(
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         const float xf = to_f32(xv.v[i]), gf = to_f32(gv.v[i]);
-        const float s = sigmoid(xf);
-        const float silu = xf * s;
-        dxv[i] = gf * wv * fmaf(silu, 1.0f - s, s);
-        acc = fmaf(gf, silu, acc);
+        // s = sg.s * sg.k; silu = x s.  Where k < 1, s < 2^-126 so 1 - s
+        // rounds to 1 and dx is formed from the scaled s and scaled back once.
+        const ScaledSigmoid sg = sigmoid_for<T>(xf);
+        const float silu = xf * sg.s;
+        dxv[i] = (gf * wv * fmaf(silu, 1.0f - sg.s * sg.k, sg.s)) * sg.k;
+        acc = fmaf(gf, silu * sg.k, acc);
       }
       if (i0 < end) store_f32_tail<T, VEC>(dx + i0, end - i0, dxv);
     }

@@ -22,3 +22,17 @@ def gpu_lib():
     import row_wise_backward_amd as rwb
 
     return rwb
+
+
+@pytest.fixture(autouse=True)
+def _sentinel_bands(request):
+    """After every GPU test: the sentinel bands around every 2-D input and
+    output buffer, and the gaps between the rows of padded layouts, are
+    unchanged."""
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    import gpu_util
+
+    bad = gpu_util.guards_broken()
+    assert not bad, f"write outside a buffer: {bad}"

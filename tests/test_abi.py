@@ -339,3 +339,11 @@ def test_copy_rejections():
     assert L.vjp_copy(P(A), P(A + 8), 16, None) == EALIAS      # overlapping ranges
     assert L.vjp_copy(P(A + 8), P(A), 16, None) == EALIAS
     assert L.vjp_copy(None, None, 0, None) == OK               # nothing to do
+    sh = lambda **k: L.vjp_copy_shaped(P(k.get("src", A)), P(k.get("dst", B)), k.get("n", 64),
+                                       k.get("vpl", 4), k.get("wg", 32768), None)
+    for vpl in (0, 3, 5, 16, -4):
+        assert sh(vpl=vpl) == EINVAL
+    assert sh(wg=0) == EINVAL and sh(wg=1 << 31) == EINVAL
+    assert sh(n=-1) == EINVAL and sh(src=None) == EINVAL
+    assert sh(dst=A + 8) == EALIAS
+    assert sh(src=None, dst=None, n=0) == OK

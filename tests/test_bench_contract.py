@@ -41,8 +41,14 @@ def test_byte_models_count_each_tensor_once(es):
 
 
 def test_cpu_baseline_small_sample():
-    out = bench.cpu_baseline(scale=0.01, min_seconds=0.0)
+    """Both legs: all cores (one worker process per core) and one core."""
+    out = bench.cpu_baseline(scale=0.01, min_seconds=0.0, cores=2)
     assert out["kind"] == "oracle" and out["unit"] == "GB/s"
-    assert out["value"] > 0 and out["cores"] >= 1
-    assert "repetitions" in out["sample"]
+    assert out["value"] > 0 and out["cores"] == 2
+    assert "2 worker processes" in out["sample"] and "passes" in out["sample"]
+    assert out["one_core"]["cores"] == 1 and out["one_core"]["value"] > 0
     json.dumps(out)                                  # serialisable into the bench line
+
+
+def test_cpu_cores_is_bounded():
+    assert 1 <= bench.cpu_cores() <= 16

@@ -26,3 +26,18 @@ def test_copy(gpu_lib, nbytes, src_off, dst_off):
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
     assert bool((dst_buf[:dst_off] == 0xA5).all()) and bool((dst_buf[dst_off + nbytes:] == 0xA5).all())
+
+
+@pytest.mark.parametrize("vpl", [1, 2, 4, 8])
+@pytest.mark.parametrize("max_wg", [1, 3, 32768])
+@pytest.mark.parametrize("nbytes", [4097, 65536 * 16 + 5, 5 * 1024 * 1024 + 24])
+def test_copy_shaped(gpu_lib, vpl, max_wg, nbytes):
+    """Every launch shape of the copy reference: few workgroups loop over the
+    data many times; the last partial group and the byte tail land too."""
+    print(f"\n[copy shaped] bytes={nbytes} vpl={vpl} max_wg={max_wg}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(nbytes + vpl + max_wg)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).to(DEV)
+    dst_buf = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    gpu_lib.vjp_copy_shaped(src, dst_buf[:nbytes], vpl, max_wg)
+    torch.cuda.synchronize()
+    assert torch.equal(dst_buf[:nbytes], src) and bool((dst_buf[nbytes:] == 0xA5).all())

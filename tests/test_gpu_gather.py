@@ -50,7 +50,9 @@ def run_case(rwb, M, V, D, act, seed, kind="zipf", ld=None, offset=0, accumulate
 
     dyd = padded(dy, act, ld, offset)
     old = np.random.default_rng(seed + 1).standard_normal((V, D)).astype(np.float32)
-    dt = torch.from_numpy(old).to(DEV) if accumulate else torch.full((V, D), float("nan"), device=DEV)
+    dt, _ = empty_padded(V, D, "f32")
+    if accumulate and V and D:
+        dt.copy_(torch.from_numpy(old).to(DEV))
     need = rwb.vjp_gather_rows_bwd_workspace_size(M, V, D)
     wsg = Guarded(max(need // 4, 1), torch.float32)
     ninv = Guarded(1, torch.int32)

@@ -272,19 +272,24 @@ def test_full_size(gpu_lib, kind):
     dx_ref = nm.rmsnorm_bwd(dys, xs, w64, eps)[0] if rms else nm.layernorm_bwd(dys, xs, w64, eps)[0]
     reps.append(_check(to_host(dx, "bf16")[idx], dx_ref, bwd_bound(dys, xs, w64, eps, rms, saved=False),
                        "bf16", "dx(sampled)"))
-    dw_ref = np.zeros(cols)
-    db_ref = np.zeros(cols)
+    dw_ref, db_ref = np.zeros(cols), np.zeros(cols)
+    S_dw, S_db = np.zeros(cols), np.zeros(cols)     # sums of |terms|: condition numbers
     for i in range(0, rows, 4096):
         xc, dyc = synth.to_f64(x[i:i + 4096], "bf16"), synth.to_f64(dy[i:i + 4096], "bf16")
         if rms:
             dw_ref += nm.rmsnorm_bwd(dyc, xc, w64, eps)[1]
+            xhat = xc * nm.rmsnorm_rstd(xc, eps)[:, None]
         else:
             _, a1, a2 = nm.layernorm_bwd(dyc, xc, w64, eps)
             dw_ref += a1
             db_ref += a2
-    reps.append(reduced(to_host(dw, "f32"), dw_ref, name="dw"))
+            mu, rs = nm.layernorm_stats(xc, eps)
+            xhat = (xc - mu[:, None]) * rs[:, None]
+        S_dw += np.sum(np.abs(dyc * xhat), axis=0)
+        S_db += np.sum(np.abs(dyc), axis=0)
+    reps.append(reduced(to_host(dw, "f32"), dw_ref, name="dw", S=S_dw))
     if not rms:
-        reps.append(reduced(to_host(db, "f32"), db_ref, name="db"))
+        reps.append(reduced(to_host(db, "f32"), db_ref, name="db", S=S_db))
     for r in reps:
         print("   ", r, flush=True)
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]

@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, empty_padded, padded, pick_rows, to_host
-from oracle.compare import U32, pointwise
+from gpu_util import DEV, chunked, empty_padded, padded, to_host
+from oracle.compare import U32, combine, pointwise
 from oracle.rounding import round_to, to_storage
 from synth.workloads import SOFTMAX
 
@@ -50,10 +50,8 @@ def run_case(rwb, rows, cols, act, seed, sigma=3.0, ld=None, offset=0):
     rwb.vjp_softmax_bwd(dyd, yd, dx=dx)
     S, F = _dx_tols(dy64, y_saved64)
     rep_dx = pointwise(to_host(dx, act), sm.bwd(dy64, y_saved64), act, S=S, floor=F, name="dx")
-    # nothing written between the rows of a padded layout
-    if ld is not None and ld > cols and rows > 1:
-        gap = ybuf.as_strided((rows - 1, ld - cols), (ld, 1), offset + cols)
-        assert bool(torch.isnan(gap.float()).all()), "write between rows"
+    # nothing written before, after or between the rows of either output
+    assert ybuf.intact() and dxbuf.intact(), "write outside an output"
     for r in (rep_y, rep_dx):
         print("   ", r, flush=True)
     assert rep_y.ok and rep_dx.ok, [str(rep_y), str(rep_dx)]
@@ -121,26 +119,40 @@ def test_empty(gpu_lib):
 
 
 def test_full_size(gpu_lib):
-    """The 32768 x 4096 bf16 workload: y on sampled rows; dx on sampled rows from
-    the oracle's full bf16 y."""
+    """The 32768 x 4096 bf16 workload: y on every row against the oracle; dx on
+    every row from the oracle's bf16 y (compared in chunks of 4096 rows)."""
     c = SOFTMAX
     rows, cols = c.shape
     print(f"\n[softmax full] {rows}x{cols}", flush=True)
     x = synth.normal((rows, cols), c.sigma_x, c.dtype, c.seed, synth.STREAM_X)
     dy = synth.normal((rows, cols), c.sigma_dy, c.dtype, c.seed, synth.STREAM_DY)
     xd = padded(x, "bf16")
-    y = gpu_lib.vjp_softmax_fwd(xd)
-    idx = pick_rows(rows, 512, 2)
-    x_s = synth.to_f64(x[idx], "bf16")
-    rep_y = pointwise(to_host(y, "bf16")[idx], sm.fwd(x_s), "bf16", name="y(sampled)")
-    del xd
+    y, yg = empty_padded(rows, cols, "bf16")
+    gpu_lib.vjp_softmax_fwd(xd, y=y)
+    y_host = to_host(y, "bf16")
+    assert yg.intact(), "write outside y"
+    del xd, y
     y_saved = np.empty_like(x)
-    for i in range(0, rows, 4096):
-        y_saved[i:i + 4096] = to_storage(round_to(sm.fwd(synth.to_f64(x[i:i + 4096], "bf16")), "bf16"), "bf16")
-    dx = gpu_lib.vjp_softmax_bwd(padded(dy, "bf16"), padded(y_saved, "bf16"))
-    ys64, dys64 = synth.to_f64(y_saved[idx], "bf16"), synth.to_f64(dy[idx], "bf16")
-    S, F = _dx_tols(dys64, ys64)
-    rep_dx = pointwise(to_host(dx, "bf16")[idx], sm.bwd(dys64, ys64), "bf16", S=S, floor=F,
-                       name="dx(sampled)")
+
+    def fwd_part(i, j):
+        y_ref = sm.fwd(synth.to_f64(x[i:j], "bf16"))
+        y_saved[i:j] = to_storage(round_to(y_ref, "bf16"), "bf16")
+        return pointwise(y_host[i:j], y_ref, "bf16", name="y")
+
+    r_y = chunked(fwd_part, rows, 2048)
+    del y_host
+    dx, dxg = empty_padded(rows, cols, "bf16")
+    gpu_lib.vjp_softmax_bwd(padded(dy, "bf16"), padded(y_saved, "bf16"), dx=dx)
+    dx_host = to_host(dx, "bf16")
+    assert dxg.intact(), "write outside dx"
+
+    def bwd_part(i, j):
+        ys64, dys64 = synth.to_f64(y_saved[i:j], "bf16"), synth.to_f64(dy[i:j], "bf16")
+        S, F = _dx_tols(dys64, ys64)
+        return pointwise(dx_host[i:j], sm.bwd(dys64, ys64), "bf16", S=S, floor=F, name="dx")
+
+    r_dx = chunked(bwd_part, rows, 2048)
+    rep_y, rep_dx = combine(r_y, "y(all rows)"), combine(r_dx, "dx(all rows)")
     print("   ", rep_y, "\n   ", rep_dx, flush=True)
+    assert rep_y.n == rows * cols and rep_dx.n == rows * cols
     assert rep_y.ok and rep_dx.ok

@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, Guarded, empty_padded, padded, pick_rows, to_host
-from oracle.compare import U32, exact, pointwise, reduced
+from gpu_util import DEV, Guarded, chunked, empty_padded, padded, to_host
+from oracle.compare import U32, combine, exact, pointwise, reduced
 from synth.workloads import XENT
 
 pytestmark = pytest.mark.gpu
@@ -153,29 +153,48 @@ def test_empty(gpu_lib):
 
 def test_full_size(gpu_lib):
     """The 16384 x 32000 bf16 workload in the benchmark's launch configuration:
-    dlogits / row statistics on sampled rows, the mean loss over all rows."""
+    dlogits, row_max, row_lse and the row losses on every row (in chunks of
+    512 rows), the mean loss over all rows (its condition number reported)."""
     c = XENT
     rows, C = c.shape
     print(f"\n[softmax_xent full] {rows}x{C}", flush=True)
     z = synth.normal((rows, C), c.sigma_x, c.dtype, c.seed, synth.STREAM_X)
     t = synth.targets(rows, C, c.seed)
     zd = padded(z, "bf16")
-    need = gpu_lib.vjp_softmax_xent_workspace_size(rows)
-    wsb = torch.empty(need // 4, dtype=torch.float32, device=DEV)
-    out = gpu_lib.vjp_softmax_xent_fwd_bwd(zd, torch.from_numpy(t).to(DEV),
-                                           grad_scale=c.extra["grad_scale"], workspace=wsb)
+    dz, dzg = empty_padded(rows, C, "bf16")
+    loss, rmax, rlse = Guarded(1, torch.float32), Guarded(rows, torch.float32), Guarded(rows, torch.float32)
+    ninv = Guarded(1, torch.int32)
+    wsg = Guarded(gpu_lib.vjp_softmax_xent_workspace_size(rows) // 4, torch.float32)
+    gpu_lib.vjp_softmax_xent_fwd_bwd(zd, torch.from_numpy(t).to(DEV), grad_scale=c.extra["grad_scale"],
+                                     dlogits=dz, loss=loss.t, row_max=rmax.t, row_lse=rlse.t,
+                                     n_invalid=ninv.t, workspace=wsg.t)
     torch.cuda.synchronize()
-    idx = pick_rows(rows, 256, 3)
-    res = {"row_max": to_host(out["row_max"], "f32")[idx], "row_lse": to_host(out["row_lse"], "f32")[idx],
-           "dlogits": to_host(out["dlogits"], "bf16")[idx]}
-    _, reps = _compare(res, synth.to_f64(z[idx], "bf16"), t[idx], c.extra["grad_scale"], "bf16",
-                       ws_rows=to_host(wsb, "f32")[idx])
-    row_loss = np.concatenate([xe.fwd_bwd(synth.to_f64(z[i:i + 1024], "bf16"), t[i:i + 1024], 1.0)["row_loss"]
-                               for i in range(0, rows, 1024)])
-    reps.append(reduced(to_host(out["loss"], "f32"), np.array([np.sum(row_loss) / rows]), name="loss"))
-    assert int(out["n_invalid"].item()) == 0
+    assert dzg.intact() and loss.intact() and rmax.intact() and rlse.intact() and ninv.intact() \
+        and wsg.intact(), "write outside an output"
+    del zd
+    out = {"row_max": to_host(rmax.t, "f32"), "row_lse": to_host(rlse.t, "f32"),
+           "dlogits": to_host(dz, "bf16"), "row_loss": to_host(wsg.t, "f32")}
+    del dz
+    row_loss = np.empty(rows)
+
+    def part(i, j):
+        res = {k: v[i:j] for k, v in out.items() if k != "row_loss"}
+        ref, reps = _compare(res, synth.to_f64(z[i:j], "bf16"), t[i:j], c.extra["grad_scale"], "bf16",
+                             ws_rows=out["row_loss"][i:j])
+        row_loss[i:j] = ref["row_loss"]
+        return reps
+
+    per = {}
+    for reps in chunked(part, rows, 512):
+        for r in reps:
+            per.setdefault(r.name, []).append(r)
+    reps = [combine(v, f"{k}(all rows)") for k, v in per.items()]
+    reps.append(reduced(to_host(loss.t, "f32"), np.array([np.sum(row_loss) / rows]), name="loss",
+                        S=[np.sum(np.abs(row_loss)) / rows]))
+    assert int(ninv.t.item()) == 0
     for r in reps:
         print("   ", r, flush=True)
+    assert {r.name: r.n for r in reps}["dlogits(all rows)"] == rows * C
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
 
 

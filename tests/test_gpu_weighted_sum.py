@@ -5,8 +5,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, Guarded, empty_padded, padded, pick_rows, to_dev, to_host
-from oracle.compare import U32, exact, pointwise, reduced
+from gpu_util import DEV, Guarded, chunked, empty_padded, padded, to_dev, to_host
+from oracle.compare import U32, combine, exact, pointwise, reduced
 from synth.workloads import WS_LARGE, WS_SMALL
 
 pytestmark = pytest.mark.gpu
@@ -147,7 +147,8 @@ def test_zero_width_rows(gpu_lib):
 
 def test_large_batch_full_size(gpu_lib):
     """The 1,048,576 x 256 bf16 workload in the benchmark's launch configuration:
-    grad_w and every tile partial in full, y and grad_x on sampled rows."""
+    y and grad_x on every row (in chunks), grad_w and every tile partial in
+    full; grad_w's condition number is reported."""
     c = WS_LARGE
     n, d = c.shape
     x = synth.normal((n, d), c.sigma_x, c.dtype, c.seed, synth.STREAM_X)
@@ -155,42 +156,50 @@ def test_large_batch_full_size(gpu_lib):
     dy = synth.normal((n,), c.sigma_dy, c.dtype, c.seed, synth.STREAM_DY)
     print(f"\n[weighted_sum full] {n}x{d} bf16", flush=True)
     xd, wd, dyd = to_dev(x, "bf16").view(n, d), to_dev(w, "bf16"), to_dev(dy, "bf16")
-    y = gpu_lib.vjp_weighted_sum_fwd(xd, wd)
-    dx, dw = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd)
+    yg = Guarded(n, torch.bfloat16)
+    gpu_lib.vjp_weighted_sum_fwd(xd, wd, y=yg.t)
+    dx, dxg = empty_padded(n, d, "bf16")
+    dwg = Guarded(d, torch.float32)
     br, tiles = gpu_lib.vjp_weighted_sum_tiling(n, 0)
     need = gpu_lib.vjp_weighted_sum_bwd_workspace_size(n, d, 0)
-    wsb = torch.empty(need // 4, dtype=torch.float32, device=DEV)
-    dx2, dw2 = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd, workspace=wsb)
+    wsg = Guarded(need // 4, torch.float32)
+    gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd, dx=dx, dw=dwg.t, workspace=wsg.t)
+    dx2, dw2 = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wd)
     torch.cuda.synchronize()
     assert (br, tiles) == (32, 1024) and need == 1024 * 256 * 4
+    assert yg.intact() and dxg.intact() and dwg.intact() and wsg.intact(), "write outside an output"
+    # determinism: a second call (its own workspace), bitwise identical
+    assert torch.equal(dwg.t, dw2) and torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    del dx2
 
-    w64, dy64 = synth.to_f64(w, "bf16"), synth.to_f64(dy, "bf16")
-    rows = pick_rows(n, 4096, 1)
-    xs = synth.to_f64(x[rows], "bf16")
-    S = ws.fwd(np.abs(xs), np.abs(w64))
-    y_host = to_host(y, "bf16")[rows]
-    r_y = pointwise(y_host, ws.fwd(xs, w64), "bf16", S=S, floor=d * U32 * S, name="y(sampled)")
     from oracle.rounding import round_to, to_storage
-    gx_ref, _ = ws.bwd(dy64[rows], xs, w64)
-    r_dx = exact(to_host(dx, "bf16")[rows], to_storage(round_to(gx_ref, "bf16"), "bf16"), "bf16",
-                 name="dx(sampled)")
+    w64, dy64 = synth.to_f64(w, "bf16"), synth.to_f64(dy, "bf16")
+    y_host, dx_host = to_host(yg.t, "bf16"), to_host(dx, "bf16")
     # grad_w and the stage-1 partials over all rows, from the oracle's partials:
     # a chunk of br * tiles rows starts at block 0 of the round-robin, so the
     # partials of the chunks add tile by tile
     chunk = br * tiles
-    P_ref = np.zeros((tiles, d))
-    Pa = np.zeros((tiles, d))
-    for i in range(0, n, chunk):
-        xc = synth.to_f64(x[i:i + chunk], "bf16")
-        P_ref += ws.partials(xc, dy64[i:i + chunk], br, tiles)
-        Pa += ws.partials(np.abs(xc), np.abs(dy64[i:i + chunk]), br, tiles)
-    r_P = pointwise(to_host(wsb, "f32").reshape(-1, d), P_ref, "f32", S=Pa, name="partials")
-    r_dw = reduced(to_host(dw2, "f32"), P_ref.sum(axis=0), name="dw")
-    for r in (r_y, r_dx, r_P, r_dw):
+
+    def part(i, j):
+        xc = synth.to_f64(x[i:j], "bf16")
+        S = ws.fwd(np.abs(xc), np.abs(w64))
+        ry = pointwise(y_host[i:j], ws.fwd(xc, w64), "bf16", S=S, floor=d * U32 * S, name="y")
+        gx_ref, _ = ws.bwd(dy64[i:j], xc, w64)
+        rdx = exact(dx_host[i:j], to_storage(round_to(gx_ref, "bf16"), "bf16"), "bf16", name="dx")
+        return (ry, rdx, ws.partials(xc, dy64[i:j], br, tiles),
+                ws.partials(np.abs(xc), np.abs(dy64[i:j]), br, tiles))
+
+    parts = chunked(part, n, chunk)
+    r_y, r_dx = [q[0] for q in parts], [q[1] for q in parts]
+    P_ref = np.sum([q[2] for q in parts], axis=0)
+    Pa = np.sum([q[3] for q in parts], axis=0)
+    reps = [combine(r_y, "y(all rows)"), combine(r_dx, "dx(all rows)")]
+    reps.append(pointwise(to_host(wsg.t, "f32").reshape(-1, d), P_ref, "f32", S=Pa, name="partials"))
+    reps.append(reduced(to_host(dwg.t, "f32"), P_ref.sum(axis=0), name="dw", S=Pa.sum(axis=0)))
+    for r in reps:
         print("   ", r, flush=True)
-    assert r_y.ok and r_dx.ok and r_P.ok and r_dw.ok
-    # determinism: two calls, bitwise identical
-    assert torch.equal(dw, dw2) and torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    assert reps[0].n == n and reps[1].n == n * d
+    assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
 
 
 def test_widest_rows_unaligned(gpu_lib):
