@@ -297,6 +297,20 @@ __device__ __forceinline__ ScaledSigmoid sigmoid_for(float x) {
   }
 }
 
+// Workgroups of a launch are dispatched to the 8 XCDs (accelerator dies,
+// each with its own L2) round-robin: workgroup b runs on XCD b % 8.
+// xcd_group(b, count) renumbers [0, count) so that consecutive numbers run on
+// one XCD (XCD k takes the k-th eighth of them): work items that share cache
+// lines then share one L2 instead of fetching the lines once per XCD.  The
+// last count % 8 numbers map to themselves.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_group(int64_t b, int64_t count) {
+  const int64_t full = count / kXcds * kXcds;
+  if (b >= full) return b;
+  return (b % kXcds) * (full / kXcds) + b / kXcds;
+}
+
 // Workgroup barrier that orders LDS accesses only.  The kernels exchange only
 // LDS data across their barriers, so global loads (a prefetched next row) and
 // stores (the previous row's output) issued before it stay in flight instead

@@ -139,15 +139,19 @@ constexpr int kWriterUnroll = 4;
 //
 // Readers.  Rows are cut into blocks of block_rows rows; tile t holds blocks
 // t, t + tiles, t + 2 tiles, ... (with tiles = number of blocks this is one
-// contiguous block per tile).  Reader (g, cb) takes tiles g, g + readers,
-// ... and column block cb.  Each lane accumulates VEC fp32 partials over its
-// rows in increasing row order; the lanes holding the same columns are
-// combined by a butterfly and the four waves through LDS in wave order, and
-// the tile's partial row is written to P[t][.].
+// contiguous block per tile).  Reader (g, cb) takes tiles r, r + readers,
+// ... with r = xcd_group(g, readers), and column block cb, so that readers
+// of neighbouring tiles (whose dy values share cache lines) run on one XCD.
+// Each lane accumulates VEC fp32 partials over its rows in increasing row
+// order; the lanes holding the same columns are combined by a butterfly and
+// the four waves through LDS in wave order, and the tile's partial row is
+// written to P[t][.].  Which reader forms a tile does not change its partial.
 //
-// Writers.  Writer (h, cb) writes grad_x for the row groups h, h + writers,
-// ... (4 G consecutive rows each) and column block cb: grad_x[i, j] =
-// dy[i] w[j], one fp32 product rounded once.
+// Writers.  Writer (h, cb) writes grad_x for column block cb and the spans of
+// kWriterUnroll row groups (4 G consecutive rows each) numbered
+// m, m + writers, ... with m = xcd_group(h, writers): each span's dy values
+// are one contiguous run, and neighbouring spans run on one XCD.
+// grad_x[i, j] = dy[i] w[j], one fp32 product rounded once.
 template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ x, int64_t ld_x, const void* __restrict__ w,
@@ -165,20 +169,22 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
   if (int64_t(blockIdx.x) >= readers) {
     float wr[VEC];
     load_params<VEC>(w, col, d, wdt, wr);
-    const int64_t me = int64_t(blockIdx.x) - readers, writers = int64_t(gridDim.x) - readers;
-    // kWriterUnroll row groups per step: their dy values are loaded together
-    // (rows past the end read dy[n - 1] and store nothing).
+    const int64_t writers = int64_t(gridDim.x) - readers;
+    const int64_t me = xcd_group(int64_t(blockIdx.x) - readers, writers);
+    // One span of kWriterUnroll row groups per step: their dy values are
+    // loaded together (rows past the end read dy[n - 1] and store nothing).
     const int64_t group = int64_t(kWavesPerBlock) * G;
-    for (int64_t r0 = me * group; r0 < n; r0 += kWriterUnroll * writers * group) {
+    const int64_t span = int64_t(kWriterUnroll) * group;
+    for (int64_t r0 = me * span; r0 < n; r0 += writers * span) {
       T gv[kWriterUnroll];
 #pragma unroll
       for (int u = 0; u < kWriterUnroll; ++u) {
-        const int64_t row = r0 + u * writers * group + int64_t(wave) * G + sub;
+        const int64_t row = r0 + u * group + int64_t(wave) * G + sub;
         gv[u] = dy[row < n ? row : n - 1];
       }
 #pragma unroll
       for (int u = 0; u < kWriterUnroll; ++u) {
-        const int64_t row = r0 + u * writers * group + int64_t(wave) * G + sub;
+        const int64_t row = r0 + u * group + int64_t(wave) * G + sub;
         if (row < n && cols_left > 0) {
           const float g = to_f32(gv[u]);
           float gx[VEC];
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void ws_bwd_kernel(
   const int my_row = wave * G + sub;
   const int64_t xstep = int64_t(wg_rows) * ld_x;
 
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += readers) {
+  for (int64_t tile = xcd_group(blockIdx.x, readers); tile < tiles; tile += readers) {
     float acc[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
@@ -309,9 +315,9 @@ hipError_t bwd_typed(const void* dy, const void* x, int64_t ld_x, const void* w,
   const int L = lanes_per_row(d, v);
   const int64_t cw = int64_t(L) * v;
   const int64_t readers = tiles < kBwdReaders ? tiles : kBwdReaders;
-  const int64_t groups = (n + int64_t(kWavesPerBlock) * (kWave / L) - 1) /
-                         (int64_t(kWavesPerBlock) * (kWave / L));
-  const int64_t writers = groups < kBwdWriters ? groups : kBwdWriters;
+  const int64_t span = int64_t(kWavesPerBlock) * (kWave / L) * kWriterUnroll;
+  const int64_t spans = (n + span - 1) / span;
+  const int64_t writers = spans < kBwdWriters ? spans : kBwdWriters;
   const dim3 grid(unsigned(readers + writers), unsigned((d + cw - 1) / cw));
   if (vec)
     ws_bwd_kernel<T, V, kBwdUnroll><<<grid, kThreads, 0, s>>>(
