@@ -14,27 +14,29 @@ in autograd order (all forwards, then the backwards in reverse):
 
 Every input is synthetic, seeded and already resident in HBM when timing
 starts.  `value` is the step's algorithmic HBM bytes (what each kernel must
-read and write once; listed per op in `per_op`) divided by the measured step
-time over K steps whose only instrumentation is one pair of HIP events
-around the `roofline` op (the op with the largest share of the step), on the
-stream the kernels are launched on; its `achieved` comes from those events.
-The per-op breakdown (`per_op`) comes from a separate pass with events around
-every op (those records slow each op slightly); `pairs` sums it per forward +
-backward pair.  `per_op_cold` / `pairs_cold` time each op alone after 1 GiB
-of writes that evict L2 and the 256 MB Infinity Cache (no op finds its
-inputs, or an earlier op's pending write-back, in a cache).  `copy_ceiling` times the library's streaming copy
-(vjp_copy) of as many bytes as the roofline op moves, half read and half
-written, in the same process: the rate at which this GPU reads and writes
-each byte once, which no kernel that moves its bytes once can beat by much;
-`frac_of_copy` compares against it; `frac_of_matched_copy` compares each
-pair with copies of each of its ops' own byte counts, one launch per op.  `cpu_baseline` times the fp64 CPU oracle on a
-bounded sample of the same workloads on one host core.  `extras` times the
-save-the-statistics variants (softmax forward writing the row logsumexp and
-the backward rebuilding y from it; the split cross-entropy forward and
-backward), LayerNorm / RMSNorm forward and backward on the softmax
-workload's [32768, 4096] bf16 inputs, and the embedding gather with its
-deterministic scatter-add backward (16384 Zipf token ids, 32000 x 4096
-table), after and outside the step.
+read and write once) divided by the measured step time over K warm steps
+whose only instrumentation is one pair of HIP events around the `roofline`
+op (the op with the largest share of the step), on the stream the kernels
+are launched on; its `achieved` comes from those events.
+
+`pairs_cold` (the primary per-pair figures) follow the flushed protocol:
+before every launch group (one op: its kernels, stage 2 included; or one
+copy), 1 GiB of plain stores evicts L2 and the 256 MB Infinity Cache; each
+group runs 3 + 20 times and the median of the last 20 is kept.  By default
+the protocol runs in a child process under `rocprofv3 --kernel-trace`
+(started before this process uses the GPU) and a group's time is the sum of
+its kernel durations; if that fails, or this process already runs under a
+profiler, HIP events around each group in this process stand in (the line
+says which).  The protocol also sweeps the launch shapes of the library's
+streaming copy over the largest op's bytes (`copy_ceiling`: the best of
+them) and copies each op's own byte count (`frac_of_matched_copy`).
+`per_op` / `pairs` are the warm step's ops (a separate pass with events
+around every op); `extras` / `extra_pairs_cold` cover the widened rows
+(softmax saving the logsumexp, split cross-entropy, LayerNorm / RMSNorm on
+[32768, 4096] bf16, the embedding gather with its deterministic scatter-add
+backward over 16384 Zipf ids into a 32000 x 4096 table).  `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workloads, on all
+cores and on one.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -309,6 +311,367 @@ def cpu_baseline(scale: float = 1.0, min_seconds: float = 10.0, cores: int | Non
 
 # ----------------------------------------------------------------------------- GPU
 
+PROTOCOL_REPS, PROTOCOL_WARM = 20, 3
+FLUSH_BYTES = 1 << 30
+# Launch shapes of the copy sweep (16-byte vectors in flight per lane, grid bound).
+COPY_SHAPES = [(vpl, wg) for vpl in (2, 4, 8) for wg in (8192, 16384, 32768, 65536)]
+# Forward + backward pairs among the extras.
+EXTRA_PAIRS = [("softmax_lse", ("softmax_fwd_lse", "softmax_bwd_lse")),
+               ("softmax_xent_split", ("softmax_xent_fwd", "softmax_xent_bwd")),
+               ("layernorm", ("layernorm_fwd", "layernorm_bwd")),
+               ("rmsnorm", ("rmsnorm_fwd", "rmsnorm_bwd")),
+               ("gather_rows", ("gather_rows_fwd", "gather_rows_bwd"))]
+
+
+class Workbench:
+    """Seeded inputs (drawn on the device), outputs, workspaces and the
+    marshalled C calls of every op: ``ops`` are the step (all forwards, then
+    the backwards in reverse), ``extra_ops`` the widened rows."""
+
+    def __init__(self, dev):
+        import torch
+
+        import row_wise_backward_amd as rwb
+        import synth
+        from synth.workloads import EMBED, SILU_16M, SOFTMAX, WS_LARGE, XENT
+
+        self.torch, self.rwb, self.L = torch, rwb, rwb.lib
+        L = self.L
+        e = lambda *a, **k: torch.empty(*a, device=dev, **k)  # noqa: E731
+        bf, f32 = torch.bfloat16, torch.float32
+        n_ws, d_ws = WS_LARGE.shape
+        wx = synth.normal_device((n_ws, d_ws), WS_LARGE.sigma_x, "bf16", WS_LARGE.seed, 0, dev)
+        ww = synth.normal_device((d_ws,), WS_LARGE.sigma_w, "bf16", WS_LARGE.seed, 1, dev)
+        wg = synth.normal_device((n_ws,), WS_LARGE.sigma_dy, "bf16", WS_LARGE.seed, 2, dev)
+        wy, wdx, wdw = e(n_ws, dtype=bf), torch.empty_like(wx), e(d_ws, dtype=f32)
+        wws = e(rwb.vjp_weighted_sum_bwd_workspace_size(n_ws, d_ws), dtype=torch.uint8)
+        T_ws = wws.numel() // (4 * d_ws)
+        n_s = SILU_16M.shape[0]
+        sx = synth.normal_device((n_s,), SILU_16M.sigma_x, "f16", SILU_16M.seed, 0, dev)
+        sg = synth.normal_device((n_s,), SILU_16M.sigma_dy, "f16", SILU_16M.seed, 2, dev)
+        sw = torch.tensor([SILU_16M.w_value], dtype=f32, device=dev)
+        sy, sdx, sdw = torch.empty_like(sx), torch.empty_like(sx), e(1, dtype=f32)
+        sws = e(rwb.vjp_scaled_silu_bwd_workspace_size(n_s), dtype=torch.uint8)
+        T_s = sws.numel() // 4
+        r_m, c_m = SOFTMAX.shape
+        mx = synth.normal_device((r_m, c_m), SOFTMAX.sigma_x, "bf16", SOFTMAX.seed, 0, dev)
+        mg = synth.normal_device((r_m, c_m), SOFTMAX.sigma_dy, "bf16", SOFTMAX.seed, 2, dev)
+        my, mdx = torch.empty_like(mx), torch.empty_like(mx)
+        r_x, c_x = XENT.shape
+        z = synth.normal_device((r_x, c_x), XENT.sigma_x, "bf16", XENT.seed, 0, dev)
+        tg = synth.targets_device(r_x, c_x, XENT.seed, dev)
+        dz = torch.empty_like(z)
+        loss, rmax, rlse = e(1, dtype=f32), e(r_x, dtype=f32), e(r_x, dtype=f32)
+        ninv = e(1, dtype=torch.int32)
+        xws = e(rwb.vjp_softmax_xent_workspace_size(r_x), dtype=torch.uint8)
+        scale = XENT.extra["grad_scale"]
+
+        # one checked pass through the binding (host-side shape guards) ...
+        rwb.vjp_weighted_sum_fwd(wx, ww, y=wy)
+        rwb.vjp_scaled_silu_fwd(sx, sw, y=sy)
+        rwb.vjp_softmax_fwd(mx, y=my)
+        rwb.vjp_softmax_xent_fwd_bwd(z, tg, grad_scale=scale, dlogits=dz, loss=loss, row_max=rmax,
+                                     row_lse=rlse, n_invalid=ninv, workspace=xws)
+        rwb.vjp_softmax_bwd(mg, my, dx=mdx)
+        rwb.vjp_scaled_silu_bwd(sg, sx, sw, dx=sdx, dw=sdw, workspace=sws)
+        rwb.vjp_weighted_sum_bwd(wg, wx, ww, dx=wdx, dw=wdw, workspace=wws)
+        torch.cuda.synchronize()
+
+        # ... then the same C calls with their arguments marshalled once
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.P = P
+        self.stream = stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        BF16, F16 = rwb.VJP_BF16, rwb.VJP_F16
+        self.ops = [
+            ("weighted_sum_fwd", L.vjp_weighted_sum_fwd,
+             (P(wx), d_ws, P(ww), P(wy), n_ws, d_ws, BF16, BF16, stream),
+             bytes_weighted_sum_fwd(n_ws, d_ws), n_ws * d_ws),
+            ("scaled_silu_fwd", L.vjp_scaled_silu_fwd, (P(sx), P(sw), P(sy), n_s, F16, stream),
+             bytes_silu_fwd(n_s), n_s),
+            ("softmax_fwd", L.vjp_softmax_fwd, (P(mx), c_m, P(my), c_m, r_m, c_m, BF16, stream),
+             bytes_softmax_fwd(r_m, c_m), r_m * c_m),
+            ("softmax_xent_fwd_bwd", L.vjp_softmax_xent_fwd_bwd,
+             (P(z), c_x, P(tg), r_x, c_x, BF16, ctypes.c_float(scale), P(loss), P(rmax), P(rlse), P(dz),
+              c_x, P(ninv), P(xws), xws.numel(), stream),
+             bytes_xent(r_x, c_x), r_x * c_x),
+            ("softmax_bwd", L.vjp_softmax_bwd, (P(mg), c_m, P(my), c_m, P(mdx), c_m, r_m, c_m, BF16, stream),
+             bytes_softmax_bwd(r_m, c_m), r_m * c_m),
+            ("scaled_silu_bwd", L.vjp_scaled_silu_bwd,
+             (P(sg), P(sx), P(sw), P(sdx), P(sdw), 0, n_s, F16, P(sws), sws.numel(), stream),
+             bytes_silu_bwd(n_s, T_s), n_s),
+            ("weighted_sum_bwd", L.vjp_weighted_sum_bwd,
+             (P(wg), P(wx), d_ws, P(ww), P(wdx), d_ws, P(wdw), 0, n_ws, d_ws, 0, BF16, BF16, P(wws),
+              wws.numel(), stream),
+             bytes_weighted_sum_bwd(n_ws, d_ws, T_ws), n_ws * d_ws),
+        ]
+
+        # Widened rows: the statistics-saving softmax and split cross-entropy on
+        # the same inputs, LayerNorm / RMSNorm on the softmax workload's shape,
+        # the embedding gather and its scatter-add backward.
+        mlse, dz2 = e(r_m, dtype=f32), torch.empty_like(z)
+        dloss = torch.ones(1, dtype=f32, device=dev)
+        nw = synth.normal_device((c_m,), 0.1, "bf16", SOFTMAX.seed, 1, dev) + 1.0
+        nb = synth.normal_device((c_m,), 0.1, "bf16", SOFTMAX.seed, 3, dev)
+        nmean, nrstd = e(r_m, dtype=f32), e(r_m, dtype=f32)
+        ndw, ndb = e(c_m, dtype=f32), e(c_m, dtype=f32)
+        lnws = e(rwb.vjp_layernorm_bwd_workspace_size(r_m, c_m), dtype=torch.uint8)
+        rmsws = e(rwb.vjp_rmsnorm_bwd_workspace_size(r_m, c_m), dtype=torch.uint8)
+        T_ln, T_rms = lnws.numel() // (8 * c_m), rmsws.numel() // (4 * c_m)
+        F32 = ctypes.c_float
+        e_M, e_D = EMBED.shape
+        e_V = EMBED.extra["V"]
+        e_idx = torch.from_numpy(synth.zipf_indices(e_M, e_V, EMBED.seed, EMBED.extra["zipf_a"])).to(dev)
+        e_tab = synth.normal_device((e_V, e_D), 1.0, "bf16", EMBED.seed, 0, dev)
+        e_y = e((e_M, e_D), dtype=bf)
+        e_dy = synth.normal_device((e_M, e_D), 1.0, "bf16", EMBED.seed, 2, dev)
+        e_dt = e((e_V, e_D), dtype=f32)
+        e_ninv = e(1, dtype=torch.int32)
+        e_ws = e(rwb.vjp_gather_rows_bwd_workspace_size(e_M, e_V, e_D), dtype=torch.uint8)
+        self.extra_ops = [
+            ("softmax_fwd_lse", L.vjp_softmax_fwd_lse,
+             (P(mx), c_m, P(my), c_m, P(mlse), r_m, c_m, BF16, stream), bytes_softmax_fwd_lse(r_m, c_m),
+             r_m * c_m),
+            ("softmax_bwd_lse", L.vjp_softmax_bwd_lse,
+             (P(mg), c_m, P(mx), c_m, P(mlse), P(mdx), c_m, r_m, c_m, BF16, stream),
+             bytes_softmax_bwd_lse(r_m, c_m), r_m * c_m),
+            ("softmax_xent_fwd", L.vjp_softmax_xent_fwd,
+             (P(z), c_x, P(tg), r_x, c_x, BF16, P(loss), None, P(rlse), P(ninv), P(xws), xws.numel(),
+              stream), bytes_xent_fwd(r_x, c_x), r_x * c_x),
+            ("softmax_xent_bwd", L.vjp_softmax_xent_bwd,
+             (P(z), c_x, P(tg), P(rlse), r_x, c_x, BF16, P(dloss), P(dz2), c_x, stream),
+             bytes_xent_bwd(r_x, c_x), r_x * c_x),
+            ("layernorm_fwd", L.vjp_layernorm_fwd,
+             (P(mx), c_m, P(nw), P(nb), P(my), c_m, P(nmean), P(nrstd), r_m, c_m, F32(1e-5), BF16, BF16,
+              stream), bytes_layernorm_fwd(r_m, c_m), r_m * c_m),
+            ("layernorm_bwd", L.vjp_layernorm_bwd,
+             (P(mg), c_m, P(mx), c_m, P(nw), P(nmean), P(nrstd), P(mdx), c_m, P(ndw), P(ndb), 0, r_m,
+              c_m, F32(1e-5), BF16, BF16, P(lnws), lnws.numel(), stream),
+             bytes_layernorm_bwd(r_m, c_m, T_ln), r_m * c_m),
+            ("rmsnorm_fwd", L.vjp_rmsnorm_fwd,
+             (P(mx), c_m, P(nw), P(my), c_m, P(nrstd), r_m, c_m, F32(1e-6), BF16, BF16, stream),
+             bytes_rmsnorm_fwd(r_m, c_m), r_m * c_m),
+            ("rmsnorm_bwd", L.vjp_rmsnorm_bwd,
+             (P(mg), c_m, P(mx), c_m, P(nw), P(nrstd), P(mdx), c_m, P(ndw), 0, r_m, c_m, F32(1e-6),
+              BF16, BF16, P(rmsws), rmsws.numel(), stream),
+             bytes_rmsnorm_bwd(r_m, c_m, T_rms), r_m * c_m),
+            ("gather_rows_fwd", L.vjp_gather_rows_fwd,
+             (P(e_tab), e_D, e_V, e_D, P(e_idx), e_M, P(e_y), e_D, BF16, stream),
+             bytes_gather_fwd(e_M, e_D), e_M * e_D),
+            ("gather_rows_bwd", L.vjp_gather_rows_bwd,
+             (P(e_dy), e_D, P(e_idx), e_M, e_V, e_D, P(e_dt), e_D, 0, P(e_ninv), BF16, P(e_ws),
+              e_ws.numel(), stream),
+             bytes_gather_bwd(e_M, e_V, e_D), e_M * e_D),
+        ]
+        self.keep = [v for v in locals().values() if isinstance(v, torch.Tensor)]
+        # copy reference buffers: as many bytes as the largest op moves, half each way
+        self.copy_half = max(o[3] for o in self.ops) // 32 * 16
+        self.ca = e(self.copy_half, dtype=torch.uint8)
+        self.cb = e(self.copy_half, dtype=torch.uint8)
+
+    def call(self, op):
+        name, fn, a = op[0], op[1], op[2]
+        st = fn(*a)
+        if st != 0:
+            raise RuntimeError(f"{name}: status {st} ({self.rwb.vjp_last_error()})")
+
+    def copy(self, nbytes, vpl=4, wg=32768, offset=0):
+        """vjp_copy_shaped of nbytes (rounded down to 16) between the copy buffers."""
+        n = min(nbytes // 16 * 16, self.copy_half)
+        st = self.L.vjp_copy_shaped(ctypes.c_void_p(self.ca.data_ptr() + offset),
+                                    ctypes.c_void_p(self.cb.data_ptr() + offset), n, vpl, wg,
+                                    self.stream)
+        if st != 0:
+            raise RuntimeError(f"vjp_copy_shaped: status {st} ({self.rwb.vjp_last_error()})")
+        return n
+
+
+def protocol_items(wb):
+    """(label, bytes, elements, launch) in launch order: every op of the step and
+    of the extras, the copy of the largest op's bytes at every shape of the
+    sweep, and a copy of each op's own byte count at vjp_copy's shape."""
+    items = [(o[0], o[3], o[4], (lambda o=o: wb.call(o))) for o in wb.ops + wb.extra_ops]
+    big = 2 * wb.copy_half
+    for vpl, wg in COPY_SHAPES:
+        items.append((f"copy_sweep {vpl}x{wg}", big, big, lambda v=vpl, g=wg: wb.copy(big // 2, v, g)))
+    for o in wb.ops + wb.extra_ops:
+        nb = min(o[3] // 32 * 16, wb.copy_half)
+        items.append((f"copy_matched {o[0]}", 2 * nb, 2 * nb, lambda n=nb: wb.copy(n)))
+    return items
+
+
+def run_protocol(wb, items, log_every=10):
+    """Each item PROTOCOL_WARM + PROTOCOL_REPS times: 1 GiB of plain stores
+    (torch's fill, one kernel) that evict L2 and the 256 MB Infinity Cache,
+    then the item's launches, then a device synchronisation.  HIP events on the
+    launch stream bracket the item's launches; returns their times (ms)."""
+    torch = wb.torch
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=wb.ca.device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for k, (label, _, _, launch) in enumerate(items):
+        ts = []
+        for r in range(PROTOCOL_WARM + PROTOCOL_REPS):
+            flush.fill_(r % 251)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= PROTOCOL_WARM:
+                ts.append(e0.elapsed_time(e1))
+        out.append(ts)
+        if k % log_every == 0:
+            print(f"[bench protocol] {k + 1}/{len(items)} {label}", file=sys.stderr, flush=True)
+    del flush
+    return out
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return 0.5 * (v[(n - 1) // 2] + v[n // 2]) if n else float("nan")
+
+
+def protocol_child(plan_file) -> int:
+    """Runs the protocol (under rocprofv3, started by the parent): one marker
+    copy of 4 KiB through unaligned pointers (the only byte-loop copy_bytes
+    launch), then every item; writes the item labels and the event medians to
+    plan_file."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wb = Workbench(dev)
+    items = protocol_items(wb)
+    for it in items:                       # one untimed pass of everything
+        it[3]()
+    torch.cuda.synchronize()
+    wb.copy(4096, offset=1)                # marker (byte-loop copy kernel): the protocol starts after it
+    torch.cuda.synchronize()
+    times = run_protocol(wb, items)
+    with open(plan_file, "w") as f:
+        json.dump({"labels": [it[0] for it in items],
+                   "event_median_ms": [_median(t) for t in times]}, f)
+    return 0
+
+
+def parse_protocol_trace(csv_path, labels):
+    """Kernel durations of the protocol from a rocprofv3 kernel trace: after
+    the marker copy (the copy_bytes launch), every fill kernel (the
+    flush) opens a launch group; groups follow the labels in order, each
+    PROTOCOL_WARM + PROTOCOL_REPS times.  Returns, per label, the median over
+    the timed groups of the summed kernel durations (ms) and the median of
+    each kernel's duration."""
+    import csv
+
+    with open(csv_path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    start = next(i for i, r in enumerate(rows) if "copy_bytes" in r["Kernel_Name"])
+    groups = []
+    for r in rows[start + 1:]:
+        name = r["Kernel_Name"]
+        if "FillFunctor" in name:
+            groups.append([])
+        elif groups:
+            groups[-1].append((name, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6))
+    per = PROTOCOL_WARM + PROTOCOL_REPS
+    if len(groups) != per * len(labels):
+        raise RuntimeError(f"trace has {len(groups)} launch groups, expected {per * len(labels)}")
+    out = {}
+    for k, label in enumerate(labels):
+        gs = groups[k * per + PROTOCOL_WARM:(k + 1) * per]
+        kern = {}
+        for g in gs:
+            for name, ms in g:
+                kern.setdefault(name, []).append(ms)
+        out[label] = {"ms": _median([sum(ms for _, ms in g) for g in gs]),
+                      "kernels": {n: {"median_ms": round(_median(v), 5), "launches": len(v)}
+                                  for n, v in kern.items()}}
+    return out
+
+
+def under_profiler() -> bool:
+    return any(k.startswith("ROCPROF") for k in os.environ)
+
+
+def protocol_via_rocprof(timeout=600):
+    """The protocol in a child process under rocprofv3 --kernel-trace, started
+    before this process uses the GPU.  Returns (per-label results, command) or
+    (None, reason)."""
+    import glob
+    import shutil
+    import subprocess
+    import tempfile
+
+    exe = shutil.which("rocprofv3")
+    if exe is None:
+        return None, "rocprofv3 not found"
+    tmp = tempfile.mkdtemp(prefix="vjp_protocol_")
+    plan = os.path.join(tmp, "plan.json")
+    cmd = [exe, "--kernel-trace", "--output-format", "csv", "-d", tmp, "-o", "protocol", "--",
+           sys.executable, os.path.abspath(__file__), "--protocol-child", plan]
+    try:
+        r = subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True,
+                           timeout=timeout)
+        if not os.path.exists(plan):
+            tail = (r.stderr or "")[-600:]
+            return None, f"protocol child exited {r.returncode} without results: {tail}"
+        with open(plan) as f:
+            labels = json.load(f)["labels"]
+        csvs = glob.glob(os.path.join(tmp, "**", "protocol_kernel_trace.csv"), recursive=True)
+        if not csvs:
+            return None, "no kernel trace written"
+        return parse_protocol_trace(csvs[0], labels), " ".join(
+            ["rocprofv3", "--kernel-trace", "--output-format", "csv", "-d", "<tmp>", "-o", "protocol",
+             "--", "python3", "bench.py", "--protocol-child", "<tmp>/plan.json"])
+    except Exception as exc:  # the event protocol in this process replaces it
+        return None, f"{type(exc).__name__}: {exc}"
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def op_row(name, ms, nbytes, nelem, **extra):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    row = {"op": name, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
+           "frac_of_peak": round(gbs / PEAK_GBS, 4), "elements_per_s": round(nelem / (ms * 1e-3), 1)}
+    row.update(extra)
+    return row
+
+
+def pair_rows(pairs, by_name, copy_gbs, matched_ms=None):
+    out = []
+    for pname, members in pairs:
+        if not all(m in by_name for m in members):
+            continue
+        ms = sum(by_name[m]["ms"] for m in members)
+        nbytes = sum(by_name[m]["bytes"] for m in members)
+        row = op_row(pname, ms, nbytes, sum(by_name[m]["elements_per_s"] * by_name[m]["ms"] * 1e-3
+                                            for m in members))
+        del row["elements_per_s"]
+        row["frac_of_copy"] = round(row["GB/s"] / copy_gbs, 4) if copy_gbs else None
+        if matched_ms is not None:
+            mm = sum(matched_ms[m] for m in members)
+            row["matched_copy_ms"] = round(mm, 5)
+            row["frac_of_matched_copy"] = round(mm / ms, 4)
+        out.append(row)
+    return out
+
+
+def protocol_summary_md(res, source, command, path):
+    """Markdown table of the protocol's per-kernel medians (written for profiles/)."""
+    lines = [f"# Fwd+bwd pairs, flushed: {source}", "",
+             f"Command: `python3 bench.py --protocol-summary {path}` (its protocol child ran "
+             f"`{command}`).", "",
+             f"Each launch group ran {PROTOCOL_WARM} + {PROTOCOL_REPS} times after 1 GiB of plain "
+             "stores (torch fill) that evict L2 and the Infinity Cache; medians over the last "
+             f"{PROTOCOL_REPS}.", "",
+             "| Group | Kernel | Launches | Median µs |", "|---|---|---|---|"]
+    for label, r in res.items():
+        for name, k in r["kernels"].items():
+            lines.append(f"| {label} | `{name[:90]}` | {k['launches']} | {k['median_ms'] * 1e3:.2f} |")
+        lines.append(f"| {label} | (sum) | | {r['ms'] * 1e3:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,108 +679,50 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-scale", type=float, default=1.0)
+    ap.add_argument("--protocol", choices=["rocprof", "events", "off"], default="rocprof",
+                    help="flushed per-op medians: kernel durations from a rocprofv3 child "
+                         "(default; HIP events in this process when the child fails or this "
+                         "process already runs under a profiler), HIP events only, or none")
+    ap.add_argument("--protocol-summary", metavar="PATH",
+                    help="also write the per-kernel medians of the protocol as markdown")
+    ap.add_argument("--protocol-child", metavar="PLAN", help=argparse.SUPPRESS)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy before timing (counter calibration)")
     args = ap.parse_args()
+    if args.protocol_child:
+        return protocol_child(args.protocol_child)
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(the ops shard by rows with no exchange except one small grad_w all-reduce, "
               "which is not built here)", file=sys.stderr)
         return 2
 
-    import torch
+    # The flushed protocol first, in a child under rocprofv3, before this
+    # process touches the GPU.
+    proto, proto_source, proto_note = None, None, None
+    if args.protocol == "rocprof" and not under_profiler():
+        print("[bench] protocol child under rocprofv3 (flushed per-op medians)", file=sys.stderr,
+              flush=True)
+        proto, proto_note = protocol_via_rocprof()
+        if proto is not None:
+            proto_source = "rocprofv3 kernel trace (sum of the kernel durations of each launch group)"
+        else:
+            print(f"[bench] rocprofv3 protocol unavailable: {proto_note}", file=sys.stderr, flush=True)
 
-    import row_wise_backward_amd as rwb
-    import synth
-    from synth.workloads import SILU_16M, SOFTMAX, WS_LARGE, XENT
+    import torch
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    L = rwb.lib
     print(f"[bench] device {torch.cuda.get_device_name(dev)}; generating inputs", file=sys.stderr, flush=True)
-
-    # inputs (seeded, drawn on the device) and outputs
-    n_ws, d_ws = WS_LARGE.shape
-    wx = synth.normal_device((n_ws, d_ws), WS_LARGE.sigma_x, "bf16", WS_LARGE.seed, 0, dev)
-    ww = synth.normal_device((d_ws,), WS_LARGE.sigma_w, "bf16", WS_LARGE.seed, 1, dev)
-    wg = synth.normal_device((n_ws,), WS_LARGE.sigma_dy, "bf16", WS_LARGE.seed, 2, dev)
-    wy = torch.empty(n_ws, dtype=torch.bfloat16, device=dev)
-    wdx = torch.empty_like(wx)
-    wdw = torch.empty(d_ws, dtype=torch.float32, device=dev)
-    T_ws = rwb.vjp_weighted_sum_bwd_workspace_size(n_ws, d_ws) // (4 * d_ws)
-    wws = torch.empty(rwb.vjp_weighted_sum_bwd_workspace_size(n_ws, d_ws), dtype=torch.uint8, device=dev)
-
-    n_s = SILU_16M.shape[0]
-    sx = synth.normal_device((n_s,), SILU_16M.sigma_x, "f16", SILU_16M.seed, 0, dev)
-    sg = synth.normal_device((n_s,), SILU_16M.sigma_dy, "f16", SILU_16M.seed, 2, dev)
-    sw = torch.tensor([SILU_16M.w_value], dtype=torch.float32, device=dev)
-    sy, sdx = torch.empty_like(sx), torch.empty_like(sx)
-    sdw = torch.empty(1, dtype=torch.float32, device=dev)
-    T_s = rwb.vjp_scaled_silu_bwd_workspace_size(n_s) // 4
-    sws = torch.empty(rwb.vjp_scaled_silu_bwd_workspace_size(n_s), dtype=torch.uint8, device=dev)
-
-    r_m, c_m = SOFTMAX.shape
-    mx = synth.normal_device((r_m, c_m), SOFTMAX.sigma_x, "bf16", SOFTMAX.seed, 0, dev)
-    mg = synth.normal_device((r_m, c_m), SOFTMAX.sigma_dy, "bf16", SOFTMAX.seed, 2, dev)
-    my, mdx = torch.empty_like(mx), torch.empty_like(mx)
-
-    r_x, c_x = XENT.shape
-    z = synth.normal_device((r_x, c_x), XENT.sigma_x, "bf16", XENT.seed, 0, dev)
-    tg = synth.targets_device(r_x, c_x, XENT.seed, dev)
-    dz = torch.empty_like(z)
-    loss = torch.empty(1, dtype=torch.float32, device=dev)
-    rmax = torch.empty(r_x, dtype=torch.float32, device=dev)
-    rlse = torch.empty(r_x, dtype=torch.float32, device=dev)
-    ninv = torch.empty(1, dtype=torch.int32, device=dev)
-    xws = torch.empty(rwb.vjp_softmax_xent_workspace_size(r_x), dtype=torch.uint8, device=dev)
-    scale = XENT.extra["grad_scale"]
-
-    # one checked pass through the binding (host-side shape guards) ...
-    rwb.vjp_weighted_sum_fwd(wx, ww, y=wy)
-    rwb.vjp_scaled_silu_fwd(sx, sw, y=sy)
-    rwb.vjp_softmax_fwd(mx, y=my)
-    rwb.vjp_softmax_xent_fwd_bwd(z, tg, grad_scale=scale, dlogits=dz, loss=loss, row_max=rmax,
-                                 row_lse=rlse, n_invalid=ninv, workspace=xws)
-    rwb.vjp_softmax_bwd(mg, my, dx=mdx)
-    rwb.vjp_scaled_silu_bwd(sg, sx, sw, dx=sdx, dw=sdw, workspace=sws)
-    rwb.vjp_weighted_sum_bwd(wg, wx, ww, dx=wdx, dw=wdw, workspace=wws)
-    torch.cuda.synchronize()
-
-    # ... then the same C calls with their arguments marshalled once
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    BF16, F16 = rwb.VJP_BF16, rwb.VJP_F16
-    ops = [
-        ("weighted_sum_fwd", L.vjp_weighted_sum_fwd,
-         (P(wx), d_ws, P(ww), P(wy), n_ws, d_ws, BF16, BF16, stream),
-         bytes_weighted_sum_fwd(n_ws, d_ws), n_ws * d_ws),
-        ("scaled_silu_fwd", L.vjp_scaled_silu_fwd, (P(sx), P(sw), P(sy), n_s, F16, stream),
-         bytes_silu_fwd(n_s), n_s),
-        ("softmax_fwd", L.vjp_softmax_fwd, (P(mx), c_m, P(my), c_m, r_m, c_m, BF16, stream),
-         bytes_softmax_fwd(r_m, c_m), r_m * c_m),
-        ("softmax_xent_fwd_bwd", L.vjp_softmax_xent_fwd_bwd,
-         (P(z), c_x, P(tg), r_x, c_x, BF16, ctypes.c_float(scale), P(loss), P(rmax), P(rlse), P(dz),
-          c_x, P(ninv), P(xws), xws.numel(), stream),
-         bytes_xent(r_x, c_x), r_x * c_x),
-        ("softmax_bwd", L.vjp_softmax_bwd, (P(mg), c_m, P(my), c_m, P(mdx), c_m, r_m, c_m, BF16, stream),
-         bytes_softmax_bwd(r_m, c_m), r_m * c_m),
-        ("scaled_silu_bwd", L.vjp_scaled_silu_bwd,
-         (P(sg), P(sx), P(sw), P(sdx), P(sdw), 0, n_s, F16, P(sws), sws.numel(), stream),
-         bytes_silu_bwd(n_s, T_s), n_s),
-        ("weighted_sum_bwd", L.vjp_weighted_sum_bwd,
-         (P(wg), P(wx), d_ws, P(ww), P(wdx), d_ws, P(wdw), 0, n_ws, d_ws, 0, BF16, BF16, P(wws),
-          wws.numel(), stream),
-         bytes_weighted_sum_bwd(n_ws, d_ws, T_ws), n_ws * d_ws),
-    ]
+    wb = Workbench(dev)
+    ops = wb.ops
     step_bytes = sum(o[3] for o in ops)
 
     def step(evs=None):
-        for i, (name, fn, a, _, _) in enumerate(ops):
+        for i, op in enumerate(ops):
             if evs is not None:
                 evs[i][0].record()
-            st = fn(*a)
-            if st != 0:
-                raise RuntimeError(f"{name}: status {st} ({rwb.vjp_last_error()})")
+            wb.call(op)
             if evs is not None:
                 evs[i][1].record()
 
@@ -433,50 +738,20 @@ def main() -> int:
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # Per-op breakdown: a separate pass with HIP events around every op.  The
-    # event records between the kernels slow the step by ~7% and each op a
-    # little, so this pass is not the timed one; it also picks the op with the
-    # largest share of the step (the roofline kernel).
+    # Per-op breakdown of the warm step: a separate pass with HIP events around
+    # every op (the records between the kernels slow the step by ~7%, so this
+    # pass is not the timed one); it also picks the op with the largest share
+    # of the step (the roofline kernel).
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
             for _ in ops] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
-    per_op = []
-    for i, (name, _, _, nbytes, nelem) in enumerate(ops):
-        ms = sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)) / args.steps
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        per_op.append({"op": name, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
-                       "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                       "elements_per_s": round(nelem / (ms * 1e-3), 1)})
+    per_op = [op_row(o[0], sum(evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps))
+                     / args.steps, o[3], o[4]) for i, o in enumerate(ops)]
     i_dom = max(range(len(ops)), key=lambda i: per_op[i]["ms"])
-
-    # Cold per-op pass: before every op, 1 GiB of writes evicts L2 and the
-    # 256 MB Infinity Cache, so no op finds its inputs, or the write-back of
-    # an earlier op's outputs, in a cache.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    n_cold = max(3, args.steps // 2)
-    cold_evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                 for _ in ops] for _ in range(n_cold)]
-    for k in range(n_cold):
-        for i, (name, fn, a, _, _) in enumerate(ops):
-            flush.fill_(k % 251)
-            cold_evs[k][i][0].record()
-            st = fn(*a)
-            if st != 0:
-                raise RuntimeError(f"{name}: status {st} ({rwb.vjp_last_error()})")
-            cold_evs[k][i][1].record()
-    torch.cuda.synchronize()
-    del flush
-    per_op_cold = []
-    for i, (name, _, _, nbytes, nelem) in enumerate(ops):
-        ms = sum(cold_evs[k][i][0].elapsed_time(cold_evs[k][i][1]) for k in range(n_cold)) / n_cold
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        per_op_cold.append({"op": name, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
-                            "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                            "elements_per_s": round(nelem / (ms * 1e-3), 1)})
-    print(f"[bench] per-op passes done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] per-op pass done; timing {args.steps} steps", file=sys.stderr, flush=True)
 
     # The timed region: K steps with HIP events around the roofline kernel only
     # (on its launch stream), bracketed by device synchronisations.
@@ -485,167 +760,87 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        for i, (name, fn, a, _, _) in enumerate(ops):
+        for i, op in enumerate(ops):
             if i == i_dom:
                 dev_evs[k][0].record()
-            st = fn(*a)
-            if st != 0:
-                raise RuntimeError(f"{name}: status {st} ({rwb.vjp_last_error()})")
+            wb.call(op)
             if i == i_dom:
                 dev_evs[k][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed / args.steps * 1e3
-    ms_dom = sum(e[0].elapsed_time(e[1]) for e in dev_evs) / args.steps
-    dom = dict(per_op[i_dom])
-    dom["GB/s"] = round(dom["bytes"] / (ms_dom * 1e-3) / 1e9, 1)
+    ms_dom = sum(ev[0].elapsed_time(ev[1]) for ev in dev_evs) / args.steps
+    dom = op_row(ops[i_dom][0], ms_dom, ops[i_dom][3], ops[i_dom][4])
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; {dom['op']} {ms_dom * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
-    # Save-the-statistics variants (softmax with saved logsumexp, split
-    # cross-entropy), timed after the step on the same inputs; not part of it.
-    mlse = torch.empty(r_m, dtype=torch.float32, device=dev)
-    dz2 = torch.empty_like(z)
-    dloss = torch.ones(1, dtype=torch.float32, device=dev)
-    # LayerNorm / RMSNorm on the softmax workload's shape (x = mx, dy = mg)
-    nw = synth.normal_device((c_m,), 0.1, "bf16", SOFTMAX.seed, 1, dev) + 1.0
-    nb = synth.normal_device((c_m,), 0.1, "bf16", SOFTMAX.seed, 3, dev)
-    nmean = torch.empty(r_m, dtype=torch.float32, device=dev)
-    nrstd = torch.empty(r_m, dtype=torch.float32, device=dev)
-    ndw = torch.empty(c_m, dtype=torch.float32, device=dev)
-    ndb = torch.empty(c_m, dtype=torch.float32, device=dev)
-    T_ln = rwb.vjp_layernorm_bwd_workspace_size(r_m, c_m) // (8 * c_m)
-    lnws = torch.empty(rwb.vjp_layernorm_bwd_workspace_size(r_m, c_m), dtype=torch.uint8, device=dev)
-    T_rms = rwb.vjp_rmsnorm_bwd_workspace_size(r_m, c_m) // (4 * c_m)
-    rmsws = torch.empty(rwb.vjp_rmsnorm_bwd_workspace_size(r_m, c_m), dtype=torch.uint8, device=dev)
-    F32 = ctypes.c_float
-    # Embedding lookup and its scatter-add backward (Zipf token ids)
-    from synth.workloads import EMBED
-    e_M, e_D = EMBED.shape
-    e_V = EMBED.extra["V"]
-    e_idx = torch.from_numpy(synth.zipf_indices(e_M, e_V, EMBED.seed, EMBED.extra["zipf_a"])).to(dev)
-    e_tab = synth.normal_device((e_V, e_D), 1.0, "bf16", EMBED.seed, 0, dev)
-    e_y = torch.empty((e_M, e_D), dtype=torch.bfloat16, device=dev)
-    e_dy = synth.normal_device((e_M, e_D), 1.0, "bf16", EMBED.seed, 2, dev)
-    e_dt = torch.empty((e_V, e_D), dtype=torch.float32, device=dev)
-    e_ninv = torch.empty(1, dtype=torch.int32, device=dev)
-    e_ws = torch.empty(rwb.vjp_gather_rows_bwd_workspace_size(e_M, e_V, e_D), dtype=torch.uint8,
-                       device=dev)
-    extra_ops = [
-        ("softmax_fwd_lse", L.vjp_softmax_fwd_lse,
-         (P(mx), c_m, P(my), c_m, P(mlse), r_m, c_m, BF16, stream), bytes_softmax_fwd_lse(r_m, c_m),
-         r_m * c_m),
-        ("softmax_bwd_lse", L.vjp_softmax_bwd_lse,
-         (P(mg), c_m, P(mx), c_m, P(mlse), P(mdx), c_m, r_m, c_m, BF16, stream),
-         bytes_softmax_bwd_lse(r_m, c_m), r_m * c_m),
-        ("softmax_xent_fwd", L.vjp_softmax_xent_fwd,
-         (P(z), c_x, P(tg), r_x, c_x, BF16, P(loss), None, P(rlse), P(ninv), P(xws), xws.numel(),
-          stream), bytes_xent_fwd(r_x, c_x), r_x * c_x),
-        ("softmax_xent_bwd", L.vjp_softmax_xent_bwd,
-         (P(z), c_x, P(tg), P(rlse), r_x, c_x, BF16, P(dloss), P(dz2), c_x, stream),
-         bytes_xent_bwd(r_x, c_x), r_x * c_x),
-        ("layernorm_fwd", L.vjp_layernorm_fwd,
-         (P(mx), c_m, P(nw), P(nb), P(my), c_m, P(nmean), P(nrstd), r_m, c_m, F32(1e-5), BF16, BF16,
-          stream), bytes_layernorm_fwd(r_m, c_m), r_m * c_m),
-        ("layernorm_bwd", L.vjp_layernorm_bwd,
-         (P(mg), c_m, P(mx), c_m, P(nw), P(nmean), P(nrstd), P(mdx), c_m, P(ndw), P(ndb), 0, r_m, c_m,
-          F32(1e-5), BF16, BF16, P(lnws), lnws.numel(), stream),
-         bytes_layernorm_bwd(r_m, c_m, T_ln), r_m * c_m),
-        ("rmsnorm_fwd", L.vjp_rmsnorm_fwd,
-         (P(mx), c_m, P(nw), P(my), c_m, P(nrstd), r_m, c_m, F32(1e-6), BF16, BF16, stream),
-         bytes_rmsnorm_fwd(r_m, c_m), r_m * c_m),
-        ("gather_rows_fwd", L.vjp_gather_rows_fwd,
-         (P(e_tab), e_D, e_V, e_D, P(e_idx), e_M, P(e_y), e_D, BF16, stream),
-         bytes_gather_fwd(e_M, e_D), e_M * e_D),
-        ("gather_rows_bwd", L.vjp_gather_rows_bwd,
-         (P(e_dy), e_D, P(e_idx), e_M, e_V, e_D, P(e_dt), e_D, 0, P(e_ninv), BF16, P(e_ws),
-          e_ws.numel(), stream),
-         bytes_gather_bwd(e_M, e_V, e_D), e_M * e_D),
-        ("rmsnorm_bwd", L.vjp_rmsnorm_bwd,
-         (P(mg), c_m, P(mx), c_m, P(nw), P(nrstd), P(mdx), c_m, P(ndw), 0, r_m, c_m, F32(1e-6), BF16,
-          BF16, P(rmsws), rmsws.numel(), stream),
-         bytes_rmsnorm_bwd(r_m, c_m, T_rms), r_m * c_m),
-    ]
+    # Widened rows (warm, events around each op), after and outside the step.
     n_extra = max(3, args.steps // 2)
     xevs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-             for _ in extra_ops] for _ in range(n_extra + 1)]
+             for _ in wb.extra_ops] for _ in range(n_extra + 1)]
     for k in range(n_extra + 1):          # the first round is a warmup
-        for i, (name, fn, a, _, _) in enumerate(extra_ops):
+        for i, op in enumerate(wb.extra_ops):
             xevs[k][i][0].record()
-            st = fn(*a)
-            if st != 0:
-                raise RuntimeError(f"{name}: status {st} ({rwb.vjp_last_error()})")
+            wb.call(op)
             xevs[k][i][1].record()
     torch.cuda.synchronize()
-    extras = []
-    for i, (name, _, _, nbytes, nelem) in enumerate(extra_ops):
-        ms = sum(xevs[k][i][0].elapsed_time(xevs[k][i][1]) for k in range(1, n_extra + 1)) / n_extra
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        extras.append({"op": name, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
-                       "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                       "elements_per_s": round(nelem / (ms * 1e-3), 1)})
-    print(f"[bench] timed the statistics-saving variants ({n_extra} rounds)", file=sys.stderr, flush=True)
+    extras = [op_row(o[0], sum(xevs[k][i][0].elapsed_time(xevs[k][i][1]) for k in range(1, n_extra + 1))
+                     / n_extra, o[3], o[4]) for i, o in enumerate(wb.extra_ops)]
+    print(f"[bench] timed the widened rows ({n_extra} rounds)", file=sys.stderr, flush=True)
 
-    # Copy ceiling: vjp_copy (16-byte nontemporal loads and stores) of as many
-    # bytes as the roofline op moves, half read and half written, in this
-    # process: the rate at which this GPU reads and writes each byte once.
-    half = dom["bytes"] // 32 * 16
-    ca = torch.empty(half, dtype=torch.uint8, device=dev)
-    cb = torch.empty_like(ca)
-    cevs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(6)]
-    for e in cevs:                        # the first copy is a warmup
-        e[0].record()
-        st = L.vjp_copy(P(ca), P(cb), half, stream)
-        if st != 0:
-            raise RuntimeError(f"vjp_copy: status {st} ({rwb.vjp_last_error()})")
-        e[1].record()
+    # Flushed protocol: from the rocprofv3 child, else HIP events here.
+    items = protocol_items(wb)
+    if proto is None and args.protocol != "off":
+        times = run_protocol(wb, items)
+        proto = {it[0]: {"ms": _median(t)} for it, t in zip(items, times)}
+        proto_source = "HIP events on the launch stream around each launch group"
+        if proto_note is None and under_profiler():
+            proto_note = "this process runs under a profiler"
+    result_protocol, pairs_cold, extra_pairs_cold, copy_ceiling = None, None, None, None
+    if proto is not None:
+        by_label = {it[0]: it for it in items}
+        per_op_cold = [op_row(o[0], proto[o[0]]["ms"], o[3], o[4]) for o in ops]
+        extras_cold = [op_row(o[0], proto[o[0]]["ms"], o[3], o[4]) for o in wb.extra_ops]
+        sweep = []
+        for vpl, wg in COPY_SHAPES:
+            lab = f"copy_sweep {vpl}x{wg}"
+            sweep.append({"vectors_per_lane": vpl, "max_workgroups": wg, "ms": round(proto[lab]["ms"], 5),
+                          "GB/s": round(by_label[lab][1] / (proto[lab]["ms"] * 1e-3) / 1e9, 1)})
+        best = max(sweep, key=lambda c: c["GB/s"])
+        copy_gbs = best["GB/s"]
+        matched = {o[0]: proto[f"copy_matched {o[0]}"]["ms"] for o in ops + wb.extra_ops}
+        by_name = {r["op"]: r for r in per_op_cold + extras_cold}
+        pairs_cold = pair_rows(PAIRS, by_name, copy_gbs, matched)
+        extra_pairs_cold = pair_rows(EXTRA_PAIRS, by_name, copy_gbs, matched)
+        copy_ceiling = {"GB/s": copy_gbs, "bytes": 2 * wb.copy_half,
+                        "best_shape": {"vectors_per_lane": best["vectors_per_lane"],
+                                       "max_workgroups": best["max_workgroups"]},
+                        "sweep": sweep,
+                        "kernel": "vjp_copy_shaped (16-byte nontemporal loads and stores), flushed, median"}
+        result_protocol = {"source": proto_source, "note": proto_note, "reps": PROTOCOL_REPS,
+                           "warmup_reps": PROTOCOL_WARM, "statistic": "median",
+                           "flush": "1 GiB of plain stores (torch fill) before every launch group",
+                           "per_op": per_op_cold, "extras": extras_cold}
+        if args.protocol_summary and "kernels" in next(iter(proto.values())):
+            with open(args.protocol_summary, "w") as f:
+                f.write(protocol_summary_md(proto, proto_source, proto_note, args.protocol_summary))
+        dom_cold = by_name[dom["op"]]
+        print(f"[bench] protocol ({proto_source.split(' (')[0]}): "
+              + ", ".join(f"{p['op']} {p['frac_of_peak']:.3f}" for p in pairs_cold),
+              file=sys.stderr, flush=True)
+    else:
+        dom_cold = None
+
+    # warm pairs, against the warm copy of the roofline op's bytes
+    cevs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(6)]
+    for ev in cevs:                       # the first copy is a warmup
+        ev[0].record()
+        wb.copy(wb.copy_half)
+        ev[1].record()
     torch.cuda.synchronize()
-    ms_copy = sum(e[0].elapsed_time(e[1]) for e in cevs[1:]) / (len(cevs) - 1)
-    copy_gbs = 2 * half / (ms_copy * 1e-3) / 1e9
-
-    # Size-matched copies: a copy of each op's own byte count (half read, half
-    # written) in its own launch, so that a small op is compared with a copy
-    # that pays the same launch and ramp costs.  Successive copies move
-    # through the buffers, so a small copy does not find its source in a cache.
-    copy_ms_cache = {}
-
-    def copy_ms(nbytes):
-        n = min(nbytes // 32 * 16, half)
-        if n not in copy_ms_cache:
-            evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                   for _ in range(6)]
-            for k, e in enumerate(evs):
-                off = (k * n) % (half - n + 16) // 16 * 16
-                e[0].record()
-                st = L.vjp_copy(ctypes.c_void_p(ca.data_ptr() + off),
-                               ctypes.c_void_p(cb.data_ptr() + off), n, stream)
-                if st != 0:
-                    raise RuntimeError(f"vjp_copy: status {st} ({rwb.vjp_last_error()})")
-                e[1].record()
-            torch.cuda.synchronize()
-            copy_ms_cache[n] = sum(e[0].elapsed_time(e[1]) for e in evs[1:]) / (len(evs) - 1)
-        return copy_ms_cache[n]
-
-    # Forward + backward pairs (from the per-op passes).
-    def pair_figures(rows):
-        by_name = {o["op"]: o for o in rows}
-        out = []
-        for pname, members in PAIRS:
-            ms = sum(by_name[m]["ms"] for m in members)
-            nbytes = sum(by_name[m]["bytes"] for m in members)
-            gbs = nbytes / (ms * 1e-3) / 1e9
-            ms_matched = sum(copy_ms(by_name[m]["bytes"]) for m in members)
-            out.append({"op": pname, "ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
-                        "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                        "frac_of_copy": round(gbs / copy_gbs, 4),
-                        "matched_copy_ms": round(ms_matched, 5),
-                        "frac_of_matched_copy": round(ms_matched / ms, 4)})
-        return out
-
-    pairs = pair_figures(per_op)
-    pairs_cold = pair_figures(per_op_cold)
-    del ca, cb
+    ms_copy = sum(ev[0].elapsed_time(ev[1]) for ev in cevs[1:]) / (len(cevs) - 1)
+    warm_copy_gbs = 2 * wb.copy_half / (ms_copy * 1e-3) / 1e9
+    pairs = pair_rows(PAIRS, {r["op"]: r for r in per_op}, warm_copy_gbs)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -666,6 +861,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "storage_dtype": ("bf16 (weighted_sum, softmax, softmax_xent), fp16 (scaled_silu); fp32 "
+                          "parameter gradients, row statistics and partials; all arithmetic fp32"),
         "data": "synthetic (seeded normal draws on the device; uniform int32 targets)",
         "config": {
             "workload": ("one fwd+bwd of each op: weighted_sum bf16 1048576x256, scaled_silu "
@@ -673,12 +870,13 @@ def main() -> int:
             "step_bytes": step_bytes,
             "frac_of_peak": round(value / PEAK_GBS, 4),
         },
+        "pairs_cold": pairs_cold,
+        "extra_pairs_cold": extra_pairs_cold,
+        "protocol": result_protocol,
+        "copy_ceiling": copy_ceiling,
         "per_op": per_op,
         "pairs": pairs,
-        "per_op_timing": "separate pass, HIP events around every op (not the timed steps)",
-        "per_op_cold": per_op_cold,
-        "pairs_cold": pairs_cold,
-        "per_op_cold_timing": "each op alone after 1 GiB of writes that evict L2 and the Infinity Cache",
+        "per_op_timing": "warm step: separate pass, HIP events around every op (not the timed steps)",
         "extras": extras,
         "roofline": {
             "kernel": dom["op"],
@@ -688,18 +886,20 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(dom["GB/s"] / PEAK_GBS, 4),
             "traffic": traffic,
-        },
-        "copy_ceiling": {
-            "GB/s": round(copy_gbs, 1),
-            "bytes": 2 * half,
-            "kernel": "vjp_copy (16-byte nontemporal loads and stores), same process",
-            "roofline_frac_of_copy": round(dom["GB/s"] / copy_gbs, 4),
+            "timing": "HIP events around the kernel's launches in the timed steps, mean",
+            "frac_flushed_median": dom_cold["frac_of_peak"] if dom_cold else None,
+            "frac_of_warm_copy": round(dom["GB/s"] / warm_copy_gbs, 4),
         },
         "cpu_baseline": None,
     }
+    del wb
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(args.cpu_scale)
+        print("[bench] timing the CPU oracle on a sample (all cores, then one)", file=sys.stderr, flush=True)
+        try:
+            result["cpu_baseline"] = cpu_baseline(args.cpu_scale)
+        except Exception as exc:
+            result["cpu_baseline"] = {"error": f"{type(exc).__name__}: {exc}"}
     print(json.dumps(result), flush=True)
     return 0
 

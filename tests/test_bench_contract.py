@@ -52,3 +52,35 @@ def test_cpu_baseline_small_sample():
 
 def test_cpu_cores_is_bounded():
     assert 1 <= bench.cpu_cores() <= 16
+
+
+def test_protocol_trace_parsing(tmp_path):
+    """Launch groups open at every fill kernel after the marker copy; each
+    label's groups are its 3 + 20 repetitions; a group's time is the sum of
+    its kernel durations; medians over the last 20."""
+    labels = ["op_a", "op_b"]
+    rows = [("torch_setup_kernel", 0, 5), ("vjp::copy_bytes(...)", 10, 11)]
+    t = 100
+    per = bench.PROTOCOL_WARM + bench.PROTOCOL_REPS
+    for k, lab in enumerate(labels):
+        for r in range(per):
+            rows.append(("at::native::FillFunctor<unsigned char>", t, t + 50))
+            t += 60
+            d1 = 1000 + 10 * r + 5000 * k           # stage 1 grows with r: median is r = 12.5
+            rows.append((f"stage1_{lab}", t, t + d1))
+            t += d1 + 5
+            rows.append((f"stage2_{lab}", t, t + 4))
+            t += 10
+    path = tmp_path / "trace.csv"
+    with open(path, "w") as f:
+        f.write('"Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for name, a, b in rows:
+            f.write(f'"{name}",{a},{b}\n')
+    res = bench.parse_protocol_trace(str(path), labels)
+    for k, lab in enumerate(labels):
+        med_r = (bench.PROTOCOL_WARM + (bench.PROTOCOL_WARM + bench.PROTOCOL_REPS - 1)) / 2
+        want_ns = 1000 + 10 * med_r + 5000 * k + 4
+        assert abs(res[lab]["ms"] - want_ns * 1e-6) < 1e-12
+        assert res[lab]["kernels"][f"stage2_{lab}"]["launches"] == bench.PROTOCOL_REPS
+    with pytest.raises(RuntimeError):
+        bench.parse_protocol_trace(str(path), labels + ["missing"])
