@@ -188,6 +188,22 @@ int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx,
                         int accumulate, int64_t n, vjp_dtype_t act, void* workspace,
                         size_t workspace_bytes, vjp_stream_t stream);
 
+/* vjp_scaled_silu_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid hipMalloc).  It allocates nothing and calls no allocating routine:
+ * the stage-1 partials go to a 16 KB buffer the library holds in device
+ * memory, one per GPU it runs on, kept until the process ends.  That buffer
+ * holds at most 4096 partials, which covers every n (the backward never forms
+ * more than 4096 tiles); a larger need would return VJP_EINVAL.  Every call on
+ * one GPU uses the same buffer: calls that overlap on one GPU (different
+ * streams, no ordering between them) race and give wrong dw; calls ordered on
+ * one stream are safe.  Nothing in the buffer needs clearing between calls
+ * (each call writes every partial it reads).  Arguments, results, summation
+ * order and errors are those of vjp_scaled_silu_bwd. */
+int vjp_scaled_silu_bwd_noalloc(const void* dy, const void* x, const float* w, void* dx,
+                                float* dw, int accumulate, int64_t n, vjp_dtype_t act,
+                                vjp_stream_t stream);
+
 /* ---------------------------------------------------------------- row softmax
  * y[r, j] = exp(x[r, j] - m_r) / sum_k exp(x[r, k] - m_r), m_r = max_k x[r, k].
  * The backward needs only the saved y: with s_r = sum_j dy[r, j] y[r, j],

@@ -51,6 +51,7 @@ _SIGS = {
     "vjp_scaled_silu_elems_per_tile": ([_i64], _i64),
     "vjp_scaled_silu_bwd_workspace_size": ([_i64], _sz),
     "vjp_scaled_silu_bwd": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _int, _vp, _sz, _vp], _int),
+    "vjp_scaled_silu_bwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _int, _i64, _int, _vp], _int),
     "vjp_softmax_fwd": ([_vp, _i64, _vp, _i64, _i64, _i64, _int, _vp], _int),
     "vjp_softmax_bwd": ([_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _int, _vp], _int),
     "vjp_softmax_fwd_lse": ([_vp, _i64, _vp, _i64, _vp, _i64, _i64, _int, _vp], _int),
@@ -277,6 +278,21 @@ def vjp_scaled_silu_bwd(dy, x, w, dx=None, dw=None, accumulate=False, workspace=
     _check(lib.vjp_scaled_silu_bwd(_ptr(_flat(dy)), _ptr(x), _ptr(w), _ptr(_flat(dx)), _ptr(dw),
                                    int(bool(accumulate)), x.numel(), _dt(x), _ptr(ws),
                                    _nbytes(ws), _stream(x)), "vjp_scaled_silu_bwd")
+    return dx, dw
+
+
+def vjp_scaled_silu_bwd_noalloc(dy, x, w, dx, dw, accumulate=False):
+    """vjp_scaled_silu_bwd for callers that cannot allocate: dx and dw are the
+    caller's; the partials go to the library's per-GPU scratch (no workspace,
+    nothing allocated).  Calls that overlap on one GPU race."""
+    x = _flat(x)
+    _expect(dy, x.shape, x.dtype, x.device, "dy")
+    _expect(w, (1,), torch.float32, x.device, "w")
+    _expect(dx, x.shape, x.dtype, x.device, "dx")
+    _expect(dw, (1,), torch.float32, x.device, "dw")
+    _check(lib.vjp_scaled_silu_bwd_noalloc(_ptr(_flat(dy)), _ptr(x), _ptr(w), _ptr(_flat(dx)),
+                                           _ptr(dw), int(bool(accumulate)), x.numel(), _dt(x),
+                                           _stream(x)), "vjp_scaled_silu_bwd_noalloc")
     return dx, dw
 
 

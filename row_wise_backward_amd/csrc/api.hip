@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "launch.hpp"
 #include "libvjp.h"
@@ -299,9 +300,30 @@ VJP_API size_t vjp_scaled_silu_bwd_workspace_size(int64_t n) {
   return size_t((n + e - 1) / e) * sizeof(float);
 }
 
-VJP_API int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx,
-                                float* dw, int accumulate, int64_t n, vjp_dtype_t act, void* workspace,
-                                size_t workspace_bytes, vjp_stream_t stream) {
+namespace {
+
+// Shared body of the two scaled-SiLU backwards: validation of everything but
+// the partials buffer P (T = tiles(n) floats, checked by the caller), then
+// stage 1 and the fixed-order stage 2.
+int scaled_silu_bwd_impl(const void* dy, const void* x, const float* w, void* dx, float* dw,
+                         int accumulate, int64_t n, int act, Range scratch, float* P,
+                         vjp_stream_t stream) {
+  const int es = dtype_size(act);
+  VJP_TRY(check_alias({span(dx, n * es, "dx"), span(dw, 4, "dw"), scratch},
+                      {span(dy, n * es, "dy"), span(x, n * es, "x"), span(w, n > 0 ? 4 : 0, "w")}));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ept = resolve_elems_per_tile(n);
+  const int64_t T = (n + ept - 1) / ept;
+  if (T > 0) {
+    const bool vec = aligned(dy, 16) && aligned(x, 16) && aligned(dx, 16);
+    const hipError_t e = launch_scaled_silu_bwd_stage1(dy, x, w, dx, P, n, ept, act, vec, s);
+    if (e != hipSuccess) return hip_status(e, "scaled_silu_bwd stage 1");
+  }
+  return hip_status(launch_reduce_partials(P, T, 1, dw, accumulate, s), "scaled_silu_bwd stage 2");
+}
+
+int scaled_silu_bwd_args(const void* dy, const void* x, const float* w, void* dx, float* dw,
+                         int accumulate, int64_t n, int act) {
   if (!dtype_ok(act)) return fail(VJP_EDTYPE, "unknown dtype");
   if (n < 0) return fail(VJP_EINVAL, "negative size");
   if (n > kMaxElems) return fail(VJP_EINVAL, "size too large");
@@ -312,25 +334,79 @@ VJP_API int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, v
   VJP_TRY(check_vector("w", w, n > 0 ? 1 : 0, 4));
   VJP_TRY(check_vector("dx", dx, n, es));
   VJP_TRY(check_vector("dw", dw, 1, 4));
+  return VJP_OK;
+}
+
+}  // namespace
+
+VJP_API int vjp_scaled_silu_bwd(const void* dy, const void* x, const float* w, void* dx,
+                                float* dw, int accumulate, int64_t n, vjp_dtype_t act, void* workspace,
+                                size_t workspace_bytes, vjp_stream_t stream) {
+  VJP_TRY(scaled_silu_bwd_args(dy, x, w, dx, dw, accumulate, n, act));
   const size_t need = vjp_scaled_silu_bwd_workspace_size(n);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(VJP_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
     if (!aligned(workspace, 4)) return fail(VJP_EALIGN, "workspace is not 4-byte aligned");
   }
-  VJP_TRY(check_alias({span(dx, n * es, "dx"), span(dw, 4, "dw"),
-                       span(workspace, int64_t(need), "workspace")},
-                      {span(dy, n * es, "dy"), span(x, n * es, "x"), span(w, n > 0 ? 4 : 0, "w")}));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return scaled_silu_bwd_impl(dy, x, w, dx, dw, accumulate, n, act,
+                              span(workspace, int64_t(need), "workspace"),
+                              static_cast<float*>(workspace), stream);
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+//
+// Scratch of vjp_scaled_silu_bwd_noalloc: the stage-1 partials, one float per
+// tile.  The tiling never forms more than 4096 tiles (resolve_elems_per_tile),
+// so 16 KB serve every n.  A __device__ array: each GPU the library runs on
+// holds its own copy, at its own address, until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and only that address reaches kernels.
+constexpr int64_t kNoallocScratchFloats = 4096;
+static __device__ __align__(256) float scratch[kNoallocScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the calling thread's current device.
+hipError_t scratch_address(float** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<float*>(p) : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+}  // namespace
+
+VJP_API int vjp_scaled_silu_bwd_noalloc(const void* dy, const void* x, const float* w, void* dx,
+                                        float* dw, int accumulate, int64_t n, vjp_dtype_t act,
+                                        vjp_stream_t stream) {
+  VJP_TRY(scaled_silu_bwd_args(dy, x, w, dx, dw, accumulate, n, act));
   const int64_t ept = resolve_elems_per_tile(n);
   const int64_t T = (n + ept - 1) / ept;
-  float* P = static_cast<float*>(workspace);
+  if (T > kNoallocScratchFloats)
+    return fail(VJP_EINVAL, "n = %lld needs %lld partials, above the %lld of the scratch",
+                static_cast<long long>(n), static_cast<long long>(T),
+                static_cast<long long>(kNoallocScratchFloats));
+  float* P = nullptr;
   if (T > 0) {
-    const bool vec = aligned(dy, 16) && aligned(x, 16) && aligned(dx, 16);
-    const hipError_t e = launch_scaled_silu_bwd_stage1(dy, x, w, dx, P, n, ept, act, vec, s);
-    if (e != hipSuccess) return hip_status(e, "scaled_silu_bwd stage 1");
+    const hipError_t e = scratch_address(&P);
+    if (e != hipSuccess) return hip_status(e, "scaled_silu_bwd_noalloc scratch address");
   }
-  return hip_status(launch_reduce_partials(P, T, 1, dw, accumulate, s), "scaled_silu_bwd stage 2");
+  return scaled_silu_bwd_impl(dy, x, w, dx, dw, accumulate, n, act,
+                              span(P, T * int64_t(sizeof(float)), "scratch"), P, stream);
 }
 
 // ------------------------------------------------------------------ softmax
