@@ -672,6 +672,146 @@ def protocol_summary_md(res, source, command, path):
     return "\n".join(lines) + "\n"
 
 
+COUNTER_CMD = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c} -o run -- python3 bench.py "
+               "--protocol off --steps 2 --warmup 1 --no-cpu-baseline --calib-copy")
+
+
+def counters_summary(fetch_csv, write_csv, md_path, json_path):
+    """HBM bytes per kernel from two rocprofv3 counter runs of this script
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+    same counter reads for the 1 GiB device copy that --calib-copy runs
+    (rocclr copyBuffer), against each kernel's algorithmic bytes.  Writes the
+    markdown table and the roofline op's bytes per launch (with the digest of
+    its sources) as JSON."""
+    import csv
+    import re
+
+    def load(path, counter):
+        d = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                n = r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+                if "rocclr_copyBuffer" in n:
+                    n = "copyBuffer"
+                elif "vjp" in n:
+                    n = re.sub(r"\(.*", "", n).replace("vjp::", "")
+                    n = re.sub(r"^_ZN3vjp12_GLOBAL__N_1\d+", "", n)
+                else:
+                    continue
+                d.setdefault((n, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in d.items()}
+
+    f, w = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    calib = max((k for k in f if k[0] == "copyBuffer"), key=lambda k: f[k])
+    ff, fw = f[calib] / (1 << 20), w[calib] / (1 << 20)
+    RX, CX, RM, CM, NW, DW = 16384, 32000, 32768, 4096, 1048576, 256
+    algo = {
+        "xent_resident<bf16, 8, 16, 4, false, true>": 2 * RX * CX * 2 + RX * 4 + RX * 12,
+        "xent_resident<bf16, 8, 8, 8, false, false>": RX * CX * 2 + RX * 4 + RX * 8,
+        "xent_bwd_kernel<bf16, 8, 4, 1024>": 2 * RX * CX * 2 + RX * 8 + 4,
+        "xent_finalize_kernel": RX * 8 + 8,
+        "ws_bwd_kernel<bf16, 8, 4>": NW * 2 + 2 * NW * DW * 2 + DW * 2 + 1024 * DW * 4,
+        "ws_fwd_kernel<bf16, 8, 4, false>": NW * DW * 2 + DW * 2 + NW * 2,
+        "softmax_bwd_resident<bf16, 8, 8, 1, false>": 3 * RM * CM * 2,
+        "softmax_bwd_resident<bf16, 8, 4, 2, true>": 3 * RM * CM * 2 + RM * 4,
+        "softmax_fwd_resident<bf16, 8, 4, 2, true>": 2 * RM * CM * 2,
+        "norm_fwd_resident<bf16, 8, 4, 2, false, 2, 2>": 2 * RM * CM * 2 + 2 * CM * 2 + RM * 8,
+        "norm_fwd_resident<bf16, 8, 4, 2, true, 1, 2>": 2 * RM * CM * 2 + CM * 2 + RM * 4,
+        "norm_bwd_tile<bf16, 8, 8, 1, false>": 3 * RM * CM * 2 + CM * 2 + RM * 8 + 512 * 2 * CM * 4,
+        "norm_bwd_tile<bf16, 8, 8, 1, true>": 3 * RM * CM * 2 + CM * 2 + RM * 4 + 512 * CM * 4,
+        "silu_fwd_kernelIDF16_Li8ELi8EEEvPKT_PKfPS2_ll": 2 * (1 << 24) * 2 + 4,
+        "silu_bwd_kernelIDF16_Li8ELi2EEEvPKT_S4_PKfPS2_Pfll": 3 * (1 << 24) * 2 + 4 + 4096 * 4,
+        "reduce_scalar_kernel": 4096 * 4 + 4,
+        "gather_rows_fwd<bf16, 8>": 2 * 16384 * 4096 * 2 + 16384 * 4,
+        "copy_vec16<4>": None,
+    }
+    algo_grid = {  # the stage-2 reduction, by its grid (columns / 32 workgroups of 1024 threads)
+        ("reduce_partials_kernel<true>", 8 * 1024): 1024 * DW * 4 + DW * 4,
+        ("reduce_partials_kernel<true>", 256 * 1024): 512 * 2 * CM * 4 + 2 * CM * 4,
+        ("reduce_partials_kernel<true>", 128 * 1024): 512 * CM * 4 + CM * 4,
+    }
+    cmd_f, cmd_w = COUNTER_CMD.format(c="FETCH_SIZE"), COUNTER_CMD.format(c="WRITE_SIZE")
+    lines = ["# HBM traffic counters per kernel", "",
+             "Commands (one counter per run; `--calib-copy` runs a 1 GiB device copy for the "
+             "calibration):", "", f"`{cmd_f}`", "", f"`{cmd_w}`", "",
+             f"Summarised by `python3 bench.py --counters-summary <FETCH_SIZE csv> <WRITE_SIZE csv> "
+             f"{md_path} {json_path}`.", "",
+             f"Calibration: the 1 GiB copy reads FETCH_SIZE {f[calib]:.1f} KiB (factor {ff:.4f} of "
+             f"the bytes read) and WRITE_SIZE {w[calib]:.1f} KiB (factor {fw:.4f} of the bytes "
+             "written); every kernel's counters are divided by these factors.", "",
+             f"Cross-entropy source digest: {source_digest()}", "",
+             "| kernel | grid (threads) | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (scaled) | "
+             "written bytes (scaled) | algorithmic bytes | traffic / algorithmic |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(f, key=lambda k: -f[k]):
+        if k[0] == "copyBuffer":
+            continue
+        rd, wr = f[k] / ff * 1024, w.get(k, 0.0) / fw * 1024
+        a = algo_grid.get(k) or algo.get(k[0])
+        if k[0].startswith("copy_vec16"):
+            a = round(rd + wr)      # a copy: bytes read = bytes written
+        ratio = f"{(rd + wr) / a:.4f}" if a else "-"
+        lines.append(f"| {k[0]} | {k[1]} | {f[k]:.1f} | {w.get(k, 0.0):.1f} | {rd:.4g} | {wr:.4g} | "
+                     f"{a if a else '-'} | {ratio} |")
+    lines += ["", "The row gather reads less than its algorithmic bytes: its 16384 Zipf-distributed ids "
+              "repeat table rows, and repeated rows are served from L2.  The scatter-add's dy reads are "
+              "split between chunk_sums (positions in runs longer than 32) and scatter_listed_rows (the "
+              "rest); its writes, the whole fp32 table of 32000 x 4096 x 4 bytes, are split between the "
+              "zero rows written beside the plan (radix_pass_fused, plan_tail) and scatter_listed_rows "
+              "(the rest of the zero rows and the selected rows)."]
+    with open(md_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    main_k = next(k for k in f if k[0] == "xent_resident<bf16, 8, 16, 4, false, true>")
+    fin_k = next(k for k in f if k[0] == "xent_finalize_kernel")
+    tb = (f[main_k] / ff + w[main_k] / fw + f[fin_k] / ff + w[fin_k] / fw) * 1024
+    with open(json_path, "w") as fh:
+        json.dump({"op": "softmax_xent_fwd_bwd", "kernels": [main_k[0], fin_k[0]],
+                   "source_digest": source_digest(), "fetch_kib": f[main_k] + f[fin_k],
+                   "write_kib": w[main_k] + w[fin_k], "fetch_factor": ff, "write_factor": fw,
+                   "bytes_per_launch": round(tb),
+                   "algorithmic_bytes": algo[main_k[0]] + algo[fin_k[0]],
+                   "commands": [cmd_f, cmd_w]}, fh, indent=1)
+    return 0
+
+
+STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o run -- "
+             "python3 bench.py --protocol off --no-cpu-baseline --steps 10 --warmup 3")
+
+
+def stats_summary(stats_csv, bench_json, md_path):
+    """Markdown table of a rocprofv3 --stats kernel summary of the warm step
+    (STATS_CMD), with the bench line that run printed: the roofline kernel's
+    average duration there is the one its live HIP events are checked against."""
+    import csv
+
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    with open(bench_json) as f:
+        line = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    rf = line["roofline"]
+    ev_us = rf["bytes"] / (rf["achieved"] * 1e9) * 1e6 if "bytes" in rf else None
+    lines = ["# Warm step: rocprofv3 kernel statistics", "",
+             f"Command: `{STATS_CMD}` (kernel durations over the warmup, the per-op pass, the timed "
+             "steps, the widened rows and the warm copies; no flushed protocol).", "",
+             f"Summarised by `python3 bench.py --stats-summary <kernel_stats.csv> <bench line> {md_path}`.",
+             "", f"That run's bench line: {line['ms_per_step']} ms per step, roofline op "
+             f"{rf['kernel']} at {rf['achieved']} GB/s from HIP events around its launches in the "
+             f"timed steps ({rf['frac']} of 8 TB/s)."]
+    if ev_us is not None:
+        lines.append(f"The events give {ev_us:.1f} µs per launch of that op.")
+    lines += ["", "| Kernel | Calls | Average µs | Min µs | Max µs | Share of GPU time |",
+              "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f}% |")
+    with open(md_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -686,11 +826,19 @@ def main() -> int:
     ap.add_argument("--protocol-summary", metavar="PATH",
                     help="also write the per-kernel medians of the protocol as markdown")
     ap.add_argument("--protocol-child", metavar="PLAN", help=argparse.SUPPRESS)
+    ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "MD", "JSON"),
+                    help="summarise two rocprofv3 counter runs of this script (no GPU used)")
+    ap.add_argument("--stats-summary", nargs=3, metavar=("STATS_CSV", "BENCH_JSON", "MD"),
+                    help="summarise a rocprofv3 --stats run of this script (no GPU used)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy before timing (counter calibration)")
     args = ap.parse_args()
     if args.protocol_child:
         return protocol_child(args.protocol_child)
+    if args.counters_summary:
+        return counters_summary(*args.counters_summary)
+    if args.stats_summary:
+        return stats_summary(*args.stats_summary)
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(the ops shard by rows with no exchange except one small grad_w all-reduce, "
@@ -885,6 +1033,8 @@ def main() -> int:
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dom["GB/s"] / PEAK_GBS, 4),
+            "bytes": dom["bytes"],
+            "us_per_launch": round(ms_dom * 1e3, 2),
             "traffic": traffic,
             "timing": "HIP events around the kernel's launches in the timed steps, mean",
             "frac_flushed_median": dom_cold["frac_of_peak"] if dom_cold else None,
