@@ -24,6 +24,10 @@
 // once, nothing of their size is written); xent_bwd_kernel is then a map over
 // the logits with dz = scale * (exp(z - lse) - [j == t]), where the upstream
 // gradient of the mean loss is read from device memory, scale = dloss / rows.
+//
+// Every kernel here takes its row from xcd_block_x(): the workgroups of one
+// XCD work through one contiguous band of rows.  Which workgroup takes a row
+// does not change its results.
 #include "launch.hpp"
 #include "rowops.hpp"
 
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(NT) void xent_bwd_kernel(
     const T* z, int64_t ld, const int32_t* __restrict__ targets,
     const float* __restrict__ row_lse, const float* __restrict__ dloss, int64_t total_rows,
     int64_t C, T* dz, int64_t ld_dz) {
-  const int64_t row = blockIdx.x;
+  const int64_t row = xcd_block_x();
   const float L = row_lse[row];
   const int64_t t = targets[row];
   const float scale = *dloss / float(total_rows);
@@ -108,8 +112,7 @@ __global__ __launch_bounds__(row_block_threads<WAVES>()) void xent_resident(
   __shared__ float buf[2][WAVES];   // one slot per reduction of the row
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int64_t row = WAVES == 1 ? int64_t(blockIdx.x) * rows_per_block<1>() + wave
-                                 : int64_t(blockIdx.x);
+  const int64_t row = WAVES == 1 ? xcd_block_x() * rows_per_block<1>() + wave : xcd_block_x();
   const int wv = WAVES == 1 ? 0 : wave;
   if (WAVES == 1 && row >= rows) return;
   constexpr int64_t kStep = int64_t(WAVES) * kWave * VEC;
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(kStreamThreads) void xent_stream(
     float scale, float* __restrict__ row_max, float* __restrict__ row_lse,
     float* __restrict__ row_loss, T* __restrict__ dz, int64_t ld_dz) {
   __shared__ float bm[kStreamThreads / kWave], bl[kStreamThreads / kWave];
-  const int64_t row = blockIdx.x;
+  const int64_t row = xcd_block_x();
   const T* zr = z + row * ld;
   T* dr = dz + row * ld_dz;
   const int64_t t = targets[row];
