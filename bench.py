@@ -593,7 +593,7 @@ def under_profiler() -> bool:
     return any(k.startswith("ROCPROF") for k in os.environ)
 
 
-def protocol_via_rocprof(timeout=600):
+def protocol_via_rocprof(timeout=300):
     """The protocol in a child process under rocprofv3 --kernel-trace, started
     before this process uses the GPU.  Returns (per-label results, command) or
     (None, reason)."""
