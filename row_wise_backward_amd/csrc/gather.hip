@@ -30,15 +30,18 @@
 // order), ranking equal digits within a wave with eight ballots and across
 // waves and rounds with counts in LDS.
 //
-// For M <= 16384 the same plan takes three launches instead of a dozen: one
-// kernel per radix pass (each block counts the digits of all M keys itself
-// instead of reading a scanned table) and one workgroup for the run bounds,
-// the chunks and a list of the selected rows; step 4 then runs from that
-// list.  The rows never selected are zero-filled by extra workgroups of the
+// For M <= 16384 the plan takes one launch when the keys fit 15 bits
+// (V + 1 <= 32768: a stable counting sort, plan_count) and three otherwise
+// (one kernel per radix pass, each block counting the digits of all M keys
+// itself instead of reading a scanned table, then one workgroup for the run
+// bounds, the chunks and a list of the selected rows), instead of a dozen;
+// step 4 then runs from the list of selected rows.  The rows never selected are zero-filled by extra workgroups of the
 // plan's own launches, which otherwise leave most of the chip idle.  The
 // arrays and every result bit are the same on both paths.
 #include "launch.hpp"
 #include "common.hpp"
+
+#include <atomic>
 
 namespace vjp {
 
@@ -254,6 +257,12 @@ constexpr int64_t kFillBytes = int64_t(128) << 10;       // zeros per fill workg
 constexpr int64_t kFillFirstPassBytes = int64_t(64) << 20;
 constexpr int64_t kFillPassBytes = int64_t(128) << 20;
 constexpr int64_t kFillTailBytes = int64_t(96) << 20;
+// Zeros beside the single-launch plan (plan_count), whose 16 sort
+// workgroups take about 25 us on their own.  (Measured for the same
+// workload: plan_count 28.7 / 33.4 / 40.6 / 44.1 us with 96 / 128 / 160 /
+// 192 MB beside it, the listed-rows kernel 88.1 / 84.2 / 80.6 / 77.0 us: the
+// zeros it sheds cost it less than they cost the plan.)
+constexpr int64_t kFillCountBytes = int64_t(96) << 20;
 constexpr int kFillUnroll = 16;
 
 // Zeros to one fp32 row of D values, by the whole workgroup.
@@ -534,6 +543,231 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tail(
   }
 }
 
+// Single-launch plan (M <= kPlanMaxM indices, keys 0 .. V with V + 1 <=
+// kCountKeys): a stable counting sort.  Every sort workgroup counts the keys
+// of all M indices, and those of the indices before its own kCountBlock, in
+// LDS; the prefix sum of the counts is where each key's run starts, so the
+// workgroup places each of its keys at: run start + equal keys in earlier
+// workgroups + rank among equal keys in its own block, the rank coming from a
+// bitonic sort of its (key, local position) pairs in LDS (the composite is
+// unique, so equal keys keep increasing position: the stable order, which is
+// unique, hence the same sorted keys and positions as the radix passes).  The
+// same prefix sums give the run bounds of every key, the chunk offsets and
+// owners of runs longer than kRun, the list of selected rows and the invalid
+// count (the run of key V); the keys of scan step i are written by sort
+// workgroup i mod (sort workgroups).  Workgroups past the sort's write zero
+// rows, as beside the radix passes.  One launch instead of three.
+//
+// The counts are plain LDS atomic increments, one per index and lane: a
+// duplicate-matching step (ballots over the 15 key bits, one add per distinct
+// key) cost more than the serialised adds it saves, even on Zipf-skewed ids.
+// The scans run wave-major: wave w owns keys [2048 w, 2048 (w + 1)), lane l
+// the LDS word of keys 2 l, 2 l + 1 of each 128-key step, so the LDS reads
+// are consecutive words and the global writes consecutive keys.
+constexpr int kCountThreads = 1024;
+constexpr int kCountWaves = kCountThreads / kWave;
+constexpr int64_t kCountKeys = 32768;             // keys 0 .. V, V + 1 <= kCountKeys
+constexpr int kCountBlock = 1024;                 // keys placed per workgroup
+constexpr int kCountLoads = 16;                   // index loads in flight per lane (counting)
+constexpr int64_t kWaveKeys = kCountKeys / kCountWaves;      // keys per wave in the scans
+constexpr int kPairSteps = int(kWaveKeys / (2 * kWave));      // 128-key steps per wave
+constexpr int kCountWords = int(kCountKeys / 2);
+static_assert(kCountBlock == kCountThreads, "one key per thread in the placement");
+static_assert(2 * kPlanMaxM <= 65535, "16-bit counts");
+static_assert(kPlanMaxM / kCountBlock <= kCountWaves, "every wave's keys have a writer");
+
+// Two 16-bit counters per LDS word, key k in half k & 1 of word k / 2 (every
+// count and every sum stored below is at most 2 M <= 32768).
+__device__ __forceinline__ int32_t get16(const uint32_t* a, int64_t k) {
+  return int32_t((a[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (integers, exact): a
+// doubling scan within each row of 16 lanes on DPP row shifts (lanes shifted
+// in from before the row read 0), then the totals of rows 0, 1 and 2, read
+// from lanes 15, 31 and 47, added to the rows after them.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xF, 0xF, false));   // row_shr:1
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xF, 0xF, false));   // row_shr:2
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xF, 0xF, false));   // row_shr:4
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xF, 0xF, false));   // row_shr:8
+  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(x), 15));
+  const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(x), 31));
+  const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(x), 47));
+  const int row = int(threadIdx.x % kWave) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Per key: its count plus 2^16 if it is a selected table row (so one sum
+// carries both the run starts and the row-list offsets; neither total
+// exceeds M < 2^16), and its number of chunks.  Key V (invalid indices) has
+// a run but is no table row; keys past V count nothing.
+__device__ __forceinline__ uint32_t key_ar(uint32_t n, int64_t k, int64_t V) {
+  return n + ((k < V && n > 0) ? 0x10000u : 0u);
+}
+__device__ __forceinline__ uint32_t key_chunks(uint32_t n, int64_t k, int64_t V) {
+  return (k < V && n > uint32_t(kRun)) ? (n + kRun - 1) / kRun : 0u;
+}
+
+// The plan arrays of key k: run [run, run + n), chunk offset q with its
+// nch owner entries, its place rr in the row list; for key V the invalid count.
+__device__ __forceinline__ void emit_key(int64_t k, int64_t V, uint32_t n, uint32_t ar,
+                                         uint32_t q, uint32_t nch, int32_t* __restrict__ seg_begin,
+                                         int32_t* __restrict__ seg_end,
+                                         int32_t* __restrict__ chunk_off,
+                                         int32_t* __restrict__ owner, int32_t* __restrict__ rows,
+                                         int32_t* __restrict__ n_invalid) {
+  if (k > V) return;
+  const int32_t run = int32_t(ar & 0xFFFFu);
+  seg_begin[k] = run;
+  seg_end[k] = run + int32_t(n);
+  if (k < V) {
+    chunk_off[k] = int32_t(q);
+    for (uint32_t c = 0; c < nch; ++c) owner[q + c] = int32_t(k);
+    if (n > 0) rows[ar >> 16] = int32_t(k);
+  } else if (n_invalid != nullptr) {
+    *n_invalid = int32_t(n);                         // the run of key V
+  }
+}
+
+__global__ __launch_bounds__(kCountThreads) void plan_count(
+    const int32_t* __restrict__ idx, int64_t M, int64_t V, int32_t* __restrict__ sk,
+    int32_t* __restrict__ sv, int32_t* __restrict__ seg_begin, int32_t* __restrict__ seg_end,
+    int32_t* __restrict__ chunk_off, int32_t* __restrict__ owner, int32_t* __restrict__ rows,
+    int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid, FillShare fs) {
+  __shared__ uint32_t cnt_all[kCountWords];         // counts, then run starts + earlier equals
+  __shared__ uint32_t cnt_before[kCountWords];      // counts of the keys before this block
+  __shared__ uint32_t srt[kCountBlock];             // this block's (key, position) pairs
+  __shared__ uint32_t wsum[2][kCountWaves];         // per-wave totals of the scans
+  static_assert(kCountBlock >= kFillMaxRows / 32, "fill bitmap fits in srt");
+  const int64_t nb = (M + kCountBlock - 1) / kCountBlock;
+  const int64_t b = blockIdx.x;
+  if (b >= nb) {
+    zero_unselected_rows<kCountThreads>(fs, b - nb, srt);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t lo = b * kCountBlock;
+  const int64_t mine_j = lo + tid;
+  const int32_t mine_key = key_of(idx, mine_j < M ? mine_j : M - 1, V);   // loaded early
+  for (int i = tid; i < kCountWords; i += kCountThreads) {
+    cnt_all[i] = 0;
+    cnt_before[i] = 0;
+  }
+  lds_barrier();
+  constexpr int64_t kStride = int64_t(kCountThreads);
+  for (int64_t j0 = tid; j0 < M; j0 += kStride * kCountLoads) {
+    int32_t key[kCountLoads];
+#pragma unroll
+    for (int u = 0; u < kCountLoads; ++u) {
+      const int64_t j = j0 + u * kStride;
+      key[u] = key_of(idx, j < M ? j : M - 1, V);
+    }
+#pragma unroll
+    for (int u = 0; u < kCountLoads; ++u) {
+      const int64_t j = j0 + u * kStride;
+      if (j < M) {
+        const uint32_t one = 1u << (16 * (key[u] & 1));
+        atomicAdd(&cnt_all[key[u] >> 1], one);
+        if (j < lo) atomicAdd(&cnt_before[key[u] >> 1], one);
+      }
+    }
+  }
+  lds_barrier();
+  // Scans over the keys 0 .. V.  First each wave's totals ...
+  const int64_t kw0 = int64_t(wave) * kWaveKeys;
+  uint32_t ar = 0, ch = 0;
+  for (int i = 0; i < kPairSteps; ++i) {
+    const int64_t k = kw0 + int64_t(i) * (2 * kWave) + 2 * lane;
+    if (k - 2 * lane > V) break;                   // wave-uniform: no key left
+    const uint32_t w = cnt_all[k >> 1];
+    ar += key_ar(w & 0xFFFFu, k, V) + key_ar(w >> 16, k + 1, V);
+    ch += key_chunks(w & 0xFFFFu, k, V) + key_chunks(w >> 16, k + 1, V);
+  }
+  ar = uint32_t(wave_sum_i32(int(ar)));
+  ch = uint32_t(wave_sum_i32(int(ch)));
+  if (lane == 0) {
+    wsum[0][wave] = ar;
+    wsum[1][wave] = ch;
+  }
+  lds_barrier();
+  uint32_t base_ar = 0, base_ch = 0, tot_ar = 0, tot_ch = 0;
+#pragma unroll
+  for (int w = 0; w < kCountWaves; ++w) {
+    const uint32_t x = wsum[0][w], y = wsum[1][w];
+    if (w < wave) {
+      base_ar += x;
+      base_ch += y;
+    }
+    tot_ar += x;
+    tot_ch += y;
+  }
+  if (b == 0 && tid == 0) {
+    chunk_off[V] = int32_t(tot_ch);
+    *n_rows = int32_t(tot_ar >> 16);
+  }
+  // ... then the prefix of every key: its LDS half becomes run start + equal
+  // keys in earlier workgroups (only this lane reads or writes its word).
+  for (int i = 0; i < kPairSteps; ++i) {
+    const int64_t k = kw0 + int64_t(i) * (2 * kWave) + 2 * lane;
+    if (k - 2 * lane > V) break;                   // wave-uniform
+    const uint32_t w = cnt_all[k >> 1], wb = cnt_before[k >> 1];
+    const uint32_t n0 = w & 0xFFFFu, n1 = w >> 16;
+    const uint32_t x0 = key_ar(n0, k, V), x = x0 + key_ar(n1, k + 1, V);
+    const uint32_t y0 = key_chunks(n0, k, V), y1 = key_chunks(n1, k + 1, V), y = y0 + y1;
+    const uint32_t xi = wave_scan_incl(x);
+    const uint32_t yi = __ballot(y != 0) ? wave_scan_incl(y) : 0u;   // long runs are rare
+    const uint32_t e0 = base_ar + xi - x, e1 = e0 + x0;
+    const uint32_t q0 = base_ch + yi - y, q1 = q0 + y0;
+    base_ar += uint32_t(__builtin_amdgcn_readlane(int(xi), kWave - 1));
+    base_ch += uint32_t(__builtin_amdgcn_readlane(int(yi), kWave - 1));
+    cnt_all[k >> 1] = (((e0 & 0xFFFFu) + (wb & 0xFFFFu)) & 0xFFFFu) |
+                      (((e1 & 0xFFFFu) + (wb >> 16)) << 16);
+    if (i % nb == b) {                             // each step's keys by one workgroup
+      emit_key(k, V, n0, e0, q0, y0, seg_begin, seg_end, chunk_off, owner, rows, n_invalid);
+      emit_key(k + 1, V, n1, e1, q1, y1, seg_begin, seg_end, chunk_off, owner, rows, n_invalid);
+    }
+  }
+  // Placement: sort this block's (key, local position) pairs, ascending, on
+  // a bitonic network.  Its stages whose partners lie in the same wave run on
+  // register shuffles; the ten others exchange through LDS, alternating srt
+  // and cnt_before (free once the first of them has synchronised, as every
+  // wave is then past the scans).
+  uint32_t e = mine_j < M ? (uint32_t(mine_key) << 10) | uint32_t(tid) : 0xFFFFFFFFu;
+  int stage = 0;
+#pragma unroll
+  for (int kk = 2; kk <= kCountBlock; kk <<= 1) {
+#pragma unroll
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      uint32_t y;
+      if (jj >= kWave) {
+        uint32_t* buf = (stage++ & 1) ? cnt_before : srt;
+        buf[tid] = e;
+        lds_barrier();
+        y = buf[tid ^ jj];
+      } else {
+        y = uint32_t(__shfl_xor(int(e), jj, kWave));
+      }
+      // ascending runs (tid & kk clear) keep the smaller key at the lower index
+      e = (((tid & kk) == 0) == ((tid & jj) == 0)) ? min(e, y) : max(e, y);
+    }
+  }
+  srt[tid] = e;
+  lds_barrier();
+  if (e != 0xFFFFFFFFu) {
+    const uint32_t k = e >> 10;
+    // first sorted index holding key k (binary search in [0, tid])
+    int f0 = 0, f1 = tid;
+    while (f0 < f1) {
+      const int mid = (f0 + f1) >> 1;
+      if ((srt[mid] >> 10) < k) f0 = mid + 1; else f1 = mid;
+    }
+    const int32_t pos = get16(cnt_all, k) + (tid - f0);
+    sk[pos] = int32_t(k);
+    sv[pos] = int32_t(lo + (e & 1023u));
+  }
+}
+
 // acc[i] += dy[pos[j], col + i] for j = j0 .. j1 - 1 in order, U rows in flight.
 template <typename T, int VEC, int U>
 __device__ __forceinline__ void sum_dy_rows(const T* __restrict__ dy, int64_t ld_dy,
@@ -603,21 +837,16 @@ __global__ __launch_bounds__(256) void chunk_owners(const int32_t* __restrict__ 
   for (int32_t q = chunk_off[v]; q < chunk_off[v + 1]; ++q) owner[q] = int32_t(v);
 }
 
-// Stage A: workgroup (q, c) sums chunk q of a long run into Q[q][chunk c].
+// The partial sum of chunk q (of table row v's run) for the VEC columns of
+// this lane at col (left = D - col > 0), stored to Q[q].
 template <typename T, int VEC, int U>
-__global__ __launch_bounds__(kSortThreads) void chunk_sums(
+__device__ __forceinline__ void chunk_partial(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
     const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
-    const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ owner, int64_t V,
-    int64_t D, float* __restrict__ Q, int64_t ldq) {
-  const int64_t q = blockIdx.x;
-  if (q >= chunk_off[V]) return;   // the grid is an upper bound on the chunk count
-  const int32_t v = owner[q];
+    const int32_t* __restrict__ chunk_off, int32_t v, int64_t q, int64_t col, int64_t left,
+    float* __restrict__ Q, int64_t ldq) {
   const int32_t j0 = seg_begin[v] + int32_t(q - chunk_off[v]) * kRun;
   const int32_t j1 = min(j0 + kRun, seg_end[v]);
-  const int64_t col = int64_t(blockIdx.y) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
-  const int64_t left = D - col;
-  if (left <= 0) return;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
@@ -639,6 +868,21 @@ __global__ __launch_bounds__(kSortThreads) void chunk_sums(
     for (int i = 0; i < VEC; ++i)
       if (i < left) out[i] = acc[i];
   }
+}
+
+// Stage A: workgroup (q, c) sums chunk q of a long run into Q[q][chunk c].
+template <typename T, int VEC, int U>
+__global__ __launch_bounds__(kSortThreads) void chunk_sums(
+    const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
+    const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
+    const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ owner, int64_t V,
+    int64_t D, float* __restrict__ Q, int64_t ldq) {
+  const int64_t q = blockIdx.x;
+  if (q >= chunk_off[V]) return;   // the grid is an upper bound on the chunk count
+  const int64_t col = int64_t(blockIdx.y) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
+  if (col >= D) return;
+  chunk_partial<T, VEC, U>(dy, ld_dy, sorted_pos, seg_begin, seg_end, chunk_off, owner[q], q, col,
+                           D - col, Q, ldq);
 }
 
 // Stage B for table row v and the VEC columns of this lane at col (left =
@@ -827,13 +1071,16 @@ hipError_t scatter_typed(const void* dy, int64_t ld_dy, const int32_t* pos, cons
   const T* g = static_cast<const T*>(dy);
   constexpr int U = kScatterUnroll;
   if (nq_max > 0) {
+    // A chunk's kRun rows all in flight at once: its positions and then its
+    // dy rows are one round trip each (with U rows per round the dependent
+    // position and row loads took kRun / U rounds of both).
     const dim3 ga(unsigned(nq_max), cb);
     if (vec)
-      chunk_sums<T, V4, U><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end, chunk_off, owner,
-                                                       V, D, Q, ldq);
+      chunk_sums<T, V4, kRun><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end, chunk_off,
+                                                          owner, V, D, Q, ldq);
     else
-      chunk_sums<T, 1, U><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end, chunk_off, owner,
-                                                      V, D, Q, ldq);
+      chunk_sums<T, 1, kRun><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end, chunk_off,
+                                                         owner, V, D, Q, ldq);
   }
   if (rows != nullptr) {
     const int64_t want = 2 * V * int64_t(cb);
@@ -940,6 +1187,24 @@ hipError_t launch_gather_rows_fwd(const void* x, int64_t ld_x, const int32_t* id
   }
 }
 
+namespace {
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+}  // namespace
+
 hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* idx, int64_t M,
                                   int64_t V, int64_t D, float* dt, int64_t ld_dt, int accumulate,
                                   int32_t* n_invalid, int32_t* ws, int act, bool vec, bool pvec,
@@ -975,25 +1240,43 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
   per = per < 1 ? 1 : (per > kFillMaxRows ? kFillMaxRows : per);
   int64_t cursor = 0;   // next unassigned row
   // bytes: the most zeros this launch takes (-1: all the rest); wide: its
-  // workgroups have kPlanThreads threads, and take four times the rows.
-  auto share = [&](int64_t bytes, bool wide) {
-    const int64_t rows = wide ? (4 * per < kFillMaxRows ? 4 * per : kFillMaxRows) : per;
+  // workgroups have kPlanThreads threads, and take four times the rows;
+  // max_groups > 0: at most that many fill workgroups, each taking more rows
+  // (up to kFillMaxRows; the share shrinks if even that is not enough).
+  auto share = [&](int64_t bytes, bool wide, int64_t max_groups) {
+    int64_t rows = wide ? (4 * per < kFillMaxRows ? 4 * per : kFillMaxRows) : per;
     FillShare f{cursor, cursor, rows, 0, idx, M, D, dt, ld_dt, pvec};
     if (fill_rows) {
       const int64_t budget = bytes < 0 ? V : (bytes / 4 + D - 1) / D;
       f.r1 = V - cursor < budget ? V : cursor + budget;
+      if (max_groups > 0) {
+        const int64_t need = (f.r1 - f.r0 + max_groups - 1) / max_groups;
+        rows = need > rows ? (need < kFillMaxRows ? need : kFillMaxRows) : rows;
+        f.rows = rows;
+        if (f.r1 - f.r0 > max_groups * rows) f.r1 = f.r0 + max_groups * rows;
+      }
       f.groups = (f.r1 - f.r0 + rows - 1) / rows;
       cursor = f.r1;
     }
     return f;
   };
-  if (listed) {
+  if (listed && V + 1 <= kCountKeys) {
+    // Every workgroup of this launch holds the sort's LDS, so one fits per
+    // CU: the fill workgroups take the CUs the sort leaves, in one round.
+    const int64_t nbc = (M + kCountBlock - 1) / kCountBlock;
+    const int cus = device_cus();
+    const FillShare f = share(kFillCountBytes, true, cus > nbc + 1 ? cus - nbc : 1);
+    plan_count<<<unsigned(nbc + f.groups), kCountThreads, 0, s>>>(
+        idx, M, V, sk, sv, seg_begin, seg_end, chunk_off, owner, rows, n_rows, n_invalid, f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (V == 0 || D == 0) return hipSuccess;
+  } else if (listed) {
     const int32_t* ik = nullptr;
     const int32_t* iv = nullptr;
     for (int p = 0; p < passes; ++p) {
       int32_t* ok = p == passes - 1 ? sk : (p % 2 == 0 ? ak : bk);
       int32_t* ov = p == passes - 1 ? sv : (p % 2 == 0 ? av : bv);
-      const FillShare f = share(p == 0 ? kFillFirstPassBytes : kFillPassBytes, false);
+      const FillShare f = share(p == 0 ? kFillFirstPassBytes : kFillPassBytes, false, 0);
       const unsigned grid = unsigned(nb + f.groups);
       if (p == 0)
         radix_pass_fused<true><<<grid, kSortThreads, 0, s>>>(
@@ -1004,7 +1287,7 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
       ik = ok;
       iv = ov;
     }
-    const FillShare f = share(kFillTailBytes, true);
+    const FillShare f = share(kFillTailBytes, true, 0);
     plan_tail<<<unsigned(1 + f.groups), kPlanThreads, 0, s>>>(sk, M, V, seg_begin, seg_end,
                                                              chunk_off, owner, rows, n_rows,
                                                              n_invalid, f);
@@ -1016,7 +1299,7 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
         V == 0 || D == 0)
       return e;
   }
-  const FillShare fl = share(-1, false);   // the listed-rows kernel: the rest
+  const FillShare fl = share(-1, false, 0);   // the listed-rows kernel: the rest
 #define VJP_SC(T)                                                                            \
   scatter_typed<T>(dy, ld_dy, sv, seg_begin, seg_end, chunk_off, owner, Q, ldq, nq_max, V, D,   \
                    listed ? rows : nullptr, listed ? n_rows : nullptr, dt, ld_dt, accumulate, \

@@ -78,11 +78,14 @@ def run_case(rwb, M, V, D, act, seed, kind="zipf", ld=None, offset=0, accumulate
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
 
 
-# M <= 16384 builds the sort and run plan in one workgroup, larger M with
-# separate kernels: both sides of the boundary are covered.
+# M <= 16384 builds the sort and run plan in one launch (V + 1 <= 32768: a
+# counting sort) or three (a wider key range: radix passes), larger M with
+# separate kernels: every side of both boundaries is covered.
 CASES = [(1, 1, 1), (7, 5, 3), (1000, 37, 64), (2048, 300, 2049), (5000, 32000, 100),
          (3000, 70000, 40), (4097, 1, 16), (16384, 3000, 48), (16385, 3000, 48),
-         (40000, 70000, 24), (50, 20, 70001)]
+         (40000, 70000, 24), (50, 20, 70001),
+         # the single-launch counting plan takes keys 0 .. V with V + 1 <= 32768
+         (3000, 32767, 16), (3000, 32768, 16), (16384, 32767, 8)]
 
 
 @pytest.mark.parametrize("M,V,D", CASES)
