@@ -35,9 +35,11 @@
 // (one kernel per radix pass, each block counting the digits of all M keys
 // itself instead of reading a scanned table, then one workgroup for the run
 // bounds, the chunks and a list of the selected rows), instead of a dozen;
-// step 4 then runs from the list of selected rows.  The rows never selected are zero-filled by extra workgroups of the
-// plan's own launches, which otherwise leave most of the chip idle.  The
-// arrays and every result bit are the same on both paths.
+// step 4 then runs from the list of selected rows.  The rows never selected
+// are zero-filled by extra workgroups of the plan's own launches, which
+// otherwise leave most of the chip idle.  The sorted keys and positions, the
+// run bounds, the chunk offsets of long runs and every result bit are the
+// same on all paths.
 #include "launch.hpp"
 #include "common.hpp"
 
@@ -549,38 +551,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tail(
 // LDS; the prefix sum of the counts is where each key's run starts, so the
 // workgroup places each of its keys at: run start + equal keys in earlier
 // workgroups + rank among equal keys in its own block, the rank coming from a
-// bitonic sort of its (key, local position) pairs in LDS (the composite is
-// unique, so equal keys keep increasing position: the stable order, which is
-// unique, hence the same sorted keys and positions as the radix passes).  The
-// same prefix sums give the run bounds of every key, the chunk offsets and
-// owners of runs longer than kRun, the list of selected rows and the invalid
-// count (the run of key V); the keys of scan step i are written by sort
-// workgroup i mod (sort workgroups).  Workgroups past the sort's write zero
+// bitonic sort of its (key, local position) pairs (the composite is unique,
+// so equal keys keep increasing position: the stable order, which is unique,
+// hence the same sorted keys and positions as the radix passes).  The same
+// prefix sums give the run bounds of every key, the chunk offsets and owners
+// of runs longer than kRun, the list of selected rows and the invalid count
+// (the run of key V): the sparse ones (row list, chunk offsets and owners)
+// from the scan, by sort workgroup t mod (sort workgroups) for thread t's
+// keys, the run bounds afterwards in coalesced stores, each sort workgroup
+// a contiguous share of the keys.  Workgroups past the sort's write zero
 // rows, as beside the radix passes.  One launch instead of three.
 //
-// The counts are plain LDS atomic increments, one per index and lane: a
-// duplicate-matching step (ballots over the 15 key bits, one add per distinct
-// key) cost more than the serialised adds it saves, even on Zipf-skewed ids.
-// The scans run wave-major: wave w owns keys [2048 w, 2048 (w + 1)), lane l
-// the LDS word of keys 2 l, 2 l + 1 of each 128-key step, so the LDS reads
-// are consecutive words and the global writes consecutive keys.
+// One LDS word per key holds both counts (all indices in the low half, those
+// before this block in the high half: one atomic increment per index).  A
+// duplicate-matching step (ballots over the 15 key bits, one add per
+// distinct key) cost more than the serialised adds it saves, even on
+// Zipf-skewed ids.  Thread t owns the 32 keys [32 t, 32 t + 32): it loads
+// their words into registers, sums them, takes its offset from one
+// workgroup scan, and walks them in order, leaving in each word the key's
+// run start (low half) beside its count before this block (high half); key
+// k's word sits at k + k / 32, so the lanes of a wave reading their strips
+// in step hit distinct banks.
 constexpr int kCountThreads = 1024;
 constexpr int kCountWaves = kCountThreads / kWave;
 constexpr int64_t kCountKeys = 32768;             // keys 0 .. V, V + 1 <= kCountKeys
 constexpr int kCountBlock = 1024;                 // keys placed per workgroup
 constexpr int kCountLoads = 16;                   // index loads in flight per lane (counting)
-constexpr int64_t kWaveKeys = kCountKeys / kCountWaves;      // keys per wave in the scans
-constexpr int kPairSteps = int(kWaveKeys / (2 * kWave));      // 128-key steps per wave
-constexpr int kCountWords = int(kCountKeys / 2);
+constexpr int kStrip = int(kCountKeys / kCountThreads);      // keys per thread in the scan
+constexpr int kCountWords = int(kCountKeys + kCountKeys / kStrip);
 static_assert(kCountBlock == kCountThreads, "one key per thread in the placement");
-static_assert(2 * kPlanMaxM <= 65535, "16-bit counts");
-static_assert(kPlanMaxM / kCountBlock <= kCountWaves, "every wave's keys have a writer");
+static_assert(kPlanMaxM <= 32767, "16-bit counts");
+static_assert(kStrip == 32, "one padding word per strip");
 
-// Two 16-bit counters per LDS word, key k in half k & 1 of word k / 2 (every
-// count and every sum stored below is at most 2 M <= 32768).
-__device__ __forceinline__ int32_t get16(const uint32_t* a, int64_t k) {
-  return int32_t((a[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
-}
+__device__ __forceinline__ int64_t cnt_slot(int64_t k) { return k + (k >> 5); }
 
 // Inclusive prefix sum over the 64 lanes of a wave (integers, exact): a
 // doubling scan within each row of 16 lanes on DPP row shifts (lanes shifted
@@ -609,24 +612,16 @@ __device__ __forceinline__ uint32_t key_chunks(uint32_t n, int64_t k, int64_t V)
   return (k < V && n > uint32_t(kRun)) ? (n + kRun - 1) / kRun : 0u;
 }
 
-// The plan arrays of key k: run [run, run + n), chunk offset q with its
-// nch owner entries, its place rr in the row list; for key V the invalid count.
-__device__ __forceinline__ void emit_key(int64_t k, int64_t V, uint32_t n, uint32_t ar,
-                                         uint32_t q, uint32_t nch, int32_t* __restrict__ seg_begin,
-                                         int32_t* __restrict__ seg_end,
+// The sparse plan entries of key k < V selected n > 0 times: its place
+// ar >> 16 in the row list and, for a long run, its chunk offset q and its
+// nch chunk owners.
+__device__ __forceinline__ void emit_row(int64_t k, uint32_t ar, uint32_t q, uint32_t nch,
                                          int32_t* __restrict__ chunk_off,
-                                         int32_t* __restrict__ owner, int32_t* __restrict__ rows,
-                                         int32_t* __restrict__ n_invalid) {
-  if (k > V) return;
-  const int32_t run = int32_t(ar & 0xFFFFu);
-  seg_begin[k] = run;
-  seg_end[k] = run + int32_t(n);
-  if (k < V) {
+                                         int32_t* __restrict__ owner, int32_t* __restrict__ rows) {
+  rows[ar >> 16] = int32_t(k);
+  if (nch > 0) {
     chunk_off[k] = int32_t(q);
     for (uint32_t c = 0; c < nch; ++c) owner[q + c] = int32_t(k);
-    if (n > 0) rows[ar >> 16] = int32_t(k);
-  } else if (n_invalid != nullptr) {
-    *n_invalid = int32_t(n);                         // the run of key V
   }
 }
 
@@ -635,10 +630,10 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
     int32_t* __restrict__ sv, int32_t* __restrict__ seg_begin, int32_t* __restrict__ seg_end,
     int32_t* __restrict__ chunk_off, int32_t* __restrict__ owner, int32_t* __restrict__ rows,
     int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid, FillShare fs) {
-  __shared__ uint32_t cnt_all[kCountWords];         // counts, then run starts + earlier equals
-  __shared__ uint32_t cnt_before[kCountWords];      // counts of the keys before this block
-  __shared__ uint32_t srt[kCountBlock];             // this block's (key, position) pairs
-  __shared__ uint32_t wsum[2][kCountWaves];         // per-wave totals of the scans
+  __shared__ uint32_t cnt[kCountWords];   // per key: counts, then run start + earlier equals
+  __shared__ uint32_t srt[kCountBlock];   // this block's (key, position) pairs
+  __shared__ uint32_t srt2[kCountBlock];  // the bitonic network's second buffer
+  __shared__ uint32_t wsum[2][kCountWaves];
   static_assert(kCountBlock >= kFillMaxRows / 32, "fill bitmap fits in srt");
   const int64_t nb = (M + kCountBlock - 1) / kCountBlock;
   const int64_t b = blockIdx.x;
@@ -650,10 +645,7 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
   const int64_t lo = b * kCountBlock;
   const int64_t mine_j = lo + tid;
   const int32_t mine_key = key_of(idx, mine_j < M ? mine_j : M - 1, V);   // loaded early
-  for (int i = tid; i < kCountWords; i += kCountThreads) {
-    cnt_all[i] = 0;
-    cnt_before[i] = 0;
-  }
+  for (int i = tid; i < kCountWords; i += kCountThreads) cnt[i] = 0;
   lds_barrier();
   constexpr int64_t kStride = int64_t(kCountThreads);
   for (int64_t j0 = tid; j0 < M; j0 += kStride * kCountLoads) {
@@ -666,38 +658,40 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
 #pragma unroll
     for (int u = 0; u < kCountLoads; ++u) {
       const int64_t j = j0 + u * kStride;
-      if (j < M) {
-        const uint32_t one = 1u << (16 * (key[u] & 1));
-        atomicAdd(&cnt_all[key[u] >> 1], one);
-        if (j < lo) atomicAdd(&cnt_before[key[u] >> 1], one);
-      }
+      if (j < M) atomicAdd(&cnt[cnt_slot(key[u])], j < lo ? 0x10001u : 1u);
     }
   }
   lds_barrier();
-  // Scans over the keys 0 .. V.  First each wave's totals ...
-  const int64_t kw0 = int64_t(wave) * kWaveKeys;
+  // This thread's strip: its sums (its words read kBatch at a time, all in
+  // flight together), its offsets from the scan.
+  constexpr int kBatch = 8;
+  const int64_t k0 = int64_t(tid) * kStrip;
+  uint32_t* const strip = cnt + cnt_slot(k0);
   uint32_t ar = 0, ch = 0;
-  for (int i = 0; i < kPairSteps; ++i) {
-    const int64_t k = kw0 + int64_t(i) * (2 * kWave) + 2 * lane;
-    if (k - 2 * lane > V) break;                   // wave-uniform: no key left
-    const uint32_t w = cnt_all[k >> 1];
-    ar += key_ar(w & 0xFFFFu, k, V) + key_ar(w >> 16, k + 1, V);
-    ch += key_chunks(w & 0xFFFFu, k, V) + key_chunks(w >> 16, k + 1, V);
+#pragma unroll
+  for (int g = 0; g < kStrip; g += kBatch) {
+    uint32_t w[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) w[i] = strip[g + i];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      ar += key_ar(w[i] & 0xFFFFu, k0 + g + i, V);
+      ch += key_chunks(w[i] & 0xFFFFu, k0 + g + i, V);
+    }
   }
-  ar = uint32_t(wave_sum_i32(int(ar)));
-  ch = uint32_t(wave_sum_i32(int(ch)));
-  if (lane == 0) {
-    wsum[0][wave] = ar;
-    wsum[1][wave] = ch;
+  const uint32_t ar_i = wave_scan_incl(ar), ch_i = wave_scan_incl(ch);
+  if (lane == kWave - 1) {
+    wsum[0][wave] = ar_i;
+    wsum[1][wave] = ch_i;
   }
   lds_barrier();
-  uint32_t base_ar = 0, base_ch = 0, tot_ar = 0, tot_ch = 0;
+  uint32_t run_ar = ar_i - ar, q = ch_i - ch, tot_ar = 0, tot_ch = 0;
 #pragma unroll
-  for (int w = 0; w < kCountWaves; ++w) {
-    const uint32_t x = wsum[0][w], y = wsum[1][w];
-    if (w < wave) {
-      base_ar += x;
-      base_ch += y;
+  for (int v = 0; v < kCountWaves; ++v) {
+    const uint32_t x = wsum[0][v], y = wsum[1][v];
+    if (v < wave) {
+      run_ar += x;
+      q += y;
     }
     tot_ar += x;
     tot_ch += y;
@@ -706,33 +700,29 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
     chunk_off[V] = int32_t(tot_ch);
     *n_rows = int32_t(tot_ar >> 16);
   }
-  // ... then the prefix of every key: its LDS half becomes run start + equal
-  // keys in earlier workgroups (only this lane reads or writes its word).
-  for (int i = 0; i < kPairSteps; ++i) {
-    const int64_t k = kw0 + int64_t(i) * (2 * kWave) + 2 * lane;
-    if (k - 2 * lane > V) break;                   // wave-uniform
-    const uint32_t w = cnt_all[k >> 1], wb = cnt_before[k >> 1];
-    const uint32_t n0 = w & 0xFFFFu, n1 = w >> 16;
-    const uint32_t x0 = key_ar(n0, k, V), x = x0 + key_ar(n1, k + 1, V);
-    const uint32_t y0 = key_chunks(n0, k, V), y1 = key_chunks(n1, k + 1, V), y = y0 + y1;
-    const uint32_t xi = wave_scan_incl(x);
-    const uint32_t yi = __ballot(y != 0) ? wave_scan_incl(y) : 0u;   // long runs are rare
-    const uint32_t e0 = base_ar + xi - x, e1 = e0 + x0;
-    const uint32_t q0 = base_ch + yi - y, q1 = q0 + y0;
-    base_ar += uint32_t(__builtin_amdgcn_readlane(int(xi), kWave - 1));
-    base_ch += uint32_t(__builtin_amdgcn_readlane(int(yi), kWave - 1));
-    cnt_all[k >> 1] = (((e0 & 0xFFFFu) + (wb & 0xFFFFu)) & 0xFFFFu) |
-                      (((e1 & 0xFFFFu) + (wb >> 16)) << 16);
-    if (i % nb == b) {                             // each step's keys by one workgroup
-      emit_key(k, V, n0, e0, q0, y0, seg_begin, seg_end, chunk_off, owner, rows, n_invalid);
-      emit_key(k + 1, V, n1, e1, q1, y1, seg_begin, seg_end, chunk_off, owner, rows, n_invalid);
+  // Walk the strip: each key's word becomes its run start beside the equal
+  // keys in earlier workgroups (only this thread reads or writes these words).
+  const bool writes = int64_t(tid) % nb == b;
+#pragma unroll 1
+  for (int g = 0; g < kStrip; g += kBatch) {
+    uint32_t w[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) w[i] = strip[g + i];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t k = k0 + g + i;
+      const uint32_t n = w[i] & 0xFFFFu;
+      const uint32_t x = key_ar(n, k, V), y = key_chunks(n, k, V);
+      strip[g + i] = (run_ar & 0xFFFFu) | (w[i] & 0xFFFF0000u);
+      if (writes && k < V && n > 0) emit_row(k, run_ar, q, y, chunk_off, owner, rows);
+      run_ar += x;
+      q += y;
     }
   }
   // Placement: sort this block's (key, local position) pairs, ascending, on
   // a bitonic network.  Its stages whose partners lie in the same wave run on
-  // register shuffles; the ten others exchange through LDS, alternating srt
-  // and cnt_before (free once the first of them has synchronised, as every
-  // wave is then past the scans).
+  // register shuffles; the ten others exchange through LDS, alternating
+  // between srt and srt2.
   uint32_t e = mine_j < M ? (uint32_t(mine_key) << 10) | uint32_t(tid) : 0xFFFFFFFFu;
   int stage = 0;
 #pragma unroll
@@ -741,7 +731,7 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
       uint32_t y;
       if (jj >= kWave) {
-        uint32_t* buf = (stage++ & 1) ? cnt_before : srt;
+        uint32_t* buf = (stage++ & 1) ? srt2 : srt;
         buf[tid] = e;
         lds_barrier();
         y = buf[tid ^ jj];
@@ -754,6 +744,17 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
   }
   srt[tid] = e;
   lds_barrier();
+  // Run bounds of this workgroup's share of the keys 0 .. V (run V + 1
+  // starts at M), and the invalid count.
+  const int64_t share = (V + 1 + nb - 1) / nb;
+  const int64_t s1 = (b + 1) * share < V + 1 ? (b + 1) * share : V + 1;
+  for (int64_t k = b * share + tid; k < s1; k += kCountThreads) {
+    const int32_t r0 = int32_t(cnt[cnt_slot(k)] & 0xFFFFu);
+    const int32_t r1 = k == V ? int32_t(M) : int32_t(cnt[cnt_slot(k + 1)] & 0xFFFFu);
+    seg_begin[k] = r0;
+    seg_end[k] = r1;
+    if (k == V && n_invalid != nullptr) *n_invalid = r1 - r0;
+  }
   if (e != 0xFFFFFFFFu) {
     const uint32_t k = e >> 10;
     // first sorted index holding key k (binary search in [0, tid])
@@ -762,7 +763,8 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
       const int mid = (f0 + f1) >> 1;
       if ((srt[mid] >> 10) < k) f0 = mid + 1; else f1 = mid;
     }
-    const int32_t pos = get16(cnt_all, k) + (tid - f0);
+    const uint32_t w = cnt[cnt_slot(k)];
+    const int32_t pos = int32_t((w & 0xFFFFu) + (w >> 16)) + (tid - f0);
     sk[pos] = int32_t(k);
     sv[pos] = int32_t(lo + (e & 1023u));
   }
@@ -871,6 +873,9 @@ __device__ __forceinline__ void chunk_partial(
 }
 
 // Stage A: workgroup (q, c) sums chunk q of a long run into Q[q][chunk c].
+// (Zero rows beside it, as beside the plan, made the backward slower: 137 to
+// 144 us against 135 with 32 to 96 MB of them for 16384 Zipf ids into
+// 32000 x 4096 on MI355X.)
 template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kSortThreads) void chunk_sums(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
@@ -974,10 +979,17 @@ __global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
 // write zeros to the share's rows never selected (an empty run), so that the
 // latency-bound sums and the bandwidth-bound zero rows run side by side; the
 // rows before the share were zero-filled beside the plan.  Otherwise every
-// workgroup takes listed pairs.  Needs gridDim.x >= 2.  (Measured on MI355X
-// for 16384 Zipf ids into 32000 x 4096, all zero rows here: 99-106 us with
-// 32768 workgroups; the pairs first and the zero rows after them in every
-// workgroup, 132 us; one workgroup per table row and column chunk, 128 us.)
+// workgroup takes listed pairs.  Needs gridDim.x >= 2.
+// Consecutive workgroups go to the 8 XCDs in turn, so the sums run on XCDs
+// 0, 2, 4, 6 and the zero rows on 1, 3, 5, 7.  (Measured on MI355X for
+// 16384 Zipf ids into 32000 x 4096: 88 us; the sums alone 43 us, the zero
+// rows alone 77 us (67 us from all XCDs).  Other splits were slower: both
+// roles on every XCD, 105 us (the sums' reads queue behind the zero
+// stream); sums on XCDs 0-3 and zeros on 4-7, 95 us; sums on 3 or 2 XCDs,
+// 105 or 123 us; the chunk sums and the listed sums in one launch and the
+// zero rows in the next, 113 us for both (against 88 + 21 here); all zero
+// rows here with the pairs first in every workgroup, 132 us; one workgroup
+// per table row and column chunk, 128 us.)
 template <typename T, int VEC, int U, bool PVEC>
 __global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
