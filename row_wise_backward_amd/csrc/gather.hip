@@ -189,6 +189,15 @@ __global__ __launch_bounds__(256) void segment_bounds(const int32_t* __restrict_
 // folded into a strided scan, 330 us.)
 constexpr int kRun = 32;
 
+// Sorted-index range [j0, j1) of one chunk of a long run.
+struct ChunkSpan {
+  int32_t j0, j1;
+};
+__device__ __forceinline__ ChunkSpan chunk_span(int32_t run_begin, int32_t run_end, int32_t c) {
+  const int32_t j0 = run_begin + c * kRun;
+  return ChunkSpan{j0, min(j0 + kRun, run_end)};
+}
+
 // Plans for 0 < M <= kPlanMaxM take three launches: one kernel per radix
 // pass, in which every block counts the digits of all M keys itself (the
 // keys are L2 resident), so that it knows both where each digit starts and
@@ -459,9 +468,9 @@ __global__ __launch_bounds__(kSortThreads) void radix_pass_fused(
 // exchanges data only through LDS; its global writes are never read back.
 __global__ __launch_bounds__(kPlanThreads) void plan_tail(
     const int32_t* __restrict__ sk, int64_t M, int64_t V, int32_t* __restrict__ seg_begin,
-    int32_t* __restrict__ seg_end, int32_t* __restrict__ chunk_off, int32_t* __restrict__ owner,
-    int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid,
-    FillShare fs) {
+    int32_t* __restrict__ seg_end, int32_t* __restrict__ chunk_off, ChunkSpan* __restrict__ ctab,
+    int32_t* __restrict__ rows, int32_t* __restrict__ rbeg, int32_t* __restrict__ n_rows,
+    int32_t* __restrict__ n_invalid, FillShare fs) {
   __shared__ int32_t wmin[kPlanWaves];
   __shared__ int32_t wsum[kPlanWaves];
   __shared__ uint32_t sel[kFillMaxRows / 32];
@@ -531,17 +540,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tail(
   int32_t r = block_exclusive_scan<kPlanWaves>(my_rows, wsum, total_rows);
 #pragma unroll
   for (int i = 0; i < kPlanRounds; ++i) {
-    if (!st[i] || int64_t(kk[i]) == V) continue;
+    if (!st[i]) continue;
+    const int32_t j = int32_t(j0 + i);
+    if (int64_t(kk[i]) == V) {   // the run after the last listed row's
+      rbeg[total_rows] = j;
+      continue;
+    }
+    rbeg[r] = j;
     rows[r++] = kk[i];
     if (nch[i] > 0) {
       chunk_off[kk[i]] = q;
-      for (int32_t c = 0; c < nch[i]; ++c) owner[q + c] = kk[i];
+      for (int32_t c = 0; c < nch[i]; ++c) ctab[q + c] = chunk_span(j, end[i], c);
       q += nch[i];
     }
   }
   if (tid == 0) {
     chunk_off[V] = total_chunks;
     *n_rows = total_rows;
+    if (sk[M - 1] != int32_t(V)) rbeg[total_rows] = M32;   // no invalid index
   }
 }
 
@@ -613,23 +629,27 @@ __device__ __forceinline__ uint32_t key_chunks(uint32_t n, int64_t k, int64_t V)
 }
 
 // The sparse plan entries of key k < V selected n > 0 times: its place
-// ar >> 16 in the row list and, for a long run, its chunk offset q and its
-// nch chunk owners.
-__device__ __forceinline__ void emit_row(int64_t k, uint32_t ar, uint32_t q, uint32_t nch,
-                                         int32_t* __restrict__ chunk_off,
-                                         int32_t* __restrict__ owner, int32_t* __restrict__ rows) {
+// ar >> 16 in the row list with its run start, and for a long run its chunk
+// offset q and the spans of its nch chunks.
+__device__ __forceinline__ void emit_row(int64_t k, uint32_t n, uint32_t ar, uint32_t q,
+                                         uint32_t nch, int32_t* __restrict__ chunk_off,
+                                         ChunkSpan* __restrict__ ctab, int32_t* __restrict__ rows,
+                                         int32_t* __restrict__ rbeg) {
+  const int32_t run = int32_t(ar & 0xFFFFu);
   rows[ar >> 16] = int32_t(k);
+  rbeg[ar >> 16] = run;
   if (nch > 0) {
     chunk_off[k] = int32_t(q);
-    for (uint32_t c = 0; c < nch; ++c) owner[q + c] = int32_t(k);
+    for (uint32_t c = 0; c < nch; ++c) ctab[q + c] = chunk_span(run, run + int32_t(n), int32_t(c));
   }
 }
 
 __global__ __launch_bounds__(kCountThreads) void plan_count(
     const int32_t* __restrict__ idx, int64_t M, int64_t V, int32_t* __restrict__ sk,
     int32_t* __restrict__ sv, int32_t* __restrict__ seg_begin, int32_t* __restrict__ seg_end,
-    int32_t* __restrict__ chunk_off, int32_t* __restrict__ owner, int32_t* __restrict__ rows,
-    int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid, FillShare fs) {
+    int32_t* __restrict__ chunk_off, ChunkSpan* __restrict__ ctab, int32_t* __restrict__ rows,
+    int32_t* __restrict__ rbeg, int32_t* __restrict__ n_rows, int32_t* __restrict__ n_invalid,
+    FillShare fs) {
   __shared__ uint32_t cnt[kCountWords];   // per key: counts, then run start + earlier equals
   __shared__ uint32_t srt[kCountBlock];   // this block's (key, position) pairs
   __shared__ uint32_t srt2[kCountBlock];  // the bitonic network's second buffer
@@ -714,7 +734,7 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
       const uint32_t n = w[i] & 0xFFFFu;
       const uint32_t x = key_ar(n, k, V), y = key_chunks(n, k, V);
       strip[g + i] = (run_ar & 0xFFFFu) | (w[i] & 0xFFFF0000u);
-      if (writes && k < V && n > 0) emit_row(k, run_ar, q, y, chunk_off, owner, rows);
+      if (writes && k < V && n > 0) emit_row(k, n, run_ar, q, y, chunk_off, ctab, rows, rbeg);
       run_ar += x;
       q += y;
     }
@@ -745,7 +765,7 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
   srt[tid] = e;
   lds_barrier();
   // Run bounds of this workgroup's share of the keys 0 .. V (run V + 1
-  // starts at M), and the invalid count.
+  // starts at M), the invalid count, and the end of the listed rows' runs.
   const int64_t share = (V + 1 + nb - 1) / nb;
   const int64_t s1 = (b + 1) * share < V + 1 ? (b + 1) * share : V + 1;
   for (int64_t k = b * share + tid; k < s1; k += kCountThreads) {
@@ -753,7 +773,10 @@ __global__ __launch_bounds__(kCountThreads) void plan_count(
     const int32_t r1 = k == V ? int32_t(M) : int32_t(cnt[cnt_slot(k + 1)] & 0xFFFFu);
     seg_begin[k] = r0;
     seg_end[k] = r1;
-    if (k == V && n_invalid != nullptr) *n_invalid = r1 - r0;
+    if (k == V) {
+      if (n_invalid != nullptr) *n_invalid = r1 - r0;
+      rbeg[tot_ar >> 16] = r0;
+    }
   }
   if (e != 0xFFFFFFFFu) {
     const uint32_t k = e >> 10;
@@ -831,24 +854,24 @@ __global__ __launch_bounds__(256) void count_chunks(const int32_t* __restrict__ 
   n_chunks[v] = len > kRun ? (len + kRun - 1) / kRun : 0;
 }
 
-// owner[q] = the table row whose run chunk q belongs to.
-__global__ __launch_bounds__(256) void chunk_owners(const int32_t* __restrict__ chunk_off,
-                                                    int64_t V, int32_t* __restrict__ owner) {
+// ctab[q] = the sorted-index span of chunk q (of its table row's run).
+__global__ __launch_bounds__(256) void chunk_spans(const int32_t* __restrict__ chunk_off,
+                                                    const int32_t* __restrict__ seg_begin,
+                                                    const int32_t* __restrict__ seg_end, int64_t V,
+                                                    ChunkSpan* __restrict__ ctab) {
   const int64_t v = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (v >= V) return;
-  for (int32_t q = chunk_off[v]; q < chunk_off[v + 1]; ++q) owner[q] = int32_t(v);
+  const int32_t q0 = chunk_off[v], q1 = chunk_off[v + 1], b = seg_begin[v], e = seg_end[v];
+  for (int32_t q = q0; q < q1; ++q) ctab[q] = chunk_span(b, e, q - q0);
 }
 
-// The partial sum of chunk q (of table row v's run) for the VEC columns of
-// this lane at col (left = D - col > 0), stored to Q[q].
+// The partial sum of chunk q (sorted indices [j0, j1)) for the VEC columns
+// of this lane at col (left = D - col > 0), stored to Q[q].
 template <typename T, int VEC, int U>
-__device__ __forceinline__ void chunk_partial(
-    const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
-    const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
-    const int32_t* __restrict__ chunk_off, int32_t v, int64_t q, int64_t col, int64_t left,
-    float* __restrict__ Q, int64_t ldq) {
-  const int32_t j0 = seg_begin[v] + int32_t(q - chunk_off[v]) * kRun;
-  const int32_t j1 = min(j0 + kRun, seg_end[v]);
+__device__ __forceinline__ void chunk_partial(const T* __restrict__ dy, int64_t ld_dy,
+                                              const int32_t* __restrict__ sorted_pos, int32_t j0,
+                                              int32_t j1, int64_t q, int64_t col, int64_t left,
+                                              float* __restrict__ Q, int64_t ldq) {
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
@@ -879,30 +902,27 @@ __device__ __forceinline__ void chunk_partial(
 template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kSortThreads) void chunk_sums(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
-    const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
-    const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ owner, int64_t V,
+    const int32_t* __restrict__ chunk_off, const ChunkSpan* __restrict__ ctab, int64_t V,
     int64_t D, float* __restrict__ Q, int64_t ldq) {
   const int64_t q = blockIdx.x;
   if (q >= chunk_off[V]) return;   // the grid is an upper bound on the chunk count
   const int64_t col = int64_t(blockIdx.y) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
   if (col >= D) return;
-  chunk_partial<T, VEC, U>(dy, ld_dy, sorted_pos, seg_begin, seg_end, chunk_off, owner[q], q, col,
-                           D - col, Q, ldq);
+  const ChunkSpan c = ctab[q];
+  chunk_partial<T, VEC, U>(dy, ld_dy, sorted_pos, c.j0, c.j1, q, col, D - col, Q, ldq);
 }
 
-// Stage B for table row v and the VEC columns of this lane at col (left =
-// D - col > 0): the gradient row, written (or added into dt).  PVEC: the
-// gradient rows are 16-byte aligned, so each lane's VEC fp32 values go out
-// as 16-byte stores.
+// Stage B for table row v (its run: sorted indices [beg, end)) and the VEC
+// columns of this lane at col (left = D - col > 0): the gradient row,
+// written (or added into dt).  PVEC: the gradient rows are 16-byte aligned,
+// so each lane's VEC fp32 values go out as 16-byte stores.
 template <typename T, int VEC, int U, bool PVEC>
 __device__ __forceinline__ void row_gradient(
-    int64_t v, int64_t col, const T* __restrict__ dy, int64_t ld_dy,
-    const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ seg_begin,
-    const int32_t* __restrict__ seg_end, const int32_t* __restrict__ chunk_off,
+    int64_t v, int32_t beg, int32_t end, int64_t col, const T* __restrict__ dy, int64_t ld_dy,
+    const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ chunk_off,
     const float* __restrict__ Q, int64_t ldq, int64_t D, float* __restrict__ dt, int64_t ld_dt,
     int accumulate) {
   const int64_t left = D - col;
-  const int32_t beg = seg_begin[v], end = seg_end[v];
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
@@ -969,8 +989,8 @@ __global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
     float* __restrict__ dt, int64_t ld_dt, int accumulate) {
   const int64_t col = int64_t(blockIdx.y) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
   if (col >= D) return;
-  row_gradient<T, VEC, U, PVEC>(blockIdx.x, col, dy, ld_dy, sorted_pos, seg_begin, seg_end,
-                                chunk_off, Q, ldq, D, dt, ld_dt, accumulate);
+  row_gradient<T, VEC, U, PVEC>(blockIdx.x, seg_begin[blockIdx.x], seg_end[blockIdx.x], col, dy,
+                                ld_dy, sorted_pos, chunk_off, Q, ldq, D, dt, ld_dt, accumulate);
 }
 
 // Stage B from the list of selected rows (plans of M <= kPlanMaxM).  When
@@ -995,8 +1015,9 @@ __global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
     const int32_t* __restrict__ seg_begin, const int32_t* __restrict__ seg_end,
     const int32_t* __restrict__ chunk_off, const float* __restrict__ Q, int64_t ldq, int64_t D,
-    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows, int64_t cb,
-    float* __restrict__ dt, int64_t ld_dt, int accumulate, FillShare fs) {
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ rbeg,
+    const int32_t* __restrict__ n_rows, int64_t cb, float* __restrict__ dt, int64_t ld_dt,
+    int accumulate, FillShare fs) {
   const int64_t b = blockIdx.x;
   const bool split = fs.r1 > fs.r0;
   if (!split || b % 2 == 0) {
@@ -1005,9 +1026,10 @@ __global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
     const int64_t items = int64_t(*n_rows) * cb;
     for (int64_t it = me; it < items; it += stride) {
       const int64_t col = (it % cb) * kSortThreads * VEC + int64_t(threadIdx.x) * VEC;
+      const int64_t r = it / cb;   // the run of listed row r ends where row r + 1's begins
       if (col < D)
-        row_gradient<T, VEC, U, PVEC>(rows[it / cb], col, dy, ld_dy, sorted_pos, seg_begin,
-                                      seg_end, chunk_off, Q, ldq, D, dt, ld_dt, accumulate);
+        row_gradient<T, VEC, U, PVEC>(rows[r], rbeg[r], rbeg[r + 1], col, dy, ld_dy, sorted_pos,
+                                      chunk_off, Q, ldq, D, dt, ld_dt, accumulate);
     }
     return;
   }
@@ -1068,9 +1090,10 @@ constexpr int64_t kListedGrid = 32768;
 // or null (stage B over every table row).
 template <typename T>
 hipError_t scatter_typed(const void* dy, int64_t ld_dy, const int32_t* pos, const int32_t* beg,
-                         const int32_t* end, const int32_t* chunk_off, const int32_t* owner,
+                         const int32_t* end, const int32_t* chunk_off, const ChunkSpan* ctab,
                          float* Q, int64_t ldq, int64_t nq_max, int64_t V, int64_t D,
-                         const int32_t* rows, const int32_t* n_rows, float* dt, int64_t ld_dt,
+                         const int32_t* rows, const int32_t* rbeg, const int32_t* n_rows,
+                         float* dt, int64_t ld_dt,
                          int accumulate, bool vec, bool pvec, const FillShare& fill_listed,
                          hipStream_t s) {
   // Four columns per lane: each lane's fp32 results are one 16-byte store,
@@ -1088,18 +1111,19 @@ hipError_t scatter_typed(const void* dy, int64_t ld_dy, const int32_t* pos, cons
     // position and row loads took kRun / U rounds of both).
     const dim3 ga(unsigned(nq_max), cb);
     if (vec)
-      chunk_sums<T, V4, kRun><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end, chunk_off,
-                                                          owner, V, D, Q, ldq);
+      chunk_sums<T, V4, kRun><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, chunk_off, ctab, V, D, Q,
+                                                          ldq);
     else
-      chunk_sums<T, 1, kRun><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, beg, end, chunk_off,
-                                                         owner, V, D, Q, ldq);
+      chunk_sums<T, 1, kRun><<<ga, kSortThreads, 0, s>>>(g, ld_dy, pos, chunk_off, ctab, V, D, Q,
+                                                         ldq);
   }
   if (rows != nullptr) {
     const int64_t want = 2 * V * int64_t(cb);
     const unsigned gl = unsigned(want < 2 ? 2 : (want < kListedGrid ? want : kListedGrid));
 #define VJP_LISTED(VV, PV)                                                                      \
   scatter_listed_rows<T, VV, U, PV><<<gl, kSortThreads, 0, s>>>(                              \
-      g, ld_dy, pos, beg, end, chunk_off, Q, ldq, D, rows, n_rows, cb, dt, ld_dt, accumulate,   \
+      g, ld_dy, pos, beg, end, chunk_off, Q, ldq, D, rows, rbeg, n_rows, cb, dt, ld_dt,         \
+      accumulate,                                                                             \
       fill_listed)
     if (vec && pvec)
       VJP_LISTED(V4, true);
@@ -1133,7 +1157,7 @@ int gather_sort_passes(int64_t V) {
 
 // Workspace, in 4-byte units: sorted keys [M], sorted positions [M], two
 // ping-pong key / position buffers [4 M], the digit table [256 nb], run
-// starts and ends [2 (V + 1)], chunk offsets [V + 1], chunk owners [nq], then
+// starts and ends [2 (V + 1)], chunk offsets [V + 1], chunk spans [2 nq], then
 // (16-byte aligned) the chunk partials Q [nq][ldq] fp32, with
 // nq = M / 16 + 1 (an upper bound on the chunk count) and ldq = D rounded up
 // to a multiple of 4.
@@ -1141,7 +1165,7 @@ int64_t gather_max_chunks(int64_t M) { return M / 16 + 1; }
 
 int64_t gather_ws_q_offset(int64_t M, int64_t V) {
   const int64_t nb = (M + kSortBlock - 1) / kSortBlock;
-  const int64_t ints = 6 * M + int64_t(kDigits) * nb + 3 * (V + 1) + gather_max_chunks(M);
+  const int64_t ints = 6 * M + int64_t(kDigits) * nb + 3 * (V + 1) + 2 * gather_max_chunks(M);
   return (ints + 3) / 4 * 4;
 }
 
@@ -1150,11 +1174,11 @@ int64_t gather_workspace_ints(int64_t M, int64_t V, int64_t D) {
 }
 
 // The plan for any M: radix passes of three kernels each, then the run
-// bounds, chunk counts, their scan and the chunk owners as separate kernels.
+// bounds, chunk counts, their scan and the chunk spans as separate kernels.
 static hipError_t plan_multi(const int32_t* idx, int64_t M, int64_t V, int64_t D, int32_t* sk,
                              int32_t* sv, int32_t* ak, int32_t* av, int32_t* bk, int32_t* bv,
                              int32_t* hist, int64_t nb, int32_t* seg_begin, int32_t* seg_end,
-                             int32_t* chunk_off, int32_t* owner, int32_t* n_invalid,
+                             int32_t* chunk_off, ChunkSpan* ctab, int32_t* n_invalid,
                              hipStream_t s) {
   hipError_t e;
   if (M > 0) {
@@ -1185,7 +1209,7 @@ static hipError_t plan_multi(const int32_t* idx, int64_t M, int64_t V, int64_t D
   const unsigned gv = unsigned((V + 1 + 255) / 256);
   count_chunks<<<gv, 256, 0, s>>>(seg_begin, seg_end, V, chunk_off);
   scan_exclusive<<<1, kScanThreads, 0, s>>>(chunk_off, V + 1);
-  chunk_owners<<<gv, 256, 0, s>>>(chunk_off, V, owner);
+  chunk_spans<<<gv, 256, 0, s>>>(chunk_off, seg_begin, seg_end, V, ctab);
   return hipGetLastError();
 }
 
@@ -1232,12 +1256,13 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
   int32_t* seg_begin = hist + int64_t(kDigits) * nb;
   int32_t* seg_end = seg_begin + (V + 1);
   int32_t* chunk_off = seg_end + (V + 1);
-  int32_t* owner = chunk_off + (V + 1);
+  ChunkSpan* ctab = reinterpret_cast<ChunkSpan*>(chunk_off + (V + 1));
   const int64_t ldq = (D + 3) / 4 * 4;
   float* Q = reinterpret_cast<float*>(ws + gather_ws_q_offset(M, V));
   // Plans of M <= kPlanMaxM also list the selected rows: the list reuses the
   // sort's spare key buffer, its length the digit table's first entry.
   int32_t* rows = bk;
+  int32_t* rbeg = ak;   // run start of each listed row, then the end of the last
   int32_t* n_rows = hist;
   hipError_t e;
   const int64_t nq_max = M > kRun ? gather_max_chunks(M) : 0;
@@ -1279,7 +1304,7 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
     const int cus = device_cus();
     const FillShare f = share(kFillCountBytes, true, cus > nbc + 1 ? cus - nbc : 1);
     plan_count<<<unsigned(nbc + f.groups), kCountThreads, 0, s>>>(
-        idx, M, V, sk, sv, seg_begin, seg_end, chunk_off, owner, rows, n_rows, n_invalid, f);
+        idx, M, V, sk, sv, seg_begin, seg_end, chunk_off, ctab, rows, rbeg, n_rows, n_invalid, f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (V == 0 || D == 0) return hipSuccess;
   } else if (listed) {
@@ -1301,20 +1326,21 @@ hipError_t launch_gather_rows_bwd(const void* dy, int64_t ld_dy, const int32_t* 
     }
     const FillShare f = share(kFillTailBytes, true, 0);
     plan_tail<<<unsigned(1 + f.groups), kPlanThreads, 0, s>>>(sk, M, V, seg_begin, seg_end,
-                                                             chunk_off, owner, rows, n_rows,
+                                                             chunk_off, ctab, rows, rbeg, n_rows,
                                                              n_invalid, f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (V == 0 || D == 0) return hipSuccess;
   } else {
     if ((e = plan_multi(idx, M, V, D, sk, sv, ak, av, bk, bv, hist, nb, seg_begin, seg_end,
-                        chunk_off, owner, n_invalid, s)) != hipSuccess ||
+                        chunk_off, ctab, n_invalid, s)) != hipSuccess ||
         V == 0 || D == 0)
       return e;
   }
   const FillShare fl = share(-1, false, 0);   // the listed-rows kernel: the rest
 #define VJP_SC(T)                                                                            \
-  scatter_typed<T>(dy, ld_dy, sv, seg_begin, seg_end, chunk_off, owner, Q, ldq, nq_max, V, D,   \
-                   listed ? rows : nullptr, listed ? n_rows : nullptr, dt, ld_dt, accumulate, \
+  scatter_typed<T>(dy, ld_dy, sv, seg_begin, seg_end, chunk_off, ctab, Q, ldq, nq_max, V, D,    \
+                   listed ? rows : nullptr, rbeg, listed ? n_rows : nullptr, dt, ld_dt,       \
+                   accumulate,                                                                \
                    vec, pvec, fl, s)
   switch (act) {
     case kF32: return VJP_SC(float);
