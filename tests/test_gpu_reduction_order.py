@@ -110,11 +110,13 @@ def test_layernorm_dw_db_order(gpu_lib):
     assert np.array_equal(to_host(db, "f32").view(np.uint32), want[cols:].view(np.uint32))
 
 
-@pytest.mark.parametrize("M", [6000, 20000])
-def test_scatter_add_row_order(gpu_lib, M):
+@pytest.mark.parametrize("M,V", [(6000, 500), (6000, 40000), (20000, 500)])
+def test_scatter_add_row_order(gpu_lib, M, V):
     """Short runs (<= 32) summed in sorted order, long runs in 32-position
-    chunks; M = 6000 plans in one workgroup, M = 20000 with separate kernels."""
-    V, D = 500, 40
+    chunks, on every plan path: M <= 16384 with keys below 2^15 (the counting
+    plan), with a wider key range (radix passes), and M > 16384 (separate
+    kernels)."""
+    D = 40
     idx = synth.zipf_indices(M, V, 640)
     dy = synth.normal((M, D), 1.0, "bf16", 640, 2)
     dt, _ = gpu_lib.vjp_gather_rows_bwd(synth.to_torch(dy, "bf16", DEV).view(M, D),
