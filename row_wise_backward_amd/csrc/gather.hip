@@ -38,8 +38,9 @@
 // step 4 then runs from the list of selected rows.  The rows never selected
 // are zero-filled by extra workgroups of the plan's own launches, which
 // otherwise leave most of the chip idle.  The sorted keys and positions, the
-// run bounds, the chunk offsets of long runs and every result bit are the
-// same on all paths.
+// run bounds of the keys that occur (an absent key's empty run may sit at a
+// different place), the chunk offsets of long runs and every result bit are
+// the same on all paths.
 #include "launch.hpp"
 #include "common.hpp"
 
