@@ -32,6 +32,8 @@ def _indices(M, V, seed, kind):
     if kind == "invalid_mix":                 # about a quarter outside [0, V)
         i = g.integers(-V // 3 - 2, V + V // 3 + 2, size=M)
         return i.astype(np.int32)
+    if kind == "distinct":                    # M <= V rows, each selected once
+        return g.permutation(V)[:M].astype(np.int32)
     raise ValueError(kind)
 
 
@@ -97,6 +99,15 @@ def test_shapes(gpu_lib, M, V, D, act):
 @pytest.mark.parametrize("kind", ["uniform", "one_row", "invalid_mix"])
 def test_index_patterns(gpu_lib, kind):
     run_case(gpu_lib, 3000, 257, 130, "bf16", seed=510, kind=kind)
+
+
+@pytest.mark.parametrize("kind", ["one_row", "distinct", "invalid_mix"])
+def test_counting_plan_extremes(gpu_lib, kind):
+    """The single-launch counting plan at its largest M (16384): one row
+    selected by every index (its count at the top of the 16-bit fields), every
+    index a different row (16384 listed rows, so the list of run starts takes
+    all M + 1 entries), and a quarter of the indices invalid."""
+    run_case(gpu_lib, 16384, 32767, 16, "bf16", seed=517, kind=kind)
 
 
 def test_long_runs_and_accumulate(gpu_lib):
