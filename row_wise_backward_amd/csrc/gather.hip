@@ -305,8 +305,11 @@ __device__ void zero_unselected_rows(const FillShare& fs, int64_t f, uint32_t* s
   for (int i = threadIdx.x; i < (n + 31) / 32; i += THREADS) sel[i] = 0;
   lds_barrier();
   // Mark the selected rows (integer LDS atomics), kFillUnroll loads in
-  // flight per thread (positions past the end read index M - 1 again):
-  // groups of four indices when the array is 16-byte aligned, else single.
+  // flight per thread (positions past the end read index M - 1 again, and
+  // mark nothing: marking those repeats put tens of thousands of atomics on
+  // one LDS word in the workgroup whose rows hold index M - 1, which then
+  // finished last); groups of four indices when the array is 16-byte
+  // aligned, else single.
   auto mark = [&](int32_t k) {
     const int64_t d = int64_t(k) - a;
     if (d >= 0 && d < n) atomicOr(&sel[d >> 5], 1u << (d & 31));
@@ -323,8 +326,9 @@ __device__ void zero_unselected_rows(const FillShare& fs, int64_t f, uint32_t* s
       }
 #pragma unroll
       for (int u = 0; u < kFillUnroll; ++u)
+        if (j0 + int64_t(u) * THREADS < M4)   // clamped repeats mark nothing
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mark(k[u].v[i]);
+          for (int i = 0; i < 4; ++i) mark(k[u].v[i]);
     }
     for (int64_t j = 4 * M4 + threadIdx.x; j < M; j += THREADS) mark(idx[j]);
   } else {
@@ -336,7 +340,8 @@ __device__ void zero_unselected_rows(const FillShare& fs, int64_t f, uint32_t* s
         k[u] = idx[j < M ? j : M - 1];
       }
 #pragma unroll
-      for (int u = 0; u < kFillUnroll; ++u) mark(k[u]);
+      for (int u = 0; u < kFillUnroll; ++u)
+        if (j0 + int64_t(u) * THREADS < M) mark(k[u]);   // clamped repeats mark nothing
     }
   }
   lds_barrier();
