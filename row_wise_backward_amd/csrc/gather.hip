@@ -1014,7 +1014,8 @@ __global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
 // stream); sums on XCDs 0-3 and zeros on 4-7, 95 us; sums on 3 or 2 XCDs,
 // 105 or 123 us; the chunk sums and the listed sums in one launch and the
 // zero rows in the next, 113 us for both (against 88 + 21 here); the even
-// workgroups left without a pair writing zero rows too, 93 us; all zero
+// workgroups left without a pair writing zero rows too, 93 us; two or four
+// column groups per lane (all their loads in flight), 90-94 us; all zero
 // rows here with the pairs first in every workgroup, 132 us; one workgroup
 // per table row and column chunk, 128 us.)
 template <typename T, int VEC, int U, bool PVEC>
