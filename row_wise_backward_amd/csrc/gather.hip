@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_exclusive(int32_t* __restri
   __syncthreads();
   // Hillis-Steele inclusive scan of the chunk sums.
   for (int o = 1; o < kScanThreads; o <<= 1) {
-    const int32_t v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    const int32_t v = int(threadIdx.x) >= o ? part[threadIdx.x - o] : 0;
     __syncthreads();
     part[threadIdx.x] += v;
     __syncthreads();
