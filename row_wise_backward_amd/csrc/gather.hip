@@ -904,7 +904,8 @@ __device__ __forceinline__ void chunk_partial(const T* __restrict__ dy, int64_t 
 // Stage A: workgroup (q, c) sums chunk q of a long run into Q[q][chunk c].
 // (Zero rows beside it, as beside the plan, made the backward slower: 137 to
 // 144 us against 135 with 32 to 96 MB of them for 16384 Zipf ids into
-// 32000 x 4096 on MI355X.)
+// 32000 x 4096 on MI355X; on the odd workgroups only, the chunk sums on the
+// even ones, 145 to 150 us against 137 with 64 to 192 MB.)
 template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kSortThreads) void chunk_sums(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
