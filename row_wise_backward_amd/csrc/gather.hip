@@ -905,7 +905,10 @@ __device__ __forceinline__ void chunk_partial(const T* __restrict__ dy, int64_t 
 // (Zero rows beside it, as beside the plan, made the backward slower: 137 to
 // 144 us against 135 with 32 to 96 MB of them for 16384 Zipf ids into
 // 32000 x 4096 on MI355X; on the odd workgroups only, the chunk sums on the
-// even ones, 145 to 150 us against 137 with 64 to 192 MB.)
+// even ones, 145 to 150 us against 137 with 64 to 192 MB, whether the zero
+// workgroups read all M indices or the plan's run bounds: the zero stream
+// slows the latency-bound chunk reads even from the other XCDs, 28 -> 39 us
+// for the chunk sums on four XCDs beside 96 MB.)
 template <typename T, int VEC, int U>
 __global__ __launch_bounds__(kSortThreads) void chunk_sums(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
