@@ -23,8 +23,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, Guarded, empty_padded, padded, pick_rows, to_dev, to_host
-from oracle.compare import U32 as U, pointwise, reduced
+from gpu_util import DEV, Guarded, chunked, empty_padded, padded, pick_rows, to_dev, to_host
+from oracle.compare import U32 as U, combine, pointwise, reduced
 
 pytestmark = pytest.mark.gpu
 nm = oracle.norms
@@ -247,8 +247,8 @@ def test_deterministic(gpu_lib):
 
 @pytest.mark.parametrize("kind", ["ln", "rms"])
 def test_full_size(gpu_lib, kind):
-    """32768 x 4096 bf16 (the softmax workload's shape): y and dx on sampled rows
-    against the oracle, dw (and db) over all rows."""
+    """32768 x 4096 bf16 (the softmax workload's shape): y and dx on every row
+    against the oracle (in chunks of 1024 rows), dw (and db) over all rows."""
     rows, cols = 32768, 4096
     rms = kind == "rms"
     eps = 1e-6 if rms else 1e-5
@@ -263,33 +263,34 @@ def test_full_size(gpu_lib, kind):
         y, mu, rstd = gpu_lib.vjp_layernorm_fwd(xd, wd, bd, eps)
         dx, dw, db = gpu_lib.vjp_layernorm_bwd(dyd, xd, wd, mu, rstd, eps)
     torch.cuda.synchronize()
+    y_host, dx_host = to_host(y, "bf16"), to_host(dx, "bf16")
+    del y, dx, xd, dyd
     w64, b64 = synth.to_f64(w, "bf16"), synth.to_f64(b, "bf16")
-    idx = pick_rows(rows, 256, 9)
-    xs, dys = synth.to_f64(x[idx], "bf16"), synth.to_f64(dy[idx], "bf16")
-    y_ref = nm.rmsnorm_fwd(xs, w64, eps)[0] if rms else nm.layernorm_fwd(xs, w64, b64, eps)[0]
-    reps = [_check(to_host(y, "bf16")[idx], y_ref, fwd_bound(xs, w64, b64, eps, rms), "bf16", "y(sampled)")]
-    # the GPU's own fp32 statistics fed the backward: bound them as recomputed
-    dx_ref = nm.rmsnorm_bwd(dys, xs, w64, eps)[0] if rms else nm.layernorm_bwd(dys, xs, w64, eps)[0]
-    reps.append(_check(to_host(dx, "bf16")[idx], dx_ref, bwd_bound(dys, xs, w64, eps, rms, saved=False),
-                       "bf16", "dx(sampled)"))
-    dw_ref, db_ref = np.zeros(cols), np.zeros(cols)
-    S_dw, S_db = np.zeros(cols), np.zeros(cols)     # sums of |terms|: condition numbers
-    for i in range(0, rows, 4096):
-        xc, dyc = synth.to_f64(x[i:i + 4096], "bf16"), synth.to_f64(dy[i:i + 4096], "bf16")
+
+    def part(i, j):
+        xc, dyc = synth.to_f64(x[i:j], "bf16"), synth.to_f64(dy[i:j], "bf16")
+        y_ref = nm.rmsnorm_fwd(xc, w64, eps)[0] if rms else nm.layernorm_fwd(xc, w64, b64, eps)[0]
+        r_y = _check(y_host[i:j], y_ref, fwd_bound(xc, w64, b64, eps, rms), "bf16", "y")
+        # the GPU's own fp32 statistics fed the backward: bound them as recomputed
         if rms:
-            dw_ref += nm.rmsnorm_bwd(dyc, xc, w64, eps)[1]
+            dx_ref, a1 = nm.rmsnorm_bwd(dyc, xc, w64, eps)[:2]
+            a2 = np.zeros(cols)
             xhat = xc * nm.rmsnorm_rstd(xc, eps)[:, None]
         else:
-            _, a1, a2 = nm.layernorm_bwd(dyc, xc, w64, eps)
-            dw_ref += a1
-            db_ref += a2
+            dx_ref, a1, a2 = nm.layernorm_bwd(dyc, xc, w64, eps)
             mu, rs = nm.layernorm_stats(xc, eps)
             xhat = (xc - mu[:, None]) * rs[:, None]
-        S_dw += np.sum(np.abs(dyc * xhat), axis=0)
-        S_db += np.sum(np.abs(dyc), axis=0)
+        r_dx = _check(dx_host[i:j], dx_ref, bwd_bound(dyc, xc, w64, eps, rms, saved=False), "bf16", "dx")
+        return r_y, r_dx, a1, a2, np.sum(np.abs(dyc * xhat), axis=0), np.sum(np.abs(dyc), axis=0)
+
+    parts = chunked(part, rows, 1024)
+    reps = [combine([p[0] for p in parts], "y(all rows)"), combine([p[1] for p in parts], "dx(all rows)")]
+    dw_ref, db_ref = sum(p[2] for p in parts), sum(p[3] for p in parts)
+    S_dw, S_db = sum(p[4] for p in parts), sum(p[5] for p in parts)     # sums of |terms|
     reps.append(reduced(to_host(dw, "f32"), dw_ref, name="dw", S=S_dw))
     if not rms:
         reps.append(reduced(to_host(db, "f32"), db_ref, name="db", S=S_db))
     for r in reps:
         print("   ", r, flush=True)
+    assert reps[0].n == rows * cols and reps[1].n == rows * cols
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]

@@ -17,8 +17,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, Guarded, empty_padded, padded, pick_rows, to_host
-from oracle.compare import U32, pointwise
+from gpu_util import DEV, Guarded, chunked, empty_padded, padded, pick_rows, to_host
+from oracle.compare import U32, combine, pointwise
 from synth.workloads import SOFTMAX
 
 pytestmark = pytest.mark.gpu
@@ -142,8 +142,8 @@ def test_empty(gpu_lib):
 
 
 def test_full_size(gpu_lib):
-    """The 32768 x 4096 bf16 workload: y and L on sampled rows, the backward from
-    the oracle's L on sampled rows."""
+    """The 32768 x 4096 bf16 workload: y and L on every row, then the backward
+    from the oracle's L on every row (compared in chunks of 2048 rows)."""
     c = SOFTMAX
     rows, cols = c.shape
     print(f"\n[softmax_lse full] {rows}x{cols}", flush=True)
@@ -151,17 +151,32 @@ def test_full_size(gpu_lib):
     dy = synth.normal((rows, cols), c.sigma_dy, c.dtype, c.seed, synth.STREAM_DY)
     xd = padded(x, "bf16")
     y, L = gpu_lib.vjp_softmax_fwd_lse(xd)
-    idx = pick_rows(rows, 512, 5)
-    x_s = synth.to_f64(x[idx], "bf16")
-    reps = [pointwise(to_host(y, "bf16")[idx], sm.fwd(x_s), "bf16", name="y(sampled)"),
-            pointwise(to_host(L, "f32")[idx], sm.lse(x_s), "f32", S=_lse_S(x_s), name="lse(sampled)")]
-    L_ref = np.concatenate([sm.lse(synth.to_f64(x[i:i + 4096], "bf16")) for i in range(0, rows, 4096)])
+    y_host, L_host = to_host(y, "bf16"), to_host(L, "f32")
+    del y
+    L_ref = np.empty(rows)
+
+    def fwd_part(i, j):
+        xs = synth.to_f64(x[i:j], "bf16")
+        L_ref[i:j] = sm.lse(xs)
+        return (pointwise(y_host[i:j], sm.fwd(xs), "bf16", name="y"),
+                pointwise(L_host[i:j], L_ref[i:j], "f32", S=_lse_S(xs), name="lse"))
+
+    r_fwd = chunked(fwd_part, rows, 2048)
+    del y_host
     L32 = L_ref.astype(np.float32)
     dx = gpu_lib.vjp_softmax_bwd_lse(padded(dy, "bf16"), xd, torch.from_numpy(L32).to(DEV))
-    dy_s = synth.to_f64(dy[idx], "bf16")
-    S, F = _dx_tols(dy_s, x_s, L32[idx].astype(np.float64))
-    reps.append(pointwise(to_host(dx, "bf16")[idx], sm.bwd_from_x(dy_s, x_s), "bf16", S=S, floor=F,
-                          name="dx(sampled)"))
+    dx_host = to_host(dx, "bf16")
+    del dx
+
+    def bwd_part(i, j):
+        xs, dys = synth.to_f64(x[i:j], "bf16"), synth.to_f64(dy[i:j], "bf16")
+        S, F = _dx_tols(dys, xs, L32[i:j].astype(np.float64))
+        return pointwise(dx_host[i:j], sm.bwd_from_x(dys, xs), "bf16", S=S, floor=F, name="dx")
+
+    r_dx = chunked(bwd_part, rows, 2048)
+    reps = [combine([r[0] for r in r_fwd], "y(all rows)"), combine([r[1] for r in r_fwd], "lse(all rows)"),
+            combine(r_dx, "dx(all rows)")]
     for r in reps:
         print("   ", r, flush=True)
+    assert reps[0].n == rows * cols and reps[1].n == rows and reps[2].n == rows * cols
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]

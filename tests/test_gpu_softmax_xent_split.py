@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, Guarded, empty_padded, padded, pick_rows, to_host
-from oracle.compare import U32, exact, pointwise, reduced
+from gpu_util import DEV, Guarded, chunked, empty_padded, padded, pick_rows, to_host
+from oracle.compare import U32, combine, exact, pointwise, reduced
 from synth.workloads import XENT
 
 pytestmark = pytest.mark.gpu
@@ -192,8 +192,9 @@ def test_empty(gpu_lib):
 
 
 def test_full_size(gpu_lib):
-    """The 16384 x 32000 bf16 workload: the forward over all rows (mean loss) and
-    row statistics and dlogits on sampled rows."""
+    """The 16384 x 32000 bf16 workload: the forward on every row (row_lse,
+    row_max) and its mean loss, then dlogits on every row from the oracle's
+    lse (compared in chunks of 512 rows)."""
     c = XENT
     rows, C = c.shape
     print(f"\n[xent split full] {rows}x{C}", flush=True)
@@ -202,26 +203,38 @@ def test_full_size(gpu_lib):
     zd, td = padded(z, "bf16"), torch.from_numpy(t).to(DEV)
     wsb = torch.empty(gpu_lib.vjp_softmax_xent_workspace_size(rows) // 4, dtype=torch.float32, device=DEV)
     out = gpu_lib.vjp_softmax_xent_fwd(zd, td, want_max=True, workspace=wsb)
-    idx = pick_rows(rows, 256, 7)
-    z_s = synth.to_f64(z[idx], "bf16")
-    res = {"row_lse": to_host(out["row_lse"], "f32")[idx], "row_max": to_host(out["row_max"], "f32")[idx],
-           "loss": to_host(out["loss"], "f32")}
-    ref_s = xe.fwd(z_s, t[idx])
-    S = np.abs(ref_s["row_max"]) + np.abs(ref_s["row_lse"] - ref_s["row_max"])
-    reps = [pointwise(res["row_lse"], ref_s["row_lse"], "f32", S=S, name="row_lse(sampled)"),
-            exact(res["row_max"], ref_s["row_max"].astype(np.float32), "f32", name="row_max(sampled)")]
-    row_loss = np.concatenate([xe.fwd(synth.to_f64(z[i:i + 1024], "bf16"), t[i:i + 1024])["row_loss"]
-                               for i in range(0, rows, 1024)])
-    reps.append(reduced(res["loss"], np.array([np.sum(row_loss) / rows]), name="loss"))
-    L_all = np.concatenate([xe.fwd(synth.to_f64(z[i:i + 1024], "bf16"), t[i:i + 1024])["row_lse"]
-                            for i in range(0, rows, 1024)]).astype(np.float32)
-    dz = gpu_lib.vjp_softmax_xent_bwd(zd, td, torch.from_numpy(L_all).to(DEV), torch.ones(1, device=DEV))
-    S, F = _dz_tols(z_s, t[idx], L_all[idx].astype(np.float64), 1.0 * len(idx) / rows, "bf16")
-    # _dz_tols scales by dloss / len(rows sampled); pass dloss so that the scale is 1 / rows
-    reps.append(pointwise(to_host(dz, "bf16")[idx], xe.bwd(z_s, t[idx], 1.0 * len(idx) / rows), "bf16",
-                          S=S, floor=F, name="dlogits(sampled)"))
+    lse_host, max_host = to_host(out["row_lse"], "f32"), to_host(out["row_max"], "f32")
+    loss_host = to_host(out["loss"], "f32")
+    L_ref, row_loss = np.empty(rows), np.empty(rows)
+
+    def fwd_part(i, j):
+        ref = xe.fwd(synth.to_f64(z[i:j], "bf16"), t[i:j])
+        L_ref[i:j], row_loss[i:j] = ref["row_lse"], ref["row_loss"]
+        S = np.abs(ref["row_max"]) + np.abs(ref["row_lse"] - ref["row_max"])
+        return (pointwise(lse_host[i:j], ref["row_lse"], "f32", S=S, name="row_lse"),
+                exact(max_host[i:j], ref["row_max"].astype(np.float32), "f32", name="row_max"))
+
+    r_fwd = chunked(fwd_part, rows, 512)
+    reps = [combine([r[0] for r in r_fwd], "row_lse(all rows)"),
+            combine([r[1] for r in r_fwd], "row_max(all rows)"),
+            reduced(loss_host, np.array([np.sum(row_loss) / rows]), name="loss",
+                    S=[np.sum(np.abs(row_loss)) / rows])]
+    L32 = L_ref.astype(np.float32)
+    dz = gpu_lib.vjp_softmax_xent_bwd(zd, td, torch.from_numpy(L32).to(DEV), torch.ones(1, device=DEV))
+    dz_host = to_host(dz, "bf16")
+    del dz, zd
+
+    def bwd_part(i, j):
+        zs = synth.to_f64(z[i:j], "bf16")
+        # _dz_tols and xe.bwd scale by dloss / (j - i): pass dloss so that the scale is 1 / rows
+        dl = 1.0 * (j - i) / rows
+        S, F = _dz_tols(zs, t[i:j], L32[i:j].astype(np.float64), dl, "bf16")
+        return pointwise(dz_host[i:j], xe.bwd(zs, t[i:j], dl), "bf16", S=S, floor=F, name="dlogits")
+
+    reps.append(combine(chunked(bwd_part, rows, 512), "dlogits(all rows)"))
     for r in reps:
         print("   ", r, flush=True)
+    assert reps[0].n == rows and reps[-1].n == rows * C
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
 
 
