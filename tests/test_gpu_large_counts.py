@@ -1,16 +1,15 @@
 """Row and tile counts past the per-launch limits: more than 2^20 rows (the
 row ops launch in chunks of 2^20 rows) and more than 2^20 tiles (the
 weighted-sum backward's reader workgroups loop over the tiles).  Narrow rows keep
-the inputs small; outputs are compared with the oracle at the bars of the
-per-op suites (full reductions over all rows, the rest on sampled rows that
-include both sides of each chunk boundary)."""
+the inputs small; every output element is compared with the oracle at the
+bars of the per-op suites (both sides of each chunk boundary included)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from gpu_util import DEV, pick_rows, to_host
+from gpu_util import DEV, to_host
 from oracle.compare import U32, exact, pointwise, reduced
 from oracle.rounding import round_to, to_storage
 from test_gpu_norms import _check, _stat_errors, bwd_bound, fwd_bound
@@ -21,8 +20,8 @@ BIG = (1 << 20) + 3
 
 
 def _sample(n, seed):
-    edge = np.arange((1 << 20) - 3, min((1 << 20) + 3, n))
-    return np.unique(np.concatenate([pick_rows(n, 2000, seed), edge]))
+    """Every row (the name is kept for the call sites; seed is unused)."""
+    return np.arange(n)
 
 
 def test_weighted_sum_more_tiles_than_workgroups(gpu_lib):
@@ -46,7 +45,7 @@ def test_weighted_sum_more_tiles_than_workgroups(gpu_lib):
     P_ref = oracle.weighted_sum.partials(x64[idx], dy64[idx], 1)
     reps = [exact(to_host(dx, "f32"), to_storage(round_to(gx, "f32"), "f32"), "f32", name="dx"),
             reduced(to_host(dw, "f32"), gw, name="dw"),
-            pointwise(to_host(ws, "f32").reshape(n, d)[idx], P_ref, "f32", name="partials(sampled)")]
+            pointwise(to_host(ws, "f32").reshape(n, d)[idx], P_ref, "f32", name="partials(all rows)")]
     for r in reps:
         print("   ", r, flush=True)
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
@@ -61,9 +60,9 @@ def test_softmax_and_xent_more_rows_than_a_launch(gpu_lib):
     idx = _sample(rows, 2)
     xs = x64[idx]
     y, lse = gpu_lib.vjp_softmax_fwd_lse(xd)
-    reps = [pointwise(to_host(y, "bf16")[idx], oracle.softmax.fwd(xs), "bf16", name="y(sampled)"),
+    reps = [pointwise(to_host(y, "bf16")[idx], oracle.softmax.fwd(xs), "bf16", name="y(all rows)"),
             pointwise(to_host(lse, "f32")[idx], oracle.softmax.lse(xs), "f32", S=_lse_S(xs),
-                      name="lse(sampled)")]
+                      name="lse(all rows)")]
     t = synth.targets(rows, C, 701)
     scale = 1.0 / rows
     out = gpu_lib.vjp_softmax_xent_fwd_bwd(xd, torch.from_numpy(t).to(DEV), grad_scale=scale)
@@ -72,7 +71,7 @@ def test_softmax_and_xent_more_rows_than_a_launch(gpu_lib):
     onehot = np.zeros_like(p)
     onehot[np.arange(len(idx)), t[idx]] = 1.0
     reps.append(pointwise(to_host(out["dlogits"], "bf16")[idx], ref["dz"], "bf16",
-                          S=scale * (p + onehot), floor=16 * U32 * scale * onehot, name="dlogits(sampled)"))
+                          S=scale * (p + onehot), floor=16 * U32 * scale * onehot, name="dlogits(all rows)"))
     reps.append(reduced(to_host(out["loss"], "f32"),
                         np.array([oracle.softmax_xent.fwd(x64, t)["loss"]]), name="loss"))
     for r in reps:
@@ -100,11 +99,11 @@ def test_rmsnorm_more_rows_than_a_launch(gpu_lib):
     _, dr = _stat_errors(xs, 0.0, rstd_ref[idx, None], eps, True, saved=False)
     dx_ref, _ = oracle.norms.rmsnorm_bwd(dys, xs, w64, eps)
     _, dw_ref = oracle.norms.rmsnorm_bwd(dy64, x64, w64, eps)
-    reps = [_check(to_host(y, "f32")[idx], y_ref, fwd_bound(xs, w64, 0.0, eps, True), "f32", "y(sampled)"),
+    reps = [_check(to_host(y, "f32")[idx], y_ref, fwd_bound(xs, w64, 0.0, eps, True), "f32", "y(all rows)"),
             _check(to_host(dx, "f32")[idx], dx_ref, bwd_bound(dys, xs, w64, eps, True, True), "f32",
-                   "dx(sampled)"),
+                   "dx(all rows)"),
             pointwise(to_host(rstd, "f32")[idx], rstd_ref[idx], "f32", S=2 * dr[:, 0] * rstd_ref[idx] / 1e-5,
-                      name="rstd(sampled)"),
+                      name="rstd(all rows)"),
             reduced(to_host(dw, "f32"), dw_ref, name="dw")]
     for r in reps:
         print("   ", r, flush=True)
