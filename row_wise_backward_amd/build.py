@@ -64,5 +64,33 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+CONSUMER_SRC = os.path.join(ROOT, "tests", "c_abi_consumer.c")
+CONSUMER = os.path.join(ROOT, "tests", "_build", "c_abi_consumer")
+
+
+def consumer_cmd(out: str = CONSUMER, link: bool = True) -> list[str]:
+    """gcc command for the plain-C99 consumer of the ABI (tests/c_abi_consumer.c):
+    the header and the HIP runtime's C API only, linked against libvjp.so with
+    run paths relative to the program, so the tree can move."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), CONSUMER_SRC]
+    if not link:
+        return cmd + ["-fsyntax-only"]
+    rel = os.path.relpath(PKG, os.path.dirname(out))
+    return cmd + ["-o", out, "-L", PKG, "-lvjp", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+                  f"-Wl,-rpath,$ORIGIN/{rel}", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+
+
+def build_consumer(verbose: bool = False) -> str:
+    """Compile the C consumer against the built library (after build())."""
+    os.makedirs(os.path.dirname(CONSUMER), exist_ok=True)
+    _run(consumer_cmd())
+    if verbose:
+        print("linked", CONSUMER, flush=True)
+    return CONSUMER
+
+
 if __name__ == "__main__":
     build(verbose="-q" not in sys.argv)
+    build_consumer(verbose="-q" not in sys.argv)

@@ -21,6 +21,16 @@ def _ensure_built():
                        check=True)
 
 
+def _load_build():
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "_libvjp_build_for_tests", os.path.join(ROOT, "row_wise_backward_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 _ensure_built()
 import row_wise_backward_amd as rwb  # noqa: E402
 
@@ -347,3 +357,16 @@ def test_copy_rejections():
     assert sh(n=-1) == EINVAL and sh(src=None) == EINVAL
     assert sh(dst=A + 8) == EALIAS
     assert sh(src=None, dst=None, n=0) == OK
+
+
+def test_header_compiles_as_plain_c99():
+    """include/libvjp.h is plain C: the C consumer of the ABI compiles with gcc
+    -std=c99 -Wall -Wextra against it (and the HIP runtime's C API), with no
+    diagnostics from either file of ours."""
+    import subprocess
+
+    build = _load_build()
+    r = subprocess.run(build.consumer_cmd(link=False), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    ours = [ln for ln in r.stderr.splitlines() if "libvjp.h" in ln or "c_abi_consumer.c" in ln]
+    assert not ours, ours
