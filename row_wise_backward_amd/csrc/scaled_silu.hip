@@ -120,7 +120,10 @@ __global__ __launch_bounds__(kThreads) void silu_bwd_kernel(
 // Vectors per thread and step, every load of a step in flight together
 // (measured on MI355X for n = 2^24 fp16, HIP events: forward 8 vectors
 // 14.1-14.3 us, 4 vectors 15.4-15.9 us; backward over tiles of 4096
-// elements, 2 vectors 20.5-20.8 us, 1 vector 21.3-21.7 us).
+// elements, 2 vectors 20.5-20.8 us, 1 vector 21.3-21.7 us).  Under a
+// cache-flushed median the backward kept the same order: tiles of 4096
+// elements with 2 vectors 18.2 us, 1 vector 19.5 us; tiles of 8192 or 16384
+// elements with 2 to 8 vectors 18.7-20.2 us; tiles of 2048 with 1 vector 18.2.
 constexpr int kFwdUnroll = 8;
 constexpr int kBwdUnroll = 2;
 
