@@ -1021,7 +1021,11 @@ __global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
 // workgroups left without a pair writing zero rows too, 93 us; two or four
 // column groups per lane (all their loads in flight), 90-94 us; all zero
 // rows here with the pairs first in every workgroup, 132 us; one workgroup
-// per table row and column chunk, 128 us.)
+// per table row and column chunk, 128 us; every zero row written by a
+// kernel of its own on a second stream, beside the plan, the chunk sums and
+// the listed sums on the first, 143-175 us for the whole backward against
+// 134: its workgroups hold the CUs the latency-bound sums wait for, and the
+// chunk sums alone stretched from 20 to 43-104 us.)
 template <typename T, int VEC, int U, bool PVEC>
 __global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
