@@ -273,7 +273,10 @@ constexpr int64_t kFillTailBytes = int64_t(96) << 20;
 // workgroups take about 25 us on their own.  (Measured for the same
 // workload: plan_count 28.7 / 33.4 / 40.6 / 44.1 us with 96 / 128 / 160 /
 // 192 MB beside it, the listed-rows kernel 88.1 / 84.2 / 80.6 / 77.0 us: the
-// zeros it sheds cost it less than they cost the plan.)
+// zeros it sheds cost it less than they cost the plan.  Fill workgroups that
+// zero every row of their share, skipping the scan of the indices and
+// leaving the selected rows to be overwritten later, gave the same whole
+// backward, 132.0 against 132.2 us.)
 constexpr int64_t kFillCountBytes = int64_t(96) << 20;
 constexpr int kFillUnroll = 16;
 
