@@ -64,20 +64,30 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_softmax_xent_bf16_16384x3
 
 
 # Sources that define the fused cross-entropy kernels (the op with the largest
-# share of the step) and the build flags: stored counter readings for it expire
-# when any of them changes.
-XENT_SOURCES = ("softmax_xent.hip", "reduce.hip", "rowops.hpp", "common.hpp")
+# share of the step) and the device compile flags: stored counter readings for
+# it expire when any of them changes.
+XENT_SOURCES = ("softmax_xent.hip", "reduce.hip", "rowops.hpp", "common.hpp", "launch.hpp")
+
+
+def _compile_flags() -> list:
+    """The library's hipcc flags, include directories named without their
+    location (the tree sits at different paths on different hosts)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_vjp_build", os.path.join(ROOT, "row_wise_backward_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [os.path.basename(f) if os.path.isabs(f) else f for f in mod.compile_flags()]
 
 
 def source_digest(files=XENT_SOURCES) -> str:
-    """Hash of the named kernel sources and of the build script."""
+    """Hash of the named kernel sources and of the compile flags."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "row_wise_backward_amd", "csrc")
-    paths = [os.path.join(csrc, f) for f in files]
-    paths.append(os.path.join(ROOT, "row_wise_backward_amd", "build.py"))
-    for path in paths:
-        with open(path, "rb") as fh:
-            h.update(os.path.basename(path).encode() + fh.read())
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    h.update(" ".join(_compile_flags()).encode())
     return h.hexdigest()[:16]
 
 
