@@ -165,8 +165,15 @@ def test_full_size(gpu_lib):
     V = c.extra["V"]
     print(f"\n[gather full] M={M} V={V} D={D}", flush=True)
     idx = synth.zipf_indices(M, V, c.seed, c.extra["zipf_a"])
-    dy = synth.normal((M, D), 1.0, "bf16", c.seed, synth.STREAM_DY)
     idx_d = torch.from_numpy(idx).to(DEV)
+    x = synth.normal((V, D), c.sigma_x, "bf16", c.seed, synth.STREAM_X)
+    y = gpu_lib.vjp_gather_rows_fwd(synth.to_torch(x, "bf16", DEV).view(V, D), idx_d)
+    y_ref = ga.fwd(synth.to_f64(x, "bf16"), idx)
+    ry = exact(to_host(y, "bf16"), synth.f32_to_storage(y_ref.astype(np.float32), "bf16"), "bf16",
+               name="y")
+    print("   ", ry, flush=True)
+    del x, y, y_ref
+    dy = synth.normal((M, D), 1.0, "bf16", c.seed, synth.STREAM_DY)
     dt, n = gpu_lib.vjp_gather_rows_bwd(synth.to_torch(dy, "bf16", DEV).view(M, D), idx_d, V)
     torch.cuda.synchronize()
     dy64 = synth.to_f64(dy, "bf16")
@@ -174,7 +181,7 @@ def test_full_size(gpu_lib):
     S, _ = ga.bwd(np.abs(dy64), idx, V)
     r = pointwise(to_host(dt, "f32"), dt_ref, "f32", S=S, name="dtable")
     print("   ", r, flush=True)
-    assert r.ok and int(n.item()) == n_inv == 0
+    assert ry.ok and r.ok and int(n.item()) == n_inv == 0
 
 
 def test_widest_rows_unaligned(gpu_lib):
