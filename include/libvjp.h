@@ -38,9 +38,13 @@
  * Streams     Every call is asynchronous on `stream` (a hipStream_t; NULL is
  *             the default stream) and never synchronises the host.  A call
  *             only launches kernels on that stream (no allocation, copy or
- *             memset, and no query of the device), so calls may be captured
- *             in a HIP graph and replayed; a replay with the same inputs
- *             gives the same bits as an eager call.
+ *             memset; the only device queries are host-side: the scatter-add
+ *             backward reads the current device and, on its first call on a
+ *             device, its compute-unit count, and the no-allocation entry
+ *             point reads the current device and, once per device, its
+ *             scratch address), so calls may be captured in a HIP graph and
+ *             replayed; a replay with the same inputs gives the same bits as
+ *             an eager call.
  * Errors      Every call returns VJP_OK or a VJP_E* code.  On an error
  *             detected before launch nothing is launched and no output is
  *             touched; vjp_last_error() gives a per-thread message.
