@@ -669,7 +669,8 @@ def pair_rows(pairs, by_name, copy_gbs, matched_ms=None):
 def protocol_summary_md(res, source, command, path):
     """Markdown table of the protocol's per-kernel medians (written for profiles/)."""
     lines = [f"# Fwd+bwd pairs, flushed: {source}", "",
-             f"Command: `python3 bench.py --protocol-summary {path}` (its protocol child ran "
+             f"Command: `python3 bench.py --protocol-summary <out>/{os.path.basename(path)}` (its "
+             "protocol child ran "
              f"`{command}`).", "",
              f"Each launch group ran {PROTOCOL_WARM} + {PROTOCOL_REPS} times after 1 GiB of plain "
              "stores (torch fill) that evict L2 and the Infinity Cache; medians over the last "
@@ -682,7 +683,7 @@ def protocol_summary_md(res, source, command, path):
     return "\n".join(lines) + "\n"
 
 
-COUNTER_CMD = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c} -o run -- python3 bench.py "
+COUNTER_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_{c} -o run -- python3 bench.py "
                "--protocol off --steps 2 --warmup 1 --no-cpu-baseline --calib-copy")
 
 
@@ -786,7 +787,7 @@ def counters_summary(fetch_csv, write_csv, md_path, json_path):
     return 0
 
 
-STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o run -- "
+STATS_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof -o run -- "
              "python3 bench.py --protocol off --no-cpu-baseline --steps 10 --warmup 3")
 
 
