@@ -128,6 +128,33 @@ def test_side_stream_matches_default_stream(gpu_lib):
     _same(ref, st.snapshot())
 
 
+def test_two_streams_at_once(gpu_lib):
+    """Two steps with their own buffers and inputs, launched on two streams
+    with nothing ordering them: calls share no state (each has its own
+    workspace), so each step equals its own eager result bit for bit."""
+    a, b = Step(), Step()
+    a.load(31)
+    a.run()
+    ref_a = a.snapshot()
+    b.load(32)
+    b.run()
+    ref_b = b.snapshot()
+    for st in (a, b):
+        for k in st.out:
+            st.out[k].fill_(0)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            a.run()
+        with torch.cuda.stream(sb):
+            b.run()
+    torch.cuda.synchronize()
+    _same(ref_a, a.snapshot())
+    _same(ref_b, b.snapshot())
+
+
 def test_graph_capture_replays_bitwise(gpu_lib):
     st = Step()
     refs = {}
