@@ -277,6 +277,10 @@ int lanes_per_row(int64_t d, int vec) {
 // that; one row group: 235 us, two: 188 us, four: 185 us) beside up to
 // 32768 writer workgroups (four row groups each at this size).  More tiles
 // and readers (1024 to 4096 of each) or 16384 writers took 185-206 us.
+// A later sweep of the forward under cache-flushed medians of 20 (one
+// process): 83.6-85.2 us here; 2, 8 or 16 row groups per lane with 2048 to
+// 32768 workgroups 83.9-125.9 us, none better by more than the run-to-run
+// spread.
 constexpr int kFwdUnroll = 4;
 constexpr int64_t kFwdMaxGrid = 8192;
 constexpr int kBwdUnroll = 4;
