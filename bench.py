@@ -36,7 +36,9 @@ around every op); `extras` / `extra_pairs_cold` cover the widened rows
 [32768, 4096] bf16, the embedding gather with its deterministic scatter-add
 backward over 16384 Zipf ids into a 32000 x 4096 table).  `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workloads, on all
-cores and on one.
+cores and on one.  After timing, the outputs of every op are checked on the
+GPU (`checks`: invariants and fp32 recomputations of sampled rows, each as
+worst error / bound); a failed check ends the run with status 1 and no line.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -473,6 +475,8 @@ class Workbench:
              bytes_gather_bwd(e_M, e_V, e_D), e_M * e_D),
         ]
         self.keep = [v for v in locals().values() if isinstance(v, torch.Tensor)]
+        self.t = {k: v for k, v in locals().items() if isinstance(v, torch.Tensor)}
+        self.scale = scale
         # copy reference buffers: as many bytes as the largest op moves, half each way
         self.copy_half = max(o[3] for o in self.ops) // 32 * 16
         self.ca = e(self.copy_half, dtype=torch.uint8)
@@ -493,6 +497,154 @@ class Workbench:
         if st != 0:
             raise RuntimeError(f"vjp_copy_shaped: status {st} ({self.rwb.vjp_last_error()})")
         return n
+
+
+    # ------------------------------------------------------------- output checks
+    # Sanity checks of what the timed launches computed, on the GPU with torch
+    # in fp32: invariants of each result and recomputations of sampled rows.
+    # They are not the parity tests (those compare every element with the CPU
+    # oracle); they keep a launch that computes garbage from being reported
+    # as a throughput.  Each check is (worst error / its bound): 1 or less
+    # passes.  The bounds allow two units of the storage rounding (2^-7
+    # relative for bf16, 2^-10 for fp16) plus the fp32 error of the values.
+
+    def check_step(self):
+        """The step's outputs, right after the timed steps."""
+        torch, t = self.torch, self.t
+        f = lambda a: a.float()  # noqa: E731
+        worst = lambda err, bound: float((err / bound).max())  # noqa: E731
+        out = {}
+        # weighted sum: y and grad_x on every 257th row, grad_w against a GEMV
+        rows = torch.arange(0, t["wx"].shape[0], 257, device=t["wx"].device)
+        x, w, g = f(t["wx"][rows]), f(t["ww"]), f(t["wg"][rows])
+        ref = (x * w).sum(1)
+        out["weighted_sum_y"] = worst((f(t["wy"][rows]) - ref).abs(),
+                                      2 ** -7 * ref.abs() + 1e-5 * (x * w).abs().sum(1) + 1e-30)
+        exact = torch.equal(t["wdx"][rows], (g[:, None] * w).to(t["wdx"].dtype))
+        out["weighted_sum_grad_x_exact"] = 0.0 if exact else float("inf")
+        X, G = f(t["wx"]), f(t["wg"])
+        dw_ref = torch.mv(X.t(), G)
+        dw_abs = torch.mv(X.abs().t(), G.abs())
+        del X
+        out["weighted_sum_grad_w"] = worst((t["wdw"] - dw_ref).abs(), 1e-4 * dw_abs + 1e-30)
+        # scaled SiLU: every element of y and dx, and dw
+        x, g, wv = f(t["sx"]), f(t["sg"]), f(t["sw"])
+        sg = torch.sigmoid(x)
+        ref = wv * x * sg
+        out["scaled_silu_y"] = worst((f(t["sy"]) - ref).abs(), 2 ** -10 * ref.abs() + 1e-7)
+        ref = g * wv * (sg + x * sg * (1 - sg))
+        out["scaled_silu_dx"] = worst((f(t["sdx"]) - ref).abs(),
+                                      2 ** -10 * ref.abs() + 1e-4 * (g * wv).abs() * (1 + x.abs()) + 1e-7)
+        terms = g * x * sg
+        out["scaled_silu_dw"] = worst((t["sdw"] - terms.sum()).abs(), 1e-5 * terms.abs().sum() + 1e-30)
+        # softmax: row sums of y and dx everywhere, every 129th row recomputed
+        y, dy, dx = t["my"], t["mg"], t["mdx"]
+        out["softmax_y_row_sums"] = float((f(y).sum(1) - 1).abs().max()) / 1e-2
+        sdot = (f(dy) * f(y)).sum(1)
+        out["softmax_dx_row_sums"] = worst(f(dx).sum(1).abs(), 1e-2 * (sdot.abs() + f(dx).abs().sum(1)) + 1e-30)
+        rows = torch.arange(0, y.shape[0], 129, device=y.device)
+        ref = torch.softmax(f(t["mx"][rows]), 1)
+        out["softmax_y_rows"] = worst((f(y[rows]) - ref).abs(), 2 ** -7 * ref + 1e-30)
+        ys, gs = f(y[rows]), f(dy[rows])
+        ref = ys * (gs - sdot[rows, None])
+        sabs = (gs.abs() * ys).sum(1, keepdim=True)
+        out["softmax_dx_rows"] = worst((f(dx[rows]) - ref).abs(),
+                                       2 ** -7 * ref.abs() + 1e-4 * ys * (gs.abs() + sabs) + 1e-30)
+        out.update(self._check_xent(t["loss"], t["rlse"], t["dz"], self.scale, t["rmax"]))
+        out["softmax_xent_n_invalid"] = 0.0 if int(t["ninv"].item()) == 0 else float("inf")
+        return out
+
+    def _check_xent(self, loss, lse, dz, scale, rmax=None, tag="softmax_xent"):
+        torch, t = self.torch, self.t
+        f = lambda a: a.float()  # noqa: E731
+        worst = lambda err, bound: float((err / bound).max())  # noqa: E731
+        z, tg = t["z"], t["tg"].long()
+        R, C = z.shape
+        ar = torch.arange(R, device=z.device)
+        loss_ref = (lse - f(z[ar, tg])).mean()
+        out = {f"{tag}_loss": float((loss - loss_ref).abs() / (1e-5 * loss_ref.abs() + 1e-30))}
+        if rmax is not None:
+            ok = bool((lse >= rmax).all()) and bool((lse <= rmax + float(torch.log(torch.tensor(float(C)))) + 1e-3).all())
+            out[f"{tag}_lse_bounds"] = 0.0 if ok else float("inf")
+        sums = torch.cat([f(dz[r:r + 1024]).sum(1) for r in range(0, R, 1024)])
+        out[f"{tag}_dlogits_row_sums"] = float(sums.abs().max()) / (2e-2 * scale)
+        rows = ar[::64]
+        p = torch.exp(f(z[rows]) - lse[rows, None])
+        p[torch.arange(rows.numel(), device=z.device), tg[rows]] -= 1.0
+        ref = scale * p
+        out[f"{tag}_dlogits_rows"] = worst((f(dz[rows]) - ref).abs(), 2 ** -7 * ref.abs() + 1e-6 * scale)
+        return out
+
+    def check_extras(self):
+        """The widened rows: each op run once more, its outputs checked before
+        the next op reuses the buffers."""
+        torch, t = self.torch, self.t
+        F = torch.nn.functional
+        f = lambda a: a.float()  # noqa: E731
+        worst = lambda err, bound: float((err / bound).max())  # noqa: E731
+        ops = {o[0]: o for o in self.extra_ops}
+        out = {}
+        x, dy = t["mx"], t["mg"]
+        rows = torch.arange(0, x.shape[0], 129, device=x.device)
+        xs, gs = f(x[rows]), f(dy[rows])
+        # softmax saving the logsumexp, backward rebuilding y from x and lse
+        self.call(ops["softmax_fwd_lse"])
+        self.call(ops["softmax_bwd_lse"])
+        torch.cuda.synchronize()
+        ref = torch.logsumexp(f(x), 1)
+        out["softmax_lse_L"] = worst((t["mlse"] - ref).abs(), 1e-5 * ref.abs() + 1e-5)
+        out["softmax_lse_y_row_sums"] = float((f(t["my"]).sum(1) - 1).abs().max()) / 1e-2
+        yr = torch.exp(xs - t["mlse"][rows, None])
+        ref = yr * (gs - (gs * yr).sum(1, keepdim=True))
+        sabs = (gs.abs() * yr).sum(1, keepdim=True)
+        out["softmax_lse_dx_rows"] = worst((f(t["mdx"][rows]) - ref).abs(),
+                                           2 ** -7 * ref.abs() + 1e-4 * yr * (gs.abs() + sabs) + 1e-30)
+        # split cross-entropy: statistics forward, backward from the saved lse (dloss = 1)
+        self.call(ops["softmax_xent_fwd"])
+        self.call(ops["softmax_xent_bwd"])
+        torch.cuda.synchronize()
+        R = t["z"].shape[0]
+        out.update(self._check_xent(t["loss"], t["rlse"], t["dz2"], float(t["dloss"].item()) / R,
+                                    tag="softmax_xent_split"))
+        # LayerNorm and RMSNorm: sampled rows of y, the statistics, and dw (db)
+        w, b = f(t["nw"]), f(t["nb"])
+        for name, rms in (("layernorm", False), ("rmsnorm", True)):
+            self.call(ops[name + "_fwd"])
+            self.call(ops[name + "_bwd"])
+            torch.cuda.synchronize()
+            eps = 1e-6 if rms else 1e-5
+            X = f(x)
+            if rms:
+                rstd = torch.rsqrt((X * X).mean(1) + eps)
+                xhat = X * rstd[:, None]
+                ref_y = xhat[rows] * w
+            else:
+                mu = X.mean(1)
+                rstd = torch.rsqrt(((X - mu[:, None]) ** 2).mean(1) + eps)
+                xhat = (X - mu[:, None]) * rstd[:, None]
+                ref_y = xhat[rows] * w + b
+                out["layernorm_mean"] = worst((t["nmean"] - mu).abs(), 1e-5 * X.abs().mean(1) + 1e-30)
+            out[f"{name}_rstd"] = worst((t["nrstd"] - rstd).abs(), 1e-4 * rstd)
+            out[f"{name}_y_rows"] = worst((f(t["my"][rows]) - ref_y).abs(),
+                                          2 ** -7 * ref_y.abs() + 1e-4 * (xhat[rows] * w).abs() + 1e-30)
+            G = f(dy)
+            out[f"{name}_dw"] = worst((t["ndw"] - (G * xhat).sum(0)).abs(), 1e-4 * (G * xhat).abs().sum(0) + 1e-30)
+            if not rms:
+                out["layernorm_db"] = worst((t["ndb"] - G.sum(0)).abs(), 1e-4 * G.abs().sum(0) + 1e-30)
+            del X, xhat, G
+        # row gather (a bit copy) and its scatter-add
+        self.call(ops["gather_rows_fwd"])
+        self.call(ops["gather_rows_bwd"])
+        torch.cuda.synchronize()
+        idx = t["e_idx"].long()
+        out["gather_rows_y_exact"] = 0.0 if torch.equal(t["e_y"], t["e_tab"][idx]) else float("inf")
+        G = f(t["e_dy"])
+        ref = G.sum(0)
+        out["gather_rows_dtable_column_sums"] = worst((t["e_dt"].sum(0) - ref).abs(), 1e-4 * G.abs().sum(0) + 1e-30)
+        unsel = torch.bincount(idx, minlength=t["e_dt"].shape[0]) == 0
+        out["gather_rows_dtable_zero_rows"] = 0.0 if not bool(t["e_dt"][unsel].any()) else float("inf")
+        out["gather_rows_n_invalid"] = 0.0 if int(t["e_ninv"].item()) == 0 else float("inf")
+        return out
 
 
 def protocol_items(wb):
@@ -932,6 +1084,7 @@ def main() -> int:
     dom = op_row(ops[i_dom][0], ms_dom, ops[i_dom][3], ops[i_dom][4])
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; {dom['op']} {ms_dom * 1e3:.1f} us",
           file=sys.stderr, flush=True)
+    checks = wb.check_step()
 
     # Widened rows (warm, events around each op), after and outside the step.
     n_extra = max(3, args.steps // 2)
@@ -946,6 +1099,13 @@ def main() -> int:
     extras = [op_row(o[0], sum(xevs[k][i][0].elapsed_time(xevs[k][i][1]) for k in range(1, n_extra + 1))
                      / n_extra, o[3], o[4]) for i, o in enumerate(wb.extra_ops)]
     print(f"[bench] timed the widened rows ({n_extra} rounds)", file=sys.stderr, flush=True)
+    checks.update(wb.check_extras())
+    bad = {k: v for k, v in checks.items() if not v <= 1.0}
+    if bad:
+        print(f"[bench] output checks failed (error / bound): {bad}", file=sys.stderr, flush=True)
+        return 1
+    print(f"[bench] {len(checks)} output checks passed (worst error / bound "
+          f"{max(checks.values()):.3f})", file=sys.stderr, flush=True)
 
     # Flushed protocol: from the rocprofv3 child, else HIP events here.
     items = protocol_items(wb)
@@ -1052,6 +1212,7 @@ def main() -> int:
             "frac_of_warm_copy": round(dom["GB/s"] / warm_copy_gbs, 4),
         },
         "cpu_baseline": None,
+        "checks": {k: round(v, 4) for k, v in checks.items()},
     }
     del wb
     torch.cuda.empty_cache()
