@@ -124,6 +124,11 @@ __global__ __launch_bounds__(kThreads) void silu_bwd_kernel(
 // cache-flushed median the backward kept the same order: tiles of 4096
 // elements with 2 vectors 18.2 us, 1 vector 19.5 us; tiles of 8192 or 16384
 // elements with 2 to 8 vectors 18.7-20.2 us; tiles of 2048 with 1 vector 18.2.
+// Workgroup sizes (one process, flushed medians): the forward 12.8 us with
+// 256 threads against 12.9 / 13.5 / 14.7 us with 128 / 512 / 1024 (each over
+// 16384 elements); the backward 18.2 us against 18.4 / 19.0 / 20.7 us with
+// 512 / 128 / 64 threads over the same 4096-element tiles, 19.6 us with 1024
+// threads over tiles of 8192.
 constexpr int kFwdUnroll = 8;
 constexpr int kBwdUnroll = 2;
 
