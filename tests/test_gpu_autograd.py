@@ -315,3 +315,24 @@ def test_training_steps_norm_softmax_weighted_sum(ag):
     for r_ in reps:
         print("   ", r_, flush=True)
     assert all(r_.ok for r_ in reps), [str(r_) for r_ in reps if not r_.ok]
+
+
+def test_readme_example(ag):
+    """The Python example of README.md, run as written (full-size logits):
+    the loss equals the mean of lse - z_t, and each row of the logit gradient
+    sums to about zero."""
+    import os
+    import re
+
+    readme = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "README.md")
+    code = re.search(r"```python\n(.*?)```", open(readme).read(), re.S).group(1)
+    env = {}
+    exec(compile(code, "README.md", "exec"), env)
+    logits, targets, loss = env["logits"], env["targets"], env["loss"]
+    z = logits.detach().float()
+    ref = (torch.logsumexp(z, 1) - z[torch.arange(z.shape[0], device=z.device), targets]).mean()
+    print(f"\n[readme] loss {loss.item():.6f} ref {ref.item():.6f}", flush=True)
+    assert abs(loss.item() - ref.item()) <= 1e-5 * abs(ref.item())
+    g = logits.grad
+    assert g.shape == logits.shape and g.dtype == logits.dtype
+    assert float(g.float().sum(1).abs().max()) <= 2e-2 / z.shape[0]
