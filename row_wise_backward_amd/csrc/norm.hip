@@ -345,7 +345,9 @@ constexpr int kLaneElems = 16;
 // (w and b read once per two rows), 111 us with four; RMSNorm 90 us with
 // one, 91 us with two.  Workgroups that loop over rows with the parameters
 // held in registers measured 127 us.  (The bias loads cost LayerNorm 11 us:
-// 89-90 us without them.)  Those figures predate the register fences between
+// 89-90 us without them; with the register fences below, 95.6 against
+// 90.7 us in one process, RMSNorm 88.1.  Two row pairs per workgroup with w
+// and b loaded once take 251 VGPRs, or spill 780 bytes per lane at 64.)  Those figures predate the register fences between
 // the phases of the forward: with them LayerNorm's two-row form holds 64
 // VGPRs instead of 80 (eight waves per SIMD instead of six) and took 96 us;
 // RMSNorm with two rows (47 VGPRs) took 92 us against 90 us with one, and
