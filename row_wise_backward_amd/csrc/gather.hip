@@ -1030,7 +1030,10 @@ __global__ __launch_bounds__(kSortThreads) void scatter_add_rows(
 // kernel of its own on a second stream, beside the plan, the chunk sums and
 // the listed sums on the first, 143-175 us for the whole backward against
 // 134: its workgroups hold the CUs the latency-bound sums wait for, and the
-// chunk sums alone stretched from 20 to 43-104 us.)
+// chunk sums alone stretched from 20 to 43-104 us; the chunk sums moved into
+// this launch beside the short rows' sums, and the long rows' chunk sums
+// added up in a third launch, 164-171 us against 132 (this launch 128 us,
+// the third 13-20 us: a long row's chain of up to 92 partials is exposed).)
 template <typename T, int VEC, int U, bool PVEC>
 __global__ __launch_bounds__(kSortThreads) void scatter_listed_rows(
     const T* __restrict__ dy, int64_t ld_dy, const int32_t* __restrict__ sorted_pos,
