@@ -115,3 +115,100 @@ def test_workspace_queries(n, d, rpt):
     L.vjp_layernorm_bwd_workspace_size(n, d)
     L.vjp_rmsnorm_bwd_workspace_size(n, d)
     assert (L.vjp_scaled_silu_elems_per_tile(n) == -1) == (n < 0)
+
+
+@SETTINGS
+@given(ptr, ptr, ptr, size, dtype)
+def test_scaled_silu_fwd(x, w, y, n, act):
+    _check(L.vjp_scaled_silu_fwd(P(x), P(w), P(y), n, act, None), (n,), (act,))
+
+
+@SETTINGS
+@given(ptr, ptr, ptr, ptr, ptr, flag, size, dtype)
+def test_scaled_silu_bwd_noalloc(dy, x, w, dx, dw, acc, n, act):
+    _check(L.vjp_scaled_silu_bwd_noalloc(P(dy), P(x), P(w), P(dx), P(dw), acc, n, act, None),
+           (n,), (act,))
+
+
+@SETTINGS
+@given(ptr, size, ptr, size, ptr, size, size, size, dtype)
+def test_softmax_bwd(dy, ldg, y, ldy, dx, ldd, rows, cols, act):
+    _check(L.vjp_softmax_bwd(P(dy), ldg, P(y), ldy, P(dx), ldd, rows, cols, act, None),
+           (rows, cols), (act,))
+
+
+@SETTINGS
+@given(ptr, size, ptr, size, ptr, size, size, dtype)
+def test_softmax_fwd_lse(x, ldx, y, ldy, lse, rows, cols, act):
+    _check(L.vjp_softmax_fwd_lse(P(x), ldx, P(y), ldy, P(lse), rows, cols, act, None),
+           (rows, cols), (act,))
+
+
+@SETTINGS
+@given(ptr, size, ptr, size, ptr, ptr, size, size, size, dtype)
+def test_softmax_bwd_lse(dy, ldg, x, ldx, lse, dx, ldd, rows, cols, act):
+    _check(L.vjp_softmax_bwd_lse(P(dy), ldg, P(x), ldx, P(lse), P(dx), ldd, rows, cols, act, None),
+           (rows, cols), (act,))
+
+
+@SETTINGS
+@given(ptr, size, ptr, size, size, dtype, ptr, ptr, ptr, ptr, ptr, size)
+def test_softmax_xent_fwd(z, ld, t, rows, classes, act, loss, rmax, rlse, ninv, ws, wsb):
+    _check(L.vjp_softmax_xent_fwd(P(z), ld, P(t), rows, classes, act, P(loss), P(rmax), P(rlse),
+                                  P(ninv), P(ws), max(wsb, 0), None), (rows, classes), (act,))
+
+
+@SETTINGS
+@given(ptr, size, ptr, ptr, size, size, dtype, ptr, ptr, size)
+def test_softmax_xent_bwd(z, ld, t, lse, rows, classes, act, dloss, dz, ldz):
+    _check(L.vjp_softmax_xent_bwd(P(z), ld, P(t), P(lse), rows, classes, act, P(dloss), P(dz), ldz,
+                                  None), (rows, classes), (act,))
+
+
+@SETTINGS
+@given(ptr, size, ptr, size, ptr, ptr, ptr, ptr, size, ptr, ptr, flag, size, size, dtype, dtype,
+       ptr, size)
+def test_layernorm_bwd(dy, ldg, x, ldx, w, mean, rstd, dx, ldd, dw, db, acc, rows, cols, act, wdt,
+                       ws, wsb):
+    _check(L.vjp_layernorm_bwd(P(dy), ldg, P(x), ldx, P(w), P(mean), P(rstd), P(dx), ldd, P(dw),
+                               P(db), acc, rows, cols, ctypes.c_float(1e-5), act, wdt, P(ws),
+                               max(wsb, 0), None), (rows, cols), (act, wdt))
+
+
+@SETTINGS
+@given(ptr, size, ptr, ptr, size, ptr, size, size, dtype, dtype)
+def test_rmsnorm_fwd(x, ldx, w, y, ldy, rstd, rows, cols, act, wdt):
+    _check(L.vjp_rmsnorm_fwd(P(x), ldx, P(w), P(y), ldy, P(rstd), rows, cols, ctypes.c_float(1e-6),
+                             act, wdt, None), (rows, cols), (act, wdt))
+
+
+@SETTINGS
+@given(ptr, size, ptr, size, ptr, ptr, ptr, size, ptr, flag, size, size, dtype, dtype, ptr, size)
+def test_rmsnorm_bwd(dy, ldg, x, ldx, w, rstd, dx, ldd, dw, acc, rows, cols, act, wdt, ws, wsb):
+    _check(L.vjp_rmsnorm_bwd(P(dy), ldg, P(x), ldx, P(w), P(rstd), P(dx), ldd, P(dw), acc, rows,
+                             cols, ctypes.c_float(1e-6), act, wdt, P(ws), max(wsb, 0), None),
+           (rows, cols), (act, wdt))
+
+
+@SETTINGS
+@given(ptr, size, size, size, ptr, size, ptr, size, dtype)
+def test_gather_rows_fwd(tab, ldt, V, D, idx, M, y, ldy, act):
+    _check(L.vjp_gather_rows_fwd(P(tab), ldt, V, D, P(idx), M, P(y), ldy, act, None),
+           (V, D, M), (act,))
+
+
+@SETTINGS
+@given(ptr, ptr, size)
+def test_copy(src, dst, nbytes):
+    _check(L.vjp_copy(P(src), P(dst), nbytes, None), (nbytes,), ())
+
+
+@SETTINGS
+@given(size, size, dtype, flag)
+def test_tiling_and_norm_queries(n, rpt, act, aligned):
+    br, tiles = ctypes.c_int64(0), ctypes.c_int64(0)
+    s = L.vjp_weighted_sum_tiling(n, rpt, ctypes.byref(br), ctypes.byref(tiles))
+    assert s in (0, 1)
+    if s == 0:
+        assert br.value >= 1 and tiles.value >= 0
+    L.vjp_norm_max_cols(act, aligned)
