@@ -13,15 +13,15 @@ import ctypes
 
 import pytest
 
-torch = pytest.importorskip("torch")
-if torch.cuda.device_count() > 0:  # counts devices without initialising them
-    pytest.skip("fuzzing launches on fake addresses: only without a GPU", allow_module_level=True)
+import torch
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
-hyp = pytest.importorskip("hypothesis")
-from hypothesis import given, settings  # noqa: E402
-from hypothesis import strategies as st  # noqa: E402
+import row_wise_backward_amd as rwb
 
-import row_wise_backward_amd as rwb  # noqa: E402
+# device_count() counts devices without initialising them
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fuzzing launches on fake addresses: only without a GPU")
 
 L = rwb.lib
 P = ctypes.c_void_p

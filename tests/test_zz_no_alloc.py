@@ -62,3 +62,36 @@ def test_empty_and_errors(gpu_lib):
     assert L.vjp_scaled_silu_bwd_noalloc(P(y), P(y), P(w), P(y), P(dw), 0, 64, 7, None) == VJP_EDTYPE
     assert L.vjp_scaled_silu_bwd_noalloc(P(y), P(y), P(w), P(y), P(dw), 2, 64, 1, None) == VJP_EINVAL
     assert L.vjp_scaled_silu_bwd_noalloc(P(y), P(y), P(w), P(y), P(dw), 0, -1, 1, None) == VJP_EINVAL
+
+
+def test_graph_capture_replays(gpu_lib):
+    """The caller the entry point is for: a backward captured once in a HIP
+    graph (nothing to allocate inside the capture) and replayed with new
+    inputs copied into the captured buffers, eager work between the replays;
+    every replay equals the workspace entry point bit for bit."""
+    n, act = 100003, "f16"
+    print(f"\n[no-alloc scaled_silu_bwd graph] n={n} act={act}", flush=True)
+    x, dy = _inputs(n, act, 2001)
+    w = torch.tensor([0.75], dtype=torch.float32, device=DEV)
+    dx = torch.empty_like(x)
+    dw = torch.empty(1, dtype=torch.float32, device=DEV)
+    gpu_lib.vjp_scaled_silu_bwd_noalloc(dy, x, w, dx, dw)     # first call on the device: set-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu_lib.vjp_scaled_silu_bwd_noalloc(dy, x, w, dx, dw)
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((2002, 2003, 2002)):
+        xs, dys = _inputs(n, act, seed)
+        x.copy_(xs)
+        dy.copy_(dys)
+        dx.fill_(float("nan"))
+        dw.fill_(float(rep))
+        graph.replay()
+        dx_ref, dw_ref = gpu_lib.vjp_scaled_silu_bwd(dys, xs, w)
+        torch.cuda.synchronize()
+        same_dx = torch.equal(dx.view(torch.int16), dx_ref.view(torch.int16))
+        same_dw = torch.equal(dw.view(torch.int32), dw_ref.view(torch.int32))
+        print(f"    replay {rep}: dx bitwise equal {same_dx}; dw {dw.item()!r} vs {dw_ref.item()!r}",
+              flush=True)
+        assert same_dx and same_dw
