@@ -95,7 +95,7 @@ def _param_dev(a, dtype, offset):
 
 
 def run_case(rwb, kind, rows, cols, act, wdt, seed, ld=None, offset=0, saved=True,
-             accumulate=False, eps=None, shift=0.0, param_offset=0):
+             accumulate=False, eps=None, shift=0.0, param_offset=0, ws_offset=0):
     rms = kind == "rms"
     eps = (1e-6 if rms else 1e-5) if eps is None else eps
     print(f"\n[{kind}] rows={rows} cols={cols} act={act} w={wdt} ld={ld} off={offset} "
@@ -137,14 +137,15 @@ def run_case(rwb, kind, rows, cols, act, wdt, seed, ld=None, offset=0, saved=Tru
     rstd_in = torch.from_numpy(rstd_ref.astype(np.float32)).to(DEV) if saved else None
     dx, _ = empty_padded(rows, cols, act, ld, offset)
     need = (rwb.vjp_rmsnorm_bwd_workspace_size if rms else rwb.vjp_layernorm_bwd_workspace_size)(rows, cols)
-    wsg = Guarded(max(need // 4, 1), torch.float32)
+    wsg = Guarded(max(need // 4, 1) + ws_offset, torch.float32)
+    ws = wsg.t[ws_offset:]                 # ws_offset = 1: 4-byte but not 16-byte aligned
     if rms:
         rwb.vjp_rmsnorm_bwd(dyd, xd, wd, rstd_in, eps, dx=dx, dw=dwg.t, accumulate=accumulate,
-                            workspace=wsg.t)
+                            workspace=ws)
         dx_ref, dw_ref = nm.rmsnorm_bwd(dy64, x64, w64, eps, dw_old=old_w if accumulate else None)
     else:
         rwb.vjp_layernorm_bwd(dyd, xd, wd, mu_in, rstd_in, eps, dx=dx, dw=dwg.t, db=dbg.t,
-                              accumulate=accumulate, workspace=wsg.t)
+                              accumulate=accumulate, workspace=ws)
         dx_ref, dw_ref, db_ref = nm.layernorm_bwd(dy64, x64, w64, eps,
                                                   dw_old=old_w if accumulate else None,
                                                   db_old=old_b if accumulate else None)
@@ -191,6 +192,14 @@ def test_layouts(gpu_lib, kind, cols, layout):
 def test_unaligned_parameters(gpu_lib, kind, wdt):
     """w and b one element into their buffers: element-wise parameter loads."""
     run_case(gpu_lib, kind, 9, 1000, "bf16", wdt, seed=425, param_offset=1)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_workspace_not_16_byte_aligned(gpu_lib, kind):
+    """A workspace 4 bytes past a 16-byte boundary: the partial rows are
+    stored one element at a time instead of in 16-byte stores (same values)."""
+    run_case(gpu_lib, kind, 700, 4096, "bf16", "bf16", seed=431, ws_offset=1)
+    run_case(gpu_lib, kind, 700, 1024, "f32", "f32", seed=432, ws_offset=1)
 
 
 def test_batch1_and_batch7(gpu_lib):
