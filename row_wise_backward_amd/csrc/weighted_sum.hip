@@ -40,6 +40,37 @@ __device__ __forceinline__ float load_param(const void* __restrict__ w, int64_t 
 template <int VEC>
 __device__ __forceinline__ void load_params(const void* __restrict__ w, int64_t col, int64_t d,
                                             int dt, float (&out)[VEC]) {
+  // 16-byte loads when this lane's VEC values lie inside the row and start
+  // on a 16-byte boundary (VEC fp32 values, or VEC 16-bit ones with VEC a
+  // multiple of 8), else one load per element; the same values either way.
+  // (The grad_x writers, 32768 short workgroups at 1048576 x 256 bf16, load
+  // w first: 175.3 against 177.9 us for the backward with one load per
+  // element, interleaved medians of 77 flushed launches.)
+  const bool inside = col + VEC <= d;
+  if constexpr (VEC % 4 == 0) {
+    if (dt == kF32 && inside && (reinterpret_cast<uintptr_t>(static_cast<const float*>(w) + col) % 16) == 0) {
+#pragma unroll
+      for (int i = 0; i < VEC; i += 4) {
+        const Vec<float, 4> f = *reinterpret_cast<const Vec<float, 4>*>(static_cast<const float*>(w) + col + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[i + k] = f.v[k];
+      }
+      return;
+    }
+  }
+  if constexpr (VEC % 8 == 0) {
+    const uint16_t* h16 = static_cast<const uint16_t*>(w) + col;
+    if (dt != kF32 && inside && (reinterpret_cast<uintptr_t>(h16) % 16) == 0) {
+#pragma unroll
+      for (int i = 0; i < VEC; i += 8) {
+        const Vec<uint16_t, 8> h = *reinterpret_cast<const Vec<uint16_t, 8>*>(h16 + i);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          out[i + k] = dt == kF16 ? to_f32(__builtin_bit_cast(_Float16, h.v[k])) : to_f32(bf16{h.v[k]});
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < VEC; ++i) out[i] = (col + i < d) ? load_param(w, col + i, dt) : 0.0f;
 }

@@ -25,13 +25,19 @@ def _dx_is_one_rounding(act, wdt):
     return act == "f32" or wdt != "f32"
 
 
-def run_case(rwb, n, d, act, wdt, seed, ld=None, offset=0, rows_per_tile=0, accumulate=False):
+def run_case(rwb, n, d, act, wdt, seed, ld=None, offset=0, rows_per_tile=0, accumulate=False,
+             w_offset=0):
     x, w, dy = _inputs(n, d, act, wdt, seed)
     x64, w64, dy64 = synth.to_f64(x, act), synth.to_f64(w, wdt), synth.to_f64(dy, act)
     print(f"\n[weighted_sum] n={n} d={d} act={act} w={wdt} ld={ld} off={offset} "
           f"rpt={rows_per_tile} acc={accumulate}", flush=True)
     xd = padded(x, act, ld, offset)
-    wd = to_dev(w, wdt)
+    if w_offset:   # w starting w_offset elements into its buffer (not 16-byte aligned)
+        wbuf = torch.zeros(d + w_offset, dtype=synth.torch_dtype(wdt), device=DEV)
+        wbuf[w_offset:] = to_dev(w, wdt)
+        wd = wbuf[w_offset:]
+    else:
+        wd = to_dev(w, wdt)
     dyd = to_dev(dy, act)
     yg = Guarded(n, synth.torch_dtype(act))
     rwb.vjp_weighted_sum_fwd(xd, wd, y=yg.t)
@@ -200,6 +206,15 @@ def test_large_batch_full_size(gpu_lib):
         print("   ", r, flush=True)
     assert reps[0].n == n and reps[1].n == n * d
     assert all(r.ok for r in reps), [str(r) for r in reps if not r.ok]
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "f16", "f32"])
+def test_parameter_vector_alignment(gpu_lib, wdt):
+    """16-byte aligned rows with w aligned (16-byte parameter loads) and w one
+    element past a 16-byte boundary (one load per element): same results."""
+    run_case(gpu_lib, 3000, 512, "bf16", wdt, seed=91)
+    run_case(gpu_lib, 3000, 512, "bf16", wdt, seed=91, w_offset=1)
+    run_case(gpu_lib, 700, 300, "f32", wdt, seed=92, w_offset=1)
 
 
 def test_widest_rows_unaligned(gpu_lib):
