@@ -188,10 +188,13 @@ def test_layouts(gpu_lib, kind, cols, layout):
 
 
 @pytest.mark.parametrize("kind", ["ln", "rms"])
-@pytest.mark.parametrize("wdt", ["bf16", "f32"])
-def test_unaligned_parameters(gpu_lib, kind, wdt):
-    """w and b one element into their buffers: element-wise parameter loads."""
-    run_case(gpu_lib, kind, 9, 1000, "bf16", wdt, seed=425, param_offset=1)
+@pytest.mark.parametrize("act, wdt, off", [("bf16", "bf16", 1), ("bf16", "f32", 1),
+                                           ("bf16", "bf16", 4), ("bf16", "f32", 2),
+                                           ("f32", "bf16", 1), ("f32", "f16", 2)])
+def test_unaligned_parameters(gpu_lib, kind, act, wdt, off):
+    """w and b `off` elements into their buffers (2 to 8 bytes past a 16-byte
+    boundary): element-wise parameter loads in both passes, same values."""
+    run_case(gpu_lib, kind, 9, 1000, act, wdt, seed=425, param_offset=off)
 
 
 @pytest.mark.parametrize("kind", ["ln", "rms"])
