@@ -241,11 +241,18 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
       if constexpr (!RMS) pdb[k][i] = 0.0f;
     }
 
-  // The next row of the tile is loaded while the current one is processed
-  // (while a lane holds at most 8 values of a row; wider rows load in turn).
-  // Without it LayerNorm's backward holds 69 VGPRs instead of 79 (seven
-  // waves per SIMD instead of six) and measured the same, 153 us against
-  // 152-158 us at 32768 x 4096 bf16.
+  // The next row of the tile is requested before the current one is
+  // processed (while a lane holds at most 8 values of a row; wider rows load
+  // in turn).  The compiler's wait before the current row's first use also
+  // covers the next row's loads (on some paths none are issued, so it waits
+  // for all), so a wave has two rows in flight and then processes one.  A
+  // true overlap, the next row kept pending as raw words through the current
+  // row's work and viewed as elements after a copy at the top of the next
+  // iteration (no wait left before the work), measured slower on MI355X:
+  // 137.1 against 132.7 us for LayerNorm and 136.6 against 125.5 us for
+  // RMSNorm, medians of 80 interleaved runs at 32768 x 4096 bf16, the same
+  // bits.  Without the early request the kernel measured the same, 153 us
+  // against 152-158 us, at an earlier stage of its design.
   constexpr bool kPrefetch = K * VEC <= 8;
   constexpr int KN = kPrefetch ? K : 1;
   Vec<T, VEC> rx[K], rg[K], nx[KN], ng[KN];
