@@ -251,8 +251,11 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
   // iteration (no wait left before the work), measured slower on MI355X:
   // 137.1 against 132.7 us for LayerNorm and 136.6 against 125.5 us for
   // RMSNorm, medians of 80 interleaved runs at 32768 x 4096 bf16, the same
-  // bits.  Without the early request the kernel measured the same, 153 us
-  // against 152-158 us, at an earlier stage of its design.
+  // bits.  So did two rows per wave at once (rows r and r + tiles loaded
+  // together, their four row scalars in one exchange, the partials added in
+  // the same order): 135.3 against 133.6 us and 134.6 against 125.8 us.
+  // Without the early request the kernel measured the same, 153 us against
+  // 152-158 us, at an earlier stage of its design.
   constexpr bool kPrefetch = K * VEC <= 8;
   constexpr int KN = kPrefetch ? K : 1;
   Vec<T, VEC> rx[K], rg[K], nx[KN], ng[KN];
