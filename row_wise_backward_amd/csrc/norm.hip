@@ -222,11 +222,11 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
   const float inv_cols = 1.0f / float(cols);
   const int64_t tile = blockIdx.x;
 
-  // w is loaded once per workgroup, every vector issued before the first
-  // is widened (loaded element by element, each load waited for before the
-  // next, the start of a workgroup took 8 round trips to L2: 134.9 us against
-  // 133.1 us for LayerNorm and 126.4 against 125.6 us for RMSNorm, medians of
-  // 80 interleaved runs at 32768 x 4096 bf16, the same bits).
+  // w is loaded once per workgroup, all of a lane's vectors issued before
+  // any is widened to fp32.  (Element by element, each load waited for
+  // before the next, a workgroup's start took 8 round trips to L2: 134.9
+  // against 133.1 us for LayerNorm and 126.4 against 125.6 us for RMSNorm,
+  // medians of 80 interleaved runs at 32768 x 4096 bf16, the same bits.)
   float wv[K][VEC], pdw[K][VEC], pdb[RMS ? 1 : K][VEC];
   {
     const bool pvec = reinterpret_cast<uintptr_t>(w) % 16 == 0;
