@@ -163,7 +163,7 @@ def run_case(rwb, kind, rows, cols, act, wdt, seed, ld=None, offset=0, saved=Tru
 
 SHAPES = [(1, 1), (7, 7), (33, 100), (7, 512), (7, 513), (5, 4096), (3, 4097), (2, 16384),
           (1500, 64), (2049, 300)]
-DTYPES = [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32"), ("bf16", "f32")]
+DTYPES = [("bf16", "bf16"), ("f16", "f16"), ("f32", "f32"), ("bf16", "f32"), ("f32", "bf16")]
 
 
 @pytest.mark.parametrize("kind", ["ln", "rms"])
