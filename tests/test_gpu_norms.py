@@ -197,6 +197,42 @@ def test_unaligned_parameters(gpu_lib, kind, act, wdt, off):
     run_case(gpu_lib, kind, 9, 1000, act, wdt, seed=425, param_offset=off)
 
 
+def _all_outputs(rwb, kind, xd, dyd, wd, bd):
+    """y, the statistics, dx, dw (and db) of one forward and backward, as bits."""
+    rows, cols = xd.shape
+    y, dx = torch.empty_like(xd), torch.empty_like(xd)
+    dw, db = torch.empty(cols, device=DEV), torch.empty(cols, device=DEV)
+    if kind == "rms":
+        _, rstd = rwb.vjp_rmsnorm_fwd(xd, wd, y=y)
+        rwb.vjp_rmsnorm_bwd(dyd, xd, wd, rstd, dx=dx, dw=dw)
+        outs = [y, rstd, dx, dw]
+    else:
+        _, mean, rstd = rwb.vjp_layernorm_fwd(xd, wd, bd, y=y)
+        rwb.vjp_layernorm_bwd(dyd, xd, wd, mean, rstd, dx=dx, dw=dw, db=db)
+        outs = [y, mean, rstd, dx, dw, db]
+    torch.cuda.synchronize()
+    return [o.cpu().view(torch.int16 if o.element_size() == 2 else torch.int32) for o in outs]
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("act, wdt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"),
+                                      ("f16", "f16")])
+@pytest.mark.parametrize("cols", [4096, 1000])
+def test_parameter_loads_same_bits(gpu_lib, kind, act, wdt, cols):
+    """w and b at a 16-byte boundary (loaded as vectors) and one element past
+    it (loaded element by element) give the same bits in every output of the
+    forward and the backward: both paths widen the same values to fp32."""
+    rows = 300
+    print(f"\n[{kind} parameter loads] rows={rows} cols={cols} act={act} w={wdt}", flush=True)
+    x, w, b, dy = _inputs(rows, cols, act, wdt, 440 + cols)
+    xd, dyd = padded(x, act), padded(dy, act)
+    ref = _all_outputs(gpu_lib, kind, xd, dyd, _param_dev(w, wdt, 0), _param_dev(b, wdt, 0))
+    got = _all_outputs(gpu_lib, kind, xd, dyd, _param_dev(w, wdt, 1), _param_dev(b, wdt, 1))
+    same = [torch.equal(a, c) for a, c in zip(ref, got)]
+    print(f"    outputs bitwise equal: {same}", flush=True)
+    assert all(same)
+
+
 @pytest.mark.parametrize("kind", ["ln", "rms"])
 def test_workspace_not_16_byte_aligned(gpu_lib, kind):
     """A workspace 4 bytes past a 16-byte boundary: the partial rows are
