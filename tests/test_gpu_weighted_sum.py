@@ -217,6 +217,29 @@ def test_parameter_vector_alignment(gpu_lib, wdt):
     run_case(gpu_lib, 700, 300, "f32", wdt, seed=92, w_offset=1)
 
 
+@pytest.mark.parametrize("act, wdt", [("bf16", "bf16"), ("bf16", "f16"), ("bf16", "f32"),
+                                      ("f32", "bf16"), ("f32", "f32")])
+def test_parameter_loads_same_bits(gpu_lib, act, wdt):
+    """w at a 16-byte boundary (vector loads) and one element past it
+    (element loads): y, grad_x and grad_w bit for bit the same."""
+    n, d = 3000, 512
+    print(f"\n[weighted_sum parameter loads] n={n} d={d} act={act} w={wdt}", flush=True)
+    x, w, dy = _inputs(n, d, act, wdt, 93)
+    xd, dyd = padded(x, act), to_dev(dy, act)
+    outs = []
+    for off in (0, 1):
+        wbuf = torch.zeros(d + off, dtype=synth.torch_dtype(wdt), device=DEV)
+        wbuf[off:] = to_dev(w, wdt)
+        y = gpu_lib.vjp_weighted_sum_fwd(xd, wbuf[off:])
+        dx, dw = gpu_lib.vjp_weighted_sum_bwd(dyd, xd, wbuf[off:])
+        torch.cuda.synchronize()
+        outs.append([t.cpu().view(torch.int16 if t.element_size() == 2 else torch.int32)
+                     for t in (y, dx, dw)])
+    same = [torch.equal(a, b) for a, b in zip(*outs)]
+    print(f"    y, grad_x, grad_w bitwise equal: {same}", flush=True)
+    assert all(same)
+
+
 def test_widest_rows_unaligned(gpu_lib):
     """d = 4194240, the widest the backward takes: 65535 column blocks of 64
     in its one-element-per-load form (rows 2 bytes past a 16-byte boundary)."""
