@@ -400,7 +400,9 @@ constexpr int kLaneElems = 16;
 // the phases of the forward: with them LayerNorm's two-row form holds 64
 // VGPRs instead of 80 (eight waves per SIMD instead of six) and took 96 us;
 // RMSNorm with two rows (47 VGPRs) took 92 us against 90 us with one, and
-// LayerNorm with four rows needs 90 VGPRs.  The same fences in the backward
+// LayerNorm with four rows (88 VGPRs, w and b read by half as many
+// workgroups) 95.0 against 93.0 us with two, medians of 80 interleaved
+// runs, the same bits.  The same fences in the backward
 // raised its VGPRs and were left out.  LayerNorm statistics from one
 // exchange (each wave's sum and its sum of squares about its own mean,
 // merged across the waves with the pairwise variance update) instead of two
