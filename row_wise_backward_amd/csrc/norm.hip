@@ -241,22 +241,23 @@ __global__ __launch_bounds__(WAVES * kWave) void norm_bwd_tile(
       if constexpr (!RMS) pdb[k][i] = 0.0f;
     }
 
-  // The next row of the tile is requested before the current one is
-  // processed (while a lane holds at most 8 values of a row; wider rows load
-  // in turn).  The compiler's wait before the current row's first use also
-  // covers the next row's loads (on some paths none are issued, so it waits
-  // for all), so a wave has two rows in flight and then processes one.  A
-  // true overlap, the next row kept pending as raw words through the current
-  // row's work and viewed as elements after a copy at the top of the next
-  // iteration (no wait left before the work), measured slower on MI355X:
-  // 137.1 against 132.7 us for LayerNorm and 136.6 against 125.5 us for
-  // RMSNorm, medians of 80 interleaved runs at 32768 x 4096 bf16, the same
-  // bits.  So did two rows per wave at once (rows r and r + tiles loaded
-  // together, their four row scalars in one exchange, the partials added in
-  // the same order): 135.3 against 133.6 us and 134.6 against 125.8 us.
-  // Without the early request the kernel measured the same, 153 us against
-  // 152-158 us, at an earlier stage of its design.
-  constexpr bool kPrefetch = K * VEC <= 8;
+  // RMSNorm requests the next row of the tile before it processes the
+  // current one (while a lane holds at most 8 values of a row; wider rows
+  // load in turn); LayerNorm loads each row when it comes to it.  The
+  // compiler's wait before a row's first use also covers the next row's
+  // loads (on some paths none are issued, so it waits for all), so with the
+  // early request a wave has two rows in flight and then processes one.
+  // Measured on MI355X at 32768 x 4096 bf16, medians of 80 interleaved runs,
+  // the same bits: without the early request LayerNorm took 134.2 against
+  // 137.4 us and 133.8 against 137.0 us (two runs), RMSNorm 129.2 against
+  // 127.1 us.  A true overlap, the next row kept pending as raw words
+  // through the current row's work and viewed as elements after a copy at
+  // the top of the next iteration (no wait left before the work), was
+  // slower for both: 137.1 against 132.7 us and 136.6 against 125.5 us; so
+  // were two rows per wave at once (rows r and r + tiles loaded together,
+  // their four row scalars in one exchange, the partials added in the same
+  // order): 135.3 against 133.6 us and 134.6 against 125.8 us.
+  constexpr bool kPrefetch = RMS && K * VEC <= 8;
   constexpr int KN = kPrefetch ? K : 1;
   Vec<T, VEC> rx[K], rg[K], nx[KN], ng[KN];
   if (kPrefetch && tile < rows) {
