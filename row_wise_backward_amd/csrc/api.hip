@@ -638,7 +638,10 @@ namespace {
 // Measured on MI355X for 32768 x 4096 bf16 (LayerNorm / RMSNorm, one process):
 // 512 tiles of 8 waves x 1 vector per lane (two workgroups per CU)
 // 143-154 / 132-133 us; 256, 768, 1024 and 1536 tiles 151-198 / 140-198 us;
-// 4 waves x 2 vectors 155-176 / 141-153 us; 16 waves 189-207 us.
+// 4 waves x 2 vectors 155-176 / 141-153 us; 16 waves 189-207 us.  Again
+// with the LayerNorm backward loading each row when it reaches it
+// (medians of 39 interleaved runs): 384 / 512 / 640 / 768 / 1024 tiles
+// 146.6 / 135.6 / 147.7 / 140.3 / 161.1 us.
 constexpr int64_t kNormTiles = 512;
 
 int64_t norm_tiles(int64_t rows) { return rows < kNormTiles ? rows : kNormTiles; }
